@@ -1,0 +1,233 @@
+/*
+ * zopt.h -- one data-parallel rank's optimizer step under ZeRO-style
+ * sharding, on AMD Instinct MI355X (gfx950).
+ *
+ * libzopt holds two optimizers that a ZeRO-sharded trainer runs on each rank
+ * after its gradients are in place:
+ *
+ *  - zopt_adamw_shard_step: AdamW over the rank's flat, bucket-padded fp32
+ *    master shard, in one pass that reads the bf16 gradient, updates the fp32
+ *    master and both fp32 moments, and writes the bf16 compute weights;
+ *  - zopt_muon_step: Muon on whole 2-D matrices the rank owns (momentum with
+ *    Nesterov look-ahead, Newton-Schulz orthogonalisation on bf16 matrix
+ *    cores, a decayed and scaled update of the fp32 master);
+ *  - zopt_round_bf16: the fp32 -> bf16 round-to-nearest-even write-back on
+ *    its own.
+ *
+ * Conventions common to every call
+ * --------------------------------
+ *  - Every buffer is device memory owned by the caller.  The library
+ *    allocates nothing and keeps no state between calls; it is reentrant.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    the call returns without synchronising.  All launch parameters travel
+ *    as kernel arguments, so back-to-back calls need no host sync.
+ *  - Arguments are checked before anything is enqueued.  On any status other
+ *    than ZOPT_OK nothing has been enqueued and no buffer has been touched,
+ *    except ZOPT_ERR_DEVICE, which reports a failed launch.
+ *  - NaN and Inf in the data are not reported; they propagate as IEEE
+ *    arithmetic dictates.
+ *  - Buffers must not overlap.  No alignment is required; bases aligned to
+ *    16 bytes take the 128-bit vector path.
+ *  - bf16 is the upper half of an IEEE binary32, carried as uint16_t.
+ *  - Rounding to bf16 is round-to-nearest, ties to even, with no flush of
+ *    subnormals; a value beyond the largest finite bf16 becomes infinity and
+ *    a NaN becomes 0x7FC0 -- what a cast of an fp32 tensor to bf16 yields
+ *    [DEG zero.py, ZeroMaster docstring and gather_params: the updated shard
+ *    is rounded to bf16, bitwise the unsharded trainer's copy of the master
+ *    into the bf16 weights].
+ *  - Per-step scalars derived from the hyperparameters are formed in double
+ *    on the host and rounded once to binary32; the elementwise arithmetic is
+ *    binary32 with no fused multiply-adds, in the order stated below.
+ */
+#ifndef ZOPT_H
+#define ZOPT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ZOPT_OK = 0,
+    ZOPT_ERR_NULL = 1,      /* a required pointer is NULL                       */
+    ZOPT_ERR_SIZE = 2,      /* a size, count, rank or shard length is invalid   */
+    ZOPT_ERR_HYPER = 3,     /* a hyperparameter is out of its domain            */
+    ZOPT_ERR_WORKSPACE = 4, /* workspace too small or not 256-byte aligned      */
+    ZOPT_ERR_DEVICE = 5     /* the HIP runtime reported a launch failure        */
+} zopt_status;
+
+/* A static, human-readable name of a status code. */
+const char *zopt_status_string(zopt_status status);
+
+/*
+ * zopt_adamw_shard_step -- one AdamW step over rank `rank`'s shard.
+ *
+ * Layout [DEG zero.py: ZeroMaster module docstring, ZeroMaster.__init__,
+ * reduce_scatter, gather_params].  The trainable parameters lie end to end in
+ * a flat vector of N elements.  The bucket length is lowered to a multiple of
+ * `world` (never below `world`): B = max(world, bucket - bucket % world).
+ * Buckets [s, e) tile [0, N); bucket b has padded length
+ * L_b = ceil((e - s) / world) * world and is cut into `world` equal pieces
+ * of p_b = L_b / world elements.  Rank r owns piece r of every bucket; its
+ * shard is those pieces concatenated, so shard_len = sum_b p_b.  Shard
+ * element j of bucket b (shard offset o_b = sum of earlier pieces) is flat
+ * element f = s_b + r * p_b + (j - o_b); it is padding when f >= e_b.
+ *
+ * Per shard element, in this order [dmuon PR #16, commit "foreach AdamW":
+ * decoupled weight decay, then the moments, then the bias-corrected addcdiv,
+ * bias corrections being per-step scalars of the post-increment step;
+ * BluScript trainer source, optimizer-precision note: the decay is a
+ * (1 - lr*wd) multiply on fp32 masters and moments; DeepSpeed PR #9021,
+ * commits "bf16 gradients of fp32 params" (the bf16 gradient is promoted in
+ * registers) and "grad_scale" (multiplied as each element is loaded, after
+ * the promotion)]:
+ *
+ *   g  = fp32(grad[f]) * grad_scale          (g = 0 on padding)
+ *   p  = p * decay
+ *   m  = beta1 * m + omb1 * g
+ *   v  = beta2 * v + (omb2 * g) * g
+ *   p  = p - step_size * (m / (sqrt(v) / bc2_sqrt + eps))
+ *   weight[f] = bf16(p)                      (real elements only)
+ *
+ * with t = step and, in double rounded once to binary32,
+ *   step_size = lr / (1 - beta1^t),  bc2_sqrt = sqrt(1 - beta2^t),
+ *   decay = 1 - lr * weight_decay,   omb1 = 1 - beta1,  omb2 = 1 - beta2.
+ * The gradient here is this rank's contribution as it stands: the sum over
+ * ranks (a reduce-scatter) is not part of this call; an average over ranks
+ * is grad_scale = 1/world.
+ *
+ * Arguments
+ *   master, exp_avg, exp_avg_sq  fp32 [shard_len], device, read and written.
+ *                                Padding positions are stepped with g = 0.
+ *   grad      bf16 [N] flat gradient, device, read only at this rank's real
+ *             elements.
+ *   weight    bf16 [N] flat compute weights, device, written only at this
+ *             rank's real elements; NULL skips the write-back.
+ *   N, bucket, world, rank, shard_len   the layout above; shard_len must equal
+ *             the value it derives from (N, bucket, world).
+ *   lr, beta1, beta2, eps, weight_decay, step, grad_scale   as above; step
+ *             is 1 on the first update (already incremented by the caller).
+ *   stream    hipStream_t or NULL.
+ *
+ * Errors: ZOPT_ERR_NULL (master, exp_avg, exp_avg_sq or grad NULL);
+ * ZOPT_ERR_SIZE (N < 1, bucket < 1, world < 1, rank outside [0, world),
+ * shard_len wrong); ZOPT_ERR_HYPER (lr < 0 or not finite, beta outside
+ * [0, 1), eps <= 0 or not finite, weight_decay < 0 or not finite, step < 1,
+ * grad_scale not finite); ZOPT_ERR_DEVICE.
+ */
+zopt_status zopt_adamw_shard_step(float *master, float *exp_avg, float *exp_avg_sq,
+                                  const uint16_t *grad, uint16_t *weight,
+                                  int64_t N, int64_t bucket, int32_t world,
+                                  int32_t rank, int64_t shard_len,
+                                  float lr, float beta1, float beta2, float eps,
+                                  float weight_decay, int64_t step, float grad_scale,
+                                  void *stream);
+
+/*
+ * zopt_shard_len -- the shard length every rank holds for a flat vector of N
+ * elements in buckets of `bucket` over `world` ranks (the layout above:
+ * sum over buckets of ceil(len_b / world)).  Host-only; enqueues nothing.
+ * Returns -1 if N < 1, bucket < 1 or world < 1.
+ */
+int64_t zopt_shard_len(int64_t N, int64_t bucket, int32_t world);
+
+/*
+ * zopt_muon_step -- one Muon step on `batch` matrices of one stored shape
+ * [rows, cols] (row-major, PyTorch's [out, in]), each owned whole by this
+ * rank [BluScript trainer source, ShardedMuon comment block: Newton-Schulz is
+ * a whole-matrix operator, so Muon shards by whole parameter, the owner
+ * holding the matrix's fp32 master and momentum; dmuon PR #16, commit "NS
+ * CUDA-graph replay": Newton-Schulz runs on a small stable set of shapes,
+ * lr / wd / momentum stay in the pre- and post-steps around it].
+ *
+ * Per matrix, in this order:
+ *   1. Momentum [BluScript trainer source, Muon config block: momentum 0.95,
+ *      Nesterov; the buffer is an exponential moving average]:
+ *        g = fp32(grad);  M = mu * M + omm * g;
+ *        U = omm * g + mu * M  (nesterov)   or   U = M   (otherwise)
+ *      with mu = momentum_beta and omm = fp32(1 - mu) formed in double.
+ *   2. Pre-scale: X0 = bf16(U * s), s = 1 / (||U||_F + ns_eps), the norm a
+ *      fixed-order (run-to-run deterministic) reduction in fp32; X0 is taken
+ *      transposed when rows > cols, so X is m x n with m = min(rows, cols).
+ *   3. ns_steps Newton-Schulz iterations [BluScript trainer source, ShardedMuon
+ *      comment block: X <- aX + (bXX' + c(XX')^2)X]:
+ *        A = X X^T;  B = b A + c A A;  X = a X + B X
+ *      on bf16 matrix cores with fp32 accumulation; A, B and X are rounded to
+ *      bf16 after each product; only the upper triangle of the symmetric A
+ *      and B is computed and mirrored.
+ *   4. Post-step [BluScript trainer source, Muon config block (weight decay
+ *      pinned to AdamW's) and the note beside the MuonAdjustLr choice]:
+ *        P = P * decay - step_lr * fp32(O),  weight = bf16(P)
+ *      with O the result of step 3 in the stored orientation and, in double
+ *      rounded once to binary32, decay = 1 - lr * weight_decay and
+ *      step_lr = lr * scale, scale = 0.2 * sqrt(max(rows, cols)) when
+ *      adjust_lr = 1 (the update's entry RMS matches AdamW's 0.2) or
+ *      sqrt(max(1, rows / cols)) when adjust_lr = 0 (the original convention).
+ *
+ * Arguments
+ *   batch        1 .. 64 matrices.
+ *   rows, cols   the stored shape, >= 1, rows * cols < 2^31.
+ *   master, momentum   host arrays of `batch` device pointers, fp32
+ *                [rows * cols] each, read and written.
+ *   grad         host array of `batch` device pointers, bf16 [rows * cols].
+ *   weight       host array of `batch` device pointers, bf16 [rows * cols],
+ *                written; NULL skips the write-back (if non-NULL, every entry
+ *                must be non-NULL).
+ *   lr, momentum_beta, nesterov (0/1), weight_decay, ns_steps (0 .. 100),
+ *   ns_a, ns_b, ns_c, ns_eps, adjust_lr (0/1)   as above.
+ *   workspace    device scratch, 256-byte aligned, of at least the size the
+ *                NULL-workspace query returns.  With workspace == NULL the call
+ *                only writes that size to *workspace_bytes and returns ZOPT_OK.
+ *                Otherwise *workspace_bytes is the size provided.  The
+ *                workspace's contents need no initialisation; after the call,
+ *                zopt_muon_output_view locates the step-3 result in it.
+ *   stream       hipStream_t or NULL.
+ *
+ * Errors: ZOPT_ERR_NULL (a pointer array or one of its entries NULL,
+ * workspace_bytes NULL); ZOPT_ERR_SIZE (batch, rows, cols out of range);
+ * ZOPT_ERR_HYPER (lr or weight_decay < 0 or not finite, momentum_beta outside
+ * [0, 1), nesterov or adjust_lr not 0/1, ns_steps outside [0, 100], a
+ * coefficient not finite, ns_eps < 0 or not finite); ZOPT_ERR_WORKSPACE;
+ * ZOPT_ERR_DEVICE.
+ */
+zopt_status zopt_muon_step(int32_t batch, int64_t rows, int64_t cols,
+                           float *const *master, float *const *momentum,
+                           const uint16_t *const *grad, uint16_t *const *weight,
+                           float lr, float momentum_beta, int32_t nesterov,
+                           float weight_decay, int32_t ns_steps,
+                           float ns_a, float ns_b, float ns_c, float ns_eps,
+                           int32_t adjust_lr, void *workspace, size_t *workspace_bytes,
+                           void *stream);
+
+/*
+ * zopt_muon_output_view -- where the orthogonalised update O of matrix
+ * `index` lies in a workspace that zopt_muon_step(batch, rows, cols, ...,
+ * ns_steps, ...) has filled: bf16 O[r][c] (stored orientation, [rows, cols])
+ * is at (*out)[r * (*row_stride) + c].  Host-only; enqueues nothing.  The view
+ * is valid until the workspace is reused.  Errors: ZOPT_ERR_NULL,
+ * ZOPT_ERR_SIZE (batch, rows, cols or index out of range), ZOPT_ERR_HYPER
+ * (ns_steps out of range).
+ */
+zopt_status zopt_muon_output_view(int32_t batch, int64_t rows, int64_t cols,
+                                  int32_t ns_steps, const void *workspace,
+                                  int32_t index, const uint16_t **out,
+                                  int64_t *row_stride);
+
+/*
+ * zopt_round_bf16 -- dst[i] = bf16(src[i]) for i in [0, n), round to
+ * nearest even as above [DEG zero.py, gather_params: the updated fp32 shard
+ * cast to the bf16 compute dtype].
+ *   src  fp32 [n], device, read.   dst  bf16 [n], device, written.
+ *   n    >= 0; n = 0 enqueues nothing.
+ * Errors: ZOPT_ERR_NULL (src or dst NULL with n > 0); ZOPT_ERR_SIZE (n < 0);
+ * ZOPT_ERR_DEVICE.
+ */
+zopt_status zopt_round_bf16(const float *src, uint16_t *dst, int64_t n, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZOPT_H */

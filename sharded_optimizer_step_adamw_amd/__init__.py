@@ -1,0 +1,213 @@
+"""Python binding of libzopt: one rank's ZeRO-style optimizer step on MI355X.
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels of ``libzopt.so`` (built from ``csrc/`` by ``build.py``); this module
+checks tensor dtypes, devices and sizes (the C ABI takes plain pointers and
+cannot), passes pointers and the current HIP stream, and turns status codes
+into exceptions.  PyTorch only supplies device memory and streams.  If the
+library is not built, importing the entry points raises -- there is no
+fallback.
+
+Entry points (same names as the C ABI in include/zopt.h):
+  adamw_shard_step   fused AdamW over a flat bucketed fp32 shard
+  muon_step          Muon on a batch of same-shape matrices
+  muon_workspace_bytes / muon_output_view
+  round_bf16         fp32 -> bf16 round-to-nearest-even
+  shard_len          the shard length the layout derives (zopt_shard_len)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libzopt.so")
+
+ZOPT_OK, ZOPT_ERR_NULL, ZOPT_ERR_SIZE, ZOPT_ERR_HYPER, ZOPT_ERR_WORKSPACE, ZOPT_ERR_DEVICE = range(6)
+MAX_BATCH = 64
+
+
+class ZoptError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib_or_raise().zopt_status_string(status).decode()
+        super().__init__(f"{where}: {msg}")
+
+
+_lib = None
+
+
+def _lib_or_raise() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is not built; run `python -m sharded_optimizer_step_adamw_amd.build` "
+                "(or __graft_entry__.build()). There is no CPU fallback.")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+        L.zopt_status_string.argtypes = [ctypes.c_int]
+        L.zopt_status_string.restype = ctypes.c_char_p
+        L.zopt_adamw_shard_step.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, i64,
+                                            f32, f32, f32, f32, f32, i64, f32, vp]
+        L.zopt_adamw_shard_step.restype = ctypes.c_int
+        L.zopt_shard_len.argtypes = [i64, i64, i32]
+        L.zopt_shard_len.restype = i64
+        L.zopt_round_bf16.argtypes = [vp, vp, i64, vp]
+        L.zopt_round_bf16.restype = ctypes.c_int
+        pp = ctypes.POINTER(vp)
+        L.zopt_muon_step.argtypes = [i32, i64, i64, pp, pp, pp, pp, f32, f32, i32, f32, i32,
+                                     f32, f32, f32, f32, i32, vp,
+                                     ctypes.POINTER(ctypes.c_size_t), vp]
+        L.zopt_muon_step.restype = ctypes.c_int
+        L.zopt_muon_output_view.argtypes = [i32, i64, i64, i32, vp, i32, pp,
+                                            ctypes.POINTER(i64)]
+        L.zopt_muon_output_view.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libzopt (raises ImportError if it is not built)."""
+    return _lib_or_raise()
+
+
+def _stream(device: torch.device, stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _need(t: torch.Tensor, dtype, numel: int, name: str, device=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, need {dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name}: has {t.numel()} elements, needs {numel}")
+
+
+def _check(status: int, where: str) -> None:
+    if status != ZOPT_OK:
+        raise ZoptError(status, where)
+
+
+def shard_len(n: int, bucket: int, world: int) -> int:
+    """Shard length every rank holds (zopt_shard_len)."""
+    v = lib().zopt_shard_len(n, bucket, world)
+    if v < 0:
+        raise ValueError("shard_len: need n, bucket, world >= 1")
+    return int(v)
+
+
+def adamw_shard_step(master, exp_avg, exp_avg_sq, grad, weight, n, bucket, world, rank,
+                     lr, beta1, beta2, eps, weight_decay, step, grad_scale=1.0,
+                     shard_len_=None, stream=None) -> None:
+    """One fused AdamW step over rank `rank`'s shard (zopt_adamw_shard_step).
+    master/exp_avg/exp_avg_sq: fp32 [shard_len]; grad: bf16 [n]; weight:
+    bf16 [n] or None."""
+    sl = shard_len(n, bucket, world) if shard_len_ is None else shard_len_
+    dev = master.device
+    _need(master, torch.float32, sl, "master")
+    _need(exp_avg, torch.float32, sl, "exp_avg", dev)
+    _need(exp_avg_sq, torch.float32, sl, "exp_avg_sq", dev)
+    _need(grad, torch.bfloat16, n, "grad", dev)
+    if weight is not None:
+        _need(weight, torch.bfloat16, n, "weight", dev)
+    st = lib().zopt_adamw_shard_step(
+        master.data_ptr(), exp_avg.data_ptr(), exp_avg_sq.data_ptr(), grad.data_ptr(),
+        None if weight is None else weight.data_ptr(), n, bucket, world, rank, sl,
+        lr, beta1, beta2, eps, weight_decay, step, grad_scale, _stream(dev, stream))
+    _check(st, "zopt_adamw_shard_step")
+
+
+def round_bf16(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    """dst = bf16(src), round to nearest even (zopt_round_bf16)."""
+    n = src.numel()
+    _need(src, torch.float32, n, "src")
+    _need(dst, torch.bfloat16, n, "dst", src.device)
+    st = lib().zopt_round_bf16(src.data_ptr(), dst.data_ptr(), n, _stream(src.device, stream))
+    _check(st, "zopt_round_bf16")
+
+
+def _ptr_array(tensors) -> ctypes.Array:
+    arr = (ctypes.c_void_p * len(tensors))()
+    for i, t in enumerate(tensors):
+        arr[i] = t.data_ptr()
+    return arr
+
+
+def muon_workspace_bytes(batch: int, rows: int, cols: int) -> int:
+    size = ctypes.c_size_t(0)
+    st = lib().zopt_muon_step(batch, rows, cols, None, None, None, None, 0.0, 0.0, 0, 0.0, 0,
+                              0.0, 0.0, 0.0, 0.0, 0, None, ctypes.byref(size), None)
+    _check(st, "zopt_muon_step(workspace query)")
+    return int(size.value)
+
+
+def muon_step(master: Sequence[torch.Tensor], momentum: Sequence[torch.Tensor],
+              grad: Sequence[torch.Tensor], weight: Optional[Sequence[torch.Tensor]],
+              lr: float, momentum_beta: float = 0.95, nesterov: bool = True,
+              weight_decay: float = 0.1, ns_steps: int = 5,
+              ns_coeffs=(3.4445, -4.7750, 2.0315), ns_eps: float = 1e-7,
+              adjust_lr: int = 1, workspace: Optional[torch.Tensor] = None,
+              stream=None) -> torch.Tensor:
+    """One Muon step on a batch of same-shape [rows, cols] matrices
+    (zopt_muon_step).  master, momentum: fp32; grad, weight: bf16.  Returns
+    the workspace (allocated with torch if not given), which holds the
+    orthogonalised updates (see muon_output_view)."""
+    batch = len(master)
+    if not (1 <= batch <= MAX_BATCH) or len(momentum) != batch or len(grad) != batch or (
+            weight is not None and len(weight) != batch):
+        raise ValueError("muon_step: need 1..64 matrices and equal-length lists")
+    rows, cols = master[0].shape
+    dev = master[0].device
+    for i in range(batch):
+        for t, dt, nm in ((master[i], torch.float32, "master"),
+                          (momentum[i], torch.float32, "momentum"),
+                          (grad[i], torch.bfloat16, "grad")) + (
+                ((weight[i], torch.bfloat16, "weight"),) if weight is not None else ()):
+            _need(t, dt, rows * cols, f"{nm}[{i}]", dev)
+            if tuple(t.shape) != (rows, cols):
+                raise ValueError(f"{nm}[{i}]: shape {tuple(t.shape)}, need {(rows, cols)}")
+    need = muon_workspace_bytes(batch, rows, cols)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _need(workspace, torch.uint8, need, "workspace", dev)
+    size = ctypes.c_size_t(workspace.numel())
+    a, b, c = (float(x) for x in ns_coeffs)
+    st = lib().zopt_muon_step(
+        batch, rows, cols, _ptr_array(master), _ptr_array(momentum), _ptr_array(grad),
+        None if weight is None else _ptr_array(weight), lr, momentum_beta, int(nesterov),
+        weight_decay, ns_steps, a, b, c, ns_eps, adjust_lr, workspace.data_ptr(),
+        ctypes.byref(size), _stream(dev, stream))
+    _check(st, "zopt_muon_step")
+    return workspace
+
+
+def muon_output_view(workspace: torch.Tensor, batch: int, rows: int, cols: int,
+                     ns_steps: int, index: int) -> torch.Tensor:
+    """The bf16 [rows, cols] orthogonalised update of matrix `index` inside a
+    workspace filled by muon_step (a strided view, not a copy)."""
+    out = ctypes.c_void_p(0)
+    ld = ctypes.c_int64(0)
+    st = lib().zopt_muon_output_view(batch, rows, cols, ns_steps, workspace.data_ptr(), index,
+                                     ctypes.byref(out), ctypes.byref(ld))
+    _check(st, "zopt_muon_output_view")
+    off = out.value - workspace.data_ptr()
+    assert off % 2 == 0 and off >= 0
+    flat = workspace.view(torch.bfloat16)
+    return flat.as_strided((rows, cols), (ld.value, 1), off // 2)
+
+
+__all__ = ["adamw_shard_step", "muon_step", "muon_workspace_bytes", "muon_output_view",
+           "round_bf16", "shard_len", "lib", "ZoptError", "LIB_PATH", "MAX_BATCH"]

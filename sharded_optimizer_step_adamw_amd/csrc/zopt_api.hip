@@ -1,0 +1,255 @@
+// zopt_api.hip -- the C-ABI entry points of libzopt (declared in zopt.h).
+//
+// Each entry point checks its arguments, derives the launch parameters on the
+// host (layout of the flat shard, per-step scalars in double rounded once to
+// binary32, workspace carve-up), and enqueues its kernels on the caller's
+// stream without synchronising.  Nothing is enqueued unless every check
+// passes.
+#include <cmath>
+#include <cstring>
+
+#include "zopt.h"
+#include "zopt_internal.h"
+
+#define ZOPT_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace zopt {
+
+int32_t muon_norm_blocks(int64_t count);  // muon_prepost.hip
+
+namespace {
+
+inline bool finite(float x) { return std::isfinite(x); }
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline int64_t round_up64(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// Flat bucketed shard layout [DEG zero.py, ZeroMaster.__init__]: the bucket
+// is lowered to a multiple of world (never below world); every bucket but
+// possibly the last has that full length and no padding; the last is padded
+// to a multiple of world.  Fills the shard-region fields of p and returns
+// the shard length.
+int64_t adamw_layout(int64_t n, int64_t bucket, int32_t world, int32_t rank,
+                     AdamWParams &p) {
+    const int64_t w = world;
+    int64_t B = bucket - bucket % w;
+    if (B < w) B = w;
+    const int64_t nb = (n + B - 1) / B;
+    const int64_t piece = B / w;
+    const int64_t last_len = n - (nb - 1) * B;
+    p.piece = piece;
+    p.gap = B - piece;
+    p.rank_off = (int64_t)rank * piece;
+    p.n = n;
+    if (last_len == B) {
+        p.full_len = nb * piece;
+        p.last_flat0 = 0;
+        return p.full_len;
+    }
+    const int64_t last_piece = (last_len + w - 1) / w;  // ceil(len / w) * w / w
+    p.full_len = (nb - 1) * piece;
+    p.last_flat0 = (nb - 1) * B + (int64_t)rank * last_piece;
+    return p.full_len + last_piece;
+}
+
+}  // namespace
+
+MuonGeom muon_geometry(int32_t batch, int64_t rows, int64_t cols) {
+    MuonGeom g{};
+    g.batch = batch;
+    g.rows = (int32_t)rows;
+    g.cols = (int32_t)cols;
+    g.transposed = rows > cols ? 1 : 0;
+    g.m = (int32_t)(rows < cols ? rows : cols);
+    g.n = (int32_t)(rows < cols ? cols : rows);
+    g.tile = g.m >= 256 ? 128 : 64;
+    g.mp = (int32_t)round_up64(g.m, g.tile);
+    g.np = (int32_t)round_up64(g.n, g.tile);
+    g.norm_blocks = muon_norm_blocks(rows * cols);
+    return g;
+}
+
+MuonWorkspace muon_workspace_layout(const MuonGeom &g) {
+    MuonWorkspace L{};
+    L.x_stride = round_up((size_t)g.mp * g.np * 2, 256);
+    L.a_stride = round_up((size_t)g.mp * g.mp * 2, 256);
+    L.d_stride = round_up((size_t)g.mp * 4, 256);
+    size_t off = 0;
+    L.x = off;   off += L.x_stride * g.batch;
+    L.xt0 = off; off += L.x_stride * g.batch;
+    L.xt1 = off; off += L.x_stride * g.batch;
+    L.a = off;   off += L.a_stride * g.batch;
+    L.b = off;   off += L.a_stride * g.batch;
+    L.da = off;  off += L.d_stride * g.batch;
+    L.db = off;  off += L.d_stride * g.batch;
+    L.partials = off;
+    off += round_up(((size_t)g.batch * g.norm_blocks + g.batch) * sizeof(float), 256);
+    L.total = off;
+    return L;
+}
+
+}  // namespace zopt
+
+using namespace zopt;
+
+ZOPT_EXPORT const char *zopt_status_string(zopt_status s) {
+    switch (s) {
+        case ZOPT_OK: return "ZOPT_OK";
+        case ZOPT_ERR_NULL: return "ZOPT_ERR_NULL: a required pointer is NULL";
+        case ZOPT_ERR_SIZE: return "ZOPT_ERR_SIZE: a size, count, rank or shard length is invalid";
+        case ZOPT_ERR_HYPER: return "ZOPT_ERR_HYPER: a hyperparameter is out of its domain";
+        case ZOPT_ERR_WORKSPACE: return "ZOPT_ERR_WORKSPACE: workspace too small or misaligned";
+        case ZOPT_ERR_DEVICE: return "ZOPT_ERR_DEVICE: the HIP runtime reported a launch failure";
+    }
+    return "unknown zopt_status";
+}
+
+ZOPT_EXPORT zopt_status zopt_adamw_shard_step(float *master, float *exp_avg, float *exp_avg_sq,
+                                              const uint16_t *grad, uint16_t *weight, int64_t N,
+                                              int64_t bucket, int32_t world, int32_t rank,
+                                              int64_t shard_len, float lr, float beta1,
+                                              float beta2, float eps, float weight_decay,
+                                              int64_t step, float grad_scale, void *stream) {
+    if (!master || !exp_avg || !exp_avg_sq || !grad) return ZOPT_ERR_NULL;
+    if (N < 1 || bucket < 1 || world < 1 || rank < 0 || rank >= world) return ZOPT_ERR_SIZE;
+    // the grid holds at most 2^32 - 1 work-items of 8 elements each
+    if (N > ((int64_t)1 << 40)) return ZOPT_ERR_SIZE;
+    if (!finite(lr) || lr < 0.0f || !(beta1 >= 0.0f && beta1 < 1.0f) ||
+        !(beta2 >= 0.0f && beta2 < 1.0f) || !finite(eps) || eps <= 0.0f ||
+        !finite(weight_decay) || weight_decay < 0.0f || step < 1 || !finite(grad_scale))
+        return ZOPT_ERR_HYPER;
+    AdamWParams p{};
+    const int64_t want = adamw_layout(N, bucket, world, rank, p);
+    if (shard_len != want) return ZOPT_ERR_SIZE;
+    p.shard_len = shard_len;
+
+    const double t = (double)step;
+    const double bc1 = 1.0 - std::pow((double)beta1, t);
+    const double bc2 = 1.0 - std::pow((double)beta2, t);
+    p.beta1 = beta1;
+    p.beta2 = beta2;
+    p.eps = eps;
+    p.step_size = (float)((double)lr / bc1);
+    p.bc2_sqrt = (float)std::sqrt(bc2);
+    p.decay = (float)(1.0 - (double)lr * (double)weight_decay);
+    p.omb1 = (float)(1.0 - (double)beta1);
+    p.omb2 = (float)(1.0 - (double)beta2);
+    p.grad_scale = grad_scale;
+    hipError_t e = launch_adamw_shard(master, exp_avg, exp_avg_sq, grad, weight, p,
+                                      (hipStream_t)stream);
+    return e == hipSuccess ? ZOPT_OK : ZOPT_ERR_DEVICE;
+}
+
+ZOPT_EXPORT int64_t zopt_shard_len(int64_t N, int64_t bucket, int32_t world) {
+    if (N < 1 || bucket < 1 || world < 1) return -1;
+    AdamWParams p{};
+    return adamw_layout(N, bucket, world, 0, p);
+}
+
+ZOPT_EXPORT zopt_status zopt_round_bf16(const float *src, uint16_t *dst, int64_t n,
+                                        void *stream) {
+    if (n < 0 || n > ((int64_t)1 << 40)) return ZOPT_ERR_SIZE;
+    if (n == 0) return ZOPT_OK;
+    if (!src || !dst) return ZOPT_ERR_NULL;
+    hipError_t e = launch_round_bf16(src, dst, n, (hipStream_t)stream);
+    return e == hipSuccess ? ZOPT_OK : ZOPT_ERR_DEVICE;
+}
+
+namespace {
+
+zopt_status muon_check_shape(int32_t batch, int64_t rows, int64_t cols) {
+    if (batch < 1 || batch > kMaxBatch || rows < 1 || cols < 1) return ZOPT_ERR_SIZE;
+    if (rows * cols >= ((int64_t)1 << 31)) return ZOPT_ERR_SIZE;
+    return ZOPT_OK;
+}
+
+// Where the Newton-Schulz result of a call lies: the iteration reads X^T from
+// xt0 at even steps and xt1 at odd ones, so after k steps X holds the result
+// and xt[k % 2] its transpose.  The stored orientation is X when rows <= cols.
+void muon_output(const MuonGeom &g, const MuonWorkspace &L, int32_t ns_steps, size_t &base,
+                 int64_t &ld) {
+    if (!g.transposed) {
+        base = L.x;
+        ld = g.np;
+    } else {
+        base = (ns_steps % 2) ? L.xt1 : L.xt0;
+        ld = g.mp;
+    }
+}
+
+}  // namespace
+
+ZOPT_EXPORT zopt_status zopt_muon_step(int32_t batch, int64_t rows, int64_t cols,
+                                       float *const *master, float *const *momentum,
+                                       const uint16_t *const *grad, uint16_t *const *weight,
+                                       float lr, float momentum_beta, int32_t nesterov,
+                                       float weight_decay, int32_t ns_steps, float ns_a,
+                                       float ns_b, float ns_c, float ns_eps, int32_t adjust_lr,
+                                       void *workspace, size_t *workspace_bytes, void *stream) {
+    zopt_status st = muon_check_shape(batch, rows, cols);
+    if (!workspace_bytes) return ZOPT_ERR_NULL;
+    if (st != ZOPT_OK) return st;
+    const MuonGeom g = muon_geometry(batch, rows, cols);
+    const MuonWorkspace L = muon_workspace_layout(g);
+    if (!workspace) {
+        *workspace_bytes = L.total;
+        return ZOPT_OK;
+    }
+    if (!master || !momentum || !grad) return ZOPT_ERR_NULL;
+    for (int b = 0; b < batch; ++b) {
+        if (!master[b] || !momentum[b] || !grad[b]) return ZOPT_ERR_NULL;
+        if (weight && !weight[b]) return ZOPT_ERR_NULL;
+    }
+    if (!finite(lr) || lr < 0.0f || !(momentum_beta >= 0.0f && momentum_beta < 1.0f) ||
+        (nesterov != 0 && nesterov != 1) || !finite(weight_decay) || weight_decay < 0.0f ||
+        ns_steps < 0 || ns_steps > 100 || !finite(ns_a) || !finite(ns_b) || !finite(ns_c) ||
+        !finite(ns_eps) || ns_eps < 0.0f || (adjust_lr != 0 && adjust_lr != 1))
+        return ZOPT_ERR_HYPER;
+    if (*workspace_bytes < L.total || ((uintptr_t)workspace & 255u) != 0)
+        return ZOPT_ERR_WORKSPACE;
+
+    MuonPtrs ptrs{};
+    for (int b = 0; b < batch; ++b) {
+        ptrs.master[b] = master[b];
+        ptrs.momentum[b] = momentum[b];
+        ptrs.grad[b] = grad[b];
+        ptrs.weight[b] = weight ? weight[b] : nullptr;
+    }
+    char *ws = static_cast<char *>(workspace);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_muon_pre(g, ptrs, momentum_beta, nesterov, ns_eps, ws, L, s);
+    for (int k = 0; k < ns_steps && e == hipSuccess; ++k)
+        e = launch_ns_iteration(g, ws, L, k & 1, ns_a, ns_b, ns_c, s);
+    if (e != hipSuccess) return ZOPT_ERR_DEVICE;
+
+    const double big = (double)(rows > cols ? rows : cols);
+    const double scale = adjust_lr ? 0.2 * std::sqrt(big)
+                                   : std::sqrt(std::fmax(1.0, (double)rows / (double)cols));
+    const float decay = (float)(1.0 - (double)lr * (double)weight_decay);
+    const float step_lr = (float)((double)lr * scale);
+    size_t obase;
+    int64_t old;
+    muon_output(g, L, ns_steps, obase, old);
+    e = launch_muon_post(g, ptrs, reinterpret_cast<const uint16_t *>(ws + obase), old,
+                         L.x_stride, decay, step_lr, s);
+    return e == hipSuccess ? ZOPT_OK : ZOPT_ERR_DEVICE;
+}
+
+ZOPT_EXPORT zopt_status zopt_muon_output_view(int32_t batch, int64_t rows, int64_t cols,
+                                              int32_t ns_steps, const void *workspace,
+                                              int32_t index, const uint16_t **out,
+                                              int64_t *row_stride) {
+    if (!workspace || !out || !row_stride) return ZOPT_ERR_NULL;
+    zopt_status st = muon_check_shape(batch, rows, cols);
+    if (st != ZOPT_OK) return st;
+    if (index < 0 || index >= batch) return ZOPT_ERR_SIZE;
+    if (ns_steps < 0 || ns_steps > 100) return ZOPT_ERR_HYPER;
+    const MuonGeom g = muon_geometry(batch, rows, cols);
+    const MuonWorkspace L = muon_workspace_layout(g);
+    size_t base;
+    int64_t ld;
+    muon_output(g, L, ns_steps, base, ld);
+    *out = reinterpret_cast<const uint16_t *>(static_cast<const char *>(workspace) + base +
+                                              (size_t)index * L.x_stride);
+    *row_stride = ld;
+    return ZOPT_OK;
+}

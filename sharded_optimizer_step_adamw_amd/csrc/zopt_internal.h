@@ -1,0 +1,110 @@
+// zopt_internal.h -- shared declarations inside libzopt (not installed).
+//
+// Device helpers used by more than one kernel file, the launch-parameter
+// structs the host entry points fill, and the launchers each kernel file
+// exports to the entry points in zopt_api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace zopt {
+
+// ------------------------------------------------------------------ bf16
+
+// fp32 -> bf16, round to nearest with ties to even, by integer arithmetic on
+// the bit pattern: adding 0x7FFF plus the lowest kept bit and truncating
+// rounds to nearest-even, carries overflow into infinity, and keeps
+// subnormals.  A NaN (exponent all ones, mantissa non-zero) becomes the
+// positive quiet NaN 0x7FC0.
+__device__ __forceinline__ uint32_t rne_bf16_bits(float x) {
+    uint32_t u = __float_as_uint(x);
+    uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? 0x7FC0u : r;
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t h) {
+    return __uint_as_float(h << 16);
+}
+
+// Two fp32 -> two bf16 packed low-first into one 32-bit word.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return rne_bf16_bits(lo) | (rne_bf16_bits(hi) << 16);
+}
+
+// ------------------------------------------------------------------ AdamW
+
+// Everything one AdamW launch needs; filled by zopt_adamw_shard_step.
+// The shard is read as two regions: shard elements [0, full_len) lie in
+// buckets of the full adjusted length B (piece = B / world each, never any
+// padding); [full_len, shard_len) is the last, shorter bucket, whose piece
+// starts at flat index last_flat0 and whose positions at or past n are
+// padding.
+struct AdamWParams {
+    int64_t shard_len;
+    int64_t full_len;
+    int64_t piece;       // piece of a full bucket
+    int64_t gap;         // B - piece: flat advance per full bucket past its piece
+    int64_t rank_off;    // rank * piece
+    int64_t last_flat0;  // flat index of shard element full_len
+    int64_t n;           // flat length N
+    float beta1, beta2, eps;
+    float step_size, bc2_sqrt, decay, omb1, omb2;
+    float grad_scale;
+    int32_t vec;         // every base pointer is 16-byte aligned
+};
+
+hipError_t launch_adamw_shard(float *master, float *exp_avg, float *exp_avg_sq,
+                              const uint16_t *grad, uint16_t *weight,
+                              const AdamWParams &p, hipStream_t stream);
+
+hipError_t launch_round_bf16(const float *src, uint16_t *dst, int64_t n,
+                             hipStream_t stream);
+
+// ------------------------------------------------------------------ Muon
+
+constexpr int kMaxBatch = 64;
+
+// Per-call Muon geometry.  m x n is the Newton-Schulz orientation
+// (m = min(rows, cols)); mp x np are m and n padded up to the tile size.
+struct MuonGeom {
+    int32_t batch;
+    int32_t rows, cols;
+    int32_t transposed;  // rows > cols: X = U^T
+    int32_t m, n;
+    int32_t mp, np;
+    int32_t tile;        // square output tile of the Newton-Schulz products
+    int32_t norm_blocks; // workgroups (and norm partials) per matrix, pre-pass 1
+};
+
+struct MuonPtrs {
+    float *master[kMaxBatch];
+    float *momentum[kMaxBatch];
+    const uint16_t *grad[kMaxBatch];
+    uint16_t *weight[kMaxBatch];
+};
+
+// Workspace carve-up (byte offsets; every region 256-byte aligned).
+struct MuonWorkspace {
+    size_t x, xt0, xt1, a, b, da, db, partials, total;
+    size_t x_stride, a_stride, d_stride;  // bytes per matrix of each region kind
+};
+
+MuonGeom muon_geometry(int32_t batch, int64_t rows, int64_t cols);
+MuonWorkspace muon_workspace_layout(const MuonGeom &g);
+
+hipError_t launch_muon_pre(const MuonGeom &g, const MuonPtrs &ptrs, float mu,
+                           int32_t nesterov, float ns_eps, char *ws,
+                           const MuonWorkspace &L, hipStream_t stream);
+
+hipError_t launch_muon_post(const MuonGeom &g, const MuonPtrs &ptrs,
+                            const uint16_t *o_base, int64_t o_ld, size_t o_stride,
+                            float decay, float step_lr, hipStream_t stream);
+
+// One Newton-Schulz iteration: A = X X^T, B = b A + c A A, X = a X + B X,
+// reading XT (X transposed) and writing XT_next.
+hipError_t launch_ns_iteration(const MuonGeom &g, char *ws, const MuonWorkspace &L,
+                               int cur_xt, float a, float b, float c,
+                               hipStream_t stream);
+
+}  // namespace zopt

@@ -1,10 +1,13 @@
-"""Shared pytest setup: the `gpu` marker and the repository root on sys.path."""
+"""Shared pytest setup: the `gpu` marker; the repository root and this
+directory on sys.path."""
 import os
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-if ROOT not in sys.path:
-    sys.path.insert(0, ROOT)
+TESTS = os.path.dirname(os.path.abspath(__file__))
+for _p in (TESTS, ROOT):
+    if _p not in sys.path:
+        sys.path.insert(0, _p)
 
 
 def pytest_configure(config):

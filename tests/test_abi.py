@@ -1,0 +1,143 @@
+"""The C ABI of libzopt, without a GPU: the library loads, exports every
+function include/zopt.h declares, and rejects bad arguments synchronously,
+before any HIP call (so these tests run on a machine with no GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+import sharded_optimizer_step_adamw_amd as z
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zopt.h")
+FAKE = ctypes.c_void_p(0x100000)  # never dereferenced: every call below fails validation
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    return sorted(set(re.findall(r"\b(zopt_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert {"zopt_adamw_shard_step", "zopt_muon_step", "zopt_round_bf16"} <= set(names)
+    lib = z.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    lib = z.lib()
+    for s in range(6):
+        assert lib.zopt_status_string(s).decode().startswith("ZOPT_")
+
+
+@pytest.mark.parametrize("n,bucket,world", [(1, 1, 1), (10, 3, 4), (4103, 1000, 4),
+                                            (2_000_000_000, 1 << 25, 8), (5, 100, 8),
+                                            (1 << 14, 1 << 12, 8), (999, 7, 3)])
+def test_shard_len_matches_oracle(n, bucket, world):
+    assert z.shard_len(n, bucket, world) == oracle.shard_len(n, bucket, world)
+
+
+def test_shard_len_rejects_bad_sizes():
+    for args in ((0, 4, 1), (10, 0, 1), (10, 4, 0)):
+        assert z.lib().zopt_shard_len(*args) == -1
+
+
+def adamw(**kw):
+    a = dict(master=FAKE, exp_avg=FAKE, exp_avg_sq=FAKE, grad=FAKE, weight=None, N=16,
+             bucket=8, world=2, rank=0, shard_len=8, lr=1e-3, beta1=0.9, beta2=0.95,
+             eps=1e-8, wd=0.1, step=1, grad_scale=1.0, stream=None)
+    a.update(kw)
+    return z.lib().zopt_adamw_shard_step(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(master=None), z.ZOPT_ERR_NULL), (dict(exp_avg=None), z.ZOPT_ERR_NULL),
+    (dict(exp_avg_sq=None), z.ZOPT_ERR_NULL), (dict(grad=None), z.ZOPT_ERR_NULL),
+    (dict(N=0), z.ZOPT_ERR_SIZE), (dict(bucket=0), z.ZOPT_ERR_SIZE),
+    (dict(world=0), z.ZOPT_ERR_SIZE), (dict(rank=2), z.ZOPT_ERR_SIZE),
+    (dict(rank=-1), z.ZOPT_ERR_SIZE), (dict(shard_len=9), z.ZOPT_ERR_SIZE),
+    (dict(shard_len=7), z.ZOPT_ERR_SIZE),
+    (dict(lr=-1e-3), z.ZOPT_ERR_HYPER), (dict(lr=float("nan")), z.ZOPT_ERR_HYPER),
+    (dict(beta1=1.0), z.ZOPT_ERR_HYPER), (dict(beta2=-0.1), z.ZOPT_ERR_HYPER),
+    (dict(eps=0.0), z.ZOPT_ERR_HYPER), (dict(eps=float("inf")), z.ZOPT_ERR_HYPER),
+    (dict(wd=-0.1), z.ZOPT_ERR_HYPER), (dict(step=0), z.ZOPT_ERR_HYPER),
+    (dict(grad_scale=float("inf")), z.ZOPT_ERR_HYPER),
+])
+def test_adamw_rejects(kw, status):
+    assert adamw(**kw) == status
+
+
+def test_round_bf16_rejects_and_empty_is_a_noop():
+    lib = z.lib()
+    assert lib.zopt_round_bf16(FAKE, FAKE, -1, None) == z.ZOPT_ERR_SIZE
+    assert lib.zopt_round_bf16(None, FAKE, 4, None) == z.ZOPT_ERR_NULL
+    assert lib.zopt_round_bf16(FAKE, None, 4, None) == z.ZOPT_ERR_NULL
+    assert lib.zopt_round_bf16(None, None, 0, None) == z.ZOPT_OK  # nothing enqueued
+
+
+def ptrs(k, null_at=None):
+    arr = (ctypes.c_void_p * k)()
+    for i in range(k):
+        arr[i] = None if i == null_at else 0x100000 + 0x1000 * i
+    return arr
+
+
+def muon(**kw):
+    size = ctypes.c_size_t(1 << 40)
+    a = dict(batch=2, rows=64, cols=32, master=ptrs(2), momentum=ptrs(2), grad=ptrs(2),
+             weight=None, lr=8e-4, mu=0.95, nesterov=1, wd=0.1, ns_steps=5, a=3.4445,
+             b=-4.775, c=2.0315, eps=1e-7, adjust=1, ws=ctypes.c_void_p(1 << 20),
+             ws_bytes=ctypes.byref(size), stream=None)
+    a.update(kw)
+    return z.lib().zopt_muon_step(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), z.ZOPT_ERR_SIZE), (dict(batch=65), z.ZOPT_ERR_SIZE),
+    (dict(rows=0), z.ZOPT_ERR_SIZE), (dict(cols=-3), z.ZOPT_ERR_SIZE),
+    (dict(rows=1 << 16, cols=1 << 15), z.ZOPT_ERR_SIZE),
+    (dict(master=None), z.ZOPT_ERR_NULL), (dict(grad=ptrs(2, null_at=1)), z.ZOPT_ERR_NULL),
+    (dict(weight=ptrs(2, null_at=0)), z.ZOPT_ERR_NULL), (dict(ws_bytes=None), z.ZOPT_ERR_NULL),
+    (dict(lr=-1.0), z.ZOPT_ERR_HYPER), (dict(mu=1.0), z.ZOPT_ERR_HYPER),
+    (dict(nesterov=2), z.ZOPT_ERR_HYPER), (dict(wd=float("nan")), z.ZOPT_ERR_HYPER),
+    (dict(ns_steps=-1), z.ZOPT_ERR_HYPER), (dict(ns_steps=101), z.ZOPT_ERR_HYPER),
+    (dict(b=float("inf")), z.ZOPT_ERR_HYPER), (dict(eps=-1.0), z.ZOPT_ERR_HYPER),
+    (dict(adjust=2), z.ZOPT_ERR_HYPER),
+    (dict(ws=ctypes.c_void_p((1 << 20) + 16)), z.ZOPT_ERR_WORKSPACE),
+])
+def test_muon_rejects(kw, status):
+    assert muon(**kw) == status
+
+
+def test_muon_workspace_query_and_too_small():
+    need = z.muon_workspace_bytes(2, 64, 32)
+    assert need > 0 and need % 256 == 0
+    small = ctypes.c_size_t(need - 1)
+    assert muon(ws_bytes=ctypes.byref(small)) == z.ZOPT_ERR_WORKSPACE
+    # larger problems need more; the query enqueues nothing
+    assert z.muon_workspace_bytes(4, 64, 32) > need
+    assert z.muon_workspace_bytes(1, 4096, 14336) >= 3 * 4096 * 14336 * 2
+
+
+def test_output_view_locates_inside_the_workspace():
+    lib = z.lib()
+    out, ld = ctypes.c_void_p(), ctypes.c_int64()
+    base = 1 << 20
+    need = z.muon_workspace_bytes(3, 100, 300)
+    for rows, cols in ((100, 300), (300, 100)):
+        for steps in (0, 1, 5):
+            for i in range(3):
+                st = lib.zopt_muon_output_view(3, rows, cols, steps, ctypes.c_void_p(base), i,
+                                               ctypes.byref(out), ctypes.byref(ld))
+                assert st == z.ZOPT_OK
+                assert ld.value >= cols
+                end = out.value + 2 * ((rows - 1) * ld.value + cols)
+                assert base <= out.value and end <= base + need
+    assert lib.zopt_muon_output_view(3, 100, 300, 5, ctypes.c_void_p(base), 3,
+                                     ctypes.byref(out), ctypes.byref(ld)) == z.ZOPT_ERR_SIZE
+    assert lib.zopt_muon_output_view(3, 100, 300, 5, None, 0, ctypes.byref(out),
+                                     ctypes.byref(ld)) == z.ZOPT_ERR_NULL
