@@ -1,0 +1,335 @@
+#!/usr/bin/env python3
+"""Benchmark one rank's optimizer step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--parts step,adamw,ns]
+
+Prints ONE JSON line.  The headline workload ("step") is a GPT-2-small-shaped
+full optimizer step at world 1: AdamW on the tied 50304 x 768 embedding
+(weight decay 0.1) and 25 vectors of 768 (no decay) as two
+zopt_adamw_shard_step calls, and Muon on 12 layers x {Wq, Wk, Wv, Wo 768^2;
+fc 3072 x 768; proj 768 x 3072} as three batched zopt_muon_step calls;
+`value` is its time in ms per step.  Two sub-objects report the other two
+parts of the metric on their own workloads:
+
+  adamw_shard     the ZeRO-2 flat AdamW shard of rank 3 of 8 over a
+                  2.0e9-parameter backbone (buckets of 1 << 25, 2.5e8 shard
+                  elements): HBM GB/s at 28 algorithmic bytes per element;
+  newton_schulz   rank 0's Muon share of a 32-layer d=4096 decoder (8 x
+                  [14336, 4096], 4 x [4096, 14336], 8 x [4096, 4096],
+                  8 x [1024, 4096]): bf16 TFLOP/s at 3 m^2 n + m^3
+                  algorithmic flops per iteration, 5 iterations.
+
+Inputs are seeded and synthetic, generated on the GPU before timing, so the
+timed region starts with everything resident in HBM.  Timing: W untimed
+warm-up steps, then K steps bracketed by torch.cuda.synchronize() and HIP
+events on the stream the library launches on.  `cpu_baseline` times the CPU
+oracle (test infrastructure) on the same headline step on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
+METRIC = "AdamW shard GB/s (%HBM peak); Muon NS TFLOP/s (%MFMA); optimizer step ms"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--parts", default="step,adamw,ns",
+                    help="comma list of: step (headline), adamw, ns")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def ns_flops(m, n, steps):
+    """Algorithmic flops of `steps` iterations on an m x n input (m <= n):
+    upper-triangle X X^T (m^2 n), upper-triangle A A (m^3), B X (2 m^2 n)."""
+    return steps * (3 * m * m * n + m ** 3)
+
+
+class Timer:
+    """HIP events on the current stream (the stream the library launches on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def run(self, fn, iters):
+        torch = self.torch
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(iters):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters  # ms per iteration
+
+
+# ------------------------------------------------------------------ workloads
+
+def make_adamw(torch, w, dev, n_grads=1):
+    import workloads as wl
+    n = w.n_total
+    st = dict(master=wl.device_normal(w.wid, 0, (n,), w.master_std, dev),
+              weight=torch.zeros(n, dtype=torch.bfloat16, device=dev),
+              grads=[wl.device_grad_bf16(w.wid, 1, (n,), w.grad_std, dev,
+                                         "normal_outliers" if w.outlier_frac else "normal",
+                                         step=s) for s in range(n_grads)])
+    return st
+
+
+def adamw_zero2_state(torch, dev):
+    import workloads as wl
+    import sharded_optimizer_step_adamw_amd as z
+    w = wl.ZERO2_ADAMW
+    part = w.parts[0]
+    sl = z.shard_len(part.n, part.bucket, part.world)
+    st = dict(part=part, shard_len=sl,
+              master=wl.device_normal(w.wid, 0, (sl,), w.master_std, dev),
+              m=torch.zeros(sl, device=dev), v=torch.zeros(sl, device=dev),
+              weight=torch.zeros(part.n, dtype=torch.bfloat16, device=dev),
+              grads=[wl.device_grad_bf16(w.wid, 1, (part.n,), w.grad_std, dev, step=s)
+                     for s in range(4)])
+    return st
+
+
+def muon_groups(torch, w, dev):
+    import workloads as wl
+    import sharded_optimizer_step_adamw_amd as z
+    groups = []
+    ws_bytes = 0
+    for gi, grp in enumerate(w.groups):
+        shape = (grp.rows, grp.cols)
+        groups.append(dict(
+            rows=grp.rows, cols=grp.cols, count=grp.count,
+            master=[wl.device_normal(w.wid, 100 * gi + i, shape, w.master_std, dev)
+                    for i in range(grp.count)],
+            momentum=[torch.zeros(shape, device=dev) for _ in range(grp.count)],
+            grad=[wl.device_grad_bf16(w.wid, 5000 + 100 * gi + i, shape, w.grad_std, dev,
+                                      w.grad_dist) for i in range(grp.count)],
+            weight=[torch.empty(shape, dtype=torch.bfloat16, device=dev)
+                    for _ in range(grp.count)]))
+        ws_bytes = max(ws_bytes, z.muon_workspace_bytes(grp.count, grp.rows, grp.cols))
+    workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    return groups, workspace
+
+
+def muon_call(z, w, g, workspace, ns_steps):
+    z.muon_step(g["master"], g["momentum"], g["grad"], g["weight"], w.lr, w.momentum,
+                w.nesterov, w.weight_decay, ns_steps, w.ns_coeffs, w.ns_eps, w.adjust_lr,
+                workspace=workspace)
+
+
+# ------------------------------------------------------------------ parts
+
+def bench_step(torch, z, timer, dev, K, W):
+    """The headline: one GPT-2-small optimizer step (2 AdamW + 3 Muon calls)."""
+    import workloads as wl
+    wa, wm = wl.GPT2_ADAMW, wl.GPT2_MUON
+    a = make_adamw(torch, wa, dev)
+    n = wa.n_total
+    a["m"], a["v"] = torch.zeros(n, device=dev), torch.zeros(n, device=dev)
+    groups, workspace = muon_groups(torch, wm, dev)
+    counter = [0]
+
+    def step(_):
+        counter[0] += 1
+        t = counter[0]
+        for part in wa.parts:
+            s = slice(part.offset, part.offset + part.n)
+            z.adamw_shard_step(a["master"][s], a["m"][s], a["v"][s], a["grads"][0][s],
+                               a["weight"][s], part.n, part.bucket, part.world, part.rank,
+                               part.lr, part.beta1, part.beta2, part.eps, part.weight_decay, t)
+        for g in groups:
+            muon_call(z, wm, g, workspace, wm.ns_steps)
+
+    timer.run(step, W)
+    ms = timer.run(step, K)
+
+    # the dominant kernels: one Newton-Schulz iteration of each group is three
+    # launches (X X^T, A A with its epilogue, B X with its epilogue); its time
+    # is the difference of a Muon call with 5 and with 0 iterations, over 5
+    iter_ms, iter_flops, per_group = 0.0, 0, []
+    for g in groups:
+        t5 = timer.run(lambda _: muon_call(z, wm, g, workspace, 5), K)
+        t0 = timer.run(lambda _: muon_call(z, wm, g, workspace, 0), K)
+        mm, nn = min(g["rows"], g["cols"]), max(g["rows"], g["cols"])
+        fl = g["count"] * ns_flops(mm, nn, 1)
+        per_group.append(dict(shape=[g["rows"], g["cols"]], count=g["count"],
+                              muon_call_ms=round(t5, 4), pre_post_ms=round(t0, 4),
+                              ns_iter_ms=round((t5 - t0) / 5, 4),
+                              ns_tflops=round(fl / ((t5 - t0) / 5) / 1e9, 1)))
+        iter_ms += (t5 - t0) / 5
+        iter_flops += fl
+    adamw_bytes = 28 * n
+    ta = timer.run(lambda i: [z.adamw_shard_step(
+        a["master"][p.offset:p.offset + p.n], a["m"][p.offset:p.offset + p.n],
+        a["v"][p.offset:p.offset + p.n], a["grads"][0][p.offset:p.offset + p.n],
+        a["weight"][p.offset:p.offset + p.n], p.n, p.bucket, p.world, p.rank, p.lr, p.beta1,
+        p.beta2, p.eps, p.weight_decay, 1000 + i) for p in wa.parts], K)
+    del a, groups, workspace
+    torch.cuda.empty_cache()
+    return dict(ms=ms, ns_iter_ms=iter_ms, ns_iter_flops=iter_flops, groups=per_group,
+                adamw_ms=ta, adamw_gbs=adamw_bytes / ta / 1e6)
+
+
+def bench_adamw(torch, z, timer, dev, K, W):
+    s = adamw_zero2_state(torch, dev)
+    p, sl = s["part"], s["shard_len"]
+    counter = [0]
+
+    def step(i):
+        counter[0] += 1
+        z.adamw_shard_step(s["master"], s["m"], s["v"], s["grads"][counter[0] % 4], s["weight"],
+                           p.n, p.bucket, p.world, p.rank, p.lr, p.beta1, p.beta2, p.eps,
+                           p.weight_decay, counter[0])
+
+    timer.run(step, W)
+    ms = timer.run(step, K)
+    del s
+    torch.cuda.empty_cache()
+    gbs = 28 * sl / ms / 1e6
+    return dict(workload="zero2 flat AdamW shard: N=2.0e9, bucket 1<<25, world 8, rank 3",
+                shard_len=sl, algorithmic_bytes_per_step=28 * sl, ms_per_step=round(ms, 4),
+                gbs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4), steps=K)
+
+
+def bench_ns(torch, z, timer, dev, K, W):
+    import workloads as wl
+    w = wl.LLAMA8B_MUON
+    groups, workspace = muon_groups(torch, w, dev)
+    total_flops, ns_ms, call_ms, rows = 0, 0.0, 0.0, []
+    for g in groups:
+        mm, nn = min(g["rows"], g["cols"]), max(g["rows"], g["cols"])
+        fl = g["count"] * ns_flops(mm, nn, w.ns_steps)
+        timer.run(lambda _: muon_call(z, w, g, workspace, w.ns_steps), max(1, W))
+        t5 = timer.run(lambda _: muon_call(z, w, g, workspace, w.ns_steps), K)
+        t0 = timer.run(lambda _: muon_call(z, w, g, workspace, 0), K)
+        total_flops += fl
+        ns_ms += t5 - t0
+        call_ms += t5
+        rows.append(dict(shape=[g["rows"], g["cols"]], count=g["count"], muon_call_ms=round(t5, 3),
+                         ns_ms=round(t5 - t0, 3), ns_tflops=round(fl / (t5 - t0) / 1e9, 1)))
+    del groups, workspace
+    torch.cuda.empty_cache()
+    tf = total_flops / ns_ms / 1e9
+    return dict(workload="llama8b rank-0 Muon share (W=8, 32 layers), 5 bf16 NS iterations",
+                algorithmic_flops_per_step=total_flops, ns_ms_per_step=round(ns_ms, 3),
+                muon_ms_per_step=round(call_ms, 3), ns_tflops=round(tf, 1),
+                mfma_frac=round(tf / BF16_PEAK_TFLOPS, 4),
+                muon_step_tflops=round(total_flops / call_ms / 1e9, 1), groups=rows, steps=K)
+
+
+def cpu_baseline():
+    """The CPU oracle (test infrastructure, untuned) on the same headline step:
+    the two AdamW calls over all 38,652,672 elements (scalar C, one thread)
+    and all 72 Muon matrices (binary32 pre/post in C, float64 Newton-Schulz
+    through numpy's BLAS)."""
+    import numpy as np
+    import oracle
+    import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = os.cpu_count() or 1
+    wa, wm = wl.GPT2_ADAMW, wl.GPT2_MUON
+    n = wa.n_total
+    p = wl.host_normal(wa.wid, 0, n, wa.master_std)
+    g = wl.host_grad_bf16(wa.wid, 1, n, wa.grad_std, "normal_outliers")
+    m, v, w = np.zeros_like(p), np.zeros_like(p), np.zeros(n, np.uint16)
+    mats = []
+    for gi, grp in enumerate(wm.groups):
+        for i in range(grp.count):
+            shape = (grp.rows, grp.cols)
+            mats.append((wl.host_normal(wm.wid, 100 * gi + i, shape, wm.master_std),
+                         np.zeros(shape, np.float32),
+                         wl.host_grad_bf16(wm.wid, 5000 + 100 * gi + i, shape, wm.grad_std,
+                                           "normal_outliers")))
+    t0 = time.perf_counter()
+    for part in wa.parts:
+        s = slice(part.offset, part.offset + part.n)
+        pv, mv, vv, wv = p[s].copy(), m[s].copy(), v[s].copy(), w[s].copy()
+        oracle.adamw_shard_step(pv, mv, vv, g[s].copy(), wv, part.n, part.bucket, part.world,
+                                part.rank, part.lr, part.beta1, part.beta2, part.eps,
+                                part.weight_decay, 1)
+    t1 = time.perf_counter()
+    for master, mom, grad in mats:
+        oracle.muon_step(master, mom, grad, wm.lr, wm.momentum, wm.nesterov, wm.weight_decay,
+                         wm.ns_steps, wm.ns_coeffs, wm.ns_eps, wm.adjust_lr)
+    t2 = time.perf_counter()
+    return dict(value=round((t2 - t0) * 1e3, 1), unit="ms per optimizer step",
+                cores=int(blas_threads), kind="oracle",
+                sample=("the whole headline step, not extrapolated: AdamW over 38,652,672 "
+                        f"elements in scalar C on 1 thread ({(t1 - t0) * 1e3:.0f} ms), 72 Muon "
+                        "matrices with float64 Newton-Schulz through numpy BLAS on "
+                        f"{blas_threads} threads ({(t2 - t1) * 1e3:.0f} ms)"),
+                host_cpus=os.cpu_count(), host=platform.processor() or platform.machine())
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one rank's optimizer step on one GPU; runs on more than "
+              "one GPU are not part of this build (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (MI355X)", file=sys.stderr)
+        sys.exit(1)
+    import sharded_optimizer_step_adamw_amd as z
+    z.lib()  # fails loudly if libzopt.so is not built
+    dev = torch.device("cuda:0")
+    timer = Timer(torch)
+    parts = set(args.parts.split(","))
+    K, W = args.steps, args.warmup
+    out = dict(metric=METRIC)
+    res_step = bench_step(torch, z, timer, dev, K, W) if "step" in parts else None
+    res_adamw = bench_adamw(torch, z, timer, dev, max(K, 100), W) if "adamw" in parts else None
+    res_ns = bench_ns(torch, z, timer, dev, max(2, K // 5), W) if "ns" in parts else None
+    if res_step:
+        tf = res_step["ns_iter_flops"] / res_step["ns_iter_ms"] / 1e9
+        out.update(value=round(res_step["ms"], 4), unit="ms per optimizer step")
+        roof = dict(
+            kernel=("Newton-Schulz iteration: ns_gemm_kernel X X^T + A A + B X "
+                    "(3 launches per same-shape group), summed over the step's 3 groups"),
+            bound="mfma", achieved=round(tf, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+            frac=round(tf / BF16_PEAK_TFLOPS, 4), traffic=None,
+            algorithmic_flops_per_unit=res_step["ns_iter_flops"],
+            avg_unit_ms=round(res_step["ns_iter_ms"], 4))
+    else:
+        roof = None
+    out.update(n_gpus=1, steps=K, warmup=W,
+               ms_per_step=out.get("value"), higher_is_better=False, scaling="weak",
+               vs_baseline=None, dtype="fp32+bf16", data="synthetic",
+               config=dict(workload=("gpt2-small optimizer step, world 1: AdamW on 50304x768 "
+                                     "embedding + 25x768 vectors (2 calls), Muon on 12 layers "
+                                     "x {4x768x768, 3072x768, 768x3072} (3 batched calls), "
+                                     "5 bf16 Newton-Schulz iterations"),
+                           adamw_elements=38_652_672, muon_matrices=72),
+               roofline=roof)
+    if res_step:
+        out["step_detail"] = dict(adamw_ms=round(res_step["adamw_ms"], 4),
+                                  adamw_gbs=round(res_step["adamw_gbs"], 1),
+                                  muon_groups=res_step["groups"])
+    if res_adamw:
+        out["adamw_shard"] = res_adamw
+    if res_ns:
+        out["newton_schulz"] = res_ns
+    out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline()
+    out["device"] = torch.cuda.get_device_name(0)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
