@@ -10,10 +10,10 @@
 //
 // The step is bound by HBM bandwidth: per shard element it reads 2 B of
 // gradient and 12 B of fp32 state and writes 12 B of state and 2 B of bf16
-// weight (28 B).  Each thread takes one unit of 8 consecutive shard elements:
-// three pairs of 128-bit loads and stores for master / exp_avg / exp_avg_sq,
-// one 128-bit gradient load and one 128-bit weight store.  Nothing is
-// re-read, so every access is a streaming (non-temporal) one.
+// weight (28 B).  A workgroup streams one tile of 2048 shard elements; each
+// wave-wide load or store instruction covers one contiguous kilobyte of a
+// state array.  Nothing is re-read, so every access is a streaming
+// (non-temporal) one.
 #include "zopt_internal.h"
 
 // Bit-exact arithmetic: every + - * / below is one correctly rounded binary32
@@ -23,11 +23,13 @@
 namespace zopt {
 namespace {
 
-constexpr int kUnit = 8;            // shard elements per thread
-constexpr int kThreads = 256;       // threads per workgroup
+constexpr int kThreads = 256;            // threads per workgroup
+constexpr int kGroups = 2;               // 4-element groups per thread
+constexpr int kTile = kThreads * 4 * kGroups;  // shard elements per workgroup
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <typename T>
 __device__ __forceinline__ T ld_stream(const T *p) {
@@ -47,30 +49,91 @@ __device__ __forceinline__ void adamw_update(float &p, float &m, float &v, float
     p = p - a.step_size * (m / denom);
 }
 
+// Bucket of shard element j (j < full_len): j / piece through a double
+// reciprocal, corrected by one step either way (exact for j < 2^52).
+__device__ __forceinline__ int64_t bucket_of(int64_t j, const AdamWParams &a) {
+    int64_t b = (int64_t)((double)j * a.inv_piece);
+    if (b * a.piece > j) --b;
+    else if ((b + 1) * a.piece <= j) ++b;
+    return b;
+}
+
 // Flat index of shard element j and whether it is a real element.
 __device__ __forceinline__ int64_t flat_of(int64_t j, const AdamWParams &a, bool &real) {
     if (j < a.full_len) {
-        int64_t b = (int64_t)((uint64_t)j / (uint64_t)a.piece);
         real = true;
-        return j + b * a.gap + a.rank_off;
+        return j + bucket_of(j, a) * a.gap + a.rank_off;
     }
-    int64_t f = a.last_flat0 + (j - a.full_len);
+    const int64_t f = a.last_flat0 + (j - a.full_len);
     real = f < a.n;
     return f;
 }
 
-// One element at a time: any unit that straddles a bucket edge, touches
-// padding, is misaligned, or runs past the end of the shard.
-__device__ void adamw_unit_scalar(float *__restrict__ master, float *__restrict__ exp_avg,
-                                  float *__restrict__ exp_avg_sq,
-                                  const uint16_t *__restrict__ grad,
-                                  uint16_t *__restrict__ weight, int64_t j0,
-                                  const AdamWParams &a) {
-    for (int e = 0; e < kUnit; ++e) {
-        int64_t j = j0 + e;
+// Flat index of the first element of tile [t0, t0 + kTile) when the whole
+// tile maps to consecutive real flat positions (one bucket's piece, no
+// padding, inside the shard), else -1.
+__device__ __forceinline__ int64_t tile_flat(int64_t t0, const AdamWParams &a) {
+    const int64_t t1 = t0 + kTile;
+    if (t1 <= a.full_len) {
+        const int64_t b = bucket_of(t0, a);
+        return bucket_of(t1 - 1, a) == b ? t0 + b * a.gap + a.rank_off : -1;
+    }
+    if (t0 >= a.full_len && t1 <= a.shard_len) {
+        const int64_t f0 = a.last_flat0 + (t0 - a.full_len);
+        return f0 + kTile <= a.n ? f0 : -1;
+    }
+    return -1;
+}
+
+// One workgroup per tile of kTile shard elements.  The fast path gives each
+// thread two groups of 4 consecutive elements, a workgroup-width apart, so
+// every load and store instruction of a wave covers one contiguous kilobyte
+// of fp32 state (and 512 bytes of bf16).  A tile that straddles a bucket
+// edge, touches padding, ends the shard or is misaligned takes the generic
+// path: one element at a time, still coalesced across the workgroup.
+__global__ __launch_bounds__(kThreads) void adamw_shard_kernel(
+    float *__restrict__ master, float *__restrict__ exp_avg, float *__restrict__ exp_avg_sq,
+    const uint16_t *__restrict__ grad, uint16_t *__restrict__ weight, AdamWParams a) {
+    const int64_t t0 = (int64_t)blockIdx.x * kTile;
+    const int64_t f0 = a.vec ? tile_flat(t0, a) : -1;
+    if (f0 >= 0 && (f0 & 3) == 0) {
+        f32x4 p[kGroups], m[kGroups], v[kGroups];
+        u32x2 g[kGroups];
+#pragma unroll
+        for (int q = 0; q < kGroups; ++q) {
+            const int64_t o = (int64_t)q * kThreads * 4 + threadIdx.x * 4;
+            p[q] = ld_stream(reinterpret_cast<const f32x4 *>(master + t0 + o));
+            m[q] = ld_stream(reinterpret_cast<const f32x4 *>(exp_avg + t0 + o));
+            v[q] = ld_stream(reinterpret_cast<const f32x4 *>(exp_avg_sq + t0 + o));
+            g[q] = ld_stream(reinterpret_cast<const u32x2 *>(grad + f0 + o));
+        }
+#pragma unroll
+        for (int q = 0; q < kGroups; ++q) {
+            const int64_t o = (int64_t)q * kThreads * 4 + threadIdx.x * 4;
+            float pe[4] = {p[q].x, p[q].y, p[q].z, p[q].w};
+            float me[4] = {m[q].x, m[q].y, m[q].z, m[q].w};
+            float ve[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+            const uint32_t gb[2] = {g[q].x, g[q].y};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float ge = bf16_bits_to_float((gb[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
+                adamw_update(pe[e], me[e], ve[e], ge * a.grad_scale, a);
+            }
+            st_stream(reinterpret_cast<f32x4 *>(master + t0 + o), f32x4{pe[0], pe[1], pe[2], pe[3]});
+            st_stream(reinterpret_cast<f32x4 *>(exp_avg + t0 + o), f32x4{me[0], me[1], me[2], me[3]});
+            st_stream(reinterpret_cast<f32x4 *>(exp_avg_sq + t0 + o),
+                      f32x4{ve[0], ve[1], ve[2], ve[3]});
+            if (weight)
+                st_stream(reinterpret_cast<u32x2 *>(weight + f0 + o),
+                          u32x2{pack_bf16x2(pe[0], pe[1]), pack_bf16x2(pe[2], pe[3])});
+        }
+        return;
+    }
+    for (int k = 0; k < kTile / kThreads; ++k) {
+        const int64_t j = t0 + (int64_t)k * kThreads + threadIdx.x;
         if (j >= a.shard_len) return;
         bool real;
-        int64_t f = flat_of(j, a, real);
+        const int64_t f = flat_of(j, a, real);
         float g = 0.0f;
         if (real) g = bf16_bits_to_float(grad[f]) * a.grad_scale;
         float p = master[j], m = exp_avg[j], v = exp_avg_sq[j];
@@ -82,86 +145,30 @@ __device__ void adamw_unit_scalar(float *__restrict__ master, float *__restrict_
     }
 }
 
-__global__ __launch_bounds__(kThreads) void adamw_shard_kernel(
-    float *__restrict__ master, float *__restrict__ exp_avg, float *__restrict__ exp_avg_sq,
-    const uint16_t *__restrict__ grad, uint16_t *__restrict__ weight, AdamWParams a) {
-    const int64_t unit = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    const int64_t j0 = unit * kUnit;
-    if (j0 >= a.shard_len) return;
-
-    // Decide whether the 8 elements map to 8 consecutive, real, 8-aligned
-    // flat positions inside one bucket.
-    bool fast = false;
-    int64_t f0 = 0;
-    if (a.vec && j0 + kUnit <= a.shard_len) {
-        if (j0 + kUnit <= a.full_len) {
-            uint64_t b0 = (uint64_t)j0 / (uint64_t)a.piece;
-            uint64_t b7 = (uint64_t)(j0 + kUnit - 1) / (uint64_t)a.piece;
-            f0 = j0 + (int64_t)b0 * a.gap + a.rank_off;
-            fast = (b0 == b7) && ((f0 & (kUnit - 1)) == 0);
-        } else if (j0 >= a.full_len) {
-            f0 = a.last_flat0 + (j0 - a.full_len);
-            fast = (f0 + kUnit <= a.n) && ((f0 & (kUnit - 1)) == 0);
-        }
-    }
-    if (!fast) {
-        adamw_unit_scalar(master, exp_avg, exp_avg_sq, grad, weight, j0, a);
-        return;
-    }
-
-    const f32x4 *P = reinterpret_cast<const f32x4 *>(master + j0);
-    const f32x4 *M = reinterpret_cast<const f32x4 *>(exp_avg + j0);
-    const f32x4 *V = reinterpret_cast<const f32x4 *>(exp_avg_sq + j0);
-    const u32x4 *G = reinterpret_cast<const u32x4 *>(grad + f0);
-    f32x4 p0 = ld_stream(P), p1 = ld_stream(P + 1);
-    f32x4 m0 = ld_stream(M), m1 = ld_stream(M + 1);
-    f32x4 v0 = ld_stream(V), v1 = ld_stream(V + 1);
-    u32x4 gw = ld_stream(G);
-
-    float p[kUnit] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-    float m[kUnit] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-    float v[kUnit] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    uint32_t gbits[4] = {gw.x, gw.y, gw.z, gw.w};
-#pragma unroll
-    for (int e = 0; e < kUnit; ++e) {
-        uint32_t h = (gbits[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-        float g = bf16_bits_to_float(h) * a.grad_scale;
-        adamw_update(p[e], m[e], v[e], g, a);
-    }
-    f32x4 *Pw = reinterpret_cast<f32x4 *>(master + j0);
-    f32x4 *Mw = reinterpret_cast<f32x4 *>(exp_avg + j0);
-    f32x4 *Vw = reinterpret_cast<f32x4 *>(exp_avg_sq + j0);
-    st_stream(Pw, f32x4{p[0], p[1], p[2], p[3]});
-    st_stream(Pw + 1, f32x4{p[4], p[5], p[6], p[7]});
-    st_stream(Mw, f32x4{m[0], m[1], m[2], m[3]});
-    st_stream(Mw + 1, f32x4{m[4], m[5], m[6], m[7]});
-    st_stream(Vw, f32x4{v[0], v[1], v[2], v[3]});
-    st_stream(Vw + 1, f32x4{v[4], v[5], v[6], v[7]});
-    if (weight) {
-        u32x4 w{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-        st_stream(reinterpret_cast<u32x4 *>(weight + f0), w);
-    }
-}
-
-// dst[i] = bf16(src[i]); 8 elements per thread, 6 bytes of traffic each.
+// dst[i] = bf16(src[i]), 6 bytes of traffic per element, in the same tiles
+// as the AdamW kernel (one contiguous kilobyte of fp32 per wave instruction).
 __global__ __launch_bounds__(kThreads) void round_bf16_kernel(
     const float *__restrict__ src, uint16_t *__restrict__ dst, int64_t n, int32_t vec) {
-    const int64_t i0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * kUnit;
-    if (i0 >= n) return;
-    if (vec && i0 + kUnit <= n) {
-        const f32x4 *S = reinterpret_cast<const f32x4 *>(src + i0);
-        f32x4 a = ld_stream(S), b = ld_stream(S + 1);
-        u32x4 w{pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y),
-                pack_bf16x2(b.z, b.w)};
-        st_stream(reinterpret_cast<u32x4 *>(dst + i0), w);
+    const int64_t t0 = (int64_t)blockIdx.x * kTile;
+    if (vec && t0 + kTile <= n) {
+#pragma unroll
+        for (int q = 0; q < kGroups; ++q) {
+            const int64_t o = t0 + (int64_t)q * kThreads * 4 + threadIdx.x * 4;
+            const f32x4 x = ld_stream(reinterpret_cast<const f32x4 *>(src + o));
+            st_stream(reinterpret_cast<u32x2 *>(dst + o),
+                      u32x2{pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w)});
+        }
         return;
     }
-    for (int e = 0; e < kUnit && i0 + e < n; ++e)
-        dst[i0 + e] = (uint16_t)rne_bf16_bits(src[i0 + e]);
+    for (int k = 0; k < kTile / kThreads; ++k) {
+        const int64_t i = t0 + (int64_t)k * kThreads + threadIdx.x;
+        if (i >= n) return;
+        dst[i] = (uint16_t)rne_bf16_bits(src[i]);
+    }
 }
 
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool aligned8(const void *p) { return ((uintptr_t)p & 7u) == 0; }
 
 }  // namespace
 
@@ -170,21 +177,20 @@ hipError_t launch_adamw_shard(float *master, float *exp_avg, float *exp_avg_sq,
                               const AdamWParams &p_in, hipStream_t stream) {
     AdamWParams p = p_in;
     p.vec = aligned16(master) && aligned16(exp_avg) && aligned16(exp_avg_sq) &&
-            aligned16(grad) && (weight == nullptr || aligned16(weight));
-    const int64_t units = (p.shard_len + kUnit - 1) / kUnit;
-    const int64_t blocks = (units + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL(adamw_shard_kernel, dim3((uint32_t)blocks), dim3(kThreads), 0,
-                       stream, master, exp_avg, exp_avg_sq, grad, weight, p);
+            aligned8(grad) && (weight == nullptr || aligned8(weight));
+    p.inv_piece = 1.0 / (double)p.piece;
+    const int64_t blocks = (p.shard_len + kTile - 1) / kTile;
+    hipLaunchKernelGGL(adamw_shard_kernel, dim3((uint32_t)blocks), dim3(kThreads), 0, stream,
+                       master, exp_avg, exp_avg_sq, grad, weight, p);
     return hipGetLastError();
 }
 
 hipError_t launch_round_bf16(const float *src, uint16_t *dst, int64_t n,
                              hipStream_t stream) {
-    const int32_t vec = aligned16(src) && aligned16(dst);
-    const int64_t units = (n + kUnit - 1) / kUnit;
-    const int64_t blocks = (units + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL(round_bf16_kernel, dim3((uint32_t)blocks), dim3(kThreads), 0,
-                       stream, src, dst, n, vec);
+    const int32_t vec = aligned16(src) && aligned8(dst);
+    const int64_t blocks = (n + kTile - 1) / kTile;
+    hipLaunchKernelGGL(round_bf16_kernel, dim3((uint32_t)blocks), dim3(kThreads), 0, stream,
+                       src, dst, n, vec);
     return hipGetLastError();
 }
 

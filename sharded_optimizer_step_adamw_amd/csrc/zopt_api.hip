@@ -61,7 +61,7 @@ MuonGeom muon_geometry(int32_t batch, int64_t rows, int64_t cols) {
     g.transposed = rows > cols ? 1 : 0;
     g.m = (int32_t)(rows < cols ? rows : cols);
     g.n = (int32_t)(rows < cols ? cols : rows);
-    g.tile = g.m >= 256 ? 128 : 64;
+    g.tile = g.m >= 1024 ? 256 : g.m >= 256 ? 128 : 64;
     g.mp = (int32_t)round_up64(g.m, g.tile);
     g.np = (int32_t)round_up64(g.n, g.tile);
     g.norm_blocks = muon_norm_blocks(rows * cols);

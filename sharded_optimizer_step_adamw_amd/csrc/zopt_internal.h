@@ -51,7 +51,8 @@ struct AdamWParams {
     float beta1, beta2, eps;
     float step_size, bc2_sqrt, decay, omb1, omb2;
     float grad_scale;
-    int32_t vec;         // every base pointer is 16-byte aligned
+    int32_t vec;         // fp32 bases 16-byte and bf16 bases 8-byte aligned
+    double inv_piece;    // 1 / piece, for the bucket index
 };
 
 hipError_t launch_adamw_shard(float *master, float *exp_avg, float *exp_avg_sq,
