@@ -41,6 +41,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -243,263 +244,271 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(NsArgs args) {
 }
 
 
-// Epilogue of the 256 x 256 kernel, staged through LDS (free once the K loop
-// has ended).  Each wave owns a 128 x 128 sub-block and a 32 KB LDS region
-// holding it as bf16, rows of 256 bytes whose sixteen 16-byte chunks are
-// XOR-swizzled by the row index.  The accumulators are completed in place
-// from a staged input (A A: from Aoff; B X: the (a + dB_i) X term).  They
-// are written
-// to LDS once transposed (8-byte writes of four consecutive rows) and once
-// in row order, and each layout leaves as coalesced 16-byte row stores: the
-// transposed one to X^T (full product) or to the mirror sub-block (symmetric
-// products), the row-order one to the sub-block itself.  Sub-blocks of the
-// symmetric products below the diagonal do nothing; those on it are filled
-// symmetrically from their upper triangle, store once, and send their
-// diagonal to the fp32 vector.  Every wave passes the same barriers.
-__device__ __forceinline__ int swz(int i, int j) {
+// ----------------------------------------------------------------------------
+// 256 x 256 tiles for the large shapes.
+//
+// Eight waves (two per SIMD) each own a 128 x 64 sub-tile built from 8 x 4
+// MFMA 16x16x32 bf16 tiles (128 fp32 accumulators per lane).  K advances 64
+// columns per stage through two LDS stages of 2 x 32 KB.  Operands go from
+// global memory straight to LDS (global_load_lds, 16 bytes per lane, each
+// wave instruction filling one contiguous kilobyte = 8 rows of 64 K-columns);
+// a lane fetches the chunk that the XOR swizzle (chunk c of row r at
+// position c ^ (r & 7)) puts at its LDS slot, so fragment reads of 16
+// consecutive rows spread over all banks without padding.  Within a stage
+// the fragment reads of the next 32-column sub-step and the global loads of
+// the next stage are interleaved with the MFMAs, and the MFMA clusters run at
+// raised wave priority so one wave's matrix work overlaps the other wave's
+// memory work on the same SIMD.
+constexpr int kWaves256 = 8;
+
+#define LDS_ADDR(p) ((__attribute__((address_space(3))) void *)(p))
+
+// Swizzled byte offsets inside a wave's epilogue region: R holds the 128 x 64
+// sub-block row by row (128-byte rows of 8 chunks), T holds it transposed
+// (64 rows of 256 bytes, 16 chunks).
+__device__ __forceinline__ int swz_r(int i, int j) {
+    return i * 128 + (((j >> 3) ^ (i & 7)) << 4) + ((j & 7) << 1);
+}
+__device__ __forceinline__ int swz_t(int i, int j) {
     return i * 256 + (((j >> 3) ^ (i & 15)) << 4) + ((j & 7) << 1);
 }
 
-// Coalesced copy of the 128 x 128 bf16 sub-block at (R0, C0) of M (row
-// stride ld) into the wave's LDS region, row order.
-__device__ __forceinline__ void stage_in(uint8_t *T, const uint16_t *M, int64_t ld, int R0, int C0,
-                                         int lane) {
-#pragma unroll 8
-    for (int k = 0; k < 32; ++k) {
-        const int id = k * 64 + lane, i = id >> 4, c = id & 15;
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(M + (int64_t)(R0 + i) * ld + C0 + c * 8);
-        *reinterpret_cast<u32x4 *>(T + i * 256 + ((c ^ (i & 15)) << 4)) = v;
-    }
-}
-
-// Coalesced store of the wave's LDS region (row order) to M at (R0, C0).
-__device__ __forceinline__ void stage_out(const uint8_t *T, uint16_t *M, int64_t ld, int R0, int C0,
-                                          int lane) {
-#pragma unroll 8
-    for (int k = 0; k < 32; ++k) {
-        const int id = k * 64 + lane, i = id >> 4, c = id & 15;
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(T + i * 256 + ((c ^ (i & 15)) << 4));
-        *reinterpret_cast<u32x4 *>(M + (int64_t)(R0 + i) * ld + C0 + c * 8) = v;
-    }
-}
-
+// Epilogue: the accumulators are completed in place (A A: b Aoff + c (acc +
+// (dA_i + dA_j) Aoff), its diagonal b dA_i + c (acc + dA_i^2); B X:
+// (a + dB_i) X + acc; the inputs staged through LDS), then leave through the
+// wave's 16 KB LDS region as coalesced 16-byte row stores: row order to the
+// sub-block itself, transposed to X^T (B X) or to the mirror position (the
+// symmetric products).  A symmetric sub-block that crosses the diagonal is
+// stored element by element from its upper triangle, so the mirror of each
+// value is that same bf16 value; below the diagonal nothing is stored; the
+// diagonal goes to the fp32 vector (its bf16 entry is 0).  Every wave passes
+// the same barriers.
 template <int MODE>
-__device__ __forceinline__ void epilogue256(const NsArgs &args, f32x16 (&acc)[4][4], int batch,
-                                            int m0, int n0, int wr, int wc, int lane,
+__device__ __forceinline__ void epilogue256(const NsArgs &args, f32x4 (&acc)[8][4], int batch,
+                                            int m0, int n0, int wr, int wc, int wave, int lane,
                                             uint8_t *lds_all) {
-    constexpr int S = 128;
-    uint8_t *T = lds_all + ((wr << 1) | wc) * (S * S * 2);
-    const int R0 = m0 + wr * S, C0 = n0 + wc * S;
+    constexpr int SR = 128, SC = 64;
+    uint8_t *W = lds_all + wave * (SR * SC * 2);
+    const int R0 = m0 + wr * SR, C0 = n0 + wc * SC;
     constexpr bool sym = MODE != kGemmBX;
-    const bool below = sym && R0 > C0;
-    const bool diag = sym && R0 == C0;
+    const bool below = sym && R0 >= C0 + SC;
+    const bool above = !sym || R0 + SR <= C0;
+    const bool cross = sym && !below && !above;
     const int64_t ldc = args.ldc;
     uint16_t *Cm = args.C + batch * args.c_stride;
     const float *dIn = args.dIn + batch * args.d_stride;
     float *dOut = args.dOut + batch * args.d_stride;
-    const int h = lane >> 5, col = lane & 31;
+    const int col = lane & 15, quad = lane >> 4;
 
-    // 1. complete the accumulators (A A: b Aoff + c (acc + (dA_i + dA_j) Aoff);
-    //    B X: (a + dB_i) X + acc; diagonals of the symmetric products go to the
-    //    fp32 vector)
-    if (MODE == kSyrkAA && !below) stage_in(T, args.E + batch * args.c_stride, ldc, R0, C0, lane);
-    if (MODE == kGemmBX) stage_in(T, Cm, ldc, R0, C0, lane);
+    // 1. stage the input sub-block (row order) and complete the accumulators
+    if (MODE != kSyrkXXT && !below) {
+        const uint16_t *E = MODE == kSyrkAA ? args.E + batch * args.c_stride : Cm;
+#pragma unroll 4
+        for (int k = 0; k < 16; ++k) {
+            const int id = k * 64 + lane, i = id >> 3, c = id & 7;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(E + (int64_t)(R0 + i) * ldc + C0 + c * 8);
+            *reinterpret_cast<u32x4 *>(W + i * 128 + ((c ^ (i & 7)) << 4)) = v;
+        }
+    }
     __syncthreads();
     if (!below) {
 #pragma unroll
-        for (int is = 0; is < 4; ++is)
+        for (int i = 0; i < 8; ++i) {
 #pragma unroll
-            for (int js = 0; js < 4; ++js) {
-                const int lj = js * 32 + col, gj = C0 + lj;
+            for (int j = 0; j < 4; ++j) {
+                const int lj = j * 16 + col, gj = C0 + lj;
                 const float da_j = MODE == kSyrkAA ? dIn[gj] : 0.0f;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int li = is * 32 + 8 * (r >> 2) + 4 * h + (r & 3), gi = R0 + li;
-                    float x = acc[is][js][r];
-                    if (MODE == kGemmBX)
-                        x = (args.a + dIn[gi]) *
-                                from_bf16(*reinterpret_cast<const uint16_t *>(T + swz(li, lj))) + x;
-                    if (MODE == kSyrkAA) {
-                        // Aoff's diagonal is stored as zero: on it this is c v,
-                        // replaced by the diagonal's own formula
+                for (int r = 0; r < 4; ++r) {
+                    const int li = i * 16 + quad * 4 + r, gi = R0 + li;
+                    float x = acc[i][j][r];
+                    if (MODE == kGemmBX) {
+                        const float xv = from_bf16(*reinterpret_cast<const uint16_t *>(W + swz_r(li, lj)));
+                        x = (args.a + dIn[gi]) * xv + x;
+                    } else if (MODE == kSyrkAA) {
                         const float da_i = dIn[gi];
-                        const float aoff = from_bf16(*reinterpret_cast<const uint16_t *>(T + swz(li, lj)));
+                        const float aoff = from_bf16(*reinterpret_cast<const uint16_t *>(W + swz_r(li, lj)));
                         const float v = x;
                         x = args.b * aoff + args.c * (v + (da_i + da_j) * aoff);
                         if (gi == gj) x = args.b * da_i + args.c * (v + da_i * da_i);
                     }
-                    if (diag && gi == gj) {
+                    acc[i][j][r] = x;
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    __syncthreads();
+
+    if (cross) {
+        // element by element, upper triangle and its mirror
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int gj = C0 + j * 16 + col;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int gi = R0 + i * 16 + quad * 4 + r;
+                    const float x = acc[i][j][r];
+                    if (gi < gj) {
+                        const uint16_t h = to_bf16(x);
+                        Cm[(int64_t)gi * ldc + gj] = h;
+                        Cm[(int64_t)gj * ldc + gi] = h;
+                    } else if (gi == gj) {
                         dOut[gi] = x;
-                        x = 0.0f;
-                    }
-                    acc[is][js][r] = x;
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-    }
-    __syncthreads();
-
-    // 2. transposed layout T[lj][li]; on the diagonal, the symmetric fill
-    if (!below) {
-#pragma unroll
-        for (int is = 0; is < 4; ++is)
-#pragma unroll
-            for (int js = 0; js < 4; ++js) {
-                const int lj = js * 32 + col;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int li = is * 32 + 8 * q + 4 * h;
-                    const uint32_t lo = pack_bf16x2(acc[is][js][4 * q], acc[is][js][4 * q + 1]);
-                    const uint32_t hi = pack_bf16x2(acc[is][js][4 * q + 2], acc[is][js][4 * q + 3]);
-                    if (!diag) {
-                        *reinterpret_cast<u32x2 *>(T + swz(lj, li)) = u32x2{lo, hi};
-                    } else {
-#pragma unroll
-                        for (int s2 = 0; s2 < 4; ++s2) {
-                            const int i2 = li + s2;
-                            if (i2 > lj) continue;
-                            const uint16_t hv = (uint16_t)((s2 < 2 ? lo : hi) >> ((s2 & 1) * 16));
-                            *reinterpret_cast<uint16_t *>(T + swz(lj, i2)) = hv;
-                            *reinterpret_cast<uint16_t *>(T + swz(i2, lj)) = hv;
-                        }
+                        Cm[(int64_t)gi * ldc + gi] = 0;
                     }
                 }
-                __builtin_amdgcn_sched_barrier(0);
+            }
+    }
+    const bool coalesced = !below && !cross;
+    // 2. transposed: T[lj][li], four consecutive rows per 8-byte write
+    if (coalesced) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int lj = j * 16 + col, li = i * 16 + quad * 4;
+                *reinterpret_cast<u32x2 *>(W + swz_t(lj, li)) =
+                    u32x2{pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3])};
             }
     }
     __syncthreads();
-    if (!below) {
-        // rows of T: X^T rows (full product), the mirror sub-block, or the
-        // symmetric diagonal sub-block itself
-        if (MODE == kGemmBX)
-            stage_out(T, args.CT + batch * args.ct_stride, args.ldct, C0, R0, lane);
-        else
-            stage_out(T, Cm, ldc, C0, R0, lane);
+    if (coalesced) {
+        uint16_t *dst = MODE == kGemmBX ? args.CT + batch * args.ct_stride : Cm;
+        const int64_t ld = MODE == kGemmBX ? (int64_t)args.ldct : ldc;
+#pragma unroll 4
+        for (int k = 0; k < 16; ++k) {
+            const int id = k * 64 + lane, i = id >> 4, c = id & 15;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(W + i * 256 + ((c ^ (i & 15)) << 4));
+            *reinterpret_cast<u32x4 *>(dst + (int64_t)(C0 + i) * ld + R0 + c * 8) = v;
+        }
     }
     __syncthreads();
-
-    // 3. row order for the sub-block itself (not needed on the diagonal)
-    const bool direct = !below && !diag;
-    if (direct) {
+    // 3. row order
+    if (coalesced) {
 #pragma unroll
-        for (int is = 0; is < 4; ++is)
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int js = 0; js < 4; ++js) {
-                const int lj = js * 32 + col;
+            for (int j = 0; j < 4; ++j) {
+                const int lj = j * 16 + col;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int li = is * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                    *reinterpret_cast<uint16_t *>(T + swz(li, lj)) = to_bf16(acc[is][js][r]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
+                for (int r = 0; r < 4; ++r)
+                    *reinterpret_cast<uint16_t *>(W + swz_r(i * 16 + quad * 4 + r, lj)) = to_bf16(acc[i][j][r]);
             }
     }
     __syncthreads();
-    if (direct) stage_out(T, Cm, ldc, R0, C0, lane);
+    if (coalesced) {
+#pragma unroll 4
+        for (int k = 0; k < 16; ++k) {
+            const int id = k * 64 + lane, i = id >> 3, c = id & 7;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(W + i * 128 + ((c ^ (i & 7)) << 4));
+            *reinterpret_cast<u32x4 *>(Cm + (int64_t)(R0 + i) * ldc + C0 + c * 8) = v;
+        }
+    }
 }
 
-// 256 x 256 tiles for the large shapes.  Four waves each own a 128 x 128
-// sub-tile (4 x 4 MFMA tiles, 256 fp32 accumulators per lane), so each
-// 16-byte operand fragment read from LDS feeds four MFMAs.  The K loop moves
-// 64 columns per stage through two 64 KB LDS stages.  LDS rows are 128 bytes
-// with no padding; the eight 16-byte chunks of row r are stored XOR-swizzled
-// (chunk c at position c ^ (r & 7)), so the 32 lanes of an operand read,
-// which take one chunk from each of 32 consecutive rows, spread over all
-// banks.  Global loads for stage k+2 are issued while stage k is multiplied.
 template <int MODE>
-__global__ __launch_bounds__(kThreads) void ns_gemm256_kernel(NsArgs args) {
-    constexpr int BM = 256, BN = 256, WTM = 128, WTN = 128, FM = 4, FN = 4;
-    constexpr int ROW_BYTES = kBK * 2;                  // 128
-    constexpr int OPER_BYTES = BM * ROW_BYTES;          // 32 KB per operand per stage
-    constexpr int LOADS = BM * (kBK / 8) / kThreads;    // 8 chunks per thread per operand
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][OPER_BYTES];
+__global__ __launch_bounds__(kWaves256 * 64) void ns_gemm256_kernel(NsArgs args) {
+    constexpr int BM = 256, WTM = 128, WTN = 64, FM = 8, FN = 4, ROW = 128;
+    constexpr int OPER = BM * ROW;            // 32 KB per operand per stage
+    constexpr int LOADS = 32 / kWaves256;      // kilobyte instructions per operand per wave
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2][OPER];
 
     const int batch = blockIdx.y;
     int ti, tj;
     tile_of<MODE>(args, ti, tj);
-    const int m0 = ti * BM, n0 = tj * BN;
-    const uint16_t *__restrict__ P = args.P + batch * args.p_stride + (int64_t)m0 * args.ldp;
-    const uint16_t *__restrict__ Q = args.Q + batch * args.q_stride + (int64_t)n0 * args.ldq;
+    const int m0 = ti * BM, n0 = tj * BM;
+    const uint16_t *P = args.P + batch * args.p_stride + (int64_t)m0 * args.ldp;
+    const uint16_t *Q = args.Q + batch * args.q_stride + (int64_t)n0 * args.ldq;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave >> 2, wc = wave & 3;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wr = wave >> 1, wc = wave & 1;
-
-    f32x16 acc[FM][FN];
+    f32x4 acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // chunk ch = tid + 256 q: tile row ch / 8, 16-byte chunk ch % 8 of the
-    // row's 64 K-columns; eight consecutive threads read one 128-byte row
-    u32x4 pr[LOADS], qr[LOADS];
-    int soff[LOADS];  // swizzled LDS byte offset of each chunk (same for P and Q)
-    const uint16_t *pg[LOADS], *qg[LOADS];
+    // global -> LDS: instruction q of this wave fills kilobyte block
+    // k = q * 8 + wave (rows 8k .. 8k+7); lane l takes row 8k + l / 8 and the
+    // global chunk that the swizzle places at slot l % 8
+    const int lrow = lane >> 3, lchunk = (lane & 7) ^ (lrow & 7);
+    const uint16_t *pl = P + (int64_t)lrow * args.ldp + lchunk * 8;
+    const uint16_t *ql = Q + (int64_t)lrow * args.ldq + lchunk * 8;
+    auto gload = [&](int st, int k0) {
 #pragma unroll
-    for (int q = 0; q < LOADS; ++q) {
-        const int ch = tid + q * kThreads, row = ch >> 3, c = ch & 7;
-        soff[q] = row * ROW_BYTES + ((c ^ (row & 7)) << 4);
-        pg[q] = P + (int64_t)row * args.ldp + c * 8;
-        qg[q] = Q + (int64_t)row * args.ldq + c * 8;
-    }
-    auto gload = [&](int k0) {
-#pragma unroll
-        for (int q = 0; q < LOADS; ++q) pr[q] = *reinterpret_cast<const u32x4 *>(pg[q] + k0);
-#pragma unroll
-        for (int q = 0; q < LOADS; ++q) qr[q] = *reinterpret_cast<const u32x4 *>(qg[q] + k0);
+        for (int q = 0; q < LOADS; ++q) {
+            const int k = q * kWaves256 + wave;
+            __builtin_amdgcn_global_load_lds((const void *)(pl + (int64_t)(8 * k) * args.ldp + k0),
+                                             LDS_ADDR(&lds[st][0][k * 1024]), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void *)(ql + (int64_t)(8 * k) * args.ldq + k0),
+                                             LDS_ADDR(&lds[st][1][k * 1024]), 16, 0, 0);
+        }
     };
-    auto lstore = [&](int st) {
-#pragma unroll
-        for (int q = 0; q < LOADS; ++q)
-            *reinterpret_cast<u32x4 *>(&lds[st][0][soff[q]]) = pr[q];
-#pragma unroll
-        for (int q = 0; q < LOADS; ++q)
-            *reinterpret_cast<u32x4 *>(&lds[st][1][soff[q]]) = qr[q];
-    };
-    // operand fragment: rows base + lane % 32, chunk 2 ks + lane / 32
-    const int fr = lane & 31, fh = lane >> 5;
+    // MFMA 16x16x32 operand: lane l holds row l % 16, K-chunk l / 16 of the
+    // 32-column sub-step (chunk 4 ks + l / 16 of the stage)
+    const int fr = lane & 15, fh = lane >> 4;
     auto frag = [&](int st, int op, int rowbase, int ks) {
-        const int r = rowbase + fr, c = 2 * ks + fh;
-        return *reinterpret_cast<const bf16x8 *>(&lds[st][op][r * ROW_BYTES + ((c ^ (r & 7)) << 4)]);
+        const int r = rowbase + fr, c = 4 * ks + fh;
+        return *reinterpret_cast<const bf16x8 *>(&lds[st][op][r * ROW + ((c ^ (r & 7)) << 4)]);
     };
 
     const int KT = args.K / kBK;
-    gload(0);
-    lstore(0);
-    if (KT > 1) gload(kBK);
+    gload(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int kt = 0; kt < KT; ++kt) {
         const int st = kt & 1;
+        if (kt + 1 < KT) gload(st ^ 1, (kt + 1) * kBK);
+        bf16x8 af[2][FM], bfr[2][FN];
 #pragma unroll
-        for (int ks = 0; ks < kBK / 16; ++ks) {
-            bf16x8 af[FM], bfr[FN];
+        for (int i = 0; i < FM; ++i) af[0][i] = frag(st, 0, wr * WTM + i * 16, 0);
 #pragma unroll
-            for (int i = 0; i < FM; ++i) af[i] = frag(st, 0, wr * WTM + i * 32, ks);
+        for (int j = 0; j < FN; ++j) bfr[0][j] = frag(st, 1, wc * WTN + j * 16, 0);
 #pragma unroll
-            for (int j = 0; j < FN; ++j) bfr[j] = frag(st, 1, wc * WTN + j * 32, ks);
+        for (int ks = 0; ks < 2; ++ks) {
+            const int cb = ks & 1, nb = cb ^ 1;
+            if (ks == 0) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i) af[nb][i] = frag(st, 0, wr * WTM + i * 16, 1);
+#pragma unroll
+                for (int j = 0; j < FN; ++j) bfr[nb][j] = frag(st, 1, wc * WTN + j * 16, 1);
+            }
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j],
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[cb][i], bfr[cb][j], acc[i][j],
                                                                         0, 0, 0);
+            __builtin_amdgcn_s_setprio(0);
+            if (ks == 0) {
+                // the next stage's global loads and the next sub-step's
+                // fragment reads, one after each MFMA
+#pragma unroll
+                for (int x = 0; x < 2 * LOADS; ++x) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                }
+#pragma unroll
+                for (int x = 0; x < FM + FN; ++x) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+            }
         }
-        if (kt + 1 < KT) {
-            lstore(st ^ 1);
-            if (kt + 2 < KT) gload((kt + 2) * kBK);
-        }
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
-    epilogue256<MODE>(args, acc, batch, m0, n0, wr, wc, lane, &lds[0][0][0]);
+    epilogue256<MODE>(args, acc, batch, m0, n0, wr, wc, wave, lane, &lds[0][0][0]);
 }
 
 template <int T, int MODE>
 void launch(dim3 grid, const NsArgs &a, hipStream_t stream) {
     if constexpr (T == 256)
-        hipLaunchKernelGGL((ns_gemm256_kernel<MODE>), grid, dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((ns_gemm256_kernel<MODE>), grid, dim3(kWaves256 * 64), 0, stream, a);
     else
         hipLaunchKernelGGL((ns_gemm_kernel<T, T, MODE>), grid, dim3(kThreads), 0, stream, a);
 }
