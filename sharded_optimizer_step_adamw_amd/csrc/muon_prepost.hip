@@ -117,6 +117,7 @@ struct ScaleArgs {
     int32_t tiles_c;        // tiles along the stored columns (padded)
     float mu, omm;
     int32_t nesterov;
+    int32_t vec;            // cols % 8 == 0 and every base 16-byte aligned
 };
 
 // Pass 2.  One workgroup per 64 x 64 tile of the padded stored-orientation
@@ -147,23 +148,42 @@ __global__ __launch_bounds__(kThreads) void muon_scale_kernel(
         const int lr = grp >> 3, lc = (grp & 7) * 8;
         const int r = tr * kTile + lr, c0 = tc * kTile + lc;
         uint32_t packed[4];
+        if (a.vec && r < a.rows && c0 + 8 <= a.cols) {
+            // the 8 columns are inside the matrix: 128-bit loads
+            const int64_t i = (int64_t)r * a.cols + c0;
+            const u32x4 gw = *reinterpret_cast<const u32x4 *>(grad + i);
+            const f32x4 m0 = *reinterpret_cast<const f32x4 *>(mom + i);
+            const f32x4 m1 = *reinterpret_cast<const f32x4 *>(mom + i + 4);
+            const float mv[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+            const uint32_t gb[4] = {gw.x, gw.y, gw.z, gw.w};
+            float xs[8];
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-            float x2[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int c = c0 + e + h;
-                float x = 0.0f;
-                if (r < a.rows && c < a.cols) {
-                    const int64_t i = (int64_t)r * a.cols + c;
-                    float g = bf16_bits_to_float(grad[i]);
-                    float m = mom[i];  // already updated by pass 1
-                    float u = a.nesterov ? pa.omm * g + pa.mu * m : m;
-                    x = u * s;
-                }
-                x2[h] = x;
+            for (int e = 0; e < 8; ++e) {
+                const float g = bf16_bits_to_float((gb[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
+                const float u = a.nesterov ? pa.omm * g + pa.mu * mv[e] : mv[e];
+                xs[e] = u * s;
             }
-            packed[e >> 1] = pack_bf16x2(x2[0], x2[1]);
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) packed[e >> 1] = pack_bf16x2(xs[e], xs[e + 1]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                float x2[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int c = c0 + e + h;
+                    float x = 0.0f;
+                    if (r < a.rows && c < a.cols) {
+                        const int64_t i = (int64_t)r * a.cols + c;
+                        float g = bf16_bits_to_float(grad[i]);
+                        float m = mom[i];  // already updated by pass 1
+                        float u = a.nesterov ? pa.omm * g + pa.mu * m : m;
+                        x = u * s;
+                    }
+                    x2[h] = x;
+                }
+                packed[e >> 1] = pack_bf16x2(x2[0], x2[1]);
+            }
         }
         *reinterpret_cast<u32x4 *>(direct + (int64_t)r * ld_direct + c0) =
             u32x4{packed[0], packed[1], packed[2], packed[3]};
@@ -260,7 +280,8 @@ hipError_t launch_muon_pre(const MuonGeom &g, const MuonPtrs &ptrs, float mu,
     // stored-orientation padded extent
     const int srows = g.transposed ? g.np : g.mp;
     const int scols = g.transposed ? g.mp : g.np;
-    ScaleArgs sa{g.rows, g.cols, g.transposed, g.mp, g.np, scols / kTile, mu, omm, nesterov};
+    ScaleArgs sa{g.rows, g.cols, g.transposed, g.mp, g.np, scols / kTile, mu, omm, nesterov,
+                 (vec && g.cols % 8 == 0) ? 1 : 0};
     const int tiles = (srows / kTile) * (scols / kTile);
     hipLaunchKernelGGL(muon_scale_kernel, dim3(tiles, g.batch), dim3(kThreads), 0, stream,
                        ptrs, sa, scale, reinterpret_cast<uint16_t *>(ws + L.x),
