@@ -37,6 +37,27 @@ import time
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
 METRIC = "AdamW shard GB/s (%HBM peak); Muon NS TFLOP/s (%MFMA); optimizer step ms"
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+# HBM bytes per launch from two calibrated rocprofv3 counter passes (FETCH_SIZE,
+# WRITE_SIZE; scaled by what they read for a zopt_round_bf16 pass of known size),
+# recorded in profiles/.  Reported only while the kernel source is the one the
+# counters were taken on.
+MEASURED_TRAFFIC = {
+    "adamw_shard": dict(source="sharded_optimizer_step_adamw_amd/csrc/adamw_shard.hip",
+                        sha256="91fa9988f8538e94ab207b13fbde0560e678592907a2579947068ccfff6be1a8",
+                        bytes_per_launch=7.000e9,
+                        profile="profiles/adamw_shard_kernel_zero2_2b_rank3.md"),
+}
+
+
+def measured_traffic(key):
+    import hashlib
+    t = MEASURED_TRAFFIC[key]
+    with open(os.path.join(ROOT, t["source"]), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != t["sha256"]:
+            return None
+    return t["bytes_per_launch"]
 
 
 def parse():
@@ -45,7 +66,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--parts", default="step,adamw,ns",
-                    help="comma list of: step (headline), adamw, ns")
+                    help="comma list of: step (headline), adamw, ns, copy (a zopt_round_bf16 "
+                         "pass of known size: the calibration for HBM byte counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
 
@@ -198,9 +220,14 @@ def bench_adamw(torch, z, timer, dev, K, W):
     del s
     torch.cuda.empty_cache()
     gbs = 28 * sl / ms / 1e6
+    roof = dict(kernel="adamw_shard_kernel (one launch per step)", bound="hbm",
+                achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(gbs / HBM_PEAK_GBS, 4), traffic=measured_traffic("adamw_shard"),
+                algorithmic_bytes_per_launch=28 * sl, avg_launch_ms=round(ms, 4))
     return dict(workload="zero2 flat AdamW shard: N=2.0e9, bucket 1<<25, world 8, rank 3",
                 shard_len=sl, algorithmic_bytes_per_step=28 * sl, ms_per_step=round(ms, 4),
-                gbs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4), steps=K)
+                gbs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4), steps=K,
+                roofline=roof)
 
 
 def bench_ns(torch, z, timer, dev, K, W):
@@ -227,6 +254,20 @@ def bench_ns(torch, z, timer, dev, K, W):
                 muon_ms_per_step=round(call_ms, 3), ns_tflops=round(tf, 1),
                 mfma_frac=round(tf / BF16_PEAK_TFLOPS, 4),
                 muon_step_tflops=round(total_flops / call_ms / 1e9, 1), groups=rows, steps=K)
+
+
+def bench_copy(torch, z, timer, dev, K, W):
+    """zopt_round_bf16 over 2.5e8 fp32 values: 1.0e9 bytes read, 0.5e9 written
+    per launch, the reference for scaling FETCH_SIZE / WRITE_SIZE counters."""
+    n = 250_000_000
+    src = torch.randn(n, device=dev)
+    dst = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    timer.run(lambda _: z.round_bf16(src, dst), W)
+    ms = timer.run(lambda _: z.round_bf16(src, dst), K)
+    del src, dst
+    torch.cuda.empty_cache()
+    return dict(elements=n, bytes_read=4 * n, bytes_written=2 * n, ms=round(ms, 4),
+                gbs=round(6 * n / ms / 1e6, 1))
 
 
 def cpu_baseline():
@@ -297,6 +338,7 @@ def main():
     res_step = bench_step(torch, z, timer, dev, K, W) if "step" in parts else None
     res_adamw = bench_adamw(torch, z, timer, dev, max(K, 100), W) if "adamw" in parts else None
     res_ns = bench_ns(torch, z, timer, dev, max(2, K // 5), W) if "ns" in parts else None
+    res_copy = bench_copy(torch, z, timer, dev, K, W) if "copy" in parts else None
     if res_step:
         tf = res_step["ns_iter_flops"] / res_step["ns_iter_ms"] / 1e9
         out.update(value=round(res_step["ms"], 4), unit="ms per optimizer step")
@@ -326,8 +368,12 @@ def main():
         out["adamw_shard"] = res_adamw
     if res_ns:
         out["newton_schulz"] = res_ns
+    if res_copy:
+        out["round_bf16_calibration"] = res_copy
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline()
-    out["device"] = torch.cuda.get_device_name(0)
+    props = torch.cuda.get_device_properties(0)
+    out["device"] = f"{torch.cuda.get_device_name(0)} ({getattr(props, 'gcnArchName', '?')}, " \
+                    f"{props.multi_processor_count} CUs)"
     print(json.dumps(out), flush=True)
 
 
