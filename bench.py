@@ -7,8 +7,8 @@ Prints ONE JSON line.  The headline workload ("step") is a GPT-2-small-shaped
 full optimizer step at world 1: AdamW on the tied 50304 x 768 embedding
 (weight decay 0.1) and 25 vectors of 768 (no decay) as two
 zopt_adamw_shard_step calls, and Muon on 12 layers x {Wq, Wk, Wv, Wo 768^2;
-fc 3072 x 768; proj 768 x 3072} as three batched zopt_muon_step calls;
-`value` is its time in ms per step.  Two sub-objects report the other two
+fc 3072 x 768; proj 768 x 3072} as one zopt_muon_step_groups call over the
+three same-shape groups; `value` is its time in ms per step.  Two sub-objects report the other two
 parts of the metric on their own workloads:
 
   adamw_shard     the ZeRO-2 flat AdamW shard of rank 3 of 8 over a
@@ -128,7 +128,6 @@ def muon_groups(torch, w, dev):
     import workloads as wl
     import sharded_optimizer_step_adamw_amd as z
     groups = []
-    ws_bytes = 0
     for gi, grp in enumerate(w.groups):
         shape = (grp.rows, grp.cols)
         groups.append(dict(
@@ -140,21 +139,23 @@ def muon_groups(torch, w, dev):
                                       w.grad_dist) for i in range(grp.count)],
             weight=[torch.empty(shape, dtype=torch.bfloat16, device=dev)
                     for _ in range(grp.count)]))
-        ws_bytes = max(ws_bytes, z.muon_workspace_bytes(grp.count, grp.rows, grp.cols))
+    ws_bytes = z.muon_groups_workspace_bytes([(g["count"], g["rows"], g["cols"]) for g in groups])
     workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     return groups, workspace
 
 
-def muon_call(z, w, g, workspace, ns_steps):
-    z.muon_step(g["master"], g["momentum"], g["grad"], g["weight"], w.lr, w.momentum,
-                w.nesterov, w.weight_decay, ns_steps, w.ns_coeffs, w.ns_eps, w.adjust_lr,
-                workspace=workspace)
+def muon_call(z, w, groups, workspace, ns_steps):
+    """All groups of a workload in one zopt_muon_step_groups call."""
+    z.muon_step_groups([(g["master"], g["momentum"], g["grad"], g["weight"]) for g in groups],
+                       w.lr, w.momentum, w.nesterov, w.weight_decay, ns_steps, w.ns_coeffs,
+                       w.ns_eps, w.adjust_lr, workspace=workspace)
 
 
 # ------------------------------------------------------------------ parts
 
 def bench_step(torch, z, timer, dev, K, W):
-    """The headline: one GPT-2-small optimizer step (2 AdamW + 3 Muon calls)."""
+    """The headline: one GPT-2-small optimizer step (2 AdamW calls + 1 Muon call
+    over three groups)."""
     import workloads as wl
     wa, wm = wl.GPT2_ADAMW, wl.GPT2_MUON
     a = make_adamw(torch, wa, dev)
@@ -171,27 +172,22 @@ def bench_step(torch, z, timer, dev, K, W):
             z.adamw_shard_step(a["master"][s], a["m"][s], a["v"][s], a["grads"][0][s],
                                a["weight"][s], part.n, part.bucket, part.world, part.rank,
                                part.lr, part.beta1, part.beta2, part.eps, part.weight_decay, t)
-        for g in groups:
-            muon_call(z, wm, g, workspace, wm.ns_steps)
+        muon_call(z, wm, groups, workspace, wm.ns_steps)
 
     timer.run(step, W)
     ms = timer.run(step, K)
 
-    # the dominant kernels: one Newton-Schulz iteration of each group is three
-    # launches (X X^T, A A with its epilogue, B X with its epilogue); its time
-    # is the difference of a Muon call with 5 and with 0 iterations, over 5
-    iter_ms, iter_flops, per_group = 0.0, 0, []
-    for g in groups:
-        t5 = timer.run(lambda _: muon_call(z, wm, g, workspace, 5), K)
-        t0 = timer.run(lambda _: muon_call(z, wm, g, workspace, 0), K)
-        mm, nn = min(g["rows"], g["cols"]), max(g["rows"], g["cols"])
-        fl = g["count"] * ns_flops(mm, nn, 1)
-        per_group.append(dict(shape=[g["rows"], g["cols"]], count=g["count"],
-                              muon_call_ms=round(t5, 4), pre_post_ms=round(t0, 4),
-                              ns_iter_ms=round((t5 - t0) / 5, 4),
-                              ns_tflops=round(fl / ((t5 - t0) / 5) / 1e9, 1)))
-        iter_ms += (t5 - t0) / 5
-        iter_flops += fl
+    # the dominant kernels: one Newton-Schulz iteration of all 72 matrices is
+    # three launches (X X^T, A A with its epilogue, B X with its epilogue, each
+    # over every group); its time is the difference of the Muon call with 5
+    # and with 0 iterations, over 5
+    t5 = timer.run(lambda _: muon_call(z, wm, groups, workspace, 5), K)
+    t0 = timer.run(lambda _: muon_call(z, wm, groups, workspace, 0), K)
+    iter_ms = (t5 - t0) / 5
+    iter_flops = sum(g["count"] * ns_flops(min(g["rows"], g["cols"]), max(g["rows"], g["cols"]), 1)
+                     for g in groups)
+    per_group = dict(muon_call_ms=round(t5, 4), pre_post_ms=round(t0, 4),
+                     groups=[dict(shape=[g["rows"], g["cols"]], count=g["count"]) for g in groups])
     adamw_bytes = 28 * n
     ta = timer.run(lambda i: [z.adamw_shard_step(
         a["master"][p.offset:p.offset + p.n], a["m"][p.offset:p.offset + p.n],
@@ -200,7 +196,7 @@ def bench_step(torch, z, timer, dev, K, W):
         p.beta2, p.eps, p.weight_decay, 1000 + i) for p in wa.parts], K)
     del a, groups, workspace
     torch.cuda.empty_cache()
-    return dict(ms=ms, ns_iter_ms=iter_ms, ns_iter_flops=iter_flops, groups=per_group,
+    return dict(ms=ms, ns_iter_ms=iter_ms, ns_iter_flops=iter_flops, muon=per_group,
                 adamw_ms=ta, adamw_gbs=adamw_bytes / ta / 1e6)
 
 
@@ -234,18 +230,13 @@ def bench_ns(torch, z, timer, dev, K, W):
     import workloads as wl
     w = wl.LLAMA8B_MUON
     groups, workspace = muon_groups(torch, w, dev)
-    total_flops, ns_ms, call_ms, rows = 0, 0.0, 0.0, []
-    for g in groups:
-        mm, nn = min(g["rows"], g["cols"]), max(g["rows"], g["cols"])
-        fl = g["count"] * ns_flops(mm, nn, w.ns_steps)
-        timer.run(lambda _: muon_call(z, w, g, workspace, w.ns_steps), max(1, W))
-        t5 = timer.run(lambda _: muon_call(z, w, g, workspace, w.ns_steps), K)
-        t0 = timer.run(lambda _: muon_call(z, w, g, workspace, 0), K)
-        total_flops += fl
-        ns_ms += t5 - t0
-        call_ms += t5
-        rows.append(dict(shape=[g["rows"], g["cols"]], count=g["count"], muon_call_ms=round(t5, 3),
-                         ns_ms=round(t5 - t0, 3), ns_tflops=round(fl / (t5 - t0) / 1e9, 1)))
+    total_flops = sum(g["count"] * ns_flops(min(g["rows"], g["cols"]), max(g["rows"], g["cols"]),
+                                            w.ns_steps) for g in groups)
+    timer.run(lambda _: muon_call(z, w, groups, workspace, w.ns_steps), max(1, W))
+    t5 = timer.run(lambda _: muon_call(z, w, groups, workspace, w.ns_steps), K)
+    t0 = timer.run(lambda _: muon_call(z, w, groups, workspace, 0), K)
+    ns_ms, call_ms = t5 - t0, t5
+    rows = [dict(shape=[g["rows"], g["cols"]], count=g["count"]) for g in groups]
     del groups, workspace
     torch.cuda.empty_cache()
     tf = total_flops / ns_ms / 1e9
@@ -343,8 +334,8 @@ def main():
         tf = res_step["ns_iter_flops"] / res_step["ns_iter_ms"] / 1e9
         out.update(value=round(res_step["ms"], 4), unit="ms per optimizer step")
         roof = dict(
-            kernel=("Newton-Schulz iteration: ns_gemm_kernel X X^T + A A + B X "
-                    "(3 launches per same-shape group), summed over the step's 3 groups"),
+            kernel=("Newton-Schulz iteration: ns_gemm_kernel X X^T + A A + B X, three "
+                    "launches each covering all 72 matrices (3 groups, 128 x 128 tiles)"),
             bound="mfma", achieved=round(tf, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
             frac=round(tf / BF16_PEAK_TFLOPS, 4), traffic=None,
             algorithmic_flops_per_unit=res_step["ns_iter_flops"],
@@ -356,14 +347,14 @@ def main():
                vs_baseline=None, dtype="fp32+bf16", data="synthetic",
                config=dict(workload=("gpt2-small optimizer step, world 1: AdamW on 50304x768 "
                                      "embedding + 25x768 vectors (2 calls), Muon on 12 layers "
-                                     "x {4x768x768, 3072x768, 768x3072} (3 batched calls), "
+                                     "x {4x768x768, 3072x768, 768x3072} (1 call, 3 groups), "
                                      "5 bf16 Newton-Schulz iterations"),
                            adamw_elements=38_652_672, muon_matrices=72),
                roofline=roof)
     if res_step:
         out["step_detail"] = dict(adamw_ms=round(res_step["adamw_ms"], 4),
                                   adamw_gbs=round(res_step["adamw_gbs"], 1),
-                                  muon_groups=res_step["groups"])
+                                  muon=res_step["muon"])
     if res_adamw:
         out["adamw_shard"] = res_adamw
     if res_ns:

@@ -10,7 +10,8 @@
  *    master and both fp32 moments, and writes the bf16 compute weights;
  *  - zopt_muon_step: Muon on whole 2-D matrices the rank owns (momentum with
  *    Nesterov look-ahead, Newton-Schulz orthogonalisation on bf16 matrix
- *    cores, a decayed and scaled update of the fp32 master);
+ *    cores, a decayed and scaled update of the fp32 master), and
+ *    zopt_muon_step_groups, the same on several shapes in one call;
  *  - zopt_round_bf16: the fp32 -> bf16 round-to-nearest-even write-back on
  *    its own.
  *
@@ -214,6 +215,55 @@ zopt_status zopt_muon_output_view(int32_t batch, int64_t rows, int64_t cols,
                                   int32_t ns_steps, const void *workspace,
                                   int32_t index, const uint16_t **out,
                                   int64_t *row_stride);
+
+/*
+ * zopt_muon_step_groups -- zopt_muon_step on `ngroups` groups of matrices in
+ * one call.  A rank's Muon parameters fall into a few stored shapes, and
+ * launch count is what limits a per-shape loop of small steps [dmuon PR #16,
+ * commit "NS CUDA-graph replay": one rank steps tens of Muon matrices of a
+ * small, stable set of shapes, and the launches issued per step dominated its
+ * host time].  Here every Newton-Schulz product of every group whose short
+ * side selects the same output tile is one launch, so small groups share the
+ * GPU instead of running one after another.  Each matrix gets exactly the
+ * arithmetic zopt_muon_step gives it; the call equals ngroups separate
+ * zopt_muon_step calls, except that the groups' Newton-Schulz products
+ * interleave in time.
+ *
+ * Arguments
+ *   ngroups      1 .. 16.
+ *   batch, rows, cols   host arrays of `ngroups` entries; group g has
+ *                batch[g] (1 .. 64) matrices of stored shape
+ *                [rows[g], cols[g]] with the limits of zopt_muon_step.
+ *   master, momentum, grad, weight   host arrays of sum(batch) device
+ *                pointers, group 0's matrices first, then group 1's, ...;
+ *                weight may be NULL (no write-back for any group).
+ *   lr ... stream      as for zopt_muon_step, shared by all groups.
+ *   workspace    as for zopt_muon_step; the NULL-workspace query returns the
+ *                size for all groups together (the sum of the per-group sizes).
+ *
+ * Errors: those of zopt_muon_step; ZOPT_ERR_NULL also if batch, rows or cols
+ * is NULL, ZOPT_ERR_SIZE if ngroups is out of range.
+ */
+zopt_status zopt_muon_step_groups(int32_t ngroups, const int32_t *batch, const int64_t *rows,
+                                  const int64_t *cols, float *const *master,
+                                  float *const *momentum, const uint16_t *const *grad,
+                                  uint16_t *const *weight, float lr, float momentum_beta,
+                                  int32_t nesterov, float weight_decay, int32_t ns_steps,
+                                  float ns_a, float ns_b, float ns_c, float ns_eps,
+                                  int32_t adjust_lr, void *workspace, size_t *workspace_bytes,
+                                  void *stream);
+
+/*
+ * zopt_muon_groups_output_view -- zopt_muon_output_view for matrix `index` of
+ * group `group` of a workspace that zopt_muon_step_groups(ngroups, batch,
+ * rows, cols, ..., ns_steps, ...) has filled.  Host-only.  Errors as
+ * zopt_muon_output_view; ZOPT_ERR_SIZE also for `group` out of range.
+ */
+zopt_status zopt_muon_groups_output_view(int32_t ngroups, const int32_t *batch,
+                                         const int64_t *rows, const int64_t *cols,
+                                         int32_t ns_steps, const void *workspace, int32_t group,
+                                         int32_t index, const uint16_t **out,
+                                         int64_t *row_stride);
 
 /*
  * zopt_round_bf16 -- dst[i] = bf16(src[i]) for i in [0, n), round to

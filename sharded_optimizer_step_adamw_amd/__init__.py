@@ -12,6 +12,8 @@ Entry points (same names as the C ABI in include/zopt.h):
   adamw_shard_step   fused AdamW over a flat bucketed fp32 shard
   muon_step          Muon on a batch of same-shape matrices
   muon_workspace_bytes / muon_output_view
+  muon_step_groups   Muon on several such batches in one call (shared launches)
+  muon_groups_workspace_bytes / muon_groups_output_view
   round_bf16         fp32 -> bf16 round-to-nearest-even
   shard_len          the shard length the layout derives (zopt_shard_len)
 """
@@ -28,6 +30,7 @@ LIB_PATH = os.path.join(_HERE, "libzopt.so")
 
 ZOPT_OK, ZOPT_ERR_NULL, ZOPT_ERR_SIZE, ZOPT_ERR_HYPER, ZOPT_ERR_WORKSPACE, ZOPT_ERR_DEVICE = range(6)
 MAX_BATCH = 64
+MAX_GROUPS = 16
 
 
 class ZoptError(RuntimeError):
@@ -66,6 +69,14 @@ def _lib_or_raise() -> ctypes.CDLL:
         L.zopt_muon_output_view.argtypes = [i32, i64, i64, i32, vp, i32, pp,
                                             ctypes.POINTER(i64)]
         L.zopt_muon_output_view.restype = ctypes.c_int
+        pi32, pi64 = ctypes.POINTER(i32), ctypes.POINTER(i64)
+        L.zopt_muon_step_groups.argtypes = [i32, pi32, pi64, pi64, pp, pp, pp, pp, f32, f32, i32,
+                                            f32, i32, f32, f32, f32, f32, i32, vp,
+                                            ctypes.POINTER(ctypes.c_size_t), vp]
+        L.zopt_muon_step_groups.restype = ctypes.c_int
+        L.zopt_muon_groups_output_view.argtypes = [i32, pi32, pi64, pi64, i32, vp, i32, i32, pp,
+                                                   pi64]
+        L.zopt_muon_groups_output_view.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -209,5 +220,95 @@ def muon_output_view(workspace: torch.Tensor, batch: int, rows: int, cols: int,
     return flat.as_strided((rows, cols), (ld.value, 1), off // 2)
 
 
+def _shape_arrays(shapes):
+    n = len(shapes)
+    if not (1 <= n <= MAX_GROUPS):
+        raise ValueError(f"need 1..{MAX_GROUPS} groups, got {n}")
+    b = (ctypes.c_int32 * n)(*[int(x[0]) for x in shapes])
+    r = (ctypes.c_int64 * n)(*[int(x[1]) for x in shapes])
+    c = (ctypes.c_int64 * n)(*[int(x[2]) for x in shapes])
+    return n, b, r, c
+
+
+def muon_groups_workspace_bytes(shapes: Sequence[tuple]) -> int:
+    """Workspace bytes of a zopt_muon_step_groups call over groups given as
+    (batch, rows, cols)."""
+    n, b, r, c = _shape_arrays(shapes)
+    size = ctypes.c_size_t(0)
+    st = lib().zopt_muon_step_groups(n, b, r, c, None, None, None, None, 0.0, 0.0, 0, 0.0, 0,
+                                     0.0, 0.0, 0.0, 0.0, 0, None, ctypes.byref(size), None)
+    _check(st, "zopt_muon_step_groups(workspace query)")
+    return int(size.value)
+
+
+def muon_step_groups(groups: Sequence[tuple], lr: float, momentum_beta: float = 0.95,
+                     nesterov: bool = True, weight_decay: float = 0.1, ns_steps: int = 5,
+                     ns_coeffs=(3.4445, -4.7750, 2.0315), ns_eps: float = 1e-7,
+                     adjust_lr: int = 1, workspace: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """One Muon step on several groups of same-shape matrices in one call
+    (zopt_muon_step_groups).  Each group is (master, momentum, grad, weight)
+    with lists of equal length; weight may be None for every group or for
+    none.  Returns the workspace (see muon_groups_output_view)."""
+    if not groups:
+        raise ValueError("muon_step_groups: no groups")
+    with_w = groups[0][3] is not None
+    shapes, M, Mo, G, W = [], [], [], [], []
+    dev = groups[0][0][0].device
+    for gi, (master, momentum, grad, weight) in enumerate(groups):
+        batch = len(master)
+        if not (1 <= batch <= MAX_BATCH) or len(momentum) != batch or len(grad) != batch:
+            raise ValueError(f"group {gi}: need 1..64 matrices and equal-length lists")
+        if (weight is not None) != with_w or (weight is not None and len(weight) != batch):
+            raise ValueError(f"group {gi}: weight lists must be given for all groups or none")
+        rows, cols = master[0].shape
+        for i in range(batch):
+            for t, dt, nm in ((master[i], torch.float32, "master"),
+                              (momentum[i], torch.float32, "momentum"),
+                              (grad[i], torch.bfloat16, "grad")) + (
+                    ((weight[i], torch.bfloat16, "weight"),) if weight is not None else ()):
+                _need(t, dt, rows * cols, f"group {gi} {nm}[{i}]", dev)
+                if tuple(t.shape) != (rows, cols):
+                    raise ValueError(f"group {gi} {nm}[{i}]: shape {tuple(t.shape)}, "
+                                     f"need {(rows, cols)}")
+        shapes.append((batch, rows, cols))
+        M += list(master)
+        Mo += list(momentum)
+        G += list(grad)
+        if with_w:
+            W += list(weight)
+    need = muon_groups_workspace_bytes(shapes)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _need(workspace, torch.uint8, need, "workspace", dev)
+    n, b, r, c = _shape_arrays(shapes)
+    size = ctypes.c_size_t(workspace.numel())
+    ca, cb, cc = (float(x) for x in ns_coeffs)
+    st = lib().zopt_muon_step_groups(
+        n, b, r, c, _ptr_array(M), _ptr_array(Mo), _ptr_array(G),
+        _ptr_array(W) if with_w else None, lr, momentum_beta, int(nesterov), weight_decay,
+        ns_steps, ca, cb, cc, ns_eps, adjust_lr, workspace.data_ptr(), ctypes.byref(size),
+        _stream(dev, stream))
+    _check(st, "zopt_muon_step_groups")
+    return workspace
+
+
+def muon_groups_output_view(workspace: torch.Tensor, shapes: Sequence[tuple], ns_steps: int,
+                            group: int, index: int) -> torch.Tensor:
+    """The bf16 [rows, cols] orthogonalised update of matrix `index` of group
+    `group` inside a workspace filled by muon_step_groups (a strided view)."""
+    n, b, r, c = _shape_arrays(shapes)
+    out = ctypes.c_void_p(0)
+    ld = ctypes.c_int64(0)
+    st = lib().zopt_muon_groups_output_view(n, b, r, c, ns_steps, workspace.data_ptr(), group,
+                                            index, ctypes.byref(out), ctypes.byref(ld))
+    _check(st, "zopt_muon_groups_output_view")
+    off = out.value - workspace.data_ptr()
+    assert off % 2 == 0 and off >= 0
+    rows, cols = int(shapes[group][1]), int(shapes[group][2])
+    return workspace.view(torch.bfloat16).as_strided((rows, cols), (ld.value, 1), off // 2)
+
+
 __all__ = ["adamw_shard_step", "muon_step", "muon_workspace_bytes", "muon_output_view",
-           "round_bf16", "shard_len", "lib", "ZoptError", "LIB_PATH", "MAX_BATCH"]
+           "muon_step_groups", "muon_groups_workspace_bytes", "muon_groups_output_view",
+           "round_bf16", "shard_len", "lib", "ZoptError", "LIB_PATH", "MAX_BATCH", "MAX_GROUPS"]

@@ -25,92 +25,123 @@
 // Only the rounding points move; on every shape tried this lowers the error
 // against float64 by 1.5-4x (bf16 emulation).
 //
-// The transposed copy
-// X'^T written by the third product is the Q operand of the next iteration's
-// third product (dmuon PR #16 prior art ran X X^T as a separate SYRK kernel;
-// here all three products share one kernel template).
+// The transposed copy X'^T written by the third product is the Q operand of
+// the next iteration's third product (dmuon PR #16 prior art ran X X^T as a
+// separate SYRK kernel; here all three products share one kernel template).
+//
+// Grouped launches.  One launch computes one product for every matrix of up
+// to kMaxGroups same-tile groups (e.g. all of a model's Muon matrices whose
+// short side selects the same tile), so that small groups fill the GPU
+// together and the launch count per iteration stays at three per tile size.
+// Workgroups are numbered group by group (longest reduction first), matrix by
+// matrix, tile by tile.
 #include "zopt_internal.h"
 
 namespace zopt {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBK = 64;
-
 enum Mode : int { kSyrkXXT = 0, kSyrkAA = 1, kGemmBX = 2 };
 
-struct NsArgs {
-    const uint16_t *P;   // left operand rows (M x K)
-    const uint16_t *Q;   // right operand rows (N x K)
-    int64_t p_stride, q_stride;  // elements between batch entries
-    int32_t ldp, ldq, K;
+// One group of same-shape matrices in a launch.
+struct NsGroup {
+    const uint16_t *P;           // left operand rows (M x K)
+    const uint16_t *Q;           // right operand rows (N x K)
+    int64_t p_stride, q_stride;  // elements between matrices of the group
+    int32_t ld, K;               // operand row stride (both operands), reduction length
     int32_t tiles_m, tiles_n;    // tile grid (SYRK: tiles_m == tiles_n)
+    int32_t tiles_pm, tile0;     // tiles per matrix; first workgroup of the group
+    int32_t tiles, padded;       // tiles of the group, rounded up to a multiple of 8
+    int32_t round_tiles;         // tiles resident at once on the GPU (8 XCDs), a multiple of 8
+    int32_t ldc, ldct;
     uint16_t *C;                 // A or B (SYRK) / X, updated in place (GEMM)
     int64_t c_stride;
-    int32_t ldc;
     const uint16_t *E;           // SYRK_AA: Aoff (for b*A); unused otherwise
-    float *dIn;                  // SYRK_AA: dA; GEMM_BX: dB
+    const float *dIn;            // SYRK_AA: dA; GEMM_BX: dB
     float *dOut;                 // SYRK_XXT: dA; SYRK_AA: dB
-    int64_t d_stride;            // floats between batch entries of dA / dB
+    int64_t d_stride;            // floats between matrices of dA / dB
     uint16_t *CT;                // GEMM_BX: X'^T
     int64_t ct_stride;
-    int32_t ldct;
+};
+
+struct NsLaunch {
+    NsGroup g[kMaxGroups];
+    int32_t ngroups;
     float a, b, c;
 };
 
 __device__ __forceinline__ uint16_t to_bf16(float x) { return (uint16_t)rne_bf16_bits(x); }
 __device__ __forceinline__ float from_bf16(uint16_t h) { return bf16_bits_to_float(h); }
 
-// The tile of this workgroup: row-major over the tile grid for the full
-// product, and over the upper triangle (ti <= tj) for the symmetric ones.
+// Tile t of a matrix, in bands of kBand tile rows taken column by column, so
+// that the tiles an XCD runs at the same time share few operand row panels
+// (kBand rows of P and the columns' rows of Q).  The full product walks the
+// whole grid; the symmetric ones walk only tiles on or above the diagonal
+// (ti <= tj), each band starting at its own diagonal.
+constexpr int kBand = 4;
 template <int MODE>
-__device__ __forceinline__ void tile_of(const NsArgs &args, int &ti, int &tj) {
+__device__ __forceinline__ void tile_coords(const NsGroup &G, int t, int &ti, int &tj) {
+    const int tm = G.tiles_m;
+    int b0 = 0;
     if (MODE == kGemmBX) {
-        ti = blockIdx.x / args.tiles_n;
-        tj = blockIdx.x % args.tiles_n;
-    } else {
-        int t = blockIdx.x;
-        ti = 0;
-        while (t >= args.tiles_m - ti) {
-            t -= args.tiles_m - ti;
-            ++ti;
+        const int tn = G.tiles_n;
+        for (;;) {
+            const int h = tm - b0 < kBand ? tm - b0 : kBand;
+            if (t < h * tn) {
+                tj = t / h;
+                ti = b0 + t % h;
+                return;
+            }
+            t -= h * tn;
+            b0 += kBand;
         }
-        tj = ti + t;
+    }
+    for (;;) {
+        const int h = tm - b0 < kBand ? tm - b0 : kBand;
+        // band rows b0 .. b0+h-1, columns b0 .. tm-1; column c holds rows
+        // b0 .. min(c, b0+h-1): a triangle of h(h+1)/2 then full columns
+        const int tri = h * (h + 1) / 2, size = tri + h * (tm - b0 - h);
+        if (t < size) {
+            if (t < tri) {
+                int c = 0;
+                while (t > c) {
+                    t -= c + 1;
+                    ++c;
+                }
+                tj = b0 + c;
+                ti = b0 + t;
+            } else {
+                t -= tri;
+                tj = b0 + h + t / h;
+                ti = b0 + t % h;
+            }
+            return;
+        }
+        t -= size;
+        b0 += kBand;
     }
 }
 
 // ----------------------------------------------------------------------------
-// The kernel.  A BM x BM output tile per workgroup of WR x WC waves; each wave
+// Tiles.  A BM x BM output tile per workgroup of WR x WC waves; each wave
 // owns a (BM/WR) x (BM/WC) sub-tile built from MFMA 16x16x32 bf16 blocks
 // with fp32 accumulators:
 //   BM = 256: 8 waves (two per SIMD) of 128 x 64 -- the large shapes
 //   BM = 128: 4 waves of 64 x 64 (two workgroups per CU)
-//   BM =  64: 4 waves of 32 x 32
-// K advances 64 columns per stage through two LDS stages of 2 x BM x 128
-// bytes.  Operands go from global memory straight to LDS (global_load_lds,
-// 16 bytes per lane, each wave instruction filling one contiguous kilobyte =
-// 8 rows of 64 K-columns); a lane fetches the chunk that the XOR swizzle
-// (chunk c of row r at position c ^ (r & 7)) puts at its LDS slot, so
-// fragment reads of 16 consecutive rows spread over the banks without
-// padding.  Within a stage the next stage's global loads and the next
-// 32-column sub-step's fragment reads are interleaved with the MFMAs, and the
-// MFMA clusters run at raised wave priority so that waves sharing a SIMD
-// overlap memory work with matrix work.
-#define LDS_ADDR(p) ((__attribute__((address_space(3))) void *)(p))
-
+//   BM =  64: 4 waves of 32 x 32 (four workgroups per CU)
+// WPE is the waves per SIMD that residency needs, which caps the registers.
 template <int BM>
 struct Cfg;
 template <>
-struct Cfg<256> { static constexpr int WR = 2, WC = 4; };
+struct Cfg<256> { static constexpr int WR = 2, WC = 4, WPE = 2; };
 template <>
-struct Cfg<128> { static constexpr int WR = 2, WC = 2; };
+struct Cfg<128> { static constexpr int WR = 2, WC = 2, WPE = 2; };
 template <>
-struct Cfg<64> { static constexpr int WR = 2, WC = 2; };
+struct Cfg<64> { static constexpr int WR = 2, WC = 2, WPE = 4; };
 
 // Swizzled byte offset of element (i, j) in an LDS block whose rows hold
 // `chunks` 16-byte chunks (chunks is a power of two).
@@ -130,8 +161,9 @@ __device__ __forceinline__ int swz(int i, int j) {
 // diagonal goes to the fp32 vector (its bf16 entry is 0).  Every wave passes
 // the same barriers.
 template <int MODE, int FM, int FN>
-__device__ __forceinline__ void epilogue(const NsArgs &args, f32x4 (&acc)[FM][FN], int batch,
-                                         int R0, int C0, int wave, int lane, uint8_t *lds_all) {
+__device__ __forceinline__ void epilogue(const NsGroup &args, float ca, float cb, float cc,
+                                         f32x4 (&acc)[FM][FN], int batch, int R0, int C0, int wave,
+                                         int lane, uint8_t *lds_all) {
     constexpr int SR = FM * 16, SC = FN * 16;      // sub-block rows, columns
     constexpr int RCH = SC / 8, TCH = SR / 8;      // chunks per row: row order, transposed
     uint8_t *W = lds_all + wave * (SR * SC * 2);
@@ -171,11 +203,11 @@ __device__ __forceinline__ void epilogue(const NsArgs &args, f32x4 (&acc)[FM][FN
                     const float v = acc[i][j][r];
                     float x;
                     if (MODE == kGemmBX) {
-                        x = (args.a + dIn[gi]) * in + v;
+                        x = (ca + dIn[gi]) * in + v;
                     } else {
                         const float da_i = dIn[gi];
-                        x = args.b * in + args.c * (v + (da_i + da_j) * in);
-                        if (gi == gj) x = args.b * da_i + args.c * (v + da_i * da_i);
+                        x = cb * in + cc * (v + (da_i + da_j) * in);
+                        if (gi == gj) x = cb * da_i + cc * (v + da_i * da_i);
                     }
                     acc[i][j][r] = x;
                 }
@@ -250,23 +282,69 @@ __device__ __forceinline__ void epilogue(const NsArgs &args, f32x4 (&acc)[FM][FN
     }
 }
 
-template <int BM, int MODE>
-__global__ __launch_bounds__(Cfg<BM>::WR * Cfg<BM>::WC * 64) void ns_gemm_kernel(NsArgs args) {
-    constexpr int WR = Cfg<BM>::WR, WC = Cfg<BM>::WC, NW = WR * WC;
-    constexpr int WTM = BM / WR, WTN = BM / WC, FM = WTM / 16, FN = WTN / 16, ROW = 128;
-    constexpr int OPER = BM * ROW;               // bytes per operand per stage
-    constexpr int LOADS = OPER / 1024 / NW;      // kilobyte instructions per operand per wave
-    static_assert(LOADS * NW * 1024 == OPER, "tile");
-    static_assert(BM * BM * 2 <= 4 * OPER, "epilogue regions fit in the stages");
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2][OPER];
 
-    const int batch = blockIdx.y;
+// ----------------------------------------------------------------------------
+// The main loop.  K advances in stages of 32 columns through kStages LDS
+// buffers of 2 x BM rows x 64 bytes.  Operands go from global memory straight
+// to LDS (buffer_load ... lds, 16 bytes per lane; one wave instruction fills
+// one contiguous kilobyte = 16 rows of a stage); lane l fetches the chunk that
+// the XOR swizzle (chunk c of row r at slot c ^ ((r >> 1) & 3)) puts at its
+// LDS slot, which keeps the 16-byte fragment reads free of bank conflicts.
+// Loads run kStages - 1 stages ahead.  Stages past the end of K read from a
+// zero-size buffer descriptor, so they return zeros without touching memory
+// and every iteration has the same shape (no branches, fixed wait counts).
+//
+// Iteration kt: wait until this wave's loads of stage kt+1 have landed ->
+// barrier (everyone's have; everyone has finished reading stage kt) -> issue
+// the loads of stage kt + kStages into stage kt's buffer -> read the
+// fragments of stage kt+1, interleaved one by one with the MFMAs of stage kt
+// (whose fragments were read in the previous iteration).
+constexpr int kStages = 4;
+constexpr int kBK = 32;
+#define LDS_ADDR(p) ((__attribute__((address_space(3))) void *)(p))
+// s_waitcnt: vmcnt <= n and lgkmcnt = 0 (gfx9 field layout: vmcnt[3:0],
+// expcnt[6:4], lgkmcnt[11:8], vmcnt high bits[15:14])
+#define WAIT_VM_LGKM0(n) ((((n) & 15) | (((n) >> 4) << 14) | (7 << 4)))
+
+template <int BM, int MODE>
+__global__ __launch_bounds__(Cfg<BM>::WR * Cfg<BM>::WC * 64)
+__attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch L) {
+    constexpr int WR = Cfg<BM>::WR, WC = Cfg<BM>::WC, NW = WR * WC;
+    constexpr int WTM = BM / WR, WTN = BM / WC, FM = WTM / 16, FN = WTN / 16;
+    constexpr int ROW = 64, OPB = BM * ROW, STAGE = 2 * OPB;
+    constexpr int LOADS = OPB / 1024 / NW, LPS = 2 * LOADS, ND = FM + FN;
+    static_assert(LOADS >= 1 && LOADS * NW * 1024 == OPB, "tile");
+    static_assert(kStages * STAGE >= BM * BM * 2, "the epilogue regions fit in the stages");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * STAGE];
+
+    // group, matrix and tile of this workgroup
+    const int bid = blockIdx.x;
+    int gi = 0;
+    while (gi + 1 < L.ngroups && bid >= L.g[gi + 1].tile0) ++gi;
+    const NsGroup &G = L.g[gi];
+    // Workgroups go to the 8 XCDs round-robin (tile0 is a multiple of 8).  The
+    // tiles resident at one time (a round) are consecutive in the banded
+    // order, a compact block of the tile grid, and XCD x takes the x-th
+    // contiguous eighth of each round: its L2 then serves few operand panels,
+    // and the XCDs together stream the round's panels through the shared
+    // memory-side cache.  The padding at the end of a group exits at once.
+    const int rel = bid - G.tile0;
+    const int base = rel - rel % G.round_tiles;
+    const int rem = G.padded - base < G.round_tiles ? G.padded - base : G.round_tiles;
+    int t = base + (rel & 7) * (rem >> 3) + ((rel - base) >> 3);
+    if (t >= G.tiles) return;
+    const int batch = t / G.tiles_pm;
+    t -= batch * G.tiles_pm;
     int ti, tj;
-    tile_of<MODE>(args, ti, tj);
+    tile_coords<MODE>(G, t, ti, tj);
     const int m0 = ti * BM, n0 = tj * BM;
-    const uint16_t *P = args.P + batch * args.p_stride + (int64_t)m0 * args.ldp;
-    const uint16_t *Q = args.Q + batch * args.q_stride + (int64_t)n0 * args.ldq;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ld = G.ld, K = G.K;
+    const uint16_t *Pb = G.P + batch * G.p_stride + (int64_t)m0 * ld;
+    const uint16_t *Qb = G.Q + batch * G.q_stride + (int64_t)n0 * ld;
+    const int panel_bytes = BM * ld * 2;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wr = wave / WC, wc = wave % WC;
 
     f32x4 acc[FM][FN];
@@ -275,88 +353,103 @@ __global__ __launch_bounds__(Cfg<BM>::WR * Cfg<BM>::WC * 64) void ns_gemm_kernel
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // global -> LDS: instruction q of this wave fills kilobyte block
-    // k = q * NW + wave (rows 8k .. 8k+7); lane l takes row 8k + l / 8 and the
-    // global chunk that the swizzle places at slot l % 8
-    const int lrow = lane >> 3, lchunk = (lane & 7) ^ (lrow & 7);
-    const uint16_t *pl = P + (int64_t)lrow * args.ldp + lchunk * 8;
-    const uint16_t *ql = Q + (int64_t)lrow * args.ldq + lchunk * 8;
-    auto gload = [&](int st, int k0) {
+    // loads: instruction q of this wave fills kilobyte k = q * NW + wave of
+    // the operand's stage (rows 16k .. 16k+15); lane l takes row 16k + l / 4
+    // and the chunk that the swizzle places at slot l % 4
+    const int lrow = lane >> 2, lchunk = (lane & 3) ^ ((lrow >> 1) & 3);
+    const int voff = (lrow * ld + lchunk * 8) * 2;
+    auto gload = [&](int sbase, int k0) {
+        const int bytes = k0 < K ? panel_bytes : 0;
+        const __amdgpu_buffer_rsrc_t rp =
+            __builtin_amdgcn_make_buffer_rsrc((void *)Pb, (short)0, bytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rq =
+            __builtin_amdgcn_make_buffer_rsrc((void *)Qb, (short)0, bytes, 0x00020000);
 #pragma unroll
         for (int q = 0; q < LOADS; ++q) {
             const int k = q * NW + wave;
-            __builtin_amdgcn_global_load_lds((const void *)(pl + (int64_t)(8 * k) * args.ldp + k0),
-                                             LDS_ADDR(&lds[st][0][k * 1024]), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void *)(ql + (int64_t)(8 * k) * args.ldq + k0),
-                                             LDS_ADDR(&lds[st][1][k * 1024]), 16, 0, 0);
+            const int soff = (16 * k * ld + k0) * 2;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, LDS_ADDR(&lds[sbase + k * 1024]), 16, voff,
+                                                     soff, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, LDS_ADDR(&lds[sbase + OPB + k * 1024]), 16,
+                                                     voff, soff, 0, 0);
         }
     };
     // MFMA 16x16x32 operand: lane l holds row l % 16, K-chunk l / 16 of the
-    // 32-column sub-step (chunk 4 ks + l / 16 of the stage)
+    // stage (rowbase is a multiple of 16)
     const int fr = lane & 15, fh = lane >> 4;
-    auto frag = [&](int st, int op, int rowbase, int ks) {
-        const int r = rowbase + fr, c = 4 * ks + fh;
-        return *reinterpret_cast<const bf16x8 *>(&lds[st][op][r * ROW + ((c ^ (r & 7)) << 4)]);
+    const int foff = fr * ROW + ((fh ^ ((fr >> 1) & 3)) << 4);
+    bf16x8 fa[2][FM], fb[2][FN];
+    auto read = [&](int buf, int sbase) {
+        const uint8_t *pa = &lds[sbase + wr * WTM * ROW + foff];
+        const uint8_t *pb = &lds[sbase + OPB + wc * WTN * ROW + foff];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[buf][i] = *reinterpret_cast<const bf16x8 *>(pa + i * 16 * ROW);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[buf][j] = *reinterpret_cast<const bf16x8 *>(pb + j * 16 * ROW);
+    };
+    auto mma = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[buf][i], fb[buf][j], acc[i][j],
+                                                                    0, 0, 0);
     };
 
-    const int KT = args.K / kBK;
-    gload(0, 0);
+    const int KT = K / kBK;
+#pragma unroll
+    for (int s = 0; s < kStages; ++s) gload(s * STAGE, s * kBK);
+    __builtin_amdgcn_s_waitcnt(WAIT_VM_LGKM0((kStages - 1) * LPS));
+    __syncthreads();
+    read(0, 0);
+    int cur = 0;  // buffer of stage kt
+    auto body = [&](int kt, auto PAR) __attribute__((always_inline)) {
+        constexpr int par = decltype(PAR)::value;
+        const int nxt = cur + 1 == kStages ? 0 : cur + 1;
+        __builtin_amdgcn_s_waitcnt(WAIT_VM_LGKM0((kStages - 2) * LPS));
+        __builtin_amdgcn_s_barrier();
+        gload(cur * STAGE, (kt + kStages) * kBK);
+        read(par ^ 1, nxt * STAGE);
+        mma(par);
+#pragma unroll
+        for (int x = 0; x < LPS; ++x) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one global load
+        }
+#pragma unroll
+        for (int x = 0; x < ND; ++x) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        cur = nxt;
+    };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    int kt = 0;
+    // two stages per trip, so that the fragment buffer of each is static
+#pragma clang loop unroll(disable)
+    for (; kt + 2 <= KT; kt += 2) {
+        body(kt, P0{});
+        body(kt + 1, P1{});
+    }
+    if (kt < KT) body(kt, P0{});
+    // the loads past the end still write (zeros) to LDS: drain them before
+    // the epilogue reuses the buffers
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-        const int st = kt & 1;
-        if (kt + 1 < KT) gload(st ^ 1, (kt + 1) * kBK);
-        bf16x8 af[2][FM], bfr[2][FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) af[0][i] = frag(st, 0, wr * WTM + i * 16, 0);
-#pragma unroll
-        for (int j = 0; j < FN; ++j) bfr[0][j] = frag(st, 1, wc * WTN + j * 16, 0);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int cb = ks & 1, nb = cb ^ 1;
-            if (ks == 0) {
-#pragma unroll
-                for (int i = 0; i < FM; ++i) af[nb][i] = frag(st, 0, wr * WTM + i * 16, 1);
-#pragma unroll
-                for (int j = 0; j < FN; ++j) bfr[nb][j] = frag(st, 1, wc * WTN + j * 16, 1);
-            }
-            __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[cb][i], bfr[cb][j], acc[i][j],
-                                                                        0, 0, 0);
-            __builtin_amdgcn_s_setprio(0);
-            if (ks == 0) {
-                // the next stage's global loads and the next sub-step's
-                // fragment reads, one after each MFMA
-                constexpr int NV = (2 * LOADS < FM * FN) ? 2 * LOADS : FM * FN;
-                constexpr int ND = (FM + FN < FM * FN - NV) ? FM + FN : FM * FN - NV;
-#pragma unroll
-                for (int x = 0; x < NV; ++x) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-                }
-#pragma unroll
-                for (int x = 0; x < ND; ++x) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                }
-            }
-        }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-    }
-    epilogue<MODE, FM, FN>(args, acc, batch, m0 + wr * WTM, n0 + wc * WTN, wave, lane, &lds[0][0][0]);
+    epilogue<MODE, FM, FN>(G, L.a, L.b, L.c, acc, batch, m0 + wr * WTM, n0 + wc * WTN, wave, lane,
+                           lds);
 }
 
 template <int T>
 constexpr int kThreadsOf = Cfg<T>::WR * Cfg<T>::WC * 64;
 
-template <int T>
-hipError_t run_iteration(const MuonGeom &g, char *ws, const MuonWorkspace &L, int cur_xt,
-                         float a, float b, float c, hipStream_t stream) {
+// The per-group operands of one product.
+NsGroup product_group(int mode, const NsGroupRef &r, int cur_xt) {
+    const MuonGeom &g = *r.geom;
+    const MuonWorkspace &L = *r.layout;
+    char *ws = r.base;
     uint16_t *X = reinterpret_cast<uint16_t *>(ws + L.x);
     uint16_t *XT = reinterpret_cast<uint16_t *>(ws + (cur_xt ? L.xt1 : L.xt0));
     uint16_t *XTn = reinterpret_cast<uint16_t *>(ws + (cur_xt ? L.xt0 : L.xt1));
@@ -366,46 +459,121 @@ hipError_t run_iteration(const MuonGeom &g, char *ws, const MuonWorkspace &L, in
     float *dB = reinterpret_cast<float *>(ws + L.db);
     const int64_t ds = (int64_t)(L.d_stride / 4);
     const int64_t xs = (int64_t)(L.x_stride / 2), as = (int64_t)(L.a_stride / 2);
-    const int tm = g.mp / T, tn = g.np / T;
-    const int tri = tm * (tm + 1) / 2;
+    const int tm = g.mp / g.tile, tn = g.np / g.tile;
+    NsGroup s{};
+    s.d_stride = ds;
+    s.tiles_m = tm;
+    if (mode == kSyrkXXT) {
+        s.P = X; s.Q = X; s.p_stride = xs; s.q_stride = xs; s.ld = g.np; s.K = g.np;
+        s.tiles_n = tm; s.tiles_pm = tm * (tm + 1) / 2;
+        s.C = A; s.c_stride = as; s.ldc = g.mp;
+        s.dIn = dA; s.dOut = dA;
+    } else if (mode == kSyrkAA) {
+        s.P = A; s.Q = A; s.p_stride = as; s.q_stride = as; s.ld = g.mp; s.K = g.mp;
+        s.tiles_n = tm; s.tiles_pm = tm * (tm + 1) / 2;
+        s.C = B; s.c_stride = as; s.ldc = g.mp; s.E = A;
+        s.dIn = dA; s.dOut = dB;
+    } else {
+        s.P = B; s.Q = XT; s.p_stride = as; s.q_stride = xs; s.ld = g.mp; s.K = g.mp;
+        s.tiles_n = tn; s.tiles_pm = tm * tn;
+        s.C = X; s.c_stride = xs; s.ldc = g.np;
+        s.CT = XTn; s.ct_stride = xs; s.ldct = g.mp;
+        s.dIn = dB; s.dOut = dB;
+    }
+    return s;
+}
 
-    NsArgs s1{};
-    s1.P = X; s1.Q = X; s1.p_stride = xs; s1.q_stride = xs;
-    s1.ldp = g.np; s1.ldq = g.np; s1.K = g.np; s1.tiles_m = tm; s1.tiles_n = tm;
-    s1.C = A; s1.c_stride = as; s1.ldc = g.mp;
-    s1.dIn = dA; s1.dOut = dA; s1.d_stride = ds;
-    hipLaunchKernelGGL((ns_gemm_kernel<T, kSyrkXXT>), dim3(tri, g.batch), dim3(kThreadsOf<T>), 0,
-                       stream, s1);
+template <int T>
+int round_tiles_of() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 8)
+        cus = 256;
+    const int per_cu = Cfg<T>::WPE * 4 / (Cfg<T>::WR * Cfg<T>::WC);
+    return (cus / 8) * per_cu * 8;
+}
 
-    NsArgs s2{};
-    s2.P = A; s2.Q = A; s2.p_stride = as; s2.q_stride = as;
-    s2.ldp = g.mp; s2.ldq = g.mp; s2.K = g.mp; s2.tiles_m = tm; s2.tiles_n = tm;
-    s2.C = B; s2.c_stride = as; s2.ldc = g.mp; s2.E = A; s2.b = b; s2.c = c;
-    s2.dIn = dA; s2.dOut = dB; s2.d_stride = ds;
-    hipLaunchKernelGGL((ns_gemm_kernel<T, kSyrkAA>), dim3(tri, g.batch), dim3(kThreadsOf<T>), 0,
-                       stream, s2);
-
-    NsArgs s3{};
-    s3.P = B; s3.Q = XT; s3.p_stride = as; s3.q_stride = xs;
-    s3.ldp = g.mp; s3.ldq = g.mp; s3.K = g.mp; s3.tiles_m = tm; s3.tiles_n = tn;
-    s3.C = X; s3.c_stride = xs; s3.ldc = g.np;
-    s3.CT = XTn; s3.ct_stride = xs; s3.ldct = g.mp; s3.a = a;
-    s3.dIn = dB; s3.dOut = dB; s3.d_stride = ds;
-    hipLaunchKernelGGL((ns_gemm_kernel<T, kGemmBX>), dim3(tm * tn, g.batch), dim3(kThreadsOf<T>),
-                       0, stream, s3);
+template <int T, int MODE>
+hipError_t launch_product(const NsGroupRef *refs, const int *idx, int n, int cur_xt, float a,
+                          float b, float c, hipStream_t stream) {
+    const int32_t round_tiles = round_tiles_of<T>();
+    for (int first = 0; first < n; first += kMaxGroups) {
+        const int cnt = n - first < kMaxGroups ? n - first : kMaxGroups;
+        NsLaunch L{};
+        L.a = a;
+        L.b = b;
+        L.c = c;
+        L.ngroups = cnt;
+        int64_t tiles = 0;
+        for (int k = 0; k < cnt; ++k) {
+            const NsGroupRef &r = refs[idx[first + k]];
+            NsGroup s = product_group(MODE, r, cur_xt);
+            s.tiles = s.tiles_pm * r.geom->batch;
+            s.padded = (s.tiles + 7) / 8 * 8;
+            s.round_tiles = round_tiles;
+            s.tile0 = (int32_t)tiles;
+            tiles += s.padded;
+            L.g[k] = s;
+        }
+        if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((ns_gemm_kernel<T, MODE>), dim3((uint32_t)tiles), dim3(kThreadsOf<T>), 0,
+                           stream, L);
+    }
     return hipGetLastError();
+}
+
+template <int T>
+hipError_t run_class(const NsGroupRef *refs, int nrefs, int cur_xt, float a, float b, float c,
+                     hipStream_t stream) {
+    int idx[kMaxCallGroups];
+    int n = 0;
+    for (int i = 0; i < nrefs; ++i)
+        if (refs[i].geom->tile == T) idx[n++] = i;
+    if (n == 0) return hipSuccess;
+    // longest reduction first, so that the short tiles fill the last rounds
+    auto by_k = [&](int mode) {
+        for (int i = 1; i < n; ++i)
+            for (int j = i; j > 0; --j) {
+                const MuonGeom &p = *refs[idx[j - 1]].geom, &q = *refs[idx[j]].geom;
+                const int kp = mode == kSyrkXXT ? p.np : p.mp, kq = mode == kSyrkXXT ? q.np : q.mp;
+                if (kp >= kq) break;
+                const int t = idx[j - 1];
+                idx[j - 1] = idx[j];
+                idx[j] = t;
+            }
+    };
+    hipError_t e;
+    by_k(kSyrkXXT);
+    e = launch_product<T, kSyrkXXT>(refs, idx, n, cur_xt, a, b, c, stream);
+    if (e != hipSuccess) return e;
+    by_k(kSyrkAA);
+    e = launch_product<T, kSyrkAA>(refs, idx, n, cur_xt, a, b, c, stream);
+    if (e != hipSuccess) return e;
+    return launch_product<T, kGemmBX>(refs, idx, n, cur_xt, a, b, c, stream);
 }
 
 }  // namespace
 
-hipError_t launch_ns_iteration(const MuonGeom &g, char *ws, const MuonWorkspace &L,
-                               int cur_xt, float a, float b, float c, hipStream_t stream) {
-    switch (g.tile) {
-        case 64: return run_iteration<64>(g, ws, L, cur_xt, a, b, c, stream);
-        case 128: return run_iteration<128>(g, ws, L, cur_xt, a, b, c, stream);
-        case 256: return run_iteration<256>(g, ws, L, cur_xt, a, b, c, stream);
-        default: return hipErrorInvalidValue;
+int ns_round_tiles(int tile) {
+    switch (tile) {
+        case 64: return round_tiles_of<64>();
+        case 128: return round_tiles_of<128>();
+        default: return round_tiles_of<256>();
     }
+}
+
+hipError_t launch_ns_iteration(const NsGroupRef *refs, int nrefs, int cur_xt, float a, float b,
+                               float c, hipStream_t stream) {
+    if (nrefs < 1 || nrefs > kMaxCallGroups) return hipErrorInvalidValue;
+    for (int i = 0; i < nrefs; ++i) {
+        const int t = refs[i].geom->tile;
+        if (t != 64 && t != 128 && t != 256) return hipErrorInvalidValue;
+    }
+    hipError_t e = run_class<256>(refs, nrefs, cur_xt, a, b, c, stream);
+    if (e == hipSuccess) e = run_class<128>(refs, nrefs, cur_xt, a, b, c, stream);
+    if (e == hipSuccess) e = run_class<64>(refs, nrefs, cur_xt, a, b, c, stream);
+    return e;
 }
 
 }  // namespace zopt

@@ -176,6 +176,154 @@ void muon_output(const MuonGeom &g, const MuonWorkspace &L, int32_t ns_steps, si
     }
 }
 
+// The groups of a call, each with its own workspace carve-up, laid out one
+// after the other in the caller's workspace.
+struct GroupPlan {
+    MuonGeom g;
+    MuonWorkspace L;
+    size_t base;
+};
+
+zopt_status plan_groups(int32_t ngroups, const int32_t *batch, const int64_t *rows,
+                        const int64_t *cols, GroupPlan *plans, size_t &total, int &nmat) {
+    if (!batch || !rows || !cols) return ZOPT_ERR_NULL;
+    if (ngroups < 1 || ngroups > kMaxCallGroups) return ZOPT_ERR_SIZE;
+    total = 0;
+    nmat = 0;
+    for (int i = 0; i < ngroups; ++i) {
+        const zopt_status st = muon_check_shape(batch[i], rows[i], cols[i]);
+        if (st != ZOPT_OK) return st;
+        plans[i].g = muon_geometry(batch[i], rows[i], cols[i]);
+        plans[i].L = muon_workspace_layout(plans[i].g);
+        plans[i].base = total;
+        total += plans[i].L.total;
+        nmat += batch[i];
+    }
+    return ZOPT_OK;
+}
+
+zopt_status muon_step_groups(int32_t ngroups, const int32_t *batch, const int64_t *rows,
+                             const int64_t *cols, float *const *master, float *const *momentum,
+                             const uint16_t *const *grad, uint16_t *const *weight, float lr,
+                             float momentum_beta, int32_t nesterov, float weight_decay,
+                             int32_t ns_steps, float ns_a, float ns_b, float ns_c, float ns_eps,
+                             int32_t adjust_lr, void *workspace, size_t *workspace_bytes,
+                             void *stream) {
+    if (!workspace_bytes) return ZOPT_ERR_NULL;
+    GroupPlan plans[kMaxCallGroups];
+    size_t total = 0;
+    int nmat = 0;
+    zopt_status st = plan_groups(ngroups, batch, rows, cols, plans, total, nmat);
+    if (st != ZOPT_OK) return st;
+    if (!workspace) {
+        *workspace_bytes = total;
+        return ZOPT_OK;
+    }
+    if (!master || !momentum || !grad) return ZOPT_ERR_NULL;
+    for (int b = 0; b < nmat; ++b) {
+        if (!master[b] || !momentum[b] || !grad[b]) return ZOPT_ERR_NULL;
+        if (weight && !weight[b]) return ZOPT_ERR_NULL;
+    }
+    if (!finite(lr) || lr < 0.0f || !(momentum_beta >= 0.0f && momentum_beta < 1.0f) ||
+        (nesterov != 0 && nesterov != 1) || !finite(weight_decay) || weight_decay < 0.0f ||
+        ns_steps < 0 || ns_steps > 100 || !finite(ns_a) || !finite(ns_b) || !finite(ns_c) ||
+        !finite(ns_eps) || ns_eps < 0.0f || (adjust_lr != 0 && adjust_lr != 1))
+        return ZOPT_ERR_HYPER;
+    if (*workspace_bytes < total || ((uintptr_t)workspace & 255u) != 0)
+        return ZOPT_ERR_WORKSPACE;
+
+    char *ws = static_cast<char *>(workspace);
+    hipStream_t s = (hipStream_t)stream;
+    MuonPtrs ptrs[kMaxCallGroups];
+    NsGroupRef refs[kMaxCallGroups];
+    for (int i = 0, first = 0; i < ngroups; first += batch[i], ++i) {
+        MuonPtrs &p = ptrs[i];
+        for (int b = 0; b < batch[i]; ++b) {
+            p.master[b] = master[first + b];
+            p.momentum[b] = momentum[first + b];
+            p.grad[b] = grad[first + b];
+            p.weight[b] = weight ? weight[first + b] : nullptr;
+        }
+        refs[i] = NsGroupRef{&plans[i].g, &plans[i].L, ws + plans[i].base};
+    }
+
+    // Launch plan.  A group whose workspace fits in the memory-side cache and
+    // whose B X product alone fills two rounds of the GPU's workgroup slots
+    // runs on its own, all its iterations back to back, so its operands stay
+    // cached from one product to the next.  The other groups -- too small to
+    // fill the GPU, or too large to stay cached anyway -- share launches, so
+    // that their tiles fill each other's partial rounds.
+    int bins[kMaxCallGroups + 1][kMaxCallGroups];
+    int bin_size[kMaxCallGroups + 1] = {0};
+    int nbins = 0, shared = -1;
+    for (int i = 0; i < ngroups; ++i) {
+        const MuonGeom &g = plans[i].g;
+        const int64_t bx_tiles = (int64_t)(g.mp / g.tile) * (g.np / g.tile) * g.batch;
+        const bool alone = plans[i].L.total <= kMemCacheBytes &&
+                           bx_tiles >= 2 * (int64_t)ns_round_tiles(g.tile);
+        if (alone) {
+            bins[nbins][0] = i;
+            bin_size[nbins++] = 1;
+        } else {
+            if (shared < 0) shared = nbins++;
+            bins[shared][bin_size[shared]++] = i;
+        }
+    }
+
+    const double lr_d = (double)lr, wd_d = (double)weight_decay;
+    hipError_t e = hipSuccess;
+    for (int bi = 0; bi < nbins && e == hipSuccess; ++bi) {
+        NsGroupRef brefs[kMaxCallGroups];
+        for (int k = 0; k < bin_size[bi] && e == hipSuccess; ++k) {
+            const int i = bins[bi][k];
+            brefs[k] = refs[i];
+            e = launch_muon_pre(plans[i].g, ptrs[i], momentum_beta, nesterov, ns_eps,
+                                ws + plans[i].base, plans[i].L, s);
+        }
+        for (int k = 0; k < ns_steps && e == hipSuccess; ++k)
+            e = launch_ns_iteration(brefs, bin_size[bi], k & 1, ns_a, ns_b, ns_c, s);
+        for (int k = 0; k < bin_size[bi] && e == hipSuccess; ++k) {
+            const int i = bins[bi][k];
+            const MuonGeom &g = plans[i].g;
+            const double big = (double)(g.rows > g.cols ? g.rows : g.cols);
+            const double scale = adjust_lr
+                                     ? 0.2 * std::sqrt(big)
+                                     : std::sqrt(std::fmax(1.0, (double)g.rows / (double)g.cols));
+            const float decay = (float)(1.0 - lr_d * wd_d);
+            const float step_lr = (float)(lr_d * scale);
+            size_t obase;
+            int64_t old;
+            muon_output(g, plans[i].L, ns_steps, obase, old);
+            e = launch_muon_post(g, ptrs[i],
+                                 reinterpret_cast<const uint16_t *>(ws + plans[i].base + obase),
+                                 old, plans[i].L.x_stride, decay, step_lr, s);
+        }
+    }
+    return e == hipSuccess ? ZOPT_OK : ZOPT_ERR_DEVICE;
+}
+
+zopt_status muon_output_view(int32_t ngroups, const int32_t *batch, const int64_t *rows,
+                             const int64_t *cols, int32_t ns_steps, const void *workspace,
+                             int32_t group, int32_t index, const uint16_t **out,
+                             int64_t *row_stride) {
+    if (!workspace || !out || !row_stride) return ZOPT_ERR_NULL;
+    GroupPlan plans[kMaxCallGroups];
+    size_t total = 0;
+    int nmat = 0;
+    const zopt_status st = plan_groups(ngroups, batch, rows, cols, plans, total, nmat);
+    if (st != ZOPT_OK) return st;
+    if (group < 0 || group >= ngroups || index < 0 || index >= batch[group]) return ZOPT_ERR_SIZE;
+    if (ns_steps < 0 || ns_steps > 100) return ZOPT_ERR_HYPER;
+    const GroupPlan &p = plans[group];
+    size_t base;
+    int64_t ld;
+    muon_output(p.g, p.L, ns_steps, base, ld);
+    *out = reinterpret_cast<const uint16_t *>(static_cast<const char *>(workspace) + p.base + base +
+                                              (size_t)index * p.L.x_stride);
+    *row_stride = ld;
+    return ZOPT_OK;
+}
+
 }  // namespace
 
 ZOPT_EXPORT zopt_status zopt_muon_step(int32_t batch, int64_t rows, int64_t cols,
@@ -185,71 +333,35 @@ ZOPT_EXPORT zopt_status zopt_muon_step(int32_t batch, int64_t rows, int64_t cols
                                        float weight_decay, int32_t ns_steps, float ns_a,
                                        float ns_b, float ns_c, float ns_eps, int32_t adjust_lr,
                                        void *workspace, size_t *workspace_bytes, void *stream) {
-    zopt_status st = muon_check_shape(batch, rows, cols);
-    if (!workspace_bytes) return ZOPT_ERR_NULL;
-    if (st != ZOPT_OK) return st;
-    const MuonGeom g = muon_geometry(batch, rows, cols);
-    const MuonWorkspace L = muon_workspace_layout(g);
-    if (!workspace) {
-        *workspace_bytes = L.total;
-        return ZOPT_OK;
-    }
-    if (!master || !momentum || !grad) return ZOPT_ERR_NULL;
-    for (int b = 0; b < batch; ++b) {
-        if (!master[b] || !momentum[b] || !grad[b]) return ZOPT_ERR_NULL;
-        if (weight && !weight[b]) return ZOPT_ERR_NULL;
-    }
-    if (!finite(lr) || lr < 0.0f || !(momentum_beta >= 0.0f && momentum_beta < 1.0f) ||
-        (nesterov != 0 && nesterov != 1) || !finite(weight_decay) || weight_decay < 0.0f ||
-        ns_steps < 0 || ns_steps > 100 || !finite(ns_a) || !finite(ns_b) || !finite(ns_c) ||
-        !finite(ns_eps) || ns_eps < 0.0f || (adjust_lr != 0 && adjust_lr != 1))
-        return ZOPT_ERR_HYPER;
-    if (*workspace_bytes < L.total || ((uintptr_t)workspace & 255u) != 0)
-        return ZOPT_ERR_WORKSPACE;
+    return muon_step_groups(1, &batch, &rows, &cols, master, momentum, grad, weight, lr,
+                            momentum_beta, nesterov, weight_decay, ns_steps, ns_a, ns_b, ns_c,
+                            ns_eps, adjust_lr, workspace, workspace_bytes, stream);
+}
 
-    MuonPtrs ptrs{};
-    for (int b = 0; b < batch; ++b) {
-        ptrs.master[b] = master[b];
-        ptrs.momentum[b] = momentum[b];
-        ptrs.grad[b] = grad[b];
-        ptrs.weight[b] = weight ? weight[b] : nullptr;
-    }
-    char *ws = static_cast<char *>(workspace);
-    hipStream_t s = (hipStream_t)stream;
-    hipError_t e = launch_muon_pre(g, ptrs, momentum_beta, nesterov, ns_eps, ws, L, s);
-    for (int k = 0; k < ns_steps && e == hipSuccess; ++k)
-        e = launch_ns_iteration(g, ws, L, k & 1, ns_a, ns_b, ns_c, s);
-    if (e != hipSuccess) return ZOPT_ERR_DEVICE;
-
-    const double big = (double)(rows > cols ? rows : cols);
-    const double scale = adjust_lr ? 0.2 * std::sqrt(big)
-                                   : std::sqrt(std::fmax(1.0, (double)rows / (double)cols));
-    const float decay = (float)(1.0 - (double)lr * (double)weight_decay);
-    const float step_lr = (float)((double)lr * scale);
-    size_t obase;
-    int64_t old;
-    muon_output(g, L, ns_steps, obase, old);
-    e = launch_muon_post(g, ptrs, reinterpret_cast<const uint16_t *>(ws + obase), old,
-                         L.x_stride, decay, step_lr, s);
-    return e == hipSuccess ? ZOPT_OK : ZOPT_ERR_DEVICE;
+ZOPT_EXPORT zopt_status zopt_muon_step_groups(
+    int32_t ngroups, const int32_t *batch, const int64_t *rows, const int64_t *cols,
+    float *const *master, float *const *momentum, const uint16_t *const *grad,
+    uint16_t *const *weight, float lr, float momentum_beta, int32_t nesterov, float weight_decay,
+    int32_t ns_steps, float ns_a, float ns_b, float ns_c, float ns_eps, int32_t adjust_lr,
+    void *workspace, size_t *workspace_bytes, void *stream) {
+    return muon_step_groups(ngroups, batch, rows, cols, master, momentum, grad, weight, lr,
+                            momentum_beta, nesterov, weight_decay, ns_steps, ns_a, ns_b, ns_c,
+                            ns_eps, adjust_lr, workspace, workspace_bytes, stream);
 }
 
 ZOPT_EXPORT zopt_status zopt_muon_output_view(int32_t batch, int64_t rows, int64_t cols,
                                               int32_t ns_steps, const void *workspace,
                                               int32_t index, const uint16_t **out,
                                               int64_t *row_stride) {
-    if (!workspace || !out || !row_stride) return ZOPT_ERR_NULL;
-    zopt_status st = muon_check_shape(batch, rows, cols);
-    if (st != ZOPT_OK) return st;
-    if (index < 0 || index >= batch) return ZOPT_ERR_SIZE;
-    if (ns_steps < 0 || ns_steps > 100) return ZOPT_ERR_HYPER;
-    const MuonGeom g = muon_geometry(batch, rows, cols);
-    const MuonWorkspace L = muon_workspace_layout(g);
-    size_t base;
-    int64_t ld;
-    muon_output(g, L, ns_steps, base, ld);
-    *out = reinterpret_cast<const uint16_t *>(static_cast<const char *>(workspace) + base +
-                                              (size_t)index * L.x_stride);
-    *row_stride = ld;
-    return ZOPT_OK;
+    return muon_output_view(1, &batch, &rows, &cols, ns_steps, workspace, 0, index, out,
+                            row_stride);
+}
+
+ZOPT_EXPORT zopt_status zopt_muon_groups_output_view(int32_t ngroups, const int32_t *batch,
+                                                     const int64_t *rows, const int64_t *cols,
+                                                     int32_t ns_steps, const void *workspace,
+                                                     int32_t group, int32_t index,
+                                                     const uint16_t **out, int64_t *row_stride) {
+    return muon_output_view(ngroups, batch, rows, cols, ns_steps, workspace, group, index, out,
+                            row_stride);
 }

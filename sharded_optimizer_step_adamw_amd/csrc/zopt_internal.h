@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace zopt {
 
 // ------------------------------------------------------------------ bf16
@@ -64,7 +66,9 @@ hipError_t launch_round_bf16(const float *src, uint16_t *dst, int64_t n,
 
 // ------------------------------------------------------------------ Muon
 
-constexpr int kMaxBatch = 64;
+constexpr int kMaxBatch = 64;       // matrices per same-shape group
+constexpr int kMaxCallGroups = 16;  // groups per Muon call
+constexpr int kMaxGroups = 8;       // groups per Newton-Schulz launch (kernel argument space)
 
 // Per-call Muon geometry.  m x n is the Newton-Schulz orientation
 // (m = min(rows, cols)); mp x np are m and n padded up to the tile size.
@@ -102,10 +106,26 @@ hipError_t launch_muon_post(const MuonGeom &g, const MuonPtrs &ptrs,
                             const uint16_t *o_base, int64_t o_ld, size_t o_stride,
                             float decay, float step_lr, hipStream_t stream);
 
-// One Newton-Schulz iteration: A = X X^T, B = b A + c A A, X = a X + B X,
-// reading XT (X transposed) and writing XT_next.
-hipError_t launch_ns_iteration(const MuonGeom &g, char *ws, const MuonWorkspace &L,
-                               int cur_xt, float a, float b, float c,
-                               hipStream_t stream);
+// A group of a Muon call as the Newton-Schulz launches see it: its geometry,
+// its workspace carve-up and where its workspace starts.
+struct NsGroupRef {
+    const MuonGeom *geom;
+    const MuonWorkspace *layout;
+    char *base;
+};
+
+// One Newton-Schulz iteration of every group of a call: A = X X^T,
+// B = b A + c A A, X = a X + B X, reading X^T from xt[cur_xt] and writing
+// xt[1 - cur_xt].  Three launches per tile size in use (more if over
+// kMaxGroups groups share a tile size).
+hipError_t launch_ns_iteration(const NsGroupRef *refs, int nrefs, int cur_xt, float a, float b,
+                               float c, hipStream_t stream);
+
+// Workgroups of the Newton-Schulz kernel with the given tile size that the
+// current device holds at once (one round of tiles).
+int ns_round_tiles(int tile);
+
+// Capacity of the memory-side cache (MI355X Infinity Cache).
+constexpr size_t kMemCacheBytes = (size_t)256 << 20;
 
 }  // namespace zopt

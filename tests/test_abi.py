@@ -141,3 +141,69 @@ def test_output_view_locates_inside_the_workspace():
                                      ctypes.byref(out), ctypes.byref(ld)) == z.ZOPT_ERR_SIZE
     assert lib.zopt_muon_output_view(3, 100, 300, 5, None, 0, ctypes.byref(out),
                                      ctypes.byref(ld)) == z.ZOPT_ERR_NULL
+
+
+def groups_call(ngroups=2, batch=(2, 1), rows=(64, 300), cols=(32, 100), ws=None, ws_bytes=None):
+    lib = z.lib()
+    n = len(batch)
+    b = (ctypes.c_int32 * n)(*batch)
+    r = (ctypes.c_int64 * n)(*rows)
+    c = (ctypes.c_int64 * n)(*cols)
+    size = ctypes.c_size_t(0) if ws_bytes is None else ws_bytes
+    st = lib.zopt_muon_step_groups(ngroups, b, r, c, None, None, None, None, 0.0, 0.0, 0, 0.0, 0,
+                                   0.0, 0.0, 0.0, 0.0, 0, ws, ctypes.byref(size), None)
+    return st, size.value
+
+
+def test_groups_workspace_is_the_sum_of_the_groups():
+    shapes = [(2, 64, 32), (1, 300, 100), (3, 1100, 1300)]
+    total = z.muon_groups_workspace_bytes(shapes)
+    assert total == sum(z.muon_workspace_bytes(*s) for s in shapes)
+    assert z.muon_groups_workspace_bytes(shapes[:1]) == z.muon_workspace_bytes(*shapes[0])
+
+
+def test_groups_reject():
+    assert groups_call(ngroups=0)[0] == z.ZOPT_ERR_SIZE
+    assert groups_call(ngroups=17, batch=(1,) * 17, rows=(8,) * 17, cols=(8,) * 17)[0] == \
+        z.ZOPT_ERR_SIZE
+    assert groups_call(batch=(2, 0))[0] == z.ZOPT_ERR_SIZE
+    assert groups_call(batch=(2, 65))[0] == z.ZOPT_ERR_SIZE
+    assert groups_call(rows=(64, 0))[0] == z.ZOPT_ERR_SIZE
+    lib = z.lib()
+    size = ctypes.c_size_t(0)
+    st = lib.zopt_muon_step_groups(1, None, None, None, None, None, None, None, 0.0, 0.0, 0, 0.0,
+                                   0, 0.0, 0.0, 0.0, 0.0, 0, None, ctypes.byref(size), None)
+    assert st == z.ZOPT_ERR_NULL
+    # a non-NULL workspace with NULL matrix pointers is rejected before any launch
+    st, _ = groups_call(ws=ctypes.c_void_p(1 << 20), ws_bytes=ctypes.c_size_t(1 << 40))
+    assert st == z.ZOPT_ERR_NULL
+
+
+def test_groups_output_views_are_disjoint_and_in_bounds():
+    lib = z.lib()
+    shapes = [(2, 100, 300), (3, 300, 100), (1, 1100, 1300)]
+    n = len(shapes)
+    b = (ctypes.c_int32 * n)(*[s[0] for s in shapes])
+    r = (ctypes.c_int64 * n)(*[s[1] for s in shapes])
+    c = (ctypes.c_int64 * n)(*[s[2] for s in shapes])
+    total = z.muon_groups_workspace_bytes(shapes)
+    base = 1 << 20
+    out, ld = ctypes.c_void_p(), ctypes.c_int64()
+    spans = []
+    for steps in (0, 5):
+        spans.clear()
+        for g, (batch, rows, cols) in enumerate(shapes):
+            for i in range(batch):
+                st = lib.zopt_muon_groups_output_view(n, b, r, c, steps, ctypes.c_void_p(base), g,
+                                                      i, ctypes.byref(out), ctypes.byref(ld))
+                assert st == z.ZOPT_OK
+                lo = out.value - base
+                hi = lo + 2 * ((rows - 1) * ld.value + cols)
+                assert 0 <= lo and hi <= total and ld.value >= cols
+                spans.append((lo, hi))
+        spans.sort()
+        assert all(spans[k][1] <= spans[k + 1][0] for k in range(len(spans) - 1))
+    assert lib.zopt_muon_groups_output_view(n, b, r, c, 5, ctypes.c_void_p(base), 3, 0,
+                                            ctypes.byref(out), ctypes.byref(ld)) == z.ZOPT_ERR_SIZE
+    assert lib.zopt_muon_groups_output_view(n, b, r, c, 5, ctypes.c_void_p(base), 1, 3,
+                                            ctypes.byref(out), ctypes.byref(ld)) == z.ZOPT_ERR_SIZE

@@ -231,10 +231,12 @@ def test_gpt2_small_shapes():
 
 @pytest.mark.parametrize("workload", ["llama1b_rank0_muon", "llama8b_rank0_muon"])
 def test_full_size_groups_one_matrix_each(workload):
-    """The full batched groups of the 1B and 8B rank-0 shares in the launch
-    configuration the benchmark times; momentum and post-step are checked on
-    every matrix, NS against fp64 on one matrix per group."""
+    """The full 1B and 8B rank-0 shares in the launch configuration the
+    benchmark times (one zopt_muon_step_groups call over all groups);
+    momentum and post-step are checked on every matrix, NS against fp64 on one
+    matrix per group."""
     w = wl.MUON_WORKLOADS[workload]
+    calls, inputs = [], []
     for gi, grp in enumerate(w.groups):
         k = grp.count
         shape = (grp.rows, grp.cols)
@@ -242,22 +244,129 @@ def test_full_size_groups_one_matrix_each(workload):
         gG = [wl.device_grad_bf16(w.wid, 5000 + 100 * gi + i, shape, w.grad_std, DEV, w.grad_dist)
               for i in range(k)]
         gM = [torch.zeros(shape, dtype=torch.float32, device=DEV) for _ in range(k)]
-        P0 = [p.cpu().numpy() for p in gP]
-        G = [u16(g) for g in gG]
-        ws = z.muon_step(gP, gM, gG, None, f32(w.lr), f32(w.momentum), True,
-                         f32(w.weight_decay), 5)
-        torch.cuda.synchronize()
-        for i in range(k):
+        calls.append((gP, gM, gG, None))
+        inputs.append(([p.cpu().numpy() for p in gP], [u16(g) for g in gG]))
+    shapes = [(g.count, g.rows, g.cols) for g in w.groups]
+    ws = z.muon_step_groups(calls, f32(w.lr), f32(w.momentum), True, f32(w.weight_decay), 5)
+    torch.cuda.synchronize()
+    for gi, grp in enumerate(w.groups):
+        shape = (grp.rows, grp.cols)
+        gP, gM = calls[gi][0], calls[gi][1]
+        P0, G = inputs[gi]
+        for i in range(grp.count):
             m = np.zeros(shape, np.float32)
             u = oracle.muon_pre(m, G[i], f32(w.momentum), True)
             np.testing.assert_array_equal(gM[i].cpu().numpy().view(np.uint32), m.view(np.uint32))
-            o = oracle.bf16_bits_to_f32(u16(z.muon_output_view(ws, k, grp.rows, grp.cols, 5, i)))
+            o = oracle.bf16_bits_to_f32(u16(z.muon_groups_output_view(ws, shapes, 5, gi, i)))
             if i == 0:
                 err = rel_fro(o.astype(np.float64), oracle.newton_schulz(u))
-                print(f"{workload} group {shape} x{k}: NS rel err {err:.3e}", flush=True)
+                print(f"{workload} group {shape} x{grp.count}: NS rel err {err:.3e}", flush=True)
                 assert err <= NS_TOL
             p = P0[i]
             oracle.muon_post(p, o, f32(w.lr), f32(w.weight_decay), 1, want_weight=False)
             np.testing.assert_array_equal(gP[i].cpu().numpy().view(np.uint32), p.view(np.uint32))
-        del ws, gP, gG, gM
-        torch.cuda.empty_cache()
+
+
+def grouped_vs_separate(specs, seed, ns_steps=5, ns_check=lambda b, r, c, i: True):
+    """One zopt_muon_step_groups call over `specs` [(batch, rows, cols)]:
+    every matrix is checked against the oracle (momentum and post-step bit for
+    bit, NS within tolerance where ns_check says so) and against separate
+    zopt_muon_step calls on the same inputs, which must agree bit for bit."""
+    lr, mu, wd = f32(8e-4), f32(0.95), f32(0.1)
+    host = [make_inputs(b, r, c, seed + 31 * k, momentum_nonzero=True)
+            for k, (b, r, c) in enumerate(specs)]
+
+    def upload():
+        out = []
+        for (b, r, c), (P, M, G) in zip(specs, host):
+            out.append(([dev_f32(p) for p in P], [dev_f32(m) for m in M], [dev_bf16(g) for g in G],
+                        [torch.full((r, c), 3.0, dtype=torch.bfloat16, device=DEV)
+                         for _ in range(b)]))
+        return out
+
+    grouped = upload()
+    ws = z.muon_step_groups(grouped, lr, mu, True, wd, ns_steps)
+    separate = upload()
+    wss = [z.muon_step(*g, lr, mu, True, wd, ns_steps) for g in separate]
+    torch.cuda.synchronize()
+    worst = 0.0
+    for k, ((b, r, c), (P, M, G)) in enumerate(zip(specs, host)):
+        gP, gM, _, gW = grouped[k]
+        sP, sM, _, sW = separate[k]
+        for i in range(b):
+            o_bits = u16(z.muon_groups_output_view(ws, specs, ns_steps, k, i))
+            assert np.array_equal(o_bits, u16(z.muon_output_view(wss[k], b, r, c, ns_steps, i))), \
+                ("grouped != separate", k, i)
+            for x, y in ((gP[i], sP[i]), (gM[i], sM[i])):
+                assert np.array_equal(x.cpu().numpy().view(np.uint32),
+                                      y.cpu().numpy().view(np.uint32)), ("grouped != separate", k, i)
+            assert np.array_equal(u16(gW[i]), u16(sW[i]))
+            m = M[i].copy()
+            u = oracle.muon_pre(m, G[i], mu, True)
+            np.testing.assert_array_equal(gM[i].cpu().numpy().view(np.uint32), m.view(np.uint32))
+            o = oracle.bf16_bits_to_f32(o_bits)
+            if ns_check(b, r, c, i):
+                err = rel_fro(o.astype(np.float64), oracle.newton_schulz(u, ns_steps))
+                worst = max(worst, err)
+                assert err <= NS_TOL, (k, i, err)
+            p = P[i].copy()
+            wref = oracle.muon_post(p, o, lr, wd, 1)
+            np.testing.assert_array_equal(gP[i].cpu().numpy().view(np.uint32), p.view(np.uint32))
+            np.testing.assert_array_equal(u16(gW[i]), wref)
+    return worst
+
+
+def test_groups_mixed_tiles_match_oracle_and_separate_calls():
+    """Eight groups over all three tile sizes, both orientations and ragged
+    sizes, in one call."""
+    specs = [(3, 200, 520), (2, 1100, 1300), (2, 1300, 1100), (2, 300, 700), (4, 96, 64),
+             (1, 1030, 2100), (2, 520, 200), (3, 768, 3072)]
+    grouped_vs_separate(specs, seed=77, ns_check=lambda b, r, c, i: i == 0 or r * c < 300_000)
+
+
+def test_groups_more_than_fit_one_launch():
+    """Eleven groups of the same tile size: the products take two launches."""
+    specs = [(1 + k % 3, 64 + 9 * k, 100 + 13 * k) for k in range(11)]
+    grouped_vs_separate(specs, seed=91)
+
+
+@pytest.mark.parametrize("ns_steps", [0, 1, 4])
+def test_groups_step_counts(ns_steps):
+    grouped_vs_separate([(2, 130, 260), (1, 700, 300), (1, 1024, 1100)], seed=13,
+                        ns_steps=ns_steps)
+
+
+def test_gpt2_small_one_call():
+    """The headline's Muon call: all 72 GPT-2-small matrices in one grouped
+    call (48 x 768^2, 12 x 3072x768, 12 x 768x3072), 1% outlier gradients;
+    momentum and post-step on every matrix, NS on three matrices per group."""
+    w = wl.GPT2_MUON
+    calls, host = [], []
+    for gi, grp in enumerate(w.groups):
+        k = grp.count
+        P = [wl.host_normal(w.wid, 100 * gi + i, (grp.rows, grp.cols), w.master_std)
+             for i in range(k)]
+        G = [wl.host_grad_bf16(w.wid, 5000 + 100 * gi + i, (grp.rows, grp.cols), w.grad_std,
+                               "normal_outliers") for i in range(k)]
+        calls.append(([dev_f32(p) for p in P],
+                      [torch.zeros((grp.rows, grp.cols), device=DEV) for _ in range(k)],
+                      [dev_bf16(g) for g in G],
+                      [torch.empty((grp.rows, grp.cols), dtype=torch.bfloat16, device=DEV)
+                       for _ in range(k)]))
+        host.append((P, G))
+    shapes = [(g.count, g.rows, g.cols) for g in w.groups]
+    ws = z.muon_step_groups(calls, f32(w.lr), f32(w.momentum), True, f32(w.weight_decay), 5)
+    torch.cuda.synchronize()
+    for gi, grp in enumerate(w.groups):
+        P, G = host[gi]
+        gP, gM, _, gW = calls[gi]
+        for i in range(grp.count):
+            m = np.zeros((grp.rows, grp.cols), np.float32)
+            u = oracle.muon_pre(m, G[i], f32(w.momentum), True)
+            np.testing.assert_array_equal(gM[i].cpu().numpy().view(np.uint32), m.view(np.uint32))
+            o = oracle.bf16_bits_to_f32(u16(z.muon_groups_output_view(ws, shapes, 5, gi, i)))
+            if i in (0, grp.count // 2, grp.count - 1):
+                assert rel_fro(o.astype(np.float64), oracle.newton_schulz(u)) <= NS_TOL
+            wref = oracle.muon_post(P[i], o, f32(w.lr), f32(w.weight_decay), 1)
+            np.testing.assert_array_equal(gP[i].cpu().numpy().view(np.uint32), P[i].view(np.uint32))
+            np.testing.assert_array_equal(u16(gW[i]), wref)
