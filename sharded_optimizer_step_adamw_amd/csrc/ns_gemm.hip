@@ -151,8 +151,9 @@ __device__ __forceinline__ int swz(int i, int j) {
 }
 
 // Epilogue: the accumulators are completed in place (A A: b Aoff + c (acc +
-// (dA_i + dA_j) Aoff), its diagonal b dA_i + c (acc + dA_i^2); B X:
-// (a + dB_i) X + acc; the inputs staged through LDS), then leave through the
+// (dA_i + dA_j) Aoff), its diagonal b dA_i + c (acc + dA_i^2), with Aoff
+// staged through LDS; B X needs nothing here, its (a + dB_i) X term was added
+// in the main loop), then leave through the
 // wave's LDS region as coalesced 16-byte row stores: row order to the
 // sub-block itself, transposed to X^T (B X) or to the mirror position (the
 // symmetric products).  A symmetric sub-block that crosses the diagonal is
@@ -179,8 +180,8 @@ __device__ __forceinline__ void epilogue(const NsGroup &args, float ca, float cb
     constexpr int RCHUNKS = SR * RCH, TCHUNKS = SC * TCH;   // 16-byte chunks per layout
 
     // 1. stage the input sub-block (row order) and complete the accumulators
-    if (MODE != kSyrkXXT && !below) {
-        const uint16_t *E = MODE == kSyrkAA ? args.E + batch * args.c_stride : Cm;
+    if (MODE == kSyrkAA && !below) {
+        const uint16_t *E = args.E + batch * args.c_stride;
 #pragma unroll 4
         for (int k = 0; k < RCHUNKS / 64; ++k) {
             const int id = k * 64 + lane, i = id / RCH, c = id % RCH;
@@ -189,7 +190,7 @@ __device__ __forceinline__ void epilogue(const NsGroup &args, float ca, float cb
         }
     }
     __syncthreads();
-    if (MODE != kSyrkXXT && !below) {
+    if (MODE == kSyrkAA && !below) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -201,14 +202,9 @@ __device__ __forceinline__ void epilogue(const NsGroup &args, float ca, float cb
                     const int li = i * 16 + quad * 4 + r, gi = R0 + li;
                     const float in = from_bf16(*reinterpret_cast<const uint16_t *>(W + swz<RCH>(li, lj)));
                     const float v = acc[i][j][r];
-                    float x;
-                    if (MODE == kGemmBX) {
-                        x = (ca + dIn[gi]) * in + v;
-                    } else {
-                        const float da_i = dIn[gi];
-                        x = cb * in + cc * (v + (da_i + da_j) * in);
-                        if (gi == gj) x = cb * da_i + cc * (v + da_i * da_i);
-                    }
+                    const float da_i = dIn[gi];
+                    float x = cb * in + cc * (v + (da_i + da_j) * in);
+                    if (gi == gj) x = cb * da_i + cc * (v + da_i * da_i);
                     acc[i][j][r] = x;
                 }
             }
@@ -315,7 +311,9 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch 
     constexpr int LOADS = OPB / 1024 / NW, LPS = 2 * LOADS, ND = FM + FN;
     static_assert(LOADS >= 1 && LOADS * NW * 1024 == OPB, "tile");
     static_assert(kStages * STAGE >= BM * BM * 2, "the epilogue regions fit in the stages");
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * STAGE];
+    // the stages, then (B X) a + dB_i for the tile's rows
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * STAGE + (MODE == kGemmBX ? BM * 4 : 0)];
+    float *dl = reinterpret_cast<float *>(&lds[kStages * STAGE]);
 
     // group, matrix and tile of this workgroup
     const int bid = blockIdx.x;
@@ -346,6 +344,10 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wr = wave / WC, wc = wave % WC;
+    if constexpr (MODE == kGemmBX) {
+        const float *dB = G.dIn + batch * G.d_stride + m0;
+        for (int r = tid; r < BM; r += NW * 64) dl[r] = L.a + dB[r];
+    }
 
     f32x4 acc[FM][FN];
 #pragma unroll
@@ -396,11 +398,57 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch 
                                                                     0, 0, 0);
     };
 
+    // B X: X' = (a + dB_i) X + Boff X.  The first term needs the tile of X
+    // itself, and the Q operand X^T brings exactly that tile through LDS
+    // during the stages whose K range [k1, k1 + 32) lies inside the tile's
+    // rows: X[k1 + kk][n0 + c] = X^T[n0 + c][k1 + kk].  So in those stages
+    // each wave adds (a + dB_row) X[row][col] to the accumulators of its rows
+    // in that range (two 16-row blocks), reading X from the stage in LDS
+    // instead of from memory in the epilogue.
+    // (The X reads are issued as inline assembly: as ordinary LDS loads the
+    // compiler cannot tell them from the in-flight global->LDS copies into
+    // other stage buffers and would wait for those copies to finish.)
+    const int quad = lane >> 4;
+    const uint32_t lds_base =
+        (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t *)lds);
+    auto diag = [&](int sbase, int k1) __attribute__((always_inline)) {
+        if constexpr (MODE == kGemmBX) {
+            const int rw = m0 + wr * WTM;
+            if (k1 < rw || k1 >= rw + WTM) return;
+            const int i0 = (k1 - rw) >> 4;
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                if (i != i0 && i != i0 + 1) continue;
+                const int kk0 = (i - i0) * 16 + quad * 4;
+                const f32x4 d = *reinterpret_cast<const f32x4 *>(&dl[k1 - m0 + kk0]);
+                u32x2 xv[FN];
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int qr = wc * WTN + j * 16 + (lane & 15);
+                    const uint32_t addr = lds_base + sbase + OPB + qr * ROW +
+                                          ((((kk0 >> 3) ^ ((qr >> 1) & 3))) << 4) + (kk0 & 7) * 2;
+                    asm volatile("ds_read_b64 %0, %1" : "=v"(xv[j]) : "v"(addr));
+                }
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    // the wait is tied to the registers, so no use moves above it
+                    if (j == 0) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(xv[0]));
+                    else asm volatile("" : "+v"(xv[j]));
+                    acc[i][j][0] += d[0] * from_bf16(xv[j].x & 0xFFFFu);
+                    acc[i][j][1] += d[1] * from_bf16(xv[j].x >> 16);
+                    acc[i][j][2] += d[2] * from_bf16(xv[j].y & 0xFFFFu);
+                    acc[i][j][3] += d[3] * from_bf16(xv[j].y >> 16);
+                }
+            }
+        }
+    };
+
     const int KT = K / kBK;
 #pragma unroll
     for (int s = 0; s < kStages; ++s) gload(s * STAGE, s * kBK);
     __builtin_amdgcn_s_waitcnt(WAIT_VM_LGKM0((kStages - 1) * LPS));
     __syncthreads();
+    diag(0, 0);
     read(0, 0);
     int cur = 0;  // buffer of stage kt
     auto body = [&](int kt, auto PAR) __attribute__((always_inline)) {
@@ -408,6 +456,8 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch 
         const int nxt = cur + 1 == kStages ? 0 : cur + 1;
         __builtin_amdgcn_s_waitcnt(WAIT_VM_LGKM0((kStages - 2) * LPS));
         __builtin_amdgcn_s_barrier();
+        diag(nxt * STAGE, (kt + 1) * kBK);
+        __builtin_amdgcn_sched_barrier(0);
         gload(cur * STAGE, (kt + kStages) * kBK);
         read(par ^ 1, nxt * STAGE);
         mma(par);
