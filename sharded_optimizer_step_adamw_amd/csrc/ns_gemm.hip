@@ -509,7 +509,8 @@ NsGroup product_group(int mode, const NsGroupRef &r, int cur_xt) {
     float *dB = reinterpret_cast<float *>(ws + L.db);
     const int64_t ds = (int64_t)(L.d_stride / 4);
     const int64_t xs = (int64_t)(L.x_stride / 2), as = (int64_t)(L.a_stride / 2);
-    const int tm = g.mp / g.tile, tn = g.np / g.tile;
+    const int tile = mode == kGemmBX ? g.tile_bx : g.tile;
+    const int tm = g.mp / tile, tn = g.np / tile;
     NsGroup s{};
     s.d_stride = ds;
     s.tiles_m = tm;
@@ -573,34 +574,37 @@ hipError_t launch_product(const NsGroupRef *refs, const int *idx, int n, int cur
     return hipGetLastError();
 }
 
-template <int T>
-hipError_t run_class(const NsGroupRef *refs, int nrefs, int cur_xt, float a, float b, float c,
-                     hipStream_t stream) {
+// One product for every group whose tile size for it is T, longest reduction
+// first so that the short tiles fill the last rounds.
+template <int T, int MODE>
+hipError_t run_product(const NsGroupRef *refs, int nrefs, int cur_xt, float a, float b, float c,
+                       hipStream_t stream) {
     int idx[kMaxCallGroups];
     int n = 0;
-    for (int i = 0; i < nrefs; ++i)
-        if (refs[i].geom->tile == T) idx[n++] = i;
+    for (int i = 0; i < nrefs; ++i) {
+        const MuonGeom &g = *refs[i].geom;
+        if ((MODE == kGemmBX ? g.tile_bx : g.tile) == T) idx[n++] = i;
+    }
     if (n == 0) return hipSuccess;
-    // longest reduction first, so that the short tiles fill the last rounds
-    auto by_k = [&](int mode) {
-        for (int i = 1; i < n; ++i)
-            for (int j = i; j > 0; --j) {
-                const MuonGeom &p = *refs[idx[j - 1]].geom, &q = *refs[idx[j]].geom;
-                const int kp = mode == kSyrkXXT ? p.np : p.mp, kq = mode == kSyrkXXT ? q.np : q.mp;
-                if (kp >= kq) break;
-                const int t = idx[j - 1];
-                idx[j - 1] = idx[j];
-                idx[j] = t;
-            }
-    };
-    hipError_t e;
-    by_k(kSyrkXXT);
-    e = launch_product<T, kSyrkXXT>(refs, idx, n, cur_xt, a, b, c, stream);
-    if (e != hipSuccess) return e;
-    by_k(kSyrkAA);
-    e = launch_product<T, kSyrkAA>(refs, idx, n, cur_xt, a, b, c, stream);
-    if (e != hipSuccess) return e;
-    return launch_product<T, kGemmBX>(refs, idx, n, cur_xt, a, b, c, stream);
+    for (int i = 1; i < n; ++i)
+        for (int j = i; j > 0; --j) {
+            const MuonGeom &p = *refs[idx[j - 1]].geom, &q = *refs[idx[j]].geom;
+            const int kp = MODE == kSyrkXXT ? p.np : p.mp, kq = MODE == kSyrkXXT ? q.np : q.mp;
+            if (kp >= kq) break;
+            const int t = idx[j - 1];
+            idx[j - 1] = idx[j];
+            idx[j] = t;
+        }
+    return launch_product<T, MODE>(refs, idx, n, cur_xt, a, b, c, stream);
+}
+
+template <int MODE>
+hipError_t run_mode(const NsGroupRef *refs, int nrefs, int cur_xt, float a, float b, float c,
+                    hipStream_t stream) {
+    hipError_t e = run_product<256, MODE>(refs, nrefs, cur_xt, a, b, c, stream);
+    if (e == hipSuccess) e = run_product<128, MODE>(refs, nrefs, cur_xt, a, b, c, stream);
+    if (e == hipSuccess) e = run_product<64, MODE>(refs, nrefs, cur_xt, a, b, c, stream);
+    return e;
 }
 
 }  // namespace
@@ -617,12 +621,14 @@ hipError_t launch_ns_iteration(const NsGroupRef *refs, int nrefs, int cur_xt, fl
                                float c, hipStream_t stream) {
     if (nrefs < 1 || nrefs > kMaxCallGroups) return hipErrorInvalidValue;
     for (int i = 0; i < nrefs; ++i) {
-        const int t = refs[i].geom->tile;
-        if (t != 64 && t != 128 && t != 256) return hipErrorInvalidValue;
+        const MuonGeom &g = *refs[i].geom;
+        for (const int t : {g.tile, g.tile_bx})
+            if ((t != 64 && t != 128 && t != 256) || g.mp % t != 0 || g.np % t != 0)
+                return hipErrorInvalidValue;
     }
-    hipError_t e = run_class<256>(refs, nrefs, cur_xt, a, b, c, stream);
-    if (e == hipSuccess) e = run_class<128>(refs, nrefs, cur_xt, a, b, c, stream);
-    if (e == hipSuccess) e = run_class<64>(refs, nrefs, cur_xt, a, b, c, stream);
+    hipError_t e = run_mode<kSyrkXXT>(refs, nrefs, cur_xt, a, b, c, stream);
+    if (e == hipSuccess) e = run_mode<kSyrkAA>(refs, nrefs, cur_xt, a, b, c, stream);
+    if (e == hipSuccess) e = run_mode<kGemmBX>(refs, nrefs, cur_xt, a, b, c, stream);
     return e;
 }
 

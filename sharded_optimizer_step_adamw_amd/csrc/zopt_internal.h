@@ -78,7 +78,8 @@ struct MuonGeom {
     int32_t transposed;  // rows > cols: X = U^T
     int32_t m, n;
     int32_t mp, np;
-    int32_t tile;        // square output tile of the Newton-Schulz products
+    int32_t tile;        // square output tile of the Newton-Schulz products X X^T and A A
+    int32_t tile_bx;     // and of B X
     int32_t norm_blocks; // workgroups (and norm partials) per matrix, pre-pass 1
 };
 
