@@ -8,8 +8,8 @@ full optimizer step at world 1: AdamW on the tied 50304 x 768 embedding
 (weight decay 0.1) and 25 vectors of 768 (no decay) as two
 zopt_adamw_shard_step calls, and Muon on 12 layers x {Wq, Wk, Wv, Wo 768^2;
 fc 3072 x 768; proj 768 x 3072} as one zopt_muon_step_groups call over the
-three same-shape groups; `value` is its time in ms per step.  Two sub-objects report the other two
-parts of the metric on their own workloads:
+three same-shape groups; `value` is its time in ms per step.  Two sub-objects
+report the other two parts of the metric on their own workloads:
 
   adamw_shard     the ZeRO-2 flat AdamW shard of rank 3 of 8 over a
                   2.0e9-parameter backbone (buckets of 1 << 25, 2.5e8 shard
@@ -334,8 +334,8 @@ def main():
         tf = res_step["ns_iter_flops"] / res_step["ns_iter_ms"] / 1e9
         out.update(value=round(res_step["ms"], 4), unit="ms per optimizer step")
         roof = dict(
-            kernel=("Newton-Schulz iteration: ns_gemm_kernel X X^T + A A + B X, three "
-                    "launches each covering all 72 matrices (3 groups, 128 x 128 tiles)"),
+            kernel=("Newton-Schulz iteration: ns_gemm_kernel X X^T and A A (128 x 128 tiles) "
+                    "+ B X (256 x 256 tiles), one launch each over all 72 matrices"),
             bound="mfma", achieved=round(tf, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
             frac=round(tf / BF16_PEAK_TFLOPS, 4), traffic=None,
             algorithmic_flops_per_unit=res_step["ns_iter_flops"],
