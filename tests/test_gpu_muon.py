@@ -61,7 +61,7 @@ def dev_bf16(bits):
 
 def check_step(batch, rows, cols, seed, ns_steps=5, nesterov=True, adjust=1, lr=8e-4, mu=0.95,
                wd=0.1, dist="normal", momentum_nonzero=True, weights=True, check_ns=True,
-               P=None, M=None, G=None):
+               P=None, M=None, G=None, coeffs=oracle.NS_COEFFS):
     if P is None:
         P, M, G = make_inputs(batch, rows, cols, seed, dist, momentum_nonzero=momentum_nonzero)
     gP = [dev_f32(p) for p in P]
@@ -70,7 +70,7 @@ def check_step(batch, rows, cols, seed, ns_steps=5, nesterov=True, adjust=1, lr=
     gW = [torch.full((rows, cols), 3.0, dtype=torch.bfloat16, device=DEV) for _ in range(batch)]
     lr32, mu32, wd32 = f32(lr), f32(mu), f32(wd)
     ws = z.muon_step(gP, gM, gG, gW if weights else None, lr32, mu32, nesterov, wd32, ns_steps,
-                     adjust_lr=adjust)
+                     ns_coeffs=tuple(f32(x) for x in coeffs), adjust_lr=adjust)
     torch.cuda.synchronize()
     worst = 0.0
     for i in range(batch):
@@ -80,7 +80,7 @@ def check_step(batch, rows, cols, seed, ns_steps=5, nesterov=True, adjust=1, lr=
         o_gpu = u16(z.muon_output_view(ws, batch, rows, cols, ns_steps, i))
         o_gpu32 = oracle.bf16_bits_to_f32(o_gpu)
         if check_ns:
-            o_ref = oracle.newton_schulz(u, ns_steps)
+            o_ref = oracle.newton_schulz(u, ns_steps, tuple(f32(x) for x in coeffs))
             err = rel_fro(o_gpu32.astype(np.float64), o_ref)
             worst = max(worst, err)
             assert err <= NS_TOL, (i, err)
@@ -126,6 +126,18 @@ def test_ragged_shapes(batch, rows, cols):
 def test_ns_step_counts(ns_steps):
     check_step(2, 96, 200, seed=3, ns_steps=ns_steps)
     check_step(1, 200, 96, seed=4, ns_steps=ns_steps)
+
+
+@pytest.mark.parametrize("coeffs,steps", [
+    ((1.5, -0.5, 0.0), 8),              # cubic Newton-Schulz: c = 0, A A term read in the epilogue
+    ((1.5, -0.5, 1e-6), 6),             # b / c beyond the in-loop form's range
+    ((2.0, -1.5, 0.5), 5),              # another quintic with p(1) = 1
+    ((3.4445, -4.7750, 2.0315), 3),
+])
+def test_ns_coefficient_sets(coeffs, steps):
+    check_step(2, 200, 330, seed=11, ns_steps=steps, coeffs=coeffs)
+    check_step(1, 330, 200, seed=12, ns_steps=steps, coeffs=coeffs)
+    check_step(1, 1100, 1300, seed=13, ns_steps=steps, coeffs=coeffs)
 
 
 @pytest.mark.parametrize("nesterov,adjust", [(False, 1), (True, 0), (False, 0)])
