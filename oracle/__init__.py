@@ -9,6 +9,9 @@ calls it.
 * ``zopt_oracle.c`` (built to ``liboracle.so`` with gcc, no FMA contraction):
   the flat bucketed shard layout, binary32 AdamW, round-to-nearest-even
   bf16, the Muon momentum pre-step and the Muon post-step.
+  It also holds the squared gradient norm of a shard with the clip
+  statistics derived from it, and the Newton-Schulz health figures (update
+  ratio, divergence guard).
 * ``ns.py``: Newton-Schulz in float64.
 
 Every array argument is a numpy array of the stated dtype; bf16 values are
@@ -72,6 +75,10 @@ def lib() -> ctypes.CDLL:
         L.orc_muon_scale.argtypes = [i64, i64, ctypes.c_int]
         L.orc_muon_scale.restype = ctypes.c_double
         L.orc_muon_post.argtypes = [i64, i64, vp, vp, vp, f32, f32, ctypes.c_int]
+        L.orc_grad_sq_norm.argtypes = [vp, i64, i64, i32, i32]
+        L.orc_grad_sq_norm.restype = ctypes.c_double
+        L.orc_clip_stats.argtypes = [vp, i32, f32, f32, vp]
+        L.orc_ns_health.argtypes = [i64, i64, vp, f32, vp]
         _lib = L
     return _lib
 
@@ -164,6 +171,27 @@ def adamw_points(p, m, v, g, lr, beta1, beta2, eps, wd, step):
     return w
 
 
+# ----------------------------------------------------------------- clipping
+
+CLIP_FIELDS = ("total_norm", "clip_coef", "clipped", "found_inf", "grad_scale")
+
+
+def grad_sq_norm(grad, n, bucket, world, rank) -> float:
+    """Sum of squares of rank `rank`'s real gradient elements (see zopt_oracle.c)."""
+    _check(grad, np.uint16, "grad")
+    assert grad.size == n
+    return float(lib().orc_grad_sq_norm(_ptr(grad), n, bucket, world, rank))
+
+
+def clip_stats(sq, max_norm, inv_scale=1.0) -> np.ndarray:
+    """[total_norm, clip_coef, clipped, found_inf, grad_scale] (binary32) from
+    the partial sums of squares `sq`, added in order."""
+    sq = np.ascontiguousarray(np.atleast_1d(np.asarray(sq, dtype=np.float64)))
+    out = np.empty(5, dtype=np.float32)
+    lib().orc_clip_stats(_ptr(sq), sq.size, max_norm, inv_scale, _ptr(out))
+    return out
+
+
 # ----------------------------------------------------------------- Muon
 
 def muon_pre(momentum, grad, mu, nesterov=True) -> np.ndarray:
@@ -193,16 +221,45 @@ def muon_post(master, o, lr, wd, adjust=1, want_weight=True):
     return w
 
 
+NS_GUARD = 1000.0  # element magnitude above which an update is refused
+
+
+def ns_health(o, guard=NS_GUARD) -> np.ndarray:
+    """[ratio, absmax, rejected] of one orthogonalised update O [rows, cols]
+    (binary32): ratio = ||O||_F / sqrt(min(rows, cols)), rejected = 1 unless
+    every |O_ij| <= guard."""
+    o = np.ascontiguousarray(o, dtype=np.float32)
+    assert o.ndim == 2
+    out = np.empty(3, dtype=np.float32)
+    lib().orc_ns_health(o.shape[0], o.shape[1], _ptr(o), guard, _ptr(out))
+    return out
+
+
+def ns_call_health(os_, guard=NS_GUARD):
+    """Health of the updates of one Muon call: (number rejected, worst ratio
+    among the updates that passed (0 if none did), per-matrix [ratio, absmax,
+    rejected] rows)."""
+    rows = np.array([ns_health(o, guard) for o in os_], dtype=np.float32).reshape(-1, 3)
+    passed = rows[rows[:, 2] == 0, 0]
+    worst = np.float32(passed.max()) if passed.size else np.float32(0.0)
+    return int(rows[:, 2].sum()), worst, rows
+
+
 def muon_step(master, momentum, grad, lr, mu, nesterov, wd, ns_steps=NS_STEPS,
-              coeffs=NS_COEFFS, ns_eps=NS_EPS, adjust=1, o_override=None):
+              coeffs=NS_COEFFS, ns_eps=NS_EPS, adjust=1, o_override=None, guard=None):
     """The whole Muon step of one matrix, in place on master and momentum.
 
     Returns (weight bits, O in float64).  With ``o_override`` (binary32 O from
     another implementation) the post-step uses it instead of this oracle's own
-    float64 Newton-Schulz result -- stage-wise, teacher-forced checking."""
+    float64 Newton-Schulz result -- stage-wise, teacher-forced checking.  With
+    a ``guard``, an update the divergence guard rejects is not applied: master
+    keeps its value and the weight bits returned are None (momentum has still
+    taken its step)."""
     u = muon_pre(momentum, grad, mu, nesterov)
     o64 = newton_schulz(u, ns_steps, coeffs, ns_eps)
     o = o64.astype(np.float32) if o_override is None else o_override
+    if guard is not None and ns_health(o, guard)[2]:
+        return None, o64
     w = muon_post(master, o, lr, wd, adjust)
     return w, o64
 
@@ -211,6 +268,7 @@ __all__ = [
     "NS_COEFFS", "NS_EPS", "NS_STEPS", "frobenius_prescale", "newton_schulz",
     "ns_scalar_map", "build", "lib", "rne_bf16", "bf16_bits_to_f32",
     "bucket_adjust", "num_buckets", "shard_len", "shard_index_map", "adamw_scalars",
-    "adamw_shard_step", "adamw_points", "muon_pre", "muon_scale", "muon_post",
+    "adamw_shard_step", "adamw_points", "CLIP_FIELDS", "grad_sq_norm", "clip_stats",
+    "muon_pre", "muon_scale", "muon_post", "NS_GUARD", "ns_health", "ns_call_health",
     "muon_step",
 ]

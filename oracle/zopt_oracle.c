@@ -35,6 +35,18 @@
  *                                            block (momentum 0.95, nesterov, wd
  *                                            pinned to AdamW's) and the ShardedMuon
  *                                            note on adjust_lr conventions]
+ *   - the squared gradient norm of a rank's shard, and the clip statistics
+ *     (total norm, clip coefficient, clipped, found_inf) derived from the
+ *     summed squares              [DEG zero.py: ZeroMaster.grad_sq_norm;
+ *                                  BluScript trainer source, cross-group
+ *                                  global clipping block (coefficient
+ *                                  min(1, clip / (norm + 1e-6))); dmuon PR
+ *                                  #16, commit "device-tensor stats"
+ *                                  (finiteness judged on the norm)]
+ *   - Newton-Schulz health: the update-size ratio ||O||_F / sqrt(min(r, c))
+ *     and the element-magnitude divergence guard
+ *                                 [BluScript trainer source, per-step report:
+ *                                  the nsrej / nsratio diagnostics]
  * Newton-Schulz itself is in ns.py (fp64, numpy).
  */
 #include <math.h>
@@ -296,4 +308,96 @@ void orc_muon_post(int64_t rows, int64_t cols, float *master, const float *o,
         if (w)
             w[i] = orc_rne_bf16(pp);
     }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Gradient norm and clip statistics                                          */
+/* ------------------------------------------------------------------------- */
+/* Sum of the squares of rank r's real gradient elements (padding and other
+ * ranks' positions are never read).  Each square of a bf16 value is exact in
+ * double; the sum runs in index order in long double (x86 extended, 64-bit
+ * significand), so the returned double is within about n * 2^-64 of the exact
+ * sum plus one final rounding. */
+double orc_grad_sq_norm(const uint16_t *grad, int64_t n, int64_t bucket, int32_t world,
+                        int32_t rank)
+{
+    int64_t b = orc_bucket_adjust(bucket, world);
+    long double acc = 0.0L;
+    for (int64_t s = 0; s < n; s += b) {
+        int64_t e = s + b < n ? s + b : n;
+        int64_t padded = ((e - s + world - 1) / world) * world;
+        int64_t piece = padded / world;
+        for (int64_t k = 0; k < piece; ++k) {
+            int64_t f = s + (int64_t)rank * piece + k;
+            if (f < e) {
+                double g = (double)bf16_to_f32(grad[f]);
+                acc += (long double)(g * g);
+            }
+        }
+    }
+    return (double)acc;
+}
+
+/* Clip statistics from summed squares.  sq[0..count) are partial sums (one
+ * per rank, say), added in index order in double.
+ *   total_norm = fp32( sqrt(sum) * inv_scale )           (inv_scale undoes a
+ *                                                         loss scale; 1 = none)
+ *   found_inf  = total_norm is not finite                 (judged on the norm)
+ *   clip_coef  = min(1, max_norm / (total_norm + 1e-6))  binary32; a NaN
+ *                quotient stays NaN, an infinite norm gives 0
+ *   clipped    = !found_inf && clip_coef < 1
+ *   grad_scale = inv_scale * clip_coef                    binary32: the factor
+ *                the AdamW step multiplies each promoted gradient by
+ * out = {total_norm, clip_coef, clipped, found_inf, grad_scale}, flags as
+ * 0.0 / 1.0. */
+void orc_clip_stats(const double *sq, int32_t count, float max_norm, float inv_scale,
+                    float out[5])
+{
+    double total = 0.0;
+    for (int32_t i = 0; i < count; ++i)
+        total += sq[i];
+    float norm = (float)(sqrt(total) * (double)inv_scale);
+    int found_inf = !isfinite(norm);
+    float coef = max_norm / (norm + 1e-6f);
+    if (coef > 1.0f)
+        coef = 1.0f;
+    out[0] = norm;
+    out[1] = coef;
+    out[2] = (!found_inf && coef < 1.0f) ? 1.0f : 0.0f;
+    out[3] = found_inf ? 1.0f : 0.0f;
+    out[4] = inv_scale * coef;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Newton-Schulz health                                                       */
+/* ------------------------------------------------------------------------- */
+/* For one orthogonalised update O ([rows, cols] binary32):
+ *   ratio    = ||O||_F / sqrt(min(rows, cols)), 1 for a semi-orthogonal O
+ *              (its min(rows, cols) singular values are all 1); the squares
+ *              are summed in long double, the ratio formed in double and
+ *              rounded to binary32 once
+ *   absmax   = max |O_ij| (NaN if any element is NaN)
+ *   rejected = 1 unless absmax <= guard: the divergence guard refuses the
+ *              update of a matrix with an element beyond the guard or not a
+ *              number
+ * out = {ratio, absmax, rejected}. */
+void orc_ns_health(int64_t rows, int64_t cols, const float *o, float guard, float out[3])
+{
+    long double acc = 0.0L;
+    float amax = 0.0f;
+    int nan_seen = 0;
+    int64_t count = rows * cols;
+    for (int64_t i = 0; i < count; ++i) {
+        double x = (double)o[i];
+        acc += (long double)(x * x);
+        float a = fabsf(o[i]);
+        if (isnan(a))
+            nan_seen = 1;
+        else if (a > amax)
+            amax = a;
+    }
+    double mn = (double)(rows < cols ? rows : cols);
+    out[0] = (float)(sqrt((double)acc) / sqrt(mn));
+    out[1] = nan_seen ? NAN : amax;
+    out[2] = (out[1] <= guard) ? 0.0f : 1.0f;
 }
