@@ -14,6 +14,9 @@ report the other two parts of the metric on their own workloads:
   adamw_shard     the ZeRO-2 flat AdamW shard of rank 3 of 8 over a
                   2.0e9-parameter backbone (buckets of 1 << 25, 2.5e8 shard
                   elements): HBM GB/s at 28 algorithmic bytes per element;
+                  With it, the clipped step on the same shard: the
+                  gradient-norm pass (2 B per element), the clip statistics and
+                  the AdamW step reading grad_scale from device memory;
   newton_schulz   rank 0's Muon share of a 32-layer d=4096 decoder (8 x
                   [14336, 4096], 4 x [4096, 14336], 8 x [4096, 4096],
                   8 x [1024, 4096]): bf16 TFLOP/s at 3 m^2 n + m^3
@@ -45,9 +48,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 # counters were taken on.
 MEASURED_TRAFFIC = {
     "adamw_shard": dict(source="sharded_optimizer_step_adamw_amd/csrc/adamw_shard.hip",
-                        sha256="91fa9988f8538e94ab207b13fbde0560e678592907a2579947068ccfff6be1a8",
+                        sha256="7700ae2a639bcc25367d613767f5358e3cf6fd68c9ed57b1a25e6a6842b9f4a0",
                         bytes_per_launch=7.000e9,
                         profile="profiles/adamw_shard_kernel_zero2_2b_rank3.md"),
+    "grad_sq_norm": dict(source="sharded_optimizer_step_adamw_amd/csrc/adamw_shard.hip",
+                         sha256="7700ae2a639bcc25367d613767f5358e3cf6fd68c9ed57b1a25e6a6842b9f4a0",
+                         bytes_per_launch=0.5004e9,
+                         profile="profiles/grad_sq_norm_kernel_zero2_2b_rank3.md"),
 }
 
 
@@ -65,9 +72,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--parts", default="step,adamw,ns",
-                    help="comma list of: step (headline), adamw, ns, copy (a zopt_round_bf16 "
-                         "pass of known size: the calibration for HBM byte counters)")
+    ap.add_argument("--parts", default="step,adamw,clip,ns",
+                    help="comma list of: step (headline), adamw, clip (the clipped step on the "
+                         "adamw shard; needs adamw), ns, copy (a zopt_round_bf16 pass of known "
+                         "size: the calibration for HBM byte counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
 
@@ -200,7 +208,7 @@ def bench_step(torch, z, timer, dev, K, W):
                 adamw_ms=ta, adamw_gbs=adamw_bytes / ta / 1e6)
 
 
-def bench_adamw(torch, z, timer, dev, K, W):
+def bench_adamw(torch, z, timer, dev, K, W, clip_leg=False):
     s = adamw_zero2_state(torch, dev)
     p, sl = s["part"], s["shard_len"]
     counter = [0]
@@ -213,6 +221,7 @@ def bench_adamw(torch, z, timer, dev, K, W):
 
     timer.run(step, W)
     ms = timer.run(step, K)
+    clip = bench_clip(torch, z, timer, s, K, W) if clip_leg else None
     del s
     torch.cuda.empty_cache()
     gbs = 28 * sl / ms / 1e6
@@ -220,10 +229,55 @@ def bench_adamw(torch, z, timer, dev, K, W):
                 achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=round(gbs / HBM_PEAK_GBS, 4), traffic=measured_traffic("adamw_shard"),
                 algorithmic_bytes_per_launch=28 * sl, avg_launch_ms=round(ms, 4))
-    return dict(workload="zero2 flat AdamW shard: N=2.0e9, bucket 1<<25, world 8, rank 3",
-                shard_len=sl, algorithmic_bytes_per_step=28 * sl, ms_per_step=round(ms, 4),
-                gbs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4), steps=K,
-                roofline=roof)
+    out = dict(workload="zero2 flat AdamW shard: N=2.0e9, bucket 1<<25, world 8, rank 3",
+               shard_len=sl, algorithmic_bytes_per_step=28 * sl, ms_per_step=round(ms, 4),
+               gbs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4), steps=K,
+               roofline=roof)
+    if clip:
+        out["clipped_step"] = clip
+    return out
+
+
+def bench_clip(torch, z, timer, s, K, W):
+    """The clipped step on the same shard: zopt_grad_sq_norm (2 B read per
+    element: the norm pass and its one-workgroup final sum), zopt_grad_clip_stats
+    and zopt_adamw_shard_step_clipped reading grad_scale from device memory --
+    no host round trip anywhere in the step."""
+    p, sl = s["part"], s["shard_len"]
+    dev = s["master"].device
+    ws = torch.empty(z.grad_sq_norm_workspace_bytes(p.n, p.bucket, p.world, p.rank),
+                     dtype=torch.uint8, device=dev)
+    sq = torch.empty(1, dtype=torch.float64, device=dev)
+    stats = torch.empty(z.CLIP_STATS, dtype=torch.float32, device=dev)
+    counter = [0]
+
+    def norm(i):
+        z.grad_sq_norm(s["grads"][i % 4], p.n, p.bucket, p.world, p.rank, out=sq, workspace=ws)
+
+    def step(i):
+        counter[0] += 1
+        g = s["grads"][counter[0] % 4]
+        z.grad_sq_norm(g, p.n, p.bucket, p.world, p.rank, out=sq, workspace=ws)
+        z.grad_clip_stats(sq, 1.0, out=stats)
+        z.adamw_shard_step_clipped(s["master"], s["m"], s["v"], g, s["weight"], p.n, p.bucket,
+                                   p.world, p.rank, p.lr, p.beta1, p.beta2, p.eps,
+                                   p.weight_decay, 10_000 + counter[0], stats,
+                                   skip_nonfinite=True)
+
+    timer.run(norm, W)
+    norm_ms = timer.run(norm, K)
+    timer.run(step, W)
+    step_ms = timer.run(step, K)
+    norm_gbs = 2 * sl / norm_ms / 1e6
+    return dict(
+        norm_ms=round(norm_ms, 4), clipped_step_ms=round(step_ms, 4),
+        clipped_step_gbs=round(30 * sl / step_ms / 1e6, 1), algorithmic_bytes_per_step=30 * sl,
+        clip_coef_last=round(float(stats[z.CLIP_COEF].item()), 6),
+        roofline=dict(kernel="grad_sq_norm_kernel + its one-workgroup final sum (one call)",
+                      bound="hbm", achieved=round(norm_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=round(norm_gbs / HBM_PEAK_GBS, 4),
+                      traffic=measured_traffic("grad_sq_norm"),
+                      algorithmic_bytes_per_launch=2 * sl, avg_launch_ms=round(norm_ms, 4)))
 
 
 def bench_ns(torch, z, timer, dev, K, W):
@@ -327,7 +381,8 @@ def main():
     K, W = args.steps, args.warmup
     out = dict(metric=METRIC)
     res_step = bench_step(torch, z, timer, dev, K, W) if "step" in parts else None
-    res_adamw = bench_adamw(torch, z, timer, dev, max(K, 100), W) if "adamw" in parts else None
+    res_adamw = (bench_adamw(torch, z, timer, dev, max(K, 100), W, clip_leg="clip" in parts)
+                 if "adamw" in parts else None)
     res_ns = bench_ns(torch, z, timer, dev, max(2, K // 5), W) if "ns" in parts else None
     res_copy = bench_copy(torch, z, timer, dev, K, W) if "copy" in parts else None
     if res_step:

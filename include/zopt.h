@@ -13,7 +13,10 @@
  *    cores, a decayed and scaled update of the fp32 master), and
  *    zopt_muon_step_groups, the same on several shapes in one call;
  *  - zopt_round_bf16: the fp32 -> bf16 round-to-nearest-even write-back on
- *    its own.
+ *    its own;
+ *  - zopt_grad_sq_norm, zopt_grad_clip_stats and zopt_adamw_shard_step_clipped:
+ *    the gradient norm of the shard, the clip statistics, and the AdamW step
+ *    taking its gradient scale from them in device memory.
  *
  * Conventions common to every call
  * --------------------------------
@@ -125,6 +128,106 @@ zopt_status zopt_adamw_shard_step(float *master, float *exp_avg, float *exp_avg_
                                   float lr, float beta1, float beta2, float eps,
                                   float weight_decay, int64_t step, float grad_scale,
                                   void *stream);
+
+/*
+ * Gradient clipping without a host round trip.  A ZeRO rank clips on the
+ * norm of the whole summed gradient: each rank squares and sums its own real
+ * gradient elements, the ranks' sums are added (an all-reduce, not part of
+ * this library), and the clip coefficient derived from the total scales the
+ * gradient as the AdamW step loads it [DEG zero.py: ZeroMaster.grad_sq_norm;
+ * BluScript trainer source, cross-group global clipping block: coefficient
+ * min(1, clip / (norm + 1e-6)), and the Muon path does not apply it; DeepSpeed
+ * PR #9021, commit "grad_scale": the factor is multiplied in as each gradient
+ * element is loaded].  The statistics stay in device memory as binary32
+ * scalars, so nothing waits for the host [dmuon PR #16, commit "device-tensor
+ * stats": total_norm / clip_coef / clipped / found_inf as device scalars,
+ * finiteness judged on the norm, so an infinite norm reports found_inf and
+ * not clipped].  A clipped step is three calls on one stream:
+ *
+ *   zopt_grad_sq_norm(grad, ..., sq, ws, &ws_bytes, s);     per rank
+ *   (all-reduce sq over ranks, or pass the per-rank sums to the next call)
+ *   zopt_grad_clip_stats(sq, 1, max_norm, inv_scale, stats, s);
+ *   zopt_adamw_shard_step_clipped(..., stats, skip_nonfinite, s);
+ */
+
+/* Layout of the clip statistics: ZOPT_CLIP_STATS binary32 values. */
+enum {
+    ZOPT_CLIP_TOTAL_NORM = 0, /* fp32(sqrt(sum of squares) * inv_scale)            */
+    ZOPT_CLIP_COEF = 1,       /* min(1, max_norm / (total_norm + 1e-6)), binary32   */
+    ZOPT_CLIP_CLIPPED = 2,    /* 1 if !found_inf and clip_coef < 1, else 0          */
+    ZOPT_CLIP_FOUND_INF = 3,  /* 1 if total_norm is not finite, else 0              */
+    ZOPT_CLIP_GRAD_SCALE = 4, /* inv_scale * clip_coef: the AdamW gradient factor   */
+    ZOPT_CLIP_STATS = 5
+};
+
+/*
+ * zopt_grad_sq_norm -- *sq = the sum of the squares of rank `rank`'s real
+ * gradient elements (the layout of zopt_adamw_shard_step; padding and other
+ * ranks' positions are not read).  Each square is exact in double and the sum
+ * is double, in an order fixed by shard_len alone: the result is the same on
+ * every run.
+ *
+ * Arguments
+ *   grad      bf16 [N] flat gradient, device, read.
+ *   N, bucket, world, rank, shard_len   as for zopt_adamw_shard_step.
+ *   sq        one double, device, written.
+ *   workspace device scratch, 256-byte aligned, of at least the size the
+ *             NULL-workspace query writes to *workspace_bytes (at most 16 KiB);
+ *             with workspace == NULL the call only writes that size.
+ *   stream    hipStream_t or NULL.
+ *
+ * Errors: ZOPT_ERR_NULL (workspace_bytes NULL; grad or sq NULL with a
+ * workspace); ZOPT_ERR_SIZE (the layout arguments as for
+ * zopt_adamw_shard_step); ZOPT_ERR_WORKSPACE; ZOPT_ERR_DEVICE.
+ */
+zopt_status zopt_grad_sq_norm(const uint16_t *grad, int64_t N, int64_t bucket, int32_t world,
+                              int32_t rank, int64_t shard_len, double *sq, void *workspace,
+                              size_t *workspace_bytes, void *stream);
+
+/*
+ * zopt_grad_clip_stats -- the clip statistics (layout above) from `count`
+ * sums of squares, added in index order in double:
+ *   total_norm = fp32(sqrt(sum) * inv_scale)
+ *   clip_coef  = min(1, max_norm / (total_norm + 1e-6f)), binary32; an
+ *                infinite norm gives 0, a NaN norm gives NaN
+ *   clipped    = !found_inf && clip_coef < 1,  found_inf = !isfinite(total_norm)
+ *   grad_scale = inv_scale * clip_coef
+ *
+ * Arguments
+ *   sq         `count` doubles, device, read (per-rank sums, or one total).
+ *   count      1 .. 65536.
+ *   max_norm   > 0 (+inf reports the norm without clipping).
+ *   inv_scale  finite, > 0: the gradients are a loss scale times the true
+ *              ones; 1 = none.
+ *   stats      ZOPT_CLIP_STATS floats, device, written.
+ *   stream     hipStream_t or NULL.
+ *
+ * Errors: ZOPT_ERR_NULL; ZOPT_ERR_SIZE (count); ZOPT_ERR_HYPER (max_norm,
+ * inv_scale); ZOPT_ERR_DEVICE.
+ */
+zopt_status zopt_grad_clip_stats(const double *sq, int32_t count, float max_norm,
+                                 float inv_scale, float *stats, void *stream);
+
+/*
+ * zopt_adamw_shard_step_clipped -- zopt_adamw_shard_step with grad_scale
+ * read from device memory when the kernel runs: grad_scale =
+ * clip_stats[ZOPT_CLIP_GRAD_SCALE].  With skip_nonfinite = 1 a step whose
+ * clip_stats[ZOPT_CLIP_FOUND_INF] is non-zero writes nothing (master, moments
+ * and weights keep their values); the step count is the caller's, who may
+ * read found_inf later and not count that step.  Every other argument,
+ * and the arithmetic, as zopt_adamw_shard_step: given the same grad_scale
+ * value the two calls give the same bits.
+ *
+ * Errors: those of zopt_adamw_shard_step; ZOPT_ERR_NULL also for clip_stats
+ * NULL; ZOPT_ERR_HYPER also for skip_nonfinite not 0/1.
+ */
+zopt_status zopt_adamw_shard_step_clipped(float *master, float *exp_avg, float *exp_avg_sq,
+                                          const uint16_t *grad, uint16_t *weight, int64_t N,
+                                          int64_t bucket, int32_t world, int32_t rank,
+                                          int64_t shard_len, float lr, float beta1, float beta2,
+                                          float eps, float weight_decay, int64_t step,
+                                          const float *clip_stats, int32_t skip_nonfinite,
+                                          void *stream);
 
 /*
  * zopt_shard_len -- the shard length every rank holds for a flat vector of N

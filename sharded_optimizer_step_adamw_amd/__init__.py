@@ -16,6 +16,9 @@ Entry points (same names as the C ABI in include/zopt.h):
   muon_groups_workspace_bytes / muon_groups_output_view
   round_bf16         fp32 -> bf16 round-to-nearest-even
   shard_len          the shard length the layout derives (zopt_shard_len)
+  grad_sq_norm       sum of squares of a rank's real gradient elements
+  grad_clip_stats    clip statistics (device scalars) from summed squares
+  adamw_shard_step_clipped   AdamW taking grad_scale from the clip statistics
 """
 from __future__ import annotations
 
@@ -29,6 +32,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libzopt.so")
 
 ZOPT_OK, ZOPT_ERR_NULL, ZOPT_ERR_SIZE, ZOPT_ERR_HYPER, ZOPT_ERR_WORKSPACE, ZOPT_ERR_DEVICE = range(6)
+# layout of the clip statistics (ZOPT_CLIP_* in zopt.h)
+CLIP_TOTAL_NORM, CLIP_COEF, CLIP_CLIPPED, CLIP_FOUND_INF, CLIP_GRAD_SCALE, CLIP_STATS = range(6)
 MAX_BATCH = 64
 MAX_GROUPS = 16
 
@@ -57,6 +62,15 @@ def _lib_or_raise() -> ctypes.CDLL:
         L.zopt_adamw_shard_step.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, i64,
                                             f32, f32, f32, f32, f32, i64, f32, vp]
         L.zopt_adamw_shard_step.restype = ctypes.c_int
+        L.zopt_adamw_shard_step_clipped.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32,
+                                                    i64, f32, f32, f32, f32, f32, i64, vp, i32,
+                                                    vp]
+        L.zopt_adamw_shard_step_clipped.restype = ctypes.c_int
+        L.zopt_grad_sq_norm.argtypes = [vp, i64, i64, i32, i32, i64, vp, vp,
+                                        ctypes.POINTER(ctypes.c_size_t), vp]
+        L.zopt_grad_sq_norm.restype = ctypes.c_int
+        L.zopt_grad_clip_stats.argtypes = [vp, i32, f32, f32, vp, vp]
+        L.zopt_grad_clip_stats.restype = ctypes.c_int
         L.zopt_shard_len.argtypes = [i64, i64, i32]
         L.zopt_shard_len.restype = i64
         L.zopt_round_bf16.argtypes = [vp, vp, i64, vp]
@@ -139,6 +153,73 @@ def adamw_shard_step(master, exp_avg, exp_avg_sq, grad, weight, n, bucket, world
         None if weight is None else weight.data_ptr(), n, bucket, world, rank, sl,
         lr, beta1, beta2, eps, weight_decay, step, grad_scale, _stream(dev, stream))
     _check(st, "zopt_adamw_shard_step")
+
+
+def adamw_shard_step_clipped(master, exp_avg, exp_avg_sq, grad, weight, n, bucket, world, rank,
+                             lr, beta1, beta2, eps, weight_decay, step, clip_stats,
+                             skip_nonfinite=False, shard_len_=None, stream=None) -> None:
+    """adamw_shard_step with grad_scale read from the device clip statistics
+    (fp32 [CLIP_STATS]) when the kernel runs (zopt_adamw_shard_step_clipped)."""
+    sl = shard_len(n, bucket, world) if shard_len_ is None else shard_len_
+    dev = master.device
+    _need(master, torch.float32, sl, "master")
+    _need(exp_avg, torch.float32, sl, "exp_avg", dev)
+    _need(exp_avg_sq, torch.float32, sl, "exp_avg_sq", dev)
+    _need(grad, torch.bfloat16, n, "grad", dev)
+    _need(clip_stats, torch.float32, CLIP_STATS, "clip_stats", dev)
+    if weight is not None:
+        _need(weight, torch.bfloat16, n, "weight", dev)
+    st = lib().zopt_adamw_shard_step_clipped(
+        master.data_ptr(), exp_avg.data_ptr(), exp_avg_sq.data_ptr(), grad.data_ptr(),
+        None if weight is None else weight.data_ptr(), n, bucket, world, rank, sl,
+        lr, beta1, beta2, eps, weight_decay, step, clip_stats.data_ptr(), int(skip_nonfinite),
+        _stream(dev, stream))
+    _check(st, "zopt_adamw_shard_step_clipped")
+
+
+def grad_sq_norm_workspace_bytes(n: int, bucket: int, world: int, rank: int = 0) -> int:
+    size = ctypes.c_size_t(0)
+    st = lib().zopt_grad_sq_norm(None, n, bucket, world, rank, shard_len(n, bucket, world),
+                                 None, None, ctypes.byref(size), None)
+    _check(st, "zopt_grad_sq_norm(workspace query)")
+    return int(size.value)
+
+
+def grad_sq_norm(grad, n, bucket, world, rank, out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Sum of squares of rank `rank`'s real gradient elements, as a float64
+    [1] device tensor (zopt_grad_sq_norm); nothing is read back."""
+    dev = grad.device
+    _need(grad, torch.bfloat16, n, "grad")
+    if out is None:
+        out = torch.empty(1, dtype=torch.float64, device=dev)
+    _need(out, torch.float64, 1, "out", dev)
+    need = grad_sq_norm_workspace_bytes(n, bucket, world, rank)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _need(workspace, torch.uint8, need, "workspace", dev)
+    size = ctypes.c_size_t(workspace.numel())
+    st = lib().zopt_grad_sq_norm(grad.data_ptr(), n, bucket, world, rank,
+                                 shard_len(n, bucket, world), out.data_ptr(),
+                                 workspace.data_ptr(), ctypes.byref(size), _stream(dev, stream))
+    _check(st, "zopt_grad_sq_norm")
+    return out
+
+
+def grad_clip_stats(sq: torch.Tensor, max_norm: float, inv_scale: float = 1.0,
+                    out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Clip statistics (fp32 [CLIP_STATS] device tensor: total_norm,
+    clip_coef, clipped, found_inf, grad_scale) from the float64 sums of
+    squares in `sq`, added in order (zopt_grad_clip_stats)."""
+    dev = sq.device
+    _need(sq, torch.float64, 1, "sq")
+    if out is None:
+        out = torch.empty(CLIP_STATS, dtype=torch.float32, device=dev)
+    _need(out, torch.float32, CLIP_STATS, "out", dev)
+    st = lib().zopt_grad_clip_stats(sq.data_ptr(), sq.numel(), max_norm, inv_scale,
+                                    out.data_ptr(), _stream(dev, stream))
+    _check(st, "zopt_grad_clip_stats")
+    return out
 
 
 def round_bf16(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:

@@ -14,6 +14,13 @@
 // wave-wide load or store instruction covers one contiguous kilobyte of a
 // state array.  Nothing is re-read, so every access is a streaming
 // (non-temporal) one.
+//
+// Also here: the squared gradient norm of the same shard (2 B read per
+// element) and the clip statistics derived from it [DEG zero.py:
+// ZeroMaster.grad_sq_norm; BluScript trainer source, cross-group global
+// clipping block; dmuon PR #16, commit "device-tensor stats"], which a
+// device-scale variant of the AdamW kernel reads as its grad_scale without
+// any host round trip.
 #include "zopt_internal.h"
 
 // Bit-exact arithmetic: every + - * / below is one correctly rounded binary32
@@ -69,18 +76,18 @@ __device__ __forceinline__ int64_t flat_of(int64_t j, const AdamWParams &a, bool
     return f;
 }
 
-// Flat index of the first element of tile [t0, t0 + kTile) when the whole
+// Flat index of the first element of tile [t0, t0 + tile) when the whole
 // tile maps to consecutive real flat positions (one bucket's piece, no
 // padding, inside the shard), else -1.
-__device__ __forceinline__ int64_t tile_flat(int64_t t0, const AdamWParams &a) {
-    const int64_t t1 = t0 + kTile;
+__device__ __forceinline__ int64_t tile_flat(int64_t t0, int64_t tile, const AdamWParams &a) {
+    const int64_t t1 = t0 + tile;
     if (t1 <= a.full_len) {
         const int64_t b = bucket_of(t0, a);
         return bucket_of(t1 - 1, a) == b ? t0 + b * a.gap + a.rank_off : -1;
     }
     if (t0 >= a.full_len && t1 <= a.shard_len) {
         const int64_t f0 = a.last_flat0 + (t0 - a.full_len);
-        return f0 + kTile <= a.n ? f0 : -1;
+        return f0 + tile <= a.n ? f0 : -1;
     }
     return -1;
 }
@@ -91,11 +98,19 @@ __device__ __forceinline__ int64_t tile_flat(int64_t t0, const AdamWParams &a) {
 // of fp32 state (and 512 bytes of bf16).  A tile that straddles a bucket
 // edge, touches padding, ends the shard or is misaligned takes the generic
 // path: one element at a time, still coalesced across the workgroup.
+// kDevScale: grad_scale is read from the clip statistics in device memory
+// (a.stats), and with a.skip_nonfinite a found_inf there leaves every output
+// untouched.
+template <bool kDevScale>
 __global__ __launch_bounds__(kThreads) void adamw_shard_kernel(
     float *__restrict__ master, float *__restrict__ exp_avg, float *__restrict__ exp_avg_sq,
     const uint16_t *__restrict__ grad, uint16_t *__restrict__ weight, AdamWParams a) {
+    if constexpr (kDevScale) {
+        if (a.skip_nonfinite && a.stats[kClipFoundInf] != 0.0f) return;
+        a.grad_scale = a.stats[kClipGradScale];
+    }
     const int64_t t0 = (int64_t)blockIdx.x * kTile;
-    const int64_t f0 = a.vec ? tile_flat(t0, a) : -1;
+    const int64_t f0 = a.vec ? tile_flat(t0, kTile, a) : -1;
     if (f0 >= 0 && (f0 & 3) == 0) {
         f32x4 p[kGroups], m[kGroups], v[kGroups];
         u32x2 g[kGroups];
@@ -145,6 +160,107 @@ __global__ __launch_bounds__(kThreads) void adamw_shard_kernel(
     }
 }
 
+// ------------------------------------------------------------------ norm
+
+constexpr int kNormLoads = 4;                              // 16-byte loads per thread per tile
+constexpr int kNormTile = kThreads * 8 * kNormLoads;       // 8192 shard elements
+typedef double f64;
+
+// acc + x^2 for the bf16 value x: the square is exact in double (16
+// significant bits, exponent in range), so one fused multiply-add rounds
+// exactly as the separate multiply and add would.
+__device__ __forceinline__ f64 add_sq_bf16(f64 acc, uint32_t bits) {
+    const f64 x = (f64)bf16_bits_to_float(bits);
+    return __builtin_fma(x, x, acc);
+}
+
+// Sum over the workgroup, the same in every run: a butterfly within each
+// wave, then the waves' sums in wave order.  Valid in thread 0.
+__device__ __forceinline__ f64 block_sum(f64 v, f64 *lds) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = v;
+    __syncthreads();
+    f64 s = 0.0;
+    if (threadIdx.x == 0)
+        for (int w = 0; w < kThreads / 64; ++w) s += lds[w];
+    return s;
+}
+
+// Partial sums of squares of the real gradient elements of the shard.  The
+// grid is fixed by the shard length alone, so the summation order (each
+// thread's running sum over its tiles, then the workgroup sum) is the same on
+// every run and every device.  A tile of consecutive real flat positions is
+// read with 16-byte loads, one contiguous kilobyte per wave instruction, four
+// in flight per thread; any other tile element by element.
+__global__ __launch_bounds__(kThreads) void grad_sq_norm_kernel(
+    const uint16_t *__restrict__ grad, AdamWParams a, int64_t tiles, f64 *__restrict__ partials) {
+    __shared__ f64 lds[kThreads / 64];
+    f64 acc = 0.0;
+    for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+        const int64_t t0 = t * kNormTile;
+        const int64_t f0 = a.vec ? tile_flat(t0, kNormTile, a) : -1;
+        if (f0 >= 0 && (f0 & 7) == 0) {
+            u32x4 g[kNormLoads];
+#pragma unroll
+            for (int q = 0; q < kNormLoads; ++q)
+                g[q] = ld_stream(reinterpret_cast<const u32x4 *>(
+                    grad + f0 + (int64_t)q * kThreads * 8 + threadIdx.x * 8));
+#pragma unroll
+            for (int q = 0; q < kNormLoads; ++q) {
+                const uint32_t w[4] = {g[q].x, g[q].y, g[q].z, g[q].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc = add_sq_bf16(acc, w[e] & 0xFFFFu);
+                    acc = add_sq_bf16(acc, w[e] >> 16);
+                }
+            }
+        } else {
+            for (int k = 0; k < kNormTile / kThreads; ++k) {
+                const int64_t j = t0 + (int64_t)k * kThreads + threadIdx.x;
+                if (j >= a.shard_len) break;
+                bool real;
+                const int64_t f = flat_of(j, a, real);
+                if (real) acc = add_sq_bf16(acc, grad[f]);
+            }
+        }
+    }
+    const f64 s = block_sum(acc, lds);
+    if (threadIdx.x == 0) partials[blockIdx.x] = s;
+}
+
+// sq[0] = the partials added in a fixed order (one workgroup).
+__global__ __launch_bounds__(kThreads) void sq_norm_final_kernel(
+    const f64 *__restrict__ partials, int32_t count, f64 *__restrict__ sq) {
+    __shared__ f64 lds[kThreads / 64];
+    f64 acc = 0.0;
+    for (int i = threadIdx.x; i < count; i += kThreads) acc += partials[i];
+    const f64 s = block_sum(acc, lds);
+    if (threadIdx.x == 0) sq[0] = s;
+}
+
+// The clip statistics from `count` summed-square partials (in index order):
+//   total_norm = fp32(sqrt(sum) * inv_scale); found_inf = total_norm not
+//   finite; clip_coef = min(1, max_norm / (total_norm + 1e-6)) in binary32,
+//   NaN staying NaN; clipped = !found_inf && clip_coef < 1;
+//   grad_scale = inv_scale * clip_coef.
+__global__ __launch_bounds__(64) void clip_stats_kernel(const f64 *__restrict__ sq, int32_t count,
+                                                        float max_norm, float inv_scale,
+                                                        float *__restrict__ stats) {
+    if (threadIdx.x != 0) return;
+    f64 total = 0.0;
+    for (int i = 0; i < count; ++i) total += sq[i];
+    const float norm = (float)(__builtin_sqrt(total) * (f64)inv_scale);
+    const bool found_inf = !__builtin_isfinite(norm);
+    float coef = max_norm / (norm + 1e-6f);
+    if (coef > 1.0f) coef = 1.0f;
+    stats[kClipTotalNorm] = norm;
+    stats[kClipCoef] = coef;
+    stats[kClipClipped] = (!found_inf && coef < 1.0f) ? 1.0f : 0.0f;
+    stats[kClipFoundInf] = found_inf ? 1.0f : 0.0f;
+    stats[kClipGradScale] = inv_scale * coef;
+}
+
 // dst[i] = bf16(src[i]), 6 bytes of traffic per element, in the same tiles
 // as the AdamW kernel (one contiguous kilobyte of fp32 per wave instruction).
 __global__ __launch_bounds__(kThreads) void round_bf16_kernel(
@@ -180,8 +296,38 @@ hipError_t launch_adamw_shard(float *master, float *exp_avg, float *exp_avg_sq,
             aligned8(grad) && (weight == nullptr || aligned8(weight));
     p.inv_piece = 1.0 / (double)p.piece;
     const int64_t blocks = (p.shard_len + kTile - 1) / kTile;
-    hipLaunchKernelGGL(adamw_shard_kernel, dim3((uint32_t)blocks), dim3(kThreads), 0, stream,
-                       master, exp_avg, exp_avg_sq, grad, weight, p);
+    if (p.stats)
+        hipLaunchKernelGGL(adamw_shard_kernel<true>, dim3((uint32_t)blocks), dim3(kThreads), 0,
+                           stream, master, exp_avg, exp_avg_sq, grad, weight, p);
+    else
+        hipLaunchKernelGGL(adamw_shard_kernel<false>, dim3((uint32_t)blocks), dim3(kThreads), 0,
+                           stream, master, exp_avg, exp_avg_sq, grad, weight, p);
+    return hipGetLastError();
+}
+
+int32_t grad_sq_norm_blocks(int64_t shard_len) {
+    const int64_t tiles = (shard_len + kNormTile - 1) / kNormTile;
+    return (int32_t)(tiles < kNormBlocksMax ? tiles : kNormBlocksMax);
+}
+
+hipError_t launch_grad_sq_norm(const uint16_t *grad, const AdamWParams &p_in, double *partials,
+                               double *sq, hipStream_t stream) {
+    AdamWParams p = p_in;
+    p.vec = aligned16(grad);
+    p.inv_piece = 1.0 / (double)p.piece;
+    const int64_t tiles = (p.shard_len + kNormTile - 1) / kNormTile;
+    const int32_t blocks = grad_sq_norm_blocks(p.shard_len);
+    hipLaunchKernelGGL(grad_sq_norm_kernel, dim3((uint32_t)blocks), dim3(kThreads), 0, stream,
+                       grad, p, tiles, partials);
+    hipLaunchKernelGGL(sq_norm_final_kernel, dim3(1), dim3(kThreads), 0, stream, partials, blocks,
+                       sq);
+    return hipGetLastError();
+}
+
+hipError_t launch_clip_stats(const double *sq, int32_t count, float max_norm, float inv_scale,
+                             float *stats, hipStream_t stream) {
+    hipLaunchKernelGGL(clip_stats_kernel, dim3(1), dim3(64), 0, stream, sq, count, max_norm,
+                       inv_scale, stats);
     return hipGetLastError();
 }
 

@@ -106,21 +106,23 @@ ZOPT_EXPORT const char *zopt_status_string(zopt_status s) {
     return "unknown zopt_status";
 }
 
-ZOPT_EXPORT zopt_status zopt_adamw_shard_step(float *master, float *exp_avg, float *exp_avg_sq,
-                                              const uint16_t *grad, uint16_t *weight, int64_t N,
-                                              int64_t bucket, int32_t world, int32_t rank,
-                                              int64_t shard_len, float lr, float beta1,
-                                              float beta2, float eps, float weight_decay,
-                                              int64_t step, float grad_scale, void *stream) {
+namespace {
+
+// Checks of the AdamW arguments common to both entry points and the launch
+// parameters they derive (the per-step scalars in double, rounded once).
+zopt_status adamw_prepare(const float *master, const float *exp_avg, const float *exp_avg_sq,
+                          const uint16_t *grad, int64_t N, int64_t bucket, int32_t world,
+                          int32_t rank, int64_t shard_len, float lr, float beta1, float beta2,
+                          float eps, float weight_decay, int64_t step, AdamWParams &p) {
     if (!master || !exp_avg || !exp_avg_sq || !grad) return ZOPT_ERR_NULL;
     if (N < 1 || bucket < 1 || world < 1 || rank < 0 || rank >= world) return ZOPT_ERR_SIZE;
     // the grid holds at most 2^32 - 1 work-items of 8 elements each
     if (N > ((int64_t)1 << 40)) return ZOPT_ERR_SIZE;
     if (!finite(lr) || lr < 0.0f || !(beta1 >= 0.0f && beta1 < 1.0f) ||
         !(beta2 >= 0.0f && beta2 < 1.0f) || !finite(eps) || eps <= 0.0f ||
-        !finite(weight_decay) || weight_decay < 0.0f || step < 1 || !finite(grad_scale))
+        !finite(weight_decay) || weight_decay < 0.0f || step < 1)
         return ZOPT_ERR_HYPER;
-    AdamWParams p{};
+    p = AdamWParams{};
     const int64_t want = adamw_layout(N, bucket, world, rank, p);
     if (shard_len != want) return ZOPT_ERR_SIZE;
     p.shard_len = shard_len;
@@ -136,9 +138,76 @@ ZOPT_EXPORT zopt_status zopt_adamw_shard_step(float *master, float *exp_avg, flo
     p.decay = (float)(1.0 - (double)lr * (double)weight_decay);
     p.omb1 = (float)(1.0 - (double)beta1);
     p.omb2 = (float)(1.0 - (double)beta2);
+    p.grad_scale = 1.0f;
+    return ZOPT_OK;
+}
+
+}  // namespace
+
+ZOPT_EXPORT zopt_status zopt_adamw_shard_step(float *master, float *exp_avg, float *exp_avg_sq,
+                                              const uint16_t *grad, uint16_t *weight, int64_t N,
+                                              int64_t bucket, int32_t world, int32_t rank,
+                                              int64_t shard_len, float lr, float beta1,
+                                              float beta2, float eps, float weight_decay,
+                                              int64_t step, float grad_scale, void *stream) {
+    AdamWParams p;
+    const zopt_status st = adamw_prepare(master, exp_avg, exp_avg_sq, grad, N, bucket, world,
+                                         rank, shard_len, lr, beta1, beta2, eps, weight_decay,
+                                         step, p);
+    if (st != ZOPT_OK) return st;
+    if (!finite(grad_scale)) return ZOPT_ERR_HYPER;
     p.grad_scale = grad_scale;
     hipError_t e = launch_adamw_shard(master, exp_avg, exp_avg_sq, grad, weight, p,
                                       (hipStream_t)stream);
+    return e == hipSuccess ? ZOPT_OK : ZOPT_ERR_DEVICE;
+}
+
+ZOPT_EXPORT zopt_status zopt_adamw_shard_step_clipped(
+    float *master, float *exp_avg, float *exp_avg_sq, const uint16_t *grad, uint16_t *weight,
+    int64_t N, int64_t bucket, int32_t world, int32_t rank, int64_t shard_len, float lr,
+    float beta1, float beta2, float eps, float weight_decay, int64_t step,
+    const float *clip_stats, int32_t skip_nonfinite, void *stream) {
+    AdamWParams p;
+    const zopt_status st = adamw_prepare(master, exp_avg, exp_avg_sq, grad, N, bucket, world,
+                                         rank, shard_len, lr, beta1, beta2, eps, weight_decay,
+                                         step, p);
+    if (st != ZOPT_OK) return st;
+    if (!clip_stats) return ZOPT_ERR_NULL;
+    if (skip_nonfinite != 0 && skip_nonfinite != 1) return ZOPT_ERR_HYPER;
+    p.stats = clip_stats;
+    p.skip_nonfinite = skip_nonfinite;
+    hipError_t e = launch_adamw_shard(master, exp_avg, exp_avg_sq, grad, weight, p,
+                                      (hipStream_t)stream);
+    return e == hipSuccess ? ZOPT_OK : ZOPT_ERR_DEVICE;
+}
+
+ZOPT_EXPORT zopt_status zopt_grad_sq_norm(const uint16_t *grad, int64_t N, int64_t bucket,
+                                          int32_t world, int32_t rank, int64_t shard_len,
+                                          double *sq, void *workspace, size_t *workspace_bytes,
+                                          void *stream) {
+    if (!workspace_bytes) return ZOPT_ERR_NULL;
+    if (N < 1 || bucket < 1 || world < 1 || rank < 0 || rank >= world) return ZOPT_ERR_SIZE;
+    if (N > ((int64_t)1 << 40)) return ZOPT_ERR_SIZE;
+    AdamWParams p{};
+    if (shard_len != adamw_layout(N, bucket, world, rank, p)) return ZOPT_ERR_SIZE;
+    p.shard_len = shard_len;
+    const size_t need = round_up((size_t)grad_sq_norm_blocks(shard_len) * sizeof(double), 256);
+    if (!workspace) {
+        *workspace_bytes = need;
+        return ZOPT_OK;
+    }
+    if (!grad || !sq) return ZOPT_ERR_NULL;
+    if (*workspace_bytes < need || ((uintptr_t)workspace & 255u)) return ZOPT_ERR_WORKSPACE;
+    hipError_t e = launch_grad_sq_norm(grad, p, (double *)workspace, sq, (hipStream_t)stream);
+    return e == hipSuccess ? ZOPT_OK : ZOPT_ERR_DEVICE;
+}
+
+ZOPT_EXPORT zopt_status zopt_grad_clip_stats(const double *sq, int32_t count, float max_norm,
+                                             float inv_scale, float *stats, void *stream) {
+    if (!sq || !stats) return ZOPT_ERR_NULL;
+    if (count < 1 || count > 65536) return ZOPT_ERR_SIZE;
+    if (!(max_norm > 0.0f) || !finite(inv_scale) || !(inv_scale > 0.0f)) return ZOPT_ERR_HYPER;
+    hipError_t e = launch_clip_stats(sq, count, max_norm, inv_scale, stats, (hipStream_t)stream);
     return e == hipSuccess ? ZOPT_OK : ZOPT_ERR_DEVICE;
 }
 

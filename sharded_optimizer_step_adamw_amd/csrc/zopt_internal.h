@@ -55,7 +55,26 @@ struct AdamWParams {
     float grad_scale;
     int32_t vec;         // fp32 bases 16-byte and bf16 bases 8-byte aligned
     double inv_piece;    // 1 / piece, for the bucket index
+    const float *stats;  // clip statistics in device memory: grad_scale read there (or NULL)
+    int32_t skip_nonfinite;  // with stats: a found_inf there skips the step
 };
+
+// Indices of the clip statistics (binary32 each; flags 0 / 1).
+enum : int { kClipTotalNorm = 0, kClipCoef = 1, kClipClipped = 2, kClipFoundInf = 3,
+             kClipGradScale = 4, kClipStats = 5 };
+
+// Workgroups (and fp64 partials) of the gradient-norm pass: fixed by the
+// shard length, at most kNormBlocksMax.
+constexpr int kNormBlocksMax = 2048;
+int32_t grad_sq_norm_blocks(int64_t shard_len);
+
+// sq[0] = sum of squares of the shard's real gradient elements; partials
+// holds grad_sq_norm_blocks(shard_len) doubles of scratch.
+hipError_t launch_grad_sq_norm(const uint16_t *grad, const AdamWParams &p, double *partials,
+                               double *sq, hipStream_t stream);
+
+hipError_t launch_clip_stats(const double *sq, int32_t count, float max_norm, float inv_scale,
+                             float *stats, hipStream_t stream);
 
 hipError_t launch_adamw_shard(float *master, float *exp_avg, float *exp_avg_sq,
                               const uint16_t *grad, uint16_t *weight,

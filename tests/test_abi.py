@@ -71,6 +71,72 @@ def test_adamw_rejects(kw, status):
     assert adamw(**kw) == status
 
 
+def adamw_clipped(**kw):
+    a = dict(master=FAKE, exp_avg=FAKE, exp_avg_sq=FAKE, grad=FAKE, weight=None, N=16,
+             bucket=8, world=2, rank=0, shard_len=8, lr=1e-3, beta1=0.9, beta2=0.95,
+             eps=1e-8, wd=0.1, step=1, stats=FAKE, skip=0, stream=None)
+    a.update(kw)
+    return z.lib().zopt_adamw_shard_step_clipped(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(master=None), z.ZOPT_ERR_NULL), (dict(grad=None), z.ZOPT_ERR_NULL),
+    (dict(stats=None), z.ZOPT_ERR_NULL),
+    (dict(N=0), z.ZOPT_ERR_SIZE), (dict(rank=2), z.ZOPT_ERR_SIZE),
+    (dict(shard_len=9), z.ZOPT_ERR_SIZE),
+    (dict(lr=float("nan")), z.ZOPT_ERR_HYPER), (dict(beta1=1.0), z.ZOPT_ERR_HYPER),
+    (dict(eps=0.0), z.ZOPT_ERR_HYPER), (dict(step=0), z.ZOPT_ERR_HYPER),
+    (dict(skip=2), z.ZOPT_ERR_HYPER), (dict(skip=-1), z.ZOPT_ERR_HYPER),
+])
+def test_adamw_clipped_rejects(kw, status):
+    assert adamw_clipped(**kw) == status
+
+
+def sq_norm(**kw):
+    size = ctypes.c_size_t(1 << 20)
+    a = dict(grad=FAKE, N=16, bucket=8, world=2, rank=0, shard_len=8, sq=FAKE,
+             ws=ctypes.c_void_p(1 << 20), ws_bytes=ctypes.byref(size), stream=None)
+    a.update(kw)
+    return z.lib().zopt_grad_sq_norm(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(grad=None), z.ZOPT_ERR_NULL), (dict(sq=None), z.ZOPT_ERR_NULL),
+    (dict(ws_bytes=None), z.ZOPT_ERR_NULL),
+    (dict(N=0), z.ZOPT_ERR_SIZE), (dict(bucket=0), z.ZOPT_ERR_SIZE),
+    (dict(world=0), z.ZOPT_ERR_SIZE), (dict(rank=2), z.ZOPT_ERR_SIZE),
+    (dict(shard_len=9), z.ZOPT_ERR_SIZE),
+    (dict(ws=ctypes.c_void_p((1 << 20) + 16)), z.ZOPT_ERR_WORKSPACE),
+    (dict(ws_bytes=ctypes.byref(ctypes.c_size_t(8))), z.ZOPT_ERR_WORKSPACE),
+])
+def test_grad_sq_norm_rejects(kw, status):
+    assert sq_norm(**kw) == status
+
+
+@pytest.mark.parametrize("n,bucket,world", [(16, 8, 2), (2_000_000_000, 1 << 25, 8), (1, 1, 1)])
+def test_grad_sq_norm_workspace_query(n, bucket, world):
+    size = ctypes.c_size_t(0)
+    sl = z.shard_len(n, bucket, world)
+    st = z.lib().zopt_grad_sq_norm(None, n, bucket, world, 0, sl, None, None,
+                                   ctypes.byref(size), None)
+    assert st == z.ZOPT_OK
+    assert 256 <= size.value <= 16384 and size.value % 256 == 0
+    assert z.grad_sq_norm_workspace_bytes(n, bucket, world) == size.value
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(sq=None), z.ZOPT_ERR_NULL), (dict(stats=None), z.ZOPT_ERR_NULL),
+    (dict(count=0), z.ZOPT_ERR_SIZE), (dict(count=65537), z.ZOPT_ERR_SIZE),
+    (dict(max_norm=0.0), z.ZOPT_ERR_HYPER), (dict(max_norm=-1.0), z.ZOPT_ERR_HYPER),
+    (dict(max_norm=float("nan")), z.ZOPT_ERR_HYPER),
+    (dict(inv_scale=0.0), z.ZOPT_ERR_HYPER), (dict(inv_scale=float("inf")), z.ZOPT_ERR_HYPER),
+])
+def test_grad_clip_stats_rejects(kw, status):
+    a = dict(sq=FAKE, count=1, max_norm=1.0, inv_scale=1.0, stats=FAKE, stream=None)
+    a.update(kw)
+    assert z.lib().zopt_grad_clip_stats(*a.values()) == status
+
+
 def test_round_bf16_rejects_and_empty_is_a_noop():
     lib = z.lib()
     assert lib.zopt_round_bf16(FAKE, FAKE, -1, None) == z.ZOPT_ERR_SIZE
