@@ -152,11 +152,30 @@ def muon_groups(torch, w, dev):
     return groups, workspace
 
 
-def muon_call(z, w, groups, workspace, ns_steps):
-    """All groups of a workload in one zopt_muon_step_groups call."""
+def muon_call(z, w, groups, workspace, ns_steps, health=None):
+    """All groups of a workload in one zopt_muon_step_groups call (with a
+    health tensor: zopt_muon_step_groups_guarded, guard 1000)."""
     z.muon_step_groups([(g["master"], g["momentum"], g["grad"], g["weight"]) for g in groups],
                        w.lr, w.momentum, w.nesterov, w.weight_decay, ns_steps, w.ns_coeffs,
-                       w.ns_eps, w.adjust_lr, workspace=workspace)
+                       w.ns_eps, w.adjust_lr, workspace=workspace,
+                       ns_guard=None if health is None else 1000.0, ns_health=health)
+
+
+def ns_health_check(torch, z, timer, w, groups, workspace, K, plain_ms):
+    """The guarded call against the plain one: the health pass reads each
+    matrix's bf16 result once (2 B per element of the padded-width X)."""
+    nmat = sum(g["count"] for g in groups)
+    health = torch.empty(2 + 3 * nmat, dtype=torch.float32, device=groups[0]["master"][0].device)
+    timer.run(lambda _: muon_call(z, w, groups, workspace, w.ns_steps, health), 1)
+    ms = timer.run(lambda _: muon_call(z, w, groups, workspace, w.ns_steps, health), K)
+    h = health.cpu()
+    tile = lambda m: 256 if m >= 1024 else 128 if m >= 256 else 64
+    bytes_read = sum(2 * g["count"] * min(g["rows"], g["cols"]) *
+                     (-(-max(g["rows"], g["cols"]) // tile(min(g["rows"], g["cols"])))
+                      * tile(min(g["rows"], g["cols"]))) for g in groups)
+    return dict(guarded_call_ms=round(ms, 4), overhead_ms=round(ms - plain_ms, 4),
+                health_pass_bytes=bytes_read, rejected=int(h[0]),
+                worst_ratio=round(float(h[1]), 4))
 
 
 # ------------------------------------------------------------------ parts
@@ -195,7 +214,8 @@ def bench_step(torch, z, timer, dev, K, W):
     iter_flops = sum(g["count"] * ns_flops(min(g["rows"], g["cols"]), max(g["rows"], g["cols"]), 1)
                      for g in groups)
     per_group = dict(muon_call_ms=round(t5, 4), pre_post_ms=round(t0, 4),
-                     groups=[dict(shape=[g["rows"], g["cols"]], count=g["count"]) for g in groups])
+                     groups=[dict(shape=[g["rows"], g["cols"]], count=g["count"]) for g in groups],
+                     ns_health=ns_health_check(torch, z, timer, wm, groups, workspace, K, t5))
     adamw_bytes = 28 * n
     ta = timer.run(lambda i: [z.adamw_shard_step(
         a["master"][p.offset:p.offset + p.n], a["m"][p.offset:p.offset + p.n],
@@ -291,6 +311,7 @@ def bench_ns(torch, z, timer, dev, K, W):
     t0 = timer.run(lambda _: muon_call(z, w, groups, workspace, 0), K)
     ns_ms, call_ms = t5 - t0, t5
     rows = [dict(shape=[g["rows"], g["cols"]], count=g["count"]) for g in groups]
+    health = ns_health_check(torch, z, timer, w, groups, workspace, K, t5)
     del groups, workspace
     torch.cuda.empty_cache()
     tf = total_flops / ns_ms / 1e9
@@ -298,7 +319,8 @@ def bench_ns(torch, z, timer, dev, K, W):
                 algorithmic_flops_per_step=total_flops, ns_ms_per_step=round(ns_ms, 3),
                 muon_ms_per_step=round(call_ms, 3), ns_tflops=round(tf, 1),
                 mfma_frac=round(tf / BF16_PEAK_TFLOPS, 4),
-                muon_step_tflops=round(total_flops / call_ms / 1e9, 1), groups=rows, steps=K)
+                muon_step_tflops=round(total_flops / call_ms / 1e9, 1), groups=rows, steps=K,
+                ns_health=health)
 
 
 def bench_copy(torch, z, timer, dev, K, W):

@@ -11,7 +11,8 @@
  *  - zopt_muon_step: Muon on whole 2-D matrices the rank owns (momentum with
  *    Nesterov look-ahead, Newton-Schulz orthogonalisation on bf16 matrix
  *    cores, a decayed and scaled update of the fp32 master), and
- *    zopt_muon_step_groups, the same on several shapes in one call;
+ *    zopt_muon_step_groups, the same on several shapes in one call, with
+ *    zopt_muon_step_groups_guarded adding the Newton-Schulz health checks;
  *  - zopt_round_bf16: the fp32 -> bf16 round-to-nearest-even write-back on
  *    its own;
  *  - zopt_grad_sq_norm, zopt_grad_clip_stats and zopt_adamw_shard_step_clipped:
@@ -355,6 +356,43 @@ zopt_status zopt_muon_step_groups(int32_t ngroups, const int32_t *batch, const i
                                   float ns_a, float ns_b, float ns_c, float ns_eps,
                                   int32_t adjust_lr, void *workspace, size_t *workspace_bytes,
                                   void *stream);
+
+/*
+ * zopt_muon_step_groups_guarded -- zopt_muon_step_groups with the Newton-Schulz
+ * health checks [BluScript trainer source, per-step report: nsratio, the
+ * worst ||update||_F / sqrt(min(rows, cols)) among the applied updates (about
+ * 1 when healthy), and nsrej, the updates the divergence guard refused because
+ * an element exceeded 1000 in magnitude; dmuon PR #16, commit "device-tensor
+ * stats": diagnostics stay device scalars, read back on the caller's
+ * schedule].  After step 3, per matrix i of the call (in call order), from its
+ * bf16 result O:
+ *   ratio_i    = ||O||_F / sqrt(min(rows, cols)), the squares summed exactly
+ *                in double in a fixed order, formed in double, rounded once
+ *   absmax_i   = max |O_jk| (NaN if an element is NaN)
+ *   rejected_i = !(absmax_i <= ns_guard)
+ * A rejected matrix is not updated: step 4 leaves its master and weight as
+ * they were (its momentum has taken step 1).  The other matrices get exactly
+ * what zopt_muon_step_groups gives them.
+ *
+ * Arguments: those of zopt_muon_step_groups, and
+ *   ns_guard   > 0; 1000 is the pages' value; +inf only reports.
+ *   ns_health  device floats, written: [0] the number of matrices rejected,
+ *              [1] the worst ratio among those not rejected (0 if none), then
+ *              [2 + 3i .. 4 + 3i] = ratio_i, absmax_i, rejected_i (0 / 1) for
+ *              each of the sum(batch) matrices.
+ *
+ * Errors: those of zopt_muon_step_groups; with a workspace, ZOPT_ERR_NULL also
+ * for ns_health NULL and ZOPT_ERR_HYPER for ns_guard not > 0.
+ */
+zopt_status zopt_muon_step_groups_guarded(int32_t ngroups, const int32_t *batch,
+                                          const int64_t *rows, const int64_t *cols,
+                                          float *const *master, float *const *momentum,
+                                          const uint16_t *const *grad, uint16_t *const *weight,
+                                          float lr, float momentum_beta, int32_t nesterov,
+                                          float weight_decay, int32_t ns_steps, float ns_a,
+                                          float ns_b, float ns_c, float ns_eps, int32_t adjust_lr,
+                                          float ns_guard, float *ns_health, void *workspace,
+                                          size_t *workspace_bytes, void *stream);
 
 /*
  * zopt_muon_groups_output_view -- zopt_muon_output_view for matrix `index` of

@@ -12,7 +12,8 @@ Entry points (same names as the C ABI in include/zopt.h):
   adamw_shard_step   fused AdamW over a flat bucketed fp32 shard
   muon_step          Muon on a batch of same-shape matrices
   muon_workspace_bytes / muon_output_view
-  muon_step_groups   Muon on several such batches in one call (shared launches)
+  muon_step_groups   Muon on several such batches in one call (shared launches);
+                     with ns_guard: zopt_muon_step_groups_guarded (health checks)
   muon_groups_workspace_bytes / muon_groups_output_view
   round_bf16         fp32 -> bf16 round-to-nearest-even
   shard_len          the shard length the layout derives (zopt_shard_len)
@@ -88,6 +89,10 @@ def _lib_or_raise() -> ctypes.CDLL:
                                             f32, i32, f32, f32, f32, f32, i32, vp,
                                             ctypes.POINTER(ctypes.c_size_t), vp]
         L.zopt_muon_step_groups.restype = ctypes.c_int
+        L.zopt_muon_step_groups_guarded.argtypes = [
+            i32, pi32, pi64, pi64, pp, pp, pp, pp, f32, f32, i32, f32, i32, f32, f32, f32, f32,
+            i32, f32, vp, vp, ctypes.POINTER(ctypes.c_size_t), vp]
+        L.zopt_muon_step_groups_guarded.restype = ctypes.c_int
         L.zopt_muon_groups_output_view.argtypes = [i32, pi32, pi64, pi64, i32, vp, i32, i32, pp,
                                                    pi64]
         L.zopt_muon_groups_output_view.restype = ctypes.c_int
@@ -326,11 +331,17 @@ def muon_step_groups(groups: Sequence[tuple], lr: float, momentum_beta: float = 
                      nesterov: bool = True, weight_decay: float = 0.1, ns_steps: int = 5,
                      ns_coeffs=(3.4445, -4.7750, 2.0315), ns_eps: float = 1e-7,
                      adjust_lr: int = 1, workspace: Optional[torch.Tensor] = None,
-                     stream=None) -> torch.Tensor:
+                     stream=None, ns_guard: Optional[float] = None,
+                     ns_health: Optional[torch.Tensor] = None) -> torch.Tensor:
     """One Muon step on several groups of same-shape matrices in one call
     (zopt_muon_step_groups).  Each group is (master, momentum, grad, weight)
     with lists of equal length; weight may be None for every group or for
-    none.  Returns the workspace (see muon_groups_output_view)."""
+    none.  Returns the workspace (see muon_groups_output_view).
+
+    With ns_guard (and ns_health, fp32 [2 + 3 * matrices] on the device) the
+    call is zopt_muon_step_groups_guarded: ns_health receives the number of
+    rejected matrices, the worst passing ratio and [ratio, absmax, rejected]
+    per matrix, and a rejected matrix is not updated."""
     if not groups:
         raise ValueError("muon_step_groups: no groups")
     with_w = groups[0][3] is not None
@@ -365,12 +376,23 @@ def muon_step_groups(groups: Sequence[tuple], lr: float, momentum_beta: float = 
     n, b, r, c = _shape_arrays(shapes)
     size = ctypes.c_size_t(workspace.numel())
     ca, cb, cc = (float(x) for x in ns_coeffs)
-    st = lib().zopt_muon_step_groups(
-        n, b, r, c, _ptr_array(M), _ptr_array(Mo), _ptr_array(G),
-        _ptr_array(W) if with_w else None, lr, momentum_beta, int(nesterov), weight_decay,
-        ns_steps, ca, cb, cc, ns_eps, adjust_lr, workspace.data_ptr(), ctypes.byref(size),
-        _stream(dev, stream))
-    _check(st, "zopt_muon_step_groups")
+    common = (n, b, r, c, _ptr_array(M), _ptr_array(Mo), _ptr_array(G),
+              _ptr_array(W) if with_w else None, lr, momentum_beta, int(nesterov), weight_decay,
+              ns_steps, ca, cb, cc, ns_eps, adjust_lr)
+    if ns_guard is None:
+        if ns_health is not None:
+            raise ValueError("muon_step_groups: ns_health needs ns_guard")
+        st = lib().zopt_muon_step_groups(*common, workspace.data_ptr(), ctypes.byref(size),
+                                         _stream(dev, stream))
+        _check(st, "zopt_muon_step_groups")
+        return workspace
+    if ns_health is None:
+        raise ValueError("muon_step_groups: ns_guard needs an ns_health tensor")
+    _need(ns_health, torch.float32, 2 + 3 * len(M), "ns_health", dev)
+    st = lib().zopt_muon_step_groups_guarded(*common, ns_guard, ns_health.data_ptr(),
+                                             workspace.data_ptr(), ctypes.byref(size),
+                                             _stream(dev, stream))
+    _check(st, "zopt_muon_step_groups_guarded")
     return workspace
 
 

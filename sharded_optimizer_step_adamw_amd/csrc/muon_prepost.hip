@@ -11,9 +11,15 @@
 //   pass 2  recompute U from the new M (bitwise the same U), write
 //           X0 = bf16(U s) in the Newton-Schulz orientation and its transpose,
 //           zero-filling the tile padding                        (10 B/elem)
+// Health [BluScript trainer source, per-step report: nsratio, the update's
+// ||O||_F / sqrt(min(rows, cols)), about 1 when healthy, and nsrej, the
+// updates the divergence guard refused for an element above 1000]:
+//   pass    fp64 sum of squares and max |x| of X, per workgroup    (2 B/elem)
+//   final   per matrix: ratio, absmax, rejected = !(absmax <= guard)
 // Post-step [BluScript trainer source: Muon weight decay pinned to AdamW's;
 // the adjust_lr note on the update scale]:
 //   P = P * decay - step_lr * O, W = bf16(P)                      (12 B/elem)
+//   (a rejected matrix is left as it is)
 #include "zopt_internal.h"
 
 // M, U and P are bit-exact binary32 arithmetic: no contraction.
@@ -213,11 +219,13 @@ struct PostArgs {
     float decay, step_lr;
     int64_t o_ld;
     int64_t o_stride;
+    const int32_t *reject;  // per-matrix flags, or NULL
 };
 
 __global__ __launch_bounds__(kThreads) void muon_post_kernel(
     MuonPtrs ptrs, PostArgs a, const uint16_t *__restrict__ o_base) {
     const int b = blockIdx.y;
+    if (a.reject && a.reject[b]) return;
     const int64_t count = (int64_t)a.rows * a.cols;
     const int64_t i0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * kPerThread;
     if (i0 >= count) return;
@@ -256,9 +264,198 @@ __global__ __launch_bounds__(kThreads) void muon_post_kernel(
     }
 }
 
+// ------------------------------------------------------------------ health
+
+constexpr int kHealthLoads = 4;      // 16-byte loads in flight per thread
+constexpr int kHealthMaxBlocks = 256;
+
+// One health launch covers the groups of a launch bin (at most
+// kMaxCallGroups), described by this table in the kernel arguments.
+struct HealthGroup {
+    const uint16_t *x;     // X of matrix 0; matrix b at x + b * x_stride
+    int64_t x_stride, count;
+    double *psum;
+    float *pmax;
+    int32_t *flags;
+    float *health;         // this group's first [ratio, absmax, rejected] triple
+    int32_t hblocks, short_side;
+    int32_t block0, mat0;  // first workgroup / matrix of this group in the grid
+};
+struct HealthLaunch {
+    HealthGroup g[kMaxCallGroups];
+    int32_t ngroups;
+    float guard;
+};
+
+__device__ __forceinline__ void health_add(uint32_t bits, double &acc, float &amax) {
+    const float x = bf16_bits_to_float(bits);
+    const double xd = (double)x;
+    acc = __builtin_fma(xd, xd, acc);  // the square is exact in double
+    amax = __builtin_fmaxf(amax, __builtin_fabsf(x));  // a NaN shows in acc instead
+}
+
+// Partial sums of squares (fp64) and maxima of |x| over X of every matrix of
+// the groups in the table: count = m * np contiguous bf16 per matrix (the
+// padding columns are zero); hblocks workgroups per matrix, the groups'
+// workgroups one after the other in the grid.  Sums in a fixed order: each
+// thread's run, a wave butterfly, the waves in order.
+__global__ __launch_bounds__(kThreads) void ns_health_kernel(HealthLaunch h) {
+    __shared__ double lsum[kThreads / 64];
+    __shared__ float lmax[kThreads / 64];
+    int gi = 0;
+    while (gi + 1 < h.ngroups && (int)blockIdx.x >= h.g[gi + 1].block0) ++gi;
+    const HealthGroup &G = h.g[gi];
+    const int local = (int)blockIdx.x - G.block0;
+    const int b = local / G.hblocks, blk = local - b * G.hblocks;
+    const uint16_t *__restrict__ X = G.x + (int64_t)b * G.x_stride;
+    const int64_t step = (int64_t)G.hblocks * kThreads * 8;
+    const int64_t count = G.count;
+    int64_t i = ((int64_t)blk * kThreads + threadIdx.x) * 8;
+    double acc = 0.0;
+    float amax = 0.0f;
+    for (; i + (kHealthLoads - 1) * step < count; i += kHealthLoads * step) {
+        u32x4 w[kHealthLoads];
+#pragma unroll
+        for (int q = 0; q < kHealthLoads; ++q)
+            w[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(X + i + q * step));
+#pragma unroll
+        for (int q = 0; q < kHealthLoads; ++q) {
+            const uint32_t v[4] = {w[q].x, w[q].y, w[q].z, w[q].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                health_add(v[e] & 0xFFFFu, acc, amax);
+                health_add(v[e] >> 16, acc, amax);
+            }
+        }
+    }
+    for (; i < count; i += step) {
+        const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(X + i));
+        const uint32_t v[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            health_add(v[e] & 0xFFFFu, acc, amax);
+            health_add(v[e] >> 16, acc, amax);
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        acc += __shfl_xor(acc, off, 64);
+        amax = __builtin_fmaxf(amax, __shfl_xor(amax, off, 64));
+    }
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        lsum[wave] = acc;
+        lmax[wave] = amax;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double s = 0.0;
+        float mx = 0.0f;
+        for (int w = 0; w < kThreads / 64; ++w) {
+            s += lsum[w];
+            mx = __builtin_fmaxf(mx, lmax[w]);
+        }
+        G.psum[(int64_t)b * G.hblocks + blk] = s;
+        G.pmax[(int64_t)b * G.hblocks + blk] = mx;
+    }
+}
+
+// Per matrix (one wave each, matrices of the table's groups one after the
+// other): the partials in a fixed order (each lane's run, then a butterfly),
+// ratio = ||X||_F / sqrt(min(rows, cols)) formed in double and rounded once,
+// absmax (NaN if any element is NaN, which the sum of squares carries),
+// rejected = !(absmax <= guard).
+__global__ __launch_bounds__(64) void ns_health_matrix_kernel(HealthLaunch h) {
+    int gi = 0;
+    while (gi + 1 < h.ngroups && (int)blockIdx.x >= h.g[gi + 1].mat0) ++gi;
+    const HealthGroup &G = h.g[gi];
+    const int b = (int)blockIdx.x - G.mat0;
+    double s = 0.0;
+    float mx = 0.0f;
+    for (int i = threadIdx.x; i < G.hblocks; i += 64) {
+        s += G.psum[(int64_t)b * G.hblocks + i];
+        mx = __builtin_fmaxf(mx, G.pmax[(int64_t)b * G.hblocks + i]);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        s += __shfl_xor(s, off, 64);
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, off, 64));
+    }
+    if (threadIdx.x != 0) return;
+    if (__builtin_isnan(s)) mx = __builtin_nanf("");
+    const float ratio = (float)(__builtin_sqrt(s) / __builtin_sqrt((double)G.short_side));
+    const bool rejected = !(mx <= h.guard);
+    G.flags[b] = rejected ? 1 : 0;
+    G.health[3 * b] = ratio;
+    G.health[3 * b + 1] = mx;
+    G.health[3 * b + 2] = rejected ? 1.0f : 0.0f;
+}
+
+// The call's totals from its per-matrix triples (one wave; a count of 0/1
+// flags and a maximum, both exact in any order).
+__global__ __launch_bounds__(64) void ns_health_total_kernel(float *__restrict__ health,
+                                                             int32_t nmat) {
+    float rejected = 0.0f, worst = 0.0f;
+    for (int i = threadIdx.x; i < nmat; i += 64) {
+        const float *t = health + 2 + 3 * i;
+        if (t[2] != 0.0f) rejected += 1.0f;
+        else worst = __builtin_fmaxf(worst, t[0]);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        rejected += __shfl_xor(rejected, off, 64);
+        worst = __builtin_fmaxf(worst, __shfl_xor(worst, off, 64));
+    }
+    if (threadIdx.x == 0) {
+        health[0] = rejected;
+        health[1] = worst;
+    }
+}
+
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 }  // namespace
+
+int32_t ns_health_blocks(int64_t count) {
+    const int64_t per = (int64_t)kThreads * 8 * kHealthLoads;
+    const int64_t b = (count + per - 1) / per;
+    return (int32_t)(b < 1 ? 1 : b > kHealthMaxBlocks ? kHealthMaxBlocks : b);
+}
+
+hipError_t launch_ns_health(const NsGroupRef *refs, const int *mat_first, int nrefs,
+                            float guard, float *health, hipStream_t stream) {
+    HealthLaunch h{};
+    h.ngroups = nrefs;
+    h.guard = guard;
+    int blocks = 0, mats = 0;
+    for (int i = 0; i < nrefs; ++i) {
+        const MuonGeom &g = *refs[i].geom;
+        const MuonWorkspace &L = *refs[i].layout;
+        char *ws = refs[i].base;
+        HealthGroup &G = h.g[i];
+        G.x = reinterpret_cast<const uint16_t *>(ws + L.x);
+        G.x_stride = (int64_t)(L.x_stride / 2);
+        G.count = (int64_t)g.m * g.np;  // a multiple of 8: np is a multiple of 64
+        G.psum = reinterpret_cast<double *>(ws + L.hsum);
+        G.pmax = reinterpret_cast<float *>(ws + L.hmax);
+        G.flags = reinterpret_cast<int32_t *>(ws + L.hflag);
+        G.health = health + 2 + 3 * mat_first[i];
+        G.hblocks = g.health_blocks;
+        G.short_side = g.m;
+        G.block0 = blocks;
+        G.mat0 = mats;
+        blocks += g.batch * g.health_blocks;
+        mats += g.batch;
+    }
+    hipLaunchKernelGGL(ns_health_kernel, dim3(blocks), dim3(kThreads), 0, stream, h);
+    hipLaunchKernelGGL(ns_health_matrix_kernel, dim3(mats), dim3(64), 0, stream, h);
+    return hipGetLastError();
+}
+
+hipError_t launch_ns_health_total(float *health, int32_t nmat, hipStream_t stream) {
+    hipLaunchKernelGGL(ns_health_total_kernel, dim3(1), dim3(64), 0, stream, health, nmat);
+    return hipGetLastError();
+}
 
 int32_t muon_norm_blocks(int64_t count) { return (int32_t)((count + kChunk - 1) / kChunk); }
 
@@ -292,13 +489,15 @@ hipError_t launch_muon_pre(const MuonGeom &g, const MuonPtrs &ptrs, float mu,
 
 hipError_t launch_muon_post(const MuonGeom &g, const MuonPtrs &ptrs,
                             const uint16_t *o_base, int64_t o_ld, size_t o_stride,
-                            float decay, float step_lr, hipStream_t stream) {
+                            float decay, float step_lr, const int32_t *reject,
+                            hipStream_t stream) {
     const int64_t count = (int64_t)g.rows * g.cols;
     bool vec = (g.cols % 8) == 0;
     for (int b = 0; b < g.batch; ++b)
         vec = vec && aligned16(ptrs.master[b]) &&
               (ptrs.weight[b] == nullptr || aligned16(ptrs.weight[b]));
-    PostArgs pa{g.rows, g.cols, vec ? 1 : 0, decay, step_lr, o_ld, (int64_t)(o_stride / 2)};
+    PostArgs pa{g.rows, g.cols, vec ? 1 : 0, decay, step_lr, o_ld, (int64_t)(o_stride / 2),
+                reject};
     const int64_t units = (count + kPerThread - 1) / kPerThread;
     const int64_t blocks = (units + kThreads - 1) / kThreads;
     hipLaunchKernelGGL(muon_post_kernel, dim3((uint32_t)blocks, g.batch), dim3(kThreads), 0,

@@ -68,6 +68,7 @@ MuonGeom muon_geometry(int32_t batch, int64_t rows, int64_t cols) {
     // it takes the larger tile, which does more work per byte staged
     g.tile_bx = (g.tile == 128 && g.mp % 256 == 0 && g.np % 256 == 0) ? 256 : g.tile;
     g.norm_blocks = muon_norm_blocks(rows * cols);
+    g.health_blocks = ns_health_blocks((int64_t)g.m * g.np);
     return g;
 }
 
@@ -86,6 +87,10 @@ MuonWorkspace muon_workspace_layout(const MuonGeom &g) {
     L.db = off;  off += L.d_stride * g.batch;
     L.partials = off;
     off += round_up(((size_t)g.batch * g.norm_blocks + g.batch) * sizeof(float), 256);
+    const size_t hparts = (size_t)g.batch * g.health_blocks;
+    L.hsum = off;  off += round_up(hparts * sizeof(double), 256);
+    L.hmax = off;  off += round_up(hparts * sizeof(float), 256);
+    L.hflag = off; off += round_up((size_t)g.batch * sizeof(int32_t), 256);
     L.total = off;
     return L;
 }
@@ -279,8 +284,8 @@ zopt_status muon_step_groups(int32_t ngroups, const int32_t *batch, const int64_
                              const uint16_t *const *grad, uint16_t *const *weight, float lr,
                              float momentum_beta, int32_t nesterov, float weight_decay,
                              int32_t ns_steps, float ns_a, float ns_b, float ns_c, float ns_eps,
-                             int32_t adjust_lr, void *workspace, size_t *workspace_bytes,
-                             void *stream) {
+                             int32_t adjust_lr, float guard, float *health, void *workspace,
+                             size_t *workspace_bytes, void *stream) {
     if (!workspace_bytes) return ZOPT_ERR_NULL;
     GroupPlan plans[kMaxCallGroups];
     size_t total = 0;
@@ -308,7 +313,9 @@ zopt_status muon_step_groups(int32_t ngroups, const int32_t *batch, const int64_
     hipStream_t s = (hipStream_t)stream;
     MuonPtrs ptrs[kMaxCallGroups];
     NsGroupRef refs[kMaxCallGroups];
+    int firsts[kMaxCallGroups];
     for (int i = 0, first = 0; i < ngroups; first += batch[i], ++i) {
+        firsts[i] = first;
         MuonPtrs &p = ptrs[i];
         for (int b = 0; b < batch[i]; ++b) {
             p.master[b] = master[first + b];
@@ -354,6 +361,11 @@ zopt_status muon_step_groups(int32_t ngroups, const int32_t *batch, const int64_
         }
         for (int k = 0; k < ns_steps && e == hipSuccess; ++k)
             e = launch_ns_iteration(brefs, bin_size[bi], k & 1, ns_a, ns_b, ns_c, s);
+        if (health && e == hipSuccess) {
+            int bfirst[kMaxCallGroups];
+            for (int k = 0; k < bin_size[bi]; ++k) bfirst[k] = firsts[bins[bi][k]];
+            e = launch_ns_health(brefs, bfirst, bin_size[bi], guard, health, s);
+        }
         for (int k = 0; k < bin_size[bi] && e == hipSuccess; ++k) {
             const int i = bins[bi][k];
             const MuonGeom &g = plans[i].g;
@@ -366,11 +378,15 @@ zopt_status muon_step_groups(int32_t ngroups, const int32_t *batch, const int64_
             size_t obase;
             int64_t old;
             muon_output(g, plans[i].L, ns_steps, obase, old);
+            const int32_t *reject =
+                health ? reinterpret_cast<const int32_t *>(ws + plans[i].base + plans[i].L.hflag)
+                       : nullptr;
             e = launch_muon_post(g, ptrs[i],
                                  reinterpret_cast<const uint16_t *>(ws + plans[i].base + obase),
-                                 old, plans[i].L.x_stride, decay, step_lr, s);
+                                 old, plans[i].L.x_stride, decay, step_lr, reject, s);
         }
     }
+    if (health && e == hipSuccess) e = launch_ns_health_total(health, nmat, s);
     return e == hipSuccess ? ZOPT_OK : ZOPT_ERR_DEVICE;
 }
 
@@ -407,7 +423,8 @@ ZOPT_EXPORT zopt_status zopt_muon_step(int32_t batch, int64_t rows, int64_t cols
                                        void *workspace, size_t *workspace_bytes, void *stream) {
     return muon_step_groups(1, &batch, &rows, &cols, master, momentum, grad, weight, lr,
                             momentum_beta, nesterov, weight_decay, ns_steps, ns_a, ns_b, ns_c,
-                            ns_eps, adjust_lr, workspace, workspace_bytes, stream);
+                            ns_eps, adjust_lr, 0.0f, nullptr, workspace, workspace_bytes,
+                            stream);
 }
 
 ZOPT_EXPORT zopt_status zopt_muon_step_groups(
@@ -418,7 +435,24 @@ ZOPT_EXPORT zopt_status zopt_muon_step_groups(
     void *workspace, size_t *workspace_bytes, void *stream) {
     return muon_step_groups(ngroups, batch, rows, cols, master, momentum, grad, weight, lr,
                             momentum_beta, nesterov, weight_decay, ns_steps, ns_a, ns_b, ns_c,
-                            ns_eps, adjust_lr, workspace, workspace_bytes, stream);
+                            ns_eps, adjust_lr, 0.0f, nullptr, workspace, workspace_bytes,
+                            stream);
+}
+
+ZOPT_EXPORT zopt_status zopt_muon_step_groups_guarded(
+    int32_t ngroups, const int32_t *batch, const int64_t *rows, const int64_t *cols,
+    float *const *master, float *const *momentum, const uint16_t *const *grad,
+    uint16_t *const *weight, float lr, float momentum_beta, int32_t nesterov, float weight_decay,
+    int32_t ns_steps, float ns_a, float ns_b, float ns_c, float ns_eps, int32_t adjust_lr,
+    float ns_guard, float *ns_health, void *workspace, size_t *workspace_bytes, void *stream) {
+    if (workspace) {
+        if (!ns_health) return ZOPT_ERR_NULL;
+        if (!(ns_guard > 0.0f)) return ZOPT_ERR_HYPER;  // +inf: report only, NaN rejected
+    }
+    return muon_step_groups(ngroups, batch, rows, cols, master, momentum, grad, weight, lr,
+                            momentum_beta, nesterov, weight_decay, ns_steps, ns_a, ns_b, ns_c,
+                            ns_eps, adjust_lr, ns_guard, ns_health, workspace, workspace_bytes,
+                            stream);
 }
 
 ZOPT_EXPORT zopt_status zopt_muon_output_view(int32_t batch, int64_t rows, int64_t cols,

@@ -100,6 +100,7 @@ struct MuonGeom {
     int32_t tile;        // square output tile of the Newton-Schulz products X X^T and A A
     int32_t tile_bx;     // and of B X
     int32_t norm_blocks; // workgroups (and norm partials) per matrix, pre-pass 1
+    int32_t health_blocks;  // workgroups (and partials) per matrix of the health pass
 };
 
 struct MuonPtrs {
@@ -111,7 +112,9 @@ struct MuonPtrs {
 
 // Workspace carve-up (byte offsets; every region 256-byte aligned).
 struct MuonWorkspace {
-    size_t x, xt0, xt1, a, b, da, db, partials, total;
+    size_t x, xt0, xt1, a, b, da, db, partials;
+    size_t hsum, hmax, hflag;  // health pass: fp64 / fp32 partials, per-matrix reject flags
+    size_t total;
     size_t x_stride, a_stride, d_stride;  // bytes per matrix of each region kind
 };
 
@@ -122,9 +125,13 @@ hipError_t launch_muon_pre(const MuonGeom &g, const MuonPtrs &ptrs, float mu,
                            int32_t nesterov, float ns_eps, char *ws,
                            const MuonWorkspace &L, hipStream_t stream);
 
+// reject: per-matrix flags (non-zero: leave that matrix untouched) or NULL.
 hipError_t launch_muon_post(const MuonGeom &g, const MuonPtrs &ptrs,
                             const uint16_t *o_base, int64_t o_ld, size_t o_stride,
-                            float decay, float step_lr, hipStream_t stream);
+                            float decay, float step_lr, const int32_t *reject,
+                            hipStream_t stream);
+
+int32_t ns_health_blocks(int64_t count);
 
 // A group of a Muon call as the Newton-Schulz launches see it: its geometry,
 // its workspace carve-up and where its workspace starts.
@@ -133,6 +140,17 @@ struct NsGroupRef {
     const MuonWorkspace *layout;
     char *base;
 };
+
+// Health of each matrix's Newton-Schulz result X (in the workspaces) for
+// the nrefs groups, in two launches: writes [ratio, absmax, rejected] for
+// matrix b of group i to health + 2 + 3 * (mat_first[i] + b) and the reject
+// flags to the workspaces.
+hipError_t launch_ns_health(const NsGroupRef *refs, const int *mat_first, int nrefs,
+                            float guard, float *health, hipStream_t stream);
+
+// health[0] = matrices rejected, health[1] = worst ratio among the others
+// (0 if none), from the nmat triples at health + 2.
+hipError_t launch_ns_health_total(float *health, int32_t nmat, hipStream_t stream);
 
 // One Newton-Schulz iteration of every group of a call: A = X X^T,
 // B = b A + c A A, X = a X + B X, reading X^T from xt[cur_xt] and writing

@@ -273,3 +273,32 @@ def test_groups_output_views_are_disjoint_and_in_bounds():
                                             ctypes.byref(out), ctypes.byref(ld)) == z.ZOPT_ERR_SIZE
     assert lib.zopt_muon_groups_output_view(n, b, r, c, 5, ctypes.c_void_p(base), 1, 3,
                                             ctypes.byref(out), ctypes.byref(ld)) == z.ZOPT_ERR_SIZE
+
+
+def guarded(**kw):
+    size = ctypes.c_size_t(1 << 40)
+    a = dict(ngroups=1, batch=(ctypes.c_int32 * 1)(2), rows=(ctypes.c_int64 * 1)(64),
+             cols=(ctypes.c_int64 * 1)(32), master=ptrs(2), momentum=ptrs(2), grad=ptrs(2),
+             weight=None, lr=8e-4, mu=0.95, nesterov=1, wd=0.1, ns_steps=5, a=3.4445,
+             b=-4.775, c=2.0315, eps=1e-7, adjust=1, guard=1000.0, health=FAKE,
+             ws=ctypes.c_void_p(1 << 20), ws_bytes=ctypes.byref(size), stream=None)
+    a.update(kw)
+    return z.lib().zopt_muon_step_groups_guarded(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(health=None), z.ZOPT_ERR_NULL),
+    (dict(guard=0.0), z.ZOPT_ERR_HYPER), (dict(guard=-5.0), z.ZOPT_ERR_HYPER),
+    (dict(guard=float("nan")), z.ZOPT_ERR_HYPER),
+    (dict(batch=(ctypes.c_int32 * 1)(0)), z.ZOPT_ERR_SIZE),
+    (dict(master=None), z.ZOPT_ERR_NULL), (dict(lr=-1.0), z.ZOPT_ERR_HYPER),
+    (dict(ws=ctypes.c_void_p((1 << 20) + 16)), z.ZOPT_ERR_WORKSPACE),
+])
+def test_muon_guarded_rejects(kw, status):
+    assert guarded(**kw) == status
+
+
+def test_muon_guarded_query_needs_no_health():
+    size = ctypes.c_size_t(0)
+    assert guarded(health=None, guard=0.0, ws=None, ws_bytes=ctypes.byref(size)) == z.ZOPT_OK
+    assert size.value == z.muon_workspace_bytes(2, 64, 32)
