@@ -72,10 +72,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--parts", default="step,adamw,clip,ns",
+    ap.add_argument("--parts", default="step,adamw,clip,ns,graph",
                     help="comma list of: step (headline), adamw, clip (the clipped step on the "
-                         "adamw shard; needs adamw), ns, copy (a zopt_round_bf16 pass of known "
-                         "size: the calibration for HBM byte counters)")
+                         "adamw shard; needs adamw), ns, graph (eager vs captured Muon calls), "
+                         "copy (a zopt_round_bf16 pass of known size: the calibration for HBM "
+                         "byte counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
 
@@ -323,6 +324,68 @@ def bench_ns(torch, z, timer, dev, K, W):
                 ns_health=health)
 
 
+def bench_graph(torch, z, timer, dev, K, W):
+    """A Muon call issued eagerly against the same call captured once and
+    replayed (zopt_muon_graph_*), on the tiny workload (2 x [128, 512]) and
+    the headline's 72 GPT-2-small matrices.  GPU time per call from HIP
+    events over K back-to-back calls; host time per call is the wall time to
+    enqueue 20 calls, measured three ways: through the Python binding (its
+    tensor checks included), straight through the C ABI with prebuilt
+    arguments, and a graph launch through the C ABI."""
+    import ctypes
+    import workloads as wl
+    out = {}
+    lib = z.lib()
+    for w in (wl.TINY_MUON, wl.GPT2_MUON):
+        groups, workspace = muon_groups(torch, w, dev)
+        tup = [(g["master"], g["momentum"], g["grad"], g["weight"]) for g in groups]
+        scalars = torch.tensor([w.lr, w.momentum, w.weight_decay], dtype=torch.float32,
+                               device=dev)
+        graph = z.MuonGraph(tup, scalars, w.nesterov, w.ns_steps, w.ns_coeffs, w.ns_eps,
+                            w.adjust_lr, workspace=workspace)
+        shapes, M, Mo, G, Wt, _, _ = z._muon_group_tables(tup)
+        n, b, r, c = z._shape_arrays(shapes)
+        size = ctypes.c_size_t(workspace.numel())
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        cargs = (n, b, r, c, z._ptr_array(M), z._ptr_array(Mo), z._ptr_array(G),
+                 z._ptr_array(Wt), w.lr, w.momentum, int(w.nesterov), w.weight_decay, w.ns_steps,
+                 *(float(x) for x in w.ns_coeffs), w.ns_eps, w.adjust_lr, workspace.data_ptr(),
+                 ctypes.byref(size), stream)
+        handle = graph._handle
+
+        def eager_binding(_):
+            muon_call(z, w, groups, workspace, w.ns_steps)
+
+        def eager_c(_):
+            lib.zopt_muon_step_groups(*cargs)
+
+        def replay(_):
+            lib.zopt_muon_graph_launch(handle, stream)
+
+        def host_us(fn, calls=20):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(calls):
+                fn(i)
+            t1 = time.perf_counter()
+            torch.cuda.synchronize()
+            return (t1 - t0) / calls * 1e6
+
+        res = {}
+        for name, fn in (("eager", eager_c), ("graph", replay)):
+            timer.run(fn, W)
+            res[name + "_gpu_ms"] = round(timer.run(fn, K), 4)
+        for name, fn in (("eager_binding", eager_binding), ("eager_c_abi", eager_c),
+                         ("graph_c_abi", replay)):
+            host_us(fn)
+            res[name + "_host_us"] = round(min(host_us(fn) for _ in range(3)), 1)
+        graph.close()
+        out[w.name] = res
+        del groups, workspace, graph
+        torch.cuda.empty_cache()
+    return out
+
+
 def bench_copy(torch, z, timer, dev, K, W):
     """zopt_round_bf16 over 2.5e8 fp32 values: 1.0e9 bytes read, 0.5e9 written
     per launch, the reference for scaling FETCH_SIZE / WRITE_SIZE counters."""
@@ -407,6 +470,7 @@ def main():
                  if "adamw" in parts else None)
     res_ns = bench_ns(torch, z, timer, dev, max(2, K // 5), W) if "ns" in parts else None
     res_copy = bench_copy(torch, z, timer, dev, K, W) if "copy" in parts else None
+    res_graph = bench_graph(torch, z, timer, dev, K, W) if "graph" in parts else None
     if res_step:
         tf = res_step["ns_iter_flops"] / res_step["ns_iter_ms"] / 1e9
         out.update(value=round(res_step["ms"], 4), unit="ms per optimizer step")
@@ -438,6 +502,8 @@ def main():
         out["newton_schulz"] = res_ns
     if res_copy:
         out["round_bf16_calibration"] = res_copy
+    if res_graph:
+        out["muon_graph"] = res_graph
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline()
     props = torch.cuda.get_device_properties(0)
     out["device"] = f"{torch.cuda.get_device_name(0)} ({getattr(props, 'gcnArchName', '?')}, " \

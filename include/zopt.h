@@ -12,7 +12,8 @@
  *    Nesterov look-ahead, Newton-Schulz orthogonalisation on bf16 matrix
  *    cores, a decayed and scaled update of the fp32 master), and
  *    zopt_muon_step_groups, the same on several shapes in one call, with
- *    zopt_muon_step_groups_guarded adding the Newton-Schulz health checks;
+ *    zopt_muon_step_groups_guarded adding the Newton-Schulz health checks,
+ *    and zopt_muon_graph_* capturing a call once for replay each step;
  *  - zopt_round_bf16: the fp32 -> bf16 round-to-nearest-even write-back on
  *    its own;
  *  - zopt_grad_sq_norm, zopt_grad_clip_stats and zopt_adamw_shard_step_clipped:
@@ -22,7 +23,8 @@
  * Conventions common to every call
  * --------------------------------
  *  - Every buffer is device memory owned by the caller.  The library
- *    allocates nothing and keeps no state between calls; it is reentrant.
+ *    allocates no device memory and keeps no state between calls (a captured
+ *    Muon graph is a handle the caller owns); it is reentrant.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *    the call returns without synchronising.  All launch parameters travel
  *    as kernel arguments, so back-to-back calls need no host sync.
@@ -393,6 +395,56 @@ zopt_status zopt_muon_step_groups_guarded(int32_t ngroups, const int32_t *batch,
                                           float ns_b, float ns_c, float ns_eps, int32_t adjust_lr,
                                           float ns_guard, float *ns_health, void *workspace,
                                           size_t *workspace_bytes, void *stream);
+
+/*
+ * Captured Muon calls.  One Muon call is tens of kernel launches; issued one
+ * by one per step they cost host time that a graph replay does not [dmuon PR
+ * #16, commit "NS CUDA-graph replay": the launches of a Newton-Schulz call
+ * captured once per shape and replayed, cutting the host cost of a call from
+ * milliseconds to tens of microseconds; lr / wd / momentum are kept out of
+ * the captured part so a schedule needs no re-capture].  Here the whole call
+ * (pre-step, Newton-Schulz, optional health pass, post-step) is one hipGraph,
+ * and lr, momentum_beta and weight_decay live in device memory, read by the
+ * kernels each time the graph runs: a caller changes them with an ordinary
+ * device write (a copy or a fill on the stream) before a launch.
+ *
+ *   scalars  device float[3] = {lr, momentum_beta, weight_decay}.  Read when
+ *            the kernels run; the library cannot check these values (they
+ *            should satisfy zopt_muon_step's limits).  Every derived scalar
+ *            (1 - mu, 1 - lr*wd, lr*scale) is formed in double on the device
+ *            exactly as the host forms it, so a replay gives the bits a
+ *            zopt_muon_step_groups(_guarded) call with the same values gives.
+ *
+ * zopt_muon_graph_create captures one call with the arguments of
+ * zopt_muon_step_groups_guarded (ns_health NULL: no health pass, ns_guard
+ * ignored) -- the buffers, shapes, workspace and fixed hyperparameters are
+ * baked in and must stay valid while the graph is used -- and returns a
+ * handle.  Capture runs on a stream of its own and enqueues nothing.
+ * workspace_bytes is the size provided (the query of zopt_muon_step_groups
+ * gives the size needed).  Errors: ZOPT_ERR_NULL (graph, workspace, scalars
+ * or a buffer pointer NULL); ZOPT_ERR_SIZE; ZOPT_ERR_HYPER (nesterov,
+ * ns_steps, a coefficient, ns_eps, adjust_lr, or ns_guard with ns_health);
+ * ZOPT_ERR_WORKSPACE; ZOPT_ERR_DEVICE (capture or instantiation failed).
+ *
+ * zopt_muon_graph_launch enqueues one replay on `stream` (hipStream_t or
+ * NULL).  Replays on one workspace must not overlap (one stream, or ordered).
+ *
+ * zopt_muon_graph_destroy frees the handle (NULL is a no-op); no replay may
+ * still be pending (synchronise the stream first).  The handle is host
+ * memory owned by the caller until then; the library holds no other state.
+ */
+typedef struct zopt_muon_graph zopt_muon_graph;
+
+zopt_status zopt_muon_graph_create(int32_t ngroups, const int32_t *batch, const int64_t *rows,
+                                   const int64_t *cols, float *const *master,
+                                   float *const *momentum, const uint16_t *const *grad,
+                                   uint16_t *const *weight, const float *scalars,
+                                   int32_t nesterov, int32_t ns_steps, float ns_a, float ns_b,
+                                   float ns_c, float ns_eps, int32_t adjust_lr, float ns_guard,
+                                   float *ns_health, void *workspace, size_t workspace_bytes,
+                                   zopt_muon_graph **graph);
+zopt_status zopt_muon_graph_launch(const zopt_muon_graph *graph, void *stream);
+zopt_status zopt_muon_graph_destroy(zopt_muon_graph *graph);
 
 /*
  * zopt_muon_groups_output_view -- zopt_muon_output_view for matrix `index` of

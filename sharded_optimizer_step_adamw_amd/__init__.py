@@ -14,6 +14,8 @@ Entry points (same names as the C ABI in include/zopt.h):
   muon_workspace_bytes / muon_output_view
   muon_step_groups   Muon on several such batches in one call (shared launches);
                      with ns_guard: zopt_muon_step_groups_guarded (health checks)
+  MuonGraph          a Muon call captured once (zopt_muon_graph_*), replayed per step
+                     with lr / momentum / weight decay read from device memory
   muon_groups_workspace_bytes / muon_groups_output_view
   round_bf16         fp32 -> bf16 round-to-nearest-even
   shard_len          the shard length the layout derives (zopt_shard_len)
@@ -93,6 +95,14 @@ def _lib_or_raise() -> ctypes.CDLL:
             i32, pi32, pi64, pi64, pp, pp, pp, pp, f32, f32, i32, f32, i32, f32, f32, f32, f32,
             i32, f32, vp, vp, ctypes.POINTER(ctypes.c_size_t), vp]
         L.zopt_muon_step_groups_guarded.restype = ctypes.c_int
+        L.zopt_muon_graph_create.argtypes = [
+            i32, pi32, pi64, pi64, pp, pp, pp, pp, vp, i32, i32, f32, f32, f32, f32, i32, f32,
+            vp, vp, ctypes.c_size_t, ctypes.POINTER(vp)]
+        L.zopt_muon_graph_create.restype = ctypes.c_int
+        L.zopt_muon_graph_launch.argtypes = [vp, vp]
+        L.zopt_muon_graph_launch.restype = ctypes.c_int
+        L.zopt_muon_graph_destroy.argtypes = [vp]
+        L.zopt_muon_graph_destroy.restype = ctypes.c_int
         L.zopt_muon_groups_output_view.argtypes = [i32, pi32, pi64, pi64, i32, vp, i32, i32, pp,
                                                    pi64]
         L.zopt_muon_groups_output_view.restype = ctypes.c_int
@@ -342,6 +352,38 @@ def muon_step_groups(groups: Sequence[tuple], lr: float, momentum_beta: float = 
     call is zopt_muon_step_groups_guarded: ns_health receives the number of
     rejected matrices, the worst passing ratio and [ratio, absmax, rejected]
     per matrix, and a rejected matrix is not updated."""
+    shapes, M, Mo, G, W, with_w, dev = _muon_group_tables(groups)
+    need = muon_groups_workspace_bytes(shapes)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _need(workspace, torch.uint8, need, "workspace", dev)
+    n, b, r, c = _shape_arrays(shapes)
+    size = ctypes.c_size_t(workspace.numel())
+    ca, cb, cc = (float(x) for x in ns_coeffs)
+    common = (n, b, r, c, _ptr_array(M), _ptr_array(Mo), _ptr_array(G),
+              _ptr_array(W) if with_w else None, lr, momentum_beta, int(nesterov), weight_decay,
+              ns_steps, ca, cb, cc, ns_eps, adjust_lr)
+    if ns_guard is None:
+        if ns_health is not None:
+            raise ValueError("muon_step_groups: ns_health needs ns_guard")
+        st = lib().zopt_muon_step_groups(*common, workspace.data_ptr(), ctypes.byref(size),
+                                         _stream(dev, stream))
+        _check(st, "zopt_muon_step_groups")
+        return workspace
+    if ns_health is None:
+        raise ValueError("muon_step_groups: ns_guard needs an ns_health tensor")
+    _need(ns_health, torch.float32, 2 + 3 * len(M), "ns_health", dev)
+    st = lib().zopt_muon_step_groups_guarded(*common, ns_guard, ns_health.data_ptr(),
+                                             workspace.data_ptr(), ctypes.byref(size),
+                                             _stream(dev, stream))
+    _check(st, "zopt_muon_step_groups_guarded")
+    return workspace
+
+
+def _muon_group_tables(groups):
+    """Checks the (master, momentum, grad, weight) groups of a Muon call and
+    flattens them: (shapes, masters, momenta, grads, weights, with_weights,
+    device)."""
     if not groups:
         raise ValueError("muon_step_groups: no groups")
     with_w = groups[0][3] is not None
@@ -369,31 +411,66 @@ def muon_step_groups(groups: Sequence[tuple], lr: float, momentum_beta: float = 
         G += list(grad)
         if with_w:
             W += list(weight)
-    need = muon_groups_workspace_bytes(shapes)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    _need(workspace, torch.uint8, need, "workspace", dev)
-    n, b, r, c = _shape_arrays(shapes)
-    size = ctypes.c_size_t(workspace.numel())
-    ca, cb, cc = (float(x) for x in ns_coeffs)
-    common = (n, b, r, c, _ptr_array(M), _ptr_array(Mo), _ptr_array(G),
-              _ptr_array(W) if with_w else None, lr, momentum_beta, int(nesterov), weight_decay,
-              ns_steps, ca, cb, cc, ns_eps, adjust_lr)
-    if ns_guard is None:
+    return shapes, M, Mo, G, W, with_w, dev
+
+
+class MuonGraph:
+    """One Muon call over `groups` captured as a hipGraph
+    (zopt_muon_graph_create), replayed by launch() (zopt_muon_graph_launch).
+    lr, momentum_beta and weight_decay are read from `scalars` (fp32 [3] on
+    the device) each time the graph runs: write new values there (a copy or
+    fill on the stream) to change them.  The tensors given are kept alive
+    while the graph exists; close() (or garbage collection) synchronises the
+    device and frees the graph."""
+
+    def __init__(self, groups, scalars: torch.Tensor, nesterov: bool = True, ns_steps: int = 5,
+                 ns_coeffs=(3.4445, -4.7750, 2.0315), ns_eps: float = 1e-7, adjust_lr: int = 1,
+                 workspace: Optional[torch.Tensor] = None, ns_guard: Optional[float] = None,
+                 ns_health: Optional[torch.Tensor] = None):
+        shapes, M, Mo, G, W, with_w, dev = _muon_group_tables(groups)
+        _need(scalars, torch.float32, 3, "scalars", dev)
+        need = muon_groups_workspace_bytes(shapes)
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        _need(workspace, torch.uint8, need, "workspace", dev)
+        if (ns_guard is None) != (ns_health is None):
+            raise ValueError("MuonGraph: give ns_guard and ns_health together")
         if ns_health is not None:
-            raise ValueError("muon_step_groups: ns_health needs ns_guard")
-        st = lib().zopt_muon_step_groups(*common, workspace.data_ptr(), ctypes.byref(size),
-                                         _stream(dev, stream))
-        _check(st, "zopt_muon_step_groups")
-        return workspace
-    if ns_health is None:
-        raise ValueError("muon_step_groups: ns_guard needs an ns_health tensor")
-    _need(ns_health, torch.float32, 2 + 3 * len(M), "ns_health", dev)
-    st = lib().zopt_muon_step_groups_guarded(*common, ns_guard, ns_health.data_ptr(),
-                                             workspace.data_ptr(), ctypes.byref(size),
-                                             _stream(dev, stream))
-    _check(st, "zopt_muon_step_groups_guarded")
-    return workspace
+            _need(ns_health, torch.float32, 2 + 3 * len(M), "ns_health", dev)
+        n, b, r, c = _shape_arrays(shapes)
+        ca, cb, cc = (float(x) for x in ns_coeffs)
+        handle = ctypes.c_void_p()
+        st = lib().zopt_muon_graph_create(
+            n, b, r, c, _ptr_array(M), _ptr_array(Mo), _ptr_array(G),
+            _ptr_array(W) if with_w else None, scalars.data_ptr(), int(nesterov), ns_steps,
+            ca, cb, cc, ns_eps, adjust_lr, 0.0 if ns_guard is None else ns_guard,
+            None if ns_health is None else ns_health.data_ptr(), workspace.data_ptr(),
+            workspace.numel(), ctypes.byref(handle))
+        _check(st, "zopt_muon_graph_create")
+        self._handle = handle
+        self.device = dev
+        self.shapes = shapes
+        self.ns_steps = ns_steps
+        self.workspace = workspace
+        self._keep = (groups, scalars, ns_health)
+
+    def launch(self, stream=None) -> None:
+        if self._handle is None:
+            raise RuntimeError("MuonGraph: closed")
+        _check(lib().zopt_muon_graph_launch(self._handle, _stream(self.device, stream)),
+               "zopt_muon_graph_launch")
+
+    def close(self) -> None:
+        if getattr(self, "_handle", None) is not None:
+            torch.cuda.synchronize(self.device)
+            _check(lib().zopt_muon_graph_destroy(self._handle), "zopt_muon_graph_destroy")
+            self._handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def muon_groups_output_view(workspace: torch.Tensor, shapes: Sequence[tuple], ns_steps: int,

@@ -55,7 +55,17 @@ struct PreArgs {
     int32_t vec;          // 8-element vector path allowed
     float mu, omm;
     int32_t nesterov;
+    const float *dev;     // device scalars [lr, momentum_beta, weight_decay], or NULL
 };
+
+// mu and omm = fp32(1 - mu), formed in double as the host forms them, from
+// the device scalars when the launch carries them.
+__device__ __forceinline__ void device_momentum(const float *dev, float &mu, float &omm) {
+    if (dev) {
+        mu = dev[kDevMomentum];
+        omm = (float)(1.0 - (double)mu);
+    }
+}
 
 __device__ __forceinline__ void momentum_update(float &m, float g, float &u,
                                                 const PreArgs &a) {
@@ -66,6 +76,7 @@ __device__ __forceinline__ void momentum_update(float &m, float g, float &u,
 __global__ __launch_bounds__(kThreads) void muon_momentum_kernel(
     MuonPtrs ptrs, PreArgs a, float *__restrict__ partials, int32_t norm_blocks) {
     __shared__ float lds4[4];
+    device_momentum(a.dev, a.mu, a.omm);
     const int b = blockIdx.y;
     float *__restrict__ mom = ptrs.momentum[b];
     const uint16_t *__restrict__ grad = ptrs.grad[b];
@@ -124,6 +135,7 @@ struct ScaleArgs {
     float mu, omm;
     int32_t nesterov;
     int32_t vec;            // cols % 8 == 0 and every base 16-byte aligned
+    const float *dev;       // device scalars, or NULL
 };
 
 // Pass 2.  One workgroup per 64 x 64 tile of the padded stored-orientation
@@ -146,7 +158,8 @@ __global__ __launch_bounds__(kThreads) void muon_scale_kernel(
                                    : xt_base + (int64_t)b * xt_stride;
     const int64_t ld_direct = a.transposed ? a.mp : a.np;
     const int64_t ld_other = a.transposed ? a.np : a.mp;
-    PreArgs pa{0, 0, a.mu, a.omm, a.nesterov};
+    PreArgs pa{0, 0, a.mu, a.omm, a.nesterov, nullptr};
+    device_momentum(a.dev, pa.mu, pa.omm);
 
     // 64 rows x 8 groups of 8 columns = 512 groups; two per thread
     for (int q = 0; q < 2; ++q) {
@@ -220,12 +233,21 @@ struct PostArgs {
     int64_t o_ld;
     int64_t o_stride;
     const int32_t *reject;  // per-matrix flags, or NULL
+    const float *dev;       // device scalars, or NULL
+    double scale;           // the update scale of this shape (for dev)
 };
 
 __global__ __launch_bounds__(kThreads) void muon_post_kernel(
     MuonPtrs ptrs, PostArgs a, const uint16_t *__restrict__ o_base) {
     const int b = blockIdx.y;
     if (a.reject && a.reject[b]) return;
+    if (a.dev) {
+        // decay = fp32(1 - lr wd), step_lr = fp32(lr scale), formed in double
+        // as the host forms them
+        const double lr = (double)a.dev[kDevLr], wd = (double)a.dev[kDevWeightDecay];
+        a.decay = (float)(1.0 - lr * wd);
+        a.step_lr = (float)(lr * a.scale);
+    }
     const int64_t count = (int64_t)a.rows * a.cols;
     const int64_t i0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * kPerThread;
     if (i0 >= count) return;
@@ -461,13 +483,13 @@ int32_t muon_norm_blocks(int64_t count) { return (int32_t)((count + kChunk - 1) 
 
 hipError_t launch_muon_pre(const MuonGeom &g, const MuonPtrs &ptrs, float mu,
                            int32_t nesterov, float ns_eps, char *ws,
-                           const MuonWorkspace &L, hipStream_t stream) {
+                           const MuonWorkspace &L, const float *dev, hipStream_t stream) {
     const int64_t count = (int64_t)g.rows * g.cols;
     const float omm = (float)(1.0 - (double)mu);
     bool vec = (count % 8) == 0;
     for (int b = 0; b < g.batch; ++b)
         vec = vec && aligned16(ptrs.momentum[b]) && aligned16(ptrs.grad[b]);
-    PreArgs pa{(int32_t)count, vec ? 1 : 0, mu, omm, nesterov};
+    PreArgs pa{(int32_t)count, vec ? 1 : 0, mu, omm, nesterov, dev};
     float *partials = reinterpret_cast<float *>(ws + L.partials);
     float *scale = partials + (int64_t)g.batch * g.norm_blocks;
     hipLaunchKernelGGL(muon_momentum_kernel, dim3(g.norm_blocks, g.batch), dim3(kThreads),
@@ -478,7 +500,7 @@ hipError_t launch_muon_pre(const MuonGeom &g, const MuonPtrs &ptrs, float mu,
     const int srows = g.transposed ? g.np : g.mp;
     const int scols = g.transposed ? g.mp : g.np;
     ScaleArgs sa{g.rows, g.cols, g.transposed, g.mp, g.np, scols / kTile, mu, omm, nesterov,
-                 (vec && g.cols % 8 == 0) ? 1 : 0};
+                 (vec && g.cols % 8 == 0) ? 1 : 0, dev};
     const int tiles = (srows / kTile) * (scols / kTile);
     hipLaunchKernelGGL(muon_scale_kernel, dim3(tiles, g.batch), dim3(kThreads), 0, stream,
                        ptrs, sa, scale, reinterpret_cast<uint16_t *>(ws + L.x),
@@ -490,14 +512,14 @@ hipError_t launch_muon_pre(const MuonGeom &g, const MuonPtrs &ptrs, float mu,
 hipError_t launch_muon_post(const MuonGeom &g, const MuonPtrs &ptrs,
                             const uint16_t *o_base, int64_t o_ld, size_t o_stride,
                             float decay, float step_lr, const int32_t *reject,
-                            hipStream_t stream) {
+                            const float *dev, double scale, hipStream_t stream) {
     const int64_t count = (int64_t)g.rows * g.cols;
     bool vec = (g.cols % 8) == 0;
     for (int b = 0; b < g.batch; ++b)
         vec = vec && aligned16(ptrs.master[b]) &&
               (ptrs.weight[b] == nullptr || aligned16(ptrs.weight[b]));
     PostArgs pa{g.rows, g.cols, vec ? 1 : 0, decay, step_lr, o_ld, (int64_t)(o_stride / 2),
-                reject};
+                reject, dev, scale};
     const int64_t units = (count + kPerThread - 1) / kPerThread;
     const int64_t blocks = (units + kThreads - 1) / kThreads;
     hipLaunchKernelGGL(muon_post_kernel, dim3((uint32_t)blocks, g.batch), dim3(kThreads), 0,

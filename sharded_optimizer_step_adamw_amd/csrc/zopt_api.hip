@@ -279,96 +279,107 @@ zopt_status plan_groups(int32_t ngroups, const int32_t *batch, const int64_t *ro
     return ZOPT_OK;
 }
 
-zopt_status muon_step_groups(int32_t ngroups, const int32_t *batch, const int64_t *rows,
-                             const int64_t *cols, float *const *master, float *const *momentum,
-                             const uint16_t *const *grad, uint16_t *const *weight, float lr,
-                             float momentum_beta, int32_t nesterov, float weight_decay,
-                             int32_t ns_steps, float ns_a, float ns_b, float ns_c, float ns_eps,
-                             int32_t adjust_lr, float guard, float *health, void *workspace,
-                             size_t *workspace_bytes, void *stream) {
-    if (!workspace_bytes) return ZOPT_ERR_NULL;
+// Everything a Muon call enqueues from: the groups' geometry and workspace
+// carve-up, their pointer tables, where each group's matrices start in the
+// call, and the launch bins.
+struct MuonCallPlan {
     GroupPlan plans[kMaxCallGroups];
-    size_t total = 0;
-    int nmat = 0;
-    zopt_status st = plan_groups(ngroups, batch, rows, cols, plans, total, nmat);
-    if (st != ZOPT_OK) return st;
-    if (!workspace) {
-        *workspace_bytes = total;
-        return ZOPT_OK;
-    }
+    MuonPtrs ptrs[kMaxCallGroups];
+    NsGroupRef refs[kMaxCallGroups];
+    int firsts[kMaxCallGroups];
+    int bins[kMaxCallGroups + 1][kMaxCallGroups];
+    int bin_size[kMaxCallGroups + 1];
+    int ngroups, nmat, nbins;
+    size_t total;
+};
+
+// The pointer checks of a Muon call (the shapes are checked by plan_groups).
+zopt_status muon_check_ptrs(int nmat, float *const *master, float *const *momentum,
+                            const uint16_t *const *grad, uint16_t *const *weight) {
     if (!master || !momentum || !grad) return ZOPT_ERR_NULL;
     for (int b = 0; b < nmat; ++b) {
         if (!master[b] || !momentum[b] || !grad[b]) return ZOPT_ERR_NULL;
         if (weight && !weight[b]) return ZOPT_ERR_NULL;
     }
-    if (!finite(lr) || lr < 0.0f || !(momentum_beta >= 0.0f && momentum_beta < 1.0f) ||
-        (nesterov != 0 && nesterov != 1) || !finite(weight_decay) || weight_decay < 0.0f ||
-        ns_steps < 0 || ns_steps > 100 || !finite(ns_a) || !finite(ns_b) || !finite(ns_c) ||
-        !finite(ns_eps) || ns_eps < 0.0f || (adjust_lr != 0 && adjust_lr != 1))
-        return ZOPT_ERR_HYPER;
-    if (*workspace_bytes < total || ((uintptr_t)workspace & 255u) != 0)
-        return ZOPT_ERR_WORKSPACE;
+    return ZOPT_OK;
+}
 
-    char *ws = static_cast<char *>(workspace);
-    hipStream_t s = (hipStream_t)stream;
-    MuonPtrs ptrs[kMaxCallGroups];
-    NsGroupRef refs[kMaxCallGroups];
-    int firsts[kMaxCallGroups];
-    for (int i = 0, first = 0; i < ngroups; first += batch[i], ++i) {
-        firsts[i] = first;
-        MuonPtrs &p = ptrs[i];
+// The hyperparameters of a Muon call that never live in device memory.
+bool muon_fixed_hypers_ok(int32_t nesterov, int32_t ns_steps, float ns_a, float ns_b,
+                          float ns_c, float ns_eps, int32_t adjust_lr) {
+    return (nesterov == 0 || nesterov == 1) && ns_steps >= 0 && ns_steps <= 100 &&
+           finite(ns_a) && finite(ns_b) && finite(ns_c) && finite(ns_eps) && ns_eps >= 0.0f &&
+           (adjust_lr == 0 || adjust_lr == 1);
+}
+
+// Pointer tables and launch bins of a planned call whose workspace starts at
+// ws.  A group whose workspace fits in the memory-side cache and whose B X
+// product alone fills two rounds of the GPU's workgroup slots gets a bin of
+// its own, all its iterations back to back, so its operands stay cached from
+// one product to the next.  The other groups -- too small to fill the GPU, or
+// too large to stay cached anyway -- share one bin, so that their tiles fill
+// each other's partial rounds.
+void muon_bin_call(MuonCallPlan &c, char *ws, float *const *master, float *const *momentum,
+                   const uint16_t *const *grad, uint16_t *const *weight, const int32_t *batch) {
+    for (int i = 0, first = 0; i < c.ngroups; first += batch[i], ++i) {
+        c.firsts[i] = first;
+        MuonPtrs &p = c.ptrs[i];
         for (int b = 0; b < batch[i]; ++b) {
             p.master[b] = master[first + b];
             p.momentum[b] = momentum[first + b];
             p.grad[b] = grad[first + b];
             p.weight[b] = weight ? weight[first + b] : nullptr;
         }
-        refs[i] = NsGroupRef{&plans[i].g, &plans[i].L, ws + plans[i].base};
+        c.refs[i] = NsGroupRef{&c.plans[i].g, &c.plans[i].L, ws + c.plans[i].base};
     }
-
-    // Launch plan.  A group whose workspace fits in the memory-side cache and
-    // whose B X product alone fills two rounds of the GPU's workgroup slots
-    // runs on its own, all its iterations back to back, so its operands stay
-    // cached from one product to the next.  The other groups -- too small to
-    // fill the GPU, or too large to stay cached anyway -- share launches, so
-    // that their tiles fill each other's partial rounds.
-    int bins[kMaxCallGroups + 1][kMaxCallGroups];
-    int bin_size[kMaxCallGroups + 1] = {0};
-    int nbins = 0, shared = -1;
-    for (int i = 0; i < ngroups; ++i) {
-        const MuonGeom &g = plans[i].g;
+    c.nbins = 0;
+    int shared = -1;
+    for (int i = 0; i < c.ngroups; ++i) {
+        const MuonGeom &g = c.plans[i].g;
         const int64_t bx_tiles = (int64_t)(g.mp / g.tile_bx) * (g.np / g.tile_bx) * g.batch;
-        const bool alone = plans[i].L.total <= kMemCacheBytes &&
+        const bool alone = c.plans[i].L.total <= kMemCacheBytes &&
                            bx_tiles >= 2 * (int64_t)ns_round_tiles(g.tile_bx);
         if (alone) {
-            bins[nbins][0] = i;
-            bin_size[nbins++] = 1;
+            c.bins[c.nbins][0] = i;
+            c.bin_size[c.nbins++] = 1;
         } else {
-            if (shared < 0) shared = nbins++;
-            bins[shared][bin_size[shared]++] = i;
+            if (shared < 0) {
+                shared = c.nbins++;
+                c.bin_size[shared] = 0;
+            }
+            c.bins[shared][c.bin_size[shared]++] = i;
         }
     }
+}
 
-    const double lr_d = (double)lr, wd_d = (double)weight_decay;
+// Enqueues a planned call on stream s.  With dev (device scalars [lr,
+// momentum_beta, weight_decay]) the kernels read those when they run and
+// lr / mu / wd here are unused; with health the Newton-Schulz health pass
+// runs and rejected matrices are not updated.
+hipError_t muon_enqueue(const MuonCallPlan &c, char *ws, float lr, float mu, int32_t nesterov,
+                        float wd, int32_t ns_steps, float ns_a, float ns_b, float ns_c,
+                        float ns_eps, int32_t adjust_lr, float guard, float *health,
+                        const float *dev, hipStream_t s) {
+    const double lr_d = (double)lr, wd_d = (double)wd;
     hipError_t e = hipSuccess;
-    for (int bi = 0; bi < nbins && e == hipSuccess; ++bi) {
+    for (int bi = 0; bi < c.nbins && e == hipSuccess; ++bi) {
         NsGroupRef brefs[kMaxCallGroups];
-        for (int k = 0; k < bin_size[bi] && e == hipSuccess; ++k) {
-            const int i = bins[bi][k];
-            brefs[k] = refs[i];
-            e = launch_muon_pre(plans[i].g, ptrs[i], momentum_beta, nesterov, ns_eps,
-                                ws + plans[i].base, plans[i].L, s);
+        for (int k = 0; k < c.bin_size[bi] && e == hipSuccess; ++k) {
+            const int i = c.bins[bi][k];
+            brefs[k] = c.refs[i];
+            e = launch_muon_pre(c.plans[i].g, c.ptrs[i], mu, nesterov, ns_eps,
+                                ws + c.plans[i].base, c.plans[i].L, dev, s);
         }
         for (int k = 0; k < ns_steps && e == hipSuccess; ++k)
-            e = launch_ns_iteration(brefs, bin_size[bi], k & 1, ns_a, ns_b, ns_c, s);
+            e = launch_ns_iteration(brefs, c.bin_size[bi], k & 1, ns_a, ns_b, ns_c, s);
         if (health && e == hipSuccess) {
             int bfirst[kMaxCallGroups];
-            for (int k = 0; k < bin_size[bi]; ++k) bfirst[k] = firsts[bins[bi][k]];
-            e = launch_ns_health(brefs, bfirst, bin_size[bi], guard, health, s);
+            for (int k = 0; k < c.bin_size[bi]; ++k) bfirst[k] = c.firsts[c.bins[bi][k]];
+            e = launch_ns_health(brefs, bfirst, c.bin_size[bi], guard, health, s);
         }
-        for (int k = 0; k < bin_size[bi] && e == hipSuccess; ++k) {
-            const int i = bins[bi][k];
-            const MuonGeom &g = plans[i].g;
+        for (int k = 0; k < c.bin_size[bi] && e == hipSuccess; ++k) {
+            const int i = c.bins[bi][k];
+            const MuonGeom &g = c.plans[i].g;
             const double big = (double)(g.rows > g.cols ? g.rows : g.cols);
             const double scale = adjust_lr
                                      ? 0.2 * std::sqrt(big)
@@ -377,16 +388,49 @@ zopt_status muon_step_groups(int32_t ngroups, const int32_t *batch, const int64_
             const float step_lr = (float)(lr_d * scale);
             size_t obase;
             int64_t old;
-            muon_output(g, plans[i].L, ns_steps, obase, old);
+            muon_output(g, c.plans[i].L, ns_steps, obase, old);
             const int32_t *reject =
-                health ? reinterpret_cast<const int32_t *>(ws + plans[i].base + plans[i].L.hflag)
+                health ? reinterpret_cast<const int32_t *>(ws + c.plans[i].base + c.plans[i].L.hflag)
                        : nullptr;
-            e = launch_muon_post(g, ptrs[i],
-                                 reinterpret_cast<const uint16_t *>(ws + plans[i].base + obase),
-                                 old, plans[i].L.x_stride, decay, step_lr, reject, s);
+            e = launch_muon_post(g, c.ptrs[i],
+                                 reinterpret_cast<const uint16_t *>(ws + c.plans[i].base + obase),
+                                 old, c.plans[i].L.x_stride, decay, step_lr, reject, dev, scale,
+                                 s);
         }
     }
-    if (health && e == hipSuccess) e = launch_ns_health_total(health, nmat, s);
+    if (health && e == hipSuccess) e = launch_ns_health_total(health, c.nmat, s);
+    return e;
+}
+
+zopt_status muon_step_groups(int32_t ngroups, const int32_t *batch, const int64_t *rows,
+                             const int64_t *cols, float *const *master, float *const *momentum,
+                             const uint16_t *const *grad, uint16_t *const *weight, float lr,
+                             float momentum_beta, int32_t nesterov, float weight_decay,
+                             int32_t ns_steps, float ns_a, float ns_b, float ns_c, float ns_eps,
+                             int32_t adjust_lr, float guard, float *health, void *workspace,
+                             size_t *workspace_bytes, void *stream) {
+    if (!workspace_bytes) return ZOPT_ERR_NULL;
+    MuonCallPlan c;
+    c.ngroups = ngroups;
+    zopt_status st = plan_groups(ngroups, batch, rows, cols, c.plans, c.total, c.nmat);
+    if (st != ZOPT_OK) return st;
+    if (!workspace) {
+        *workspace_bytes = c.total;
+        return ZOPT_OK;
+    }
+    st = muon_check_ptrs(c.nmat, master, momentum, grad, weight);
+    if (st != ZOPT_OK) return st;
+    if (!finite(lr) || lr < 0.0f || !(momentum_beta >= 0.0f && momentum_beta < 1.0f) ||
+        !finite(weight_decay) || weight_decay < 0.0f ||
+        !muon_fixed_hypers_ok(nesterov, ns_steps, ns_a, ns_b, ns_c, ns_eps, adjust_lr))
+        return ZOPT_ERR_HYPER;
+    if (*workspace_bytes < c.total || ((uintptr_t)workspace & 255u) != 0)
+        return ZOPT_ERR_WORKSPACE;
+    char *ws = static_cast<char *>(workspace);
+    muon_bin_call(c, ws, master, momentum, grad, weight, batch);
+    const hipError_t e = muon_enqueue(c, ws, lr, momentum_beta, nesterov, weight_decay, ns_steps,
+                                      ns_a, ns_b, ns_c, ns_eps, adjust_lr, guard, health, nullptr,
+                                      (hipStream_t)stream);
     return e == hipSuccess ? ZOPT_OK : ZOPT_ERR_DEVICE;
 }
 
@@ -453,6 +497,75 @@ ZOPT_EXPORT zopt_status zopt_muon_step_groups_guarded(
                             momentum_beta, nesterov, weight_decay, ns_steps, ns_a, ns_b, ns_c,
                             ns_eps, adjust_lr, ns_guard, ns_health, workspace, workspace_bytes,
                             stream);
+}
+
+// A captured Muon call: the graph and its executable instance.
+struct zopt_muon_graph {
+    hipGraph_t graph;
+    hipGraphExec_t exec;
+};
+
+ZOPT_EXPORT zopt_status zopt_muon_graph_create(
+    int32_t ngroups, const int32_t *batch, const int64_t *rows, const int64_t *cols,
+    float *const *master, float *const *momentum, const uint16_t *const *grad,
+    uint16_t *const *weight, const float *scalars, int32_t nesterov, int32_t ns_steps, float ns_a,
+    float ns_b, float ns_c, float ns_eps, int32_t adjust_lr, float ns_guard, float *ns_health,
+    void *workspace, size_t workspace_bytes, zopt_muon_graph **graph) {
+    if (!graph) return ZOPT_ERR_NULL;
+    *graph = nullptr;
+    MuonCallPlan c;
+    c.ngroups = ngroups;
+    zopt_status st = plan_groups(ngroups, batch, rows, cols, c.plans, c.total, c.nmat);
+    if (st != ZOPT_OK) return st;
+    if (!workspace || !scalars) return ZOPT_ERR_NULL;
+    st = muon_check_ptrs(c.nmat, master, momentum, grad, weight);
+    if (st != ZOPT_OK) return st;
+    if (!muon_fixed_hypers_ok(nesterov, ns_steps, ns_a, ns_b, ns_c, ns_eps, adjust_lr) ||
+        (ns_health && !(ns_guard > 0.0f)))
+        return ZOPT_ERR_HYPER;
+    if (workspace_bytes < c.total || ((uintptr_t)workspace & 255u) != 0)
+        return ZOPT_ERR_WORKSPACE;
+    char *ws = static_cast<char *>(workspace);
+    muon_bin_call(c, ws, master, momentum, grad, weight, batch);
+
+    // capture on a private stream (the caller's may be the null stream, which
+    // cannot be captured); the kernels read lr / momentum / weight decay from
+    // `scalars` when they run, so one capture serves every step
+    hipStream_t cs = nullptr;
+    if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) return ZOPT_ERR_DEVICE;
+    hipGraph_t g = nullptr;
+    hipGraphExec_t ex = nullptr;
+    hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+    if (e == hipSuccess) {
+        const hipError_t e1 = muon_enqueue(c, ws, 0.0f, 0.0f, nesterov, 0.0f, ns_steps, ns_a, ns_b,
+                                           ns_c, ns_eps, adjust_lr, ns_guard, ns_health, scalars,
+                                           cs);
+        const hipError_t e2 = hipStreamEndCapture(cs, &g);
+        e = e1 != hipSuccess ? e1 : e2;
+    }
+    if (e == hipSuccess) e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+    if (hipStreamDestroy(cs) != hipSuccess && e == hipSuccess) e = hipErrorUnknown;
+    if (e != hipSuccess) {
+        if (ex) (void)hipGraphExecDestroy(ex);
+        if (g) (void)hipGraphDestroy(g);
+        return ZOPT_ERR_DEVICE;
+    }
+    *graph = new zopt_muon_graph{g, ex};
+    return ZOPT_OK;
+}
+
+ZOPT_EXPORT zopt_status zopt_muon_graph_launch(const zopt_muon_graph *graph, void *stream) {
+    if (!graph) return ZOPT_ERR_NULL;
+    return hipGraphLaunch(graph->exec, (hipStream_t)stream) == hipSuccess ? ZOPT_OK
+                                                                         : ZOPT_ERR_DEVICE;
+}
+
+ZOPT_EXPORT zopt_status zopt_muon_graph_destroy(zopt_muon_graph *graph) {
+    if (!graph) return ZOPT_OK;
+    const hipError_t e1 = hipGraphExecDestroy(graph->exec);
+    const hipError_t e2 = hipGraphDestroy(graph->graph);
+    delete graph;
+    return (e1 == hipSuccess && e2 == hipSuccess) ? ZOPT_OK : ZOPT_ERR_DEVICE;
 }
 
 ZOPT_EXPORT zopt_status zopt_muon_output_view(int32_t batch, int64_t rows, int64_t cols,

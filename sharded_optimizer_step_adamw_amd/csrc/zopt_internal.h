@@ -121,15 +121,23 @@ struct MuonWorkspace {
 MuonGeom muon_geometry(int32_t batch, int64_t rows, int64_t cols);
 MuonWorkspace muon_workspace_layout(const MuonGeom &g);
 
+// Device scalars of a Muon launch whose lr / momentum / weight decay live in
+// device memory (read when the kernels run): float[3] at these indices.
+enum : int { kDevLr = 0, kDevMomentum = 1, kDevWeightDecay = 2, kDevScalars = 3 };
+
+// dev: device scalars (mu is read there and omm formed from it) or NULL (mu
+// as given).
 hipError_t launch_muon_pre(const MuonGeom &g, const MuonPtrs &ptrs, float mu,
                            int32_t nesterov, float ns_eps, char *ws,
-                           const MuonWorkspace &L, hipStream_t stream);
+                           const MuonWorkspace &L, const float *dev, hipStream_t stream);
 
 // reject: per-matrix flags (non-zero: leave that matrix untouched) or NULL.
+// dev: device scalars, from which decay and step_lr = lr * scale are formed
+// when the kernel runs, or NULL (decay and step_lr as given).
 hipError_t launch_muon_post(const MuonGeom &g, const MuonPtrs &ptrs,
                             const uint16_t *o_base, int64_t o_ld, size_t o_stride,
                             float decay, float step_lr, const int32_t *reject,
-                            hipStream_t stream);
+                            const float *dev, double scale, hipStream_t stream);
 
 int32_t ns_health_blocks(int64_t count);
 

@@ -302,3 +302,38 @@ def test_muon_guarded_query_needs_no_health():
     size = ctypes.c_size_t(0)
     assert guarded(health=None, guard=0.0, ws=None, ws_bytes=ctypes.byref(size)) == z.ZOPT_OK
     assert size.value == z.muon_workspace_bytes(2, 64, 32)
+
+
+def graph_create(**kw):
+    out = ctypes.c_void_p(0x1234)
+    a = dict(ngroups=1, batch=(ctypes.c_int32 * 1)(2), rows=(ctypes.c_int64 * 1)(64),
+             cols=(ctypes.c_int64 * 1)(32), master=ptrs(2), momentum=ptrs(2), grad=ptrs(2),
+             weight=None, scalars=FAKE, nesterov=1, ns_steps=5, a=3.4445, b=-4.775, c=2.0315,
+             eps=1e-7, adjust=1, guard=1000.0, health=None, ws=ctypes.c_void_p(1 << 20),
+             ws_bytes=1 << 40, out=ctypes.byref(out))
+    a.update(kw)
+    st = z.lib().zopt_muon_graph_create(*a.values())
+    return st, out.value
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(out=None), z.ZOPT_ERR_NULL), (dict(scalars=None), z.ZOPT_ERR_NULL),
+    (dict(ws=None), z.ZOPT_ERR_NULL), (dict(master=None), z.ZOPT_ERR_NULL),
+    (dict(grad=ptrs(2, null_at=1)), z.ZOPT_ERR_NULL),
+    (dict(batch=(ctypes.c_int32 * 1)(65)), z.ZOPT_ERR_SIZE), (dict(ngroups=0), z.ZOPT_ERR_SIZE),
+    (dict(nesterov=3), z.ZOPT_ERR_HYPER), (dict(ns_steps=101), z.ZOPT_ERR_HYPER),
+    (dict(c=float("nan")), z.ZOPT_ERR_HYPER), (dict(adjust=-1), z.ZOPT_ERR_HYPER),
+    (dict(health=FAKE, guard=0.0), z.ZOPT_ERR_HYPER),
+    (dict(ws=ctypes.c_void_p((1 << 20) + 8)), z.ZOPT_ERR_WORKSPACE),
+    (dict(ws_bytes=1000), z.ZOPT_ERR_WORKSPACE),
+])
+def test_muon_graph_create_rejects_before_any_hip_call(kw, status):
+    st, handle = graph_create(**kw)
+    assert st == status
+    if kw.get("out", 1) is not None:
+        assert handle is None   # the handle is cleared on every error
+
+
+def test_muon_graph_launch_and_destroy_null():
+    assert z.lib().zopt_muon_graph_launch(None, None) == z.ZOPT_ERR_NULL
+    assert z.lib().zopt_muon_graph_destroy(None) == z.ZOPT_OK
