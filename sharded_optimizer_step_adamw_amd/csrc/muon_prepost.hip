@@ -9,8 +9,9 @@
 //   final   per matrix, s = 1 / (sqrt(sum of partials) + eps), the partials
 //           summed in a fixed order (deterministic)
 //   pass 2  recompute U from the new M (bitwise the same U), write
-//           X0 = bf16(U s) in the Newton-Schulz orientation and its transpose,
-//           zero-filling the tile padding                        (10 B/elem)
+//           X0 = bf16(U s) in the Newton-Schulz orientation (and its
+//           transpose only when a call with no iterations needs it as the
+//           result), zero-filling the tile padding               (8 B/elem)
 // Health [BluScript trainer source, per-step report: nsratio, the update's
 // ||O||_F / sqrt(min(rows, cols)), about 1 when healthy, and nsrej, the
 // updates the divergence guard refused for an element above 1000]:
@@ -136,6 +137,7 @@ struct ScaleArgs {
     int32_t nesterov;
     int32_t vec;            // cols % 8 == 0 and every base 16-byte aligned
     const float *dev;       // device scalars, or NULL
+    int32_t want_t;         // also write X0^T
 };
 
 // Pass 2.  One workgroup per 64 x 64 tile of the padded stored-orientation
@@ -204,12 +206,16 @@ __global__ __launch_bounds__(kThreads) void muon_scale_kernel(
                 packed[e >> 1] = pack_bf16x2(x2[0], x2[1]);
             }
         }
-        *reinterpret_cast<u32x4 *>(direct + (int64_t)r * ld_direct + c0) =
-            u32x4{packed[0], packed[1], packed[2], packed[3]};
+        // X0^T is the stored orientation of a transposed matrix: written only
+        // when wanted
+        if (!a.transposed || a.want_t)
+            *reinterpret_cast<u32x4 *>(direct + (int64_t)r * ld_direct + c0) =
+                u32x4{packed[0], packed[1], packed[2], packed[3]};
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             tile[lr][lc + e] = (uint16_t)((packed[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
     }
+    if (!a.transposed && !a.want_t) return;  // uniform: X0 alone is wanted
     __syncthreads();
     // transposed: output row = stored column, output columns = stored rows
     for (int q = 0; q < 2; ++q) {
@@ -445,7 +451,7 @@ int32_t ns_health_blocks(int64_t count) {
 }
 
 hipError_t launch_ns_health(const NsGroupRef *refs, const int *mat_first, int nrefs,
-                            float guard, float *health, hipStream_t stream) {
+                            int ns_steps, float guard, float *health, hipStream_t stream) {
     HealthLaunch h{};
     h.ngroups = nrefs;
     h.guard = guard;
@@ -455,7 +461,7 @@ hipError_t launch_ns_health(const NsGroupRef *refs, const int *mat_first, int nr
         const MuonWorkspace &L = *refs[i].layout;
         char *ws = refs[i].base;
         HealthGroup &G = h.g[i];
-        G.x = reinterpret_cast<const uint16_t *>(ws + L.x);
+        G.x = reinterpret_cast<const uint16_t *>(ws + ((ns_steps & 1) ? L.xt0 : L.x));
         G.x_stride = (int64_t)(L.x_stride / 2);
         G.count = (int64_t)g.m * g.np;  // a multiple of 8: np is a multiple of 64
         G.psum = reinterpret_cast<double *>(ws + L.hsum);
@@ -483,7 +489,8 @@ int32_t muon_norm_blocks(int64_t count) { return (int32_t)((count + kChunk - 1) 
 
 hipError_t launch_muon_pre(const MuonGeom &g, const MuonPtrs &ptrs, float mu,
                            int32_t nesterov, float ns_eps, char *ws,
-                           const MuonWorkspace &L, const float *dev, hipStream_t stream) {
+                           const MuonWorkspace &L, bool want_xt, const float *dev,
+                           hipStream_t stream) {
     const int64_t count = (int64_t)g.rows * g.cols;
     const float omm = (float)(1.0 - (double)mu);
     bool vec = (count % 8) == 0;
@@ -500,11 +507,11 @@ hipError_t launch_muon_pre(const MuonGeom &g, const MuonPtrs &ptrs, float mu,
     const int srows = g.transposed ? g.np : g.mp;
     const int scols = g.transposed ? g.mp : g.np;
     ScaleArgs sa{g.rows, g.cols, g.transposed, g.mp, g.np, scols / kTile, mu, omm, nesterov,
-                 (vec && g.cols % 8 == 0) ? 1 : 0, dev};
+                 (vec && g.cols % 8 == 0) ? 1 : 0, dev, (want_xt && g.transposed) ? 1 : 0};
     const int tiles = (srows / kTile) * (scols / kTile);
     hipLaunchKernelGGL(muon_scale_kernel, dim3(tiles, g.batch), dim3(kThreads), 0, stream,
                        ptrs, sa, scale, reinterpret_cast<uint16_t *>(ws + L.x),
-                       reinterpret_cast<uint16_t *>(ws + L.xt0),
+                       reinterpret_cast<uint16_t *>(ws + L.xt1),
                        (int64_t)(L.x_stride / 2), (int64_t)(L.x_stride / 2));
     return hipGetLastError();
 }

@@ -1,13 +1,14 @@
 // ns_gemm.hip -- the Newton-Schulz engine on bf16 matrix cores (gfx950).
 //
 // One iteration [BluScript trainer source, ShardedMuon comment block:
-// X <- aX + (bXX' + c(XX')^2)X] is three products, all of the form
-// C = P Q^T with both operands row-major and contiguous along the reduction
-// index, so every operand is read with 128-bit loads and no transposition:
+// X <- aX + (bXX' + c(XX')^2)X] is three products.  The symmetric ones are
+// C = P Q^T with both operands row-major along the reduction index; the
+// third reads X as it is, down its columns:
 //
 //   A  = X X^T           P = Q = X     (m x n, K = n)   upper tiles only
 //   B  = b A + c A A     P = Q = A     (A symmetric: A A = A A^T), upper tiles
-//   X' = a X + B X       P = B, Q = X^T (K = m); writes X' in place and X'^T
+//   X' = a X + B X       P = B (K = m), Q = X read k-major; X' goes to the
+//                        other buffer of a pair (X is still being read)
 //
 // A and B are symmetric, so only tiles on or above the diagonal are computed
 // and each is stored twice (itself and its mirror), from the upper triangle
@@ -25,9 +26,13 @@
 // Only the rounding points move; on every shape tried this lowers the error
 // against float64 by 1.5-4x (bf16 emulation).
 //
-// The transposed copy X'^T written by the third product is the Q operand of
-// the next iteration's third product (dmuon PR #16 prior art ran X X^T as a
-// separate SYRK kernel; here all three products share one kernel template).
+// B X stages X's rows [k, k + 32) x [n0, n0 + BM) as they lie in memory and
+// reads the MFMA B operand out of LDS with ds_read_b64_tr_b16, which
+// transposes 4 x 16 blocks of 16-bit values across each 16-lane group, so no
+// transposed copy of X is ever written; the last iteration alone also writes
+// X'^T for matrices stored transposed (their update is read in that
+// orientation).  (dmuon PR #16 prior art ran X X^T as a separate SYRK kernel;
+// here all three products share one kernel template.)
 //
 // Grouped launches.  One launch computes one product for every matrix of up
 // to kMaxGroups same-tile groups (e.g. all of a model's Muon matrices whose
@@ -50,9 +55,10 @@ enum Mode : int { kSyrkXXT = 0, kSyrkAA = 1, kGemmBX = 2 };
 // One group of same-shape matrices in a launch.
 struct NsGroup {
     const uint16_t *P;           // left operand rows (M x K)
-    const uint16_t *Q;           // right operand rows (N x K)
+    const uint16_t *Q;           // right operand: rows (N x K); B X: X (K x N)
     int64_t p_stride, q_stride;  // elements between matrices of the group
-    int32_t ld, K;               // operand row stride (both operands), reduction length
+    int32_t ld, K;               // operand row stride (P; Q too but B X), reduction length
+    int32_t ldq;                 // B X: row stride of X
     int32_t tiles_m, tiles_n;    // tile grid (SYRK: tiles_m == tiles_n)
     int32_t tiles_pm, tile0;     // tiles per matrix; first workgroup of the group
     int32_t tiles, padded;       // tiles of the group, rounded up to a multiple of 8
@@ -64,7 +70,7 @@ struct NsGroup {
     const float *dIn;            // SYRK_AA: dA; GEMM_BX: dB
     float *dOut;                 // SYRK_XXT: dA; SYRK_AA: dB
     int64_t d_stride;            // floats between matrices of dA / dB
-    uint16_t *CT;                // GEMM_BX: X'^T
+    uint16_t *CT;                // GEMM_BX: X'^T, or NULL (not wanted)
     int64_t ct_stride;
 };
 
@@ -235,8 +241,9 @@ __device__ __forceinline__ void epilogue(const NsGroup &args, float ca, float cb
             }
     }
     const bool coalesced = !below && !cross;
+    const bool tstore = coalesced && (MODE != kGemmBX || args.CT != nullptr);
     // 2. transposed: T[lj][li], four consecutive rows per 8-byte write
-    if (coalesced) {
+    if (tstore) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -245,7 +252,7 @@ __device__ __forceinline__ void epilogue(const NsGroup &args, float ca, float cb
                     u32x2{pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3])};
     }
     __syncthreads();
-    if (coalesced) {
+    if (tstore) {
         uint16_t *dst = MODE == kGemmBX ? args.CT + batch * args.ct_stride : Cm;
         const int64_t ld = MODE == kGemmBX ? (int64_t)args.ldct : ldc;
 #pragma unroll 4
@@ -308,7 +315,8 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch 
     constexpr int WR = Cfg<BM>::WR, WC = Cfg<BM>::WC, NW = WR * WC;
     constexpr int WTM = BM / WR, WTN = BM / WC, FM = WTM / 16, FN = WTN / 16;
     constexpr int ROW = 64, OPB = BM * ROW, STAGE = 2 * OPB;
-    constexpr int LOADS = OPB / 1024 / NW, LPS = 2 * LOADS, ND = FM + FN;
+    constexpr int LOADS = OPB / 1024 / NW, LPS = 2 * LOADS;
+    constexpr int ND = FM + (MODE == kGemmBX ? 2 : 1) * FN;  // LDS fragment reads per stage
     static_assert(LOADS >= 1 && LOADS * NW * 1024 == OPB, "tile");
     static_assert(kStages * STAGE >= BM * BM * 2, "the epilogue regions fit in the stages");
     // the stages, then (B X) a + dB_i for the tile's rows
@@ -337,9 +345,12 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch 
     tile_coords<MODE>(G, t, ti, tj);
     const int m0 = ti * BM, n0 = tj * BM;
     const int ld = G.ld, K = G.K;
+    constexpr bool NN = MODE == kGemmBX;  // Q is X itself, staged k-major
     const uint16_t *Pb = G.P + batch * G.p_stride + (int64_t)m0 * ld;
-    const uint16_t *Qb = G.Q + batch * G.q_stride + (int64_t)n0 * ld;
+    const uint16_t *Qb = NN ? G.Q + batch * G.q_stride + n0
+                            : G.Q + batch * G.q_stride + (int64_t)n0 * ld;
     const int panel_bytes = BM * ld * 2;
+    const int ldq = G.ldq;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -360,20 +371,46 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch 
     // and the chunk that the swizzle places at slot l % 4
     const int lrow = lane >> 2, lchunk = (lane & 3) ^ ((lrow >> 1) & 3);
     const int voff = (lrow * ld + lchunk * 8) * 2;
+    // B X's Q stage: X rows k0 .. k0+31, columns n0 .. n0+BM-1, as rows of
+    // QRB bytes; 32-byte unit u of row r sits at slot u ^ qsw(r).  A
+    // transposing read touches 16 rows (8g + 4h + q, or 16 in a row) x 32
+    // bytes, and qsw spreads them over all eight 32-byte bank groups, two
+    // rows each (rows of 512 or 256 bytes start in the same banks; rows of
+    // 128 bytes alternate halves).  Kilobyte k holds rows k * 1024 / QRB ...;
+    // lane l of its instruction fills slot l % (QRB / 16) (16 bytes) of row
+    // l / (QRB / 16) within it.
+    constexpr int QRB = 2 * BM, QCH = QRB / 16;
+    auto qsw = [](int r) __attribute__((always_inline)) {
+        return BM >= 128 ? (r & 3) | (((r >> 3) & 1) << 2) : ((r >> 1) & 1) | (((r >> 3) & 1) << 1);
+    };
+    int qvoff[LOADS];
+#pragma unroll
+    for (int q = 0; q < LOADS; ++q) {
+        const int r = (q * NW + wave) * (1024 / QRB) + lane / QCH, s16 = lane % QCH;
+        const int col = (((s16 >> 1) ^ qsw(r)) << 4) + ((s16 & 1) << 3);
+        qvoff[q] = (r * ldq + col) * 2;
+    }
     auto gload = [&](int sbase, int k0) {
         const int bytes = k0 < K ? panel_bytes : 0;
         const __amdgpu_buffer_rsrc_t rp =
             __builtin_amdgcn_make_buffer_rsrc((void *)Pb, (short)0, bytes, 0x00020000);
         const __amdgpu_buffer_rsrc_t rq =
-            __builtin_amdgcn_make_buffer_rsrc((void *)Qb, (short)0, bytes, 0x00020000);
+            NN ? __builtin_amdgcn_make_buffer_rsrc((void *)(Qb + (int64_t)k0 * ldq), (short)0,
+                                                   k0 < K ? kBK * ldq * 2 : 0, 0x00020000)
+               : __builtin_amdgcn_make_buffer_rsrc((void *)Qb, (short)0, bytes, 0x00020000);
 #pragma unroll
         for (int q = 0; q < LOADS; ++q) {
             const int k = q * NW + wave;
             const int soff = (16 * k * ld + k0) * 2;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, LDS_ADDR(&lds[sbase + k * 1024]), 16, voff,
                                                      soff, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, LDS_ADDR(&lds[sbase + OPB + k * 1024]), 16,
-                                                     voff, soff, 0, 0);
+            if constexpr (NN) {
+                const int qv = qvoff[q];
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, LDS_ADDR(&lds[sbase + OPB + k * 1024]),
+                                                         16, qv, 0, 0, 0);
+            } else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, LDS_ADDR(&lds[sbase + OPB + k * 1024]),
+                                                         16, voff, soff, 0, 0);
         }
     };
     // MFMA 16x16x32 operand: lane l holds row l % 16, K-chunk l / 16 of the
@@ -381,13 +418,44 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch 
     const int fr = lane & 15, fh = lane >> 4;
     const int foff = fr * ROW + ((fh ^ ((fr >> 1) & 3)) << 4);
     bf16x8 fa[2][FM], fb[2][FN];
+    const uint32_t lds_base =
+        (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t *)lds);
+    // B X: the B operand of column block j, K-chunk g = lane / 16 is two
+    // transposing reads of 4 x 16 blocks (rows 8g .. 8g+3 and 8g+4 .. 8g+7):
+    // lane 4q + p of a 16-lane group addresses row +q, columns 4p .. 4p+3 of
+    // the block, and lane i then holds rows +0..+3 of column i.
+    const int tg = lane >> 4, tq = (lane >> 2) & 3, tp = lane & 3;
+    const int tpo = ((tp >> 1) << 4) + ((tp & 1) << 3);
+    auto qbyte = [&](int r, int j) __attribute__((always_inline)) {
+        return r * QRB + ((((wc * WTN) / 16 + j) ^ qsw(r)) << 5) + tpo;
+    };
+    int qro[2][FN];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) qro[h][j] = qbyte(8 * tg + 4 * h + tq, j);
     auto read = [&](int buf, int sbase) {
         const uint8_t *pa = &lds[sbase + wr * WTM * ROW + foff];
-        const uint8_t *pb = &lds[sbase + OPB + wc * WTN * ROW + foff];
 #pragma unroll
         for (int i = 0; i < FM; ++i) fa[buf][i] = *reinterpret_cast<const bf16x8 *>(pa + i * 16 * ROW);
+        if constexpr (NN) {
+            // inline assembly, for the reason given at `diag` below; the
+            // values are used only after the next stage's wait (`tie`)
+            const uint32_t qb = lds_base + sbase;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) fb[buf][j] = *reinterpret_cast<const bf16x8 *>(pb + j * 16 * ROW);
+            for (int j = 0; j < FN; ++j) {
+                u32x2 lo, hi;
+                asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                             : "=v"(lo) : "v"(qb + qro[0][j]), "i"(OPB));
+                asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                             : "=v"(hi) : "v"(qb + qro[1][j]), "i"(OPB));
+                fb[buf][j] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+            }
+        } else {
+            const uint8_t *pb = &lds[sbase + OPB + wc * WTN * ROW + foff];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) fb[buf][j] = *reinterpret_cast<const bf16x8 *>(pb + j * 16 * ROW);
+        }
     };
     auto mma = [&](int buf) {
 #pragma unroll
@@ -399,18 +467,18 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch 
     };
 
     // B X: X' = (a + dB_i) X + Boff X.  The first term needs the tile of X
-    // itself, and the Q operand X^T brings exactly that tile through LDS
-    // during the stages whose K range [k1, k1 + 32) lies inside the tile's
-    // rows: X[k1 + kk][n0 + c] = X^T[n0 + c][k1 + kk].  So in those stages
-    // each wave adds (a + dB_row) X[row][col] to the accumulators of its rows
-    // in that range (two 16-row blocks), reading X from the stage in LDS
-    // instead of from memory in the epilogue.
+    // itself, and the Q operand brings exactly that tile through LDS during
+    // the stages whose K range [k1, k1 + 32) lies inside the tile's rows: its
+    // row k1 + kk is X's row k1 + kk, columns n0 ... So in those stages each
+    // wave adds (a + dB_row) X[row][col] to the accumulators of its rows in
+    // that range (two 16-row blocks), reading X from the stage in LDS (one
+    // transposing read per block: lane i of group g gets rows 4g .. 4g+3 of
+    // column i, the rows its accumulators hold) instead of from memory in the
+    // epilogue.
     // (The X reads are issued as inline assembly: as ordinary LDS loads the
     // compiler cannot tell them from the in-flight global->LDS copies into
     // other stage buffers and would wait for those copies to finish.)
     const int quad = lane >> 4;
-    const uint32_t lds_base =
-        (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t *)lds);
     auto diag = [&](int sbase, int k1) __attribute__((always_inline)) {
         if constexpr (MODE == kGemmBX) {
             const int rw = m0 + wr * WTM;
@@ -424,10 +492,9 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch 
                 u32x2 xv[FN];
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
-                    const int qr = wc * WTN + j * 16 + (lane & 15);
-                    const uint32_t addr = lds_base + sbase + OPB + qr * ROW +
-                                          ((((kk0 >> 3) ^ ((qr >> 1) & 3))) << 4) + (kk0 & 7) * 2;
-                    asm volatile("ds_read_b64 %0, %1" : "=v"(xv[j]) : "v"(addr));
+                    const uint32_t addr =
+                        lds_base + sbase + OPB + qbyte((i - i0) * 16 + 4 * tg + tq, j);
+                    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(xv[j]) : "v"(addr));
                 }
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
@@ -455,6 +522,12 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch 
         constexpr int par = decltype(PAR)::value;
         const int nxt = cur + 1 == kStages ? 0 : cur + 1;
         __builtin_amdgcn_s_waitcnt(WAIT_VM_LGKM0((kStages - 2) * LPS));
+        if constexpr (NN) {
+            // tie: the B operands read by inline assembly in the previous
+            // stage are complete only after the wait above
+#pragma unroll
+            for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(fb[par][j]));
+        }
         __builtin_amdgcn_s_barrier();
         diag(nxt * STAGE, (kt + 1) * kBK);
         __builtin_amdgcn_sched_barrier(0);
@@ -487,6 +560,14 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch 
     // the loads past the end still write (zeros) to LDS: drain them before
     // the epilogue reuses the buffers
     __builtin_amdgcn_s_waitcnt(0);
+    if constexpr (NN) {
+        // the last stage's B operands (never used) stay allocated until the
+        // wait above, so their late returns cannot land on other values
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) asm volatile("" : : "v"(fb[b][j]));
+    }
     __syncthreads();
     epilogue<MODE, FM, FN>(G, L.a, L.b, L.c, acc, batch, m0 + wr * WTM, n0 + wc * WTN, wave, lane,
                            lds);
@@ -495,14 +576,15 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch 
 template <int T>
 constexpr int kThreadsOf = Cfg<T>::WR * Cfg<T>::WC * 64;
 
-// The per-group operands of one product.
-NsGroup product_group(int mode, const NsGroupRef &r, int cur_xt) {
+// The per-group operands of one product of iteration `iter` (X in the x
+// buffer at even iterations, in xt0 at odd ones; the other receives X').
+NsGroup product_group(int mode, const NsGroupRef &r, int iter, bool last) {
     const MuonGeom &g = *r.geom;
     const MuonWorkspace &L = *r.layout;
     char *ws = r.base;
-    uint16_t *X = reinterpret_cast<uint16_t *>(ws + L.x);
-    uint16_t *XT = reinterpret_cast<uint16_t *>(ws + (cur_xt ? L.xt1 : L.xt0));
-    uint16_t *XTn = reinterpret_cast<uint16_t *>(ws + (cur_xt ? L.xt0 : L.xt1));
+    uint16_t *X = reinterpret_cast<uint16_t *>(ws + ((iter & 1) ? L.xt0 : L.x));
+    uint16_t *Xn = reinterpret_cast<uint16_t *>(ws + ((iter & 1) ? L.x : L.xt0));
+    uint16_t *XTout = reinterpret_cast<uint16_t *>(ws + L.xt1);
     uint16_t *A = reinterpret_cast<uint16_t *>(ws + L.a);
     uint16_t *B = reinterpret_cast<uint16_t *>(ws + L.b);
     float *dA = reinterpret_cast<float *>(ws + L.da);
@@ -525,10 +607,11 @@ NsGroup product_group(int mode, const NsGroupRef &r, int cur_xt) {
         s.C = B; s.c_stride = as; s.ldc = g.mp; s.E = A;
         s.dIn = dA; s.dOut = dB;
     } else {
-        s.P = B; s.Q = XT; s.p_stride = as; s.q_stride = xs; s.ld = g.mp; s.K = g.mp;
+        s.P = B; s.Q = X; s.p_stride = as; s.q_stride = xs; s.ld = g.mp; s.K = g.mp;
+        s.ldq = g.np;
         s.tiles_n = tn; s.tiles_pm = tm * tn;
-        s.C = X; s.c_stride = xs; s.ldc = g.np;
-        s.CT = XTn; s.ct_stride = xs; s.ldct = g.mp;
+        s.C = Xn; s.c_stride = xs; s.ldc = g.np;
+        s.CT = (last && g.transposed) ? XTout : nullptr; s.ct_stride = xs; s.ldct = g.mp;
         s.dIn = dB; s.dOut = dB;
     }
     return s;
@@ -546,8 +629,8 @@ int round_tiles_of() {
 }
 
 template <int T, int MODE>
-hipError_t launch_product(const NsGroupRef *refs, const int *idx, int n, int cur_xt, float a,
-                          float b, float c, hipStream_t stream) {
+hipError_t launch_product(const NsGroupRef *refs, const int *idx, int n, int iter, bool last,
+                          float a, float b, float c, hipStream_t stream) {
     const int32_t round_tiles = round_tiles_of<T>();
     for (int first = 0; first < n; first += kMaxGroups) {
         const int cnt = n - first < kMaxGroups ? n - first : kMaxGroups;
@@ -559,7 +642,7 @@ hipError_t launch_product(const NsGroupRef *refs, const int *idx, int n, int cur
         int64_t tiles = 0;
         for (int k = 0; k < cnt; ++k) {
             const NsGroupRef &r = refs[idx[first + k]];
-            NsGroup s = product_group(MODE, r, cur_xt);
+            NsGroup s = product_group(MODE, r, iter, last);
             s.tiles = s.tiles_pm * r.geom->batch;
             s.padded = (s.tiles + 7) / 8 * 8;
             s.round_tiles = round_tiles;
@@ -577,8 +660,8 @@ hipError_t launch_product(const NsGroupRef *refs, const int *idx, int n, int cur
 // One product for every group whose tile size for it is T, longest reduction
 // first so that the short tiles fill the last rounds.
 template <int T, int MODE>
-hipError_t run_product(const NsGroupRef *refs, int nrefs, int cur_xt, float a, float b, float c,
-                       hipStream_t stream) {
+hipError_t run_product(const NsGroupRef *refs, int nrefs, int iter, bool last, float a, float b,
+                       float c, hipStream_t stream) {
     int idx[kMaxCallGroups];
     int n = 0;
     for (int i = 0; i < nrefs; ++i) {
@@ -595,15 +678,15 @@ hipError_t run_product(const NsGroupRef *refs, int nrefs, int cur_xt, float a, f
             idx[j - 1] = idx[j];
             idx[j] = t;
         }
-    return launch_product<T, MODE>(refs, idx, n, cur_xt, a, b, c, stream);
+    return launch_product<T, MODE>(refs, idx, n, iter, last, a, b, c, stream);
 }
 
 template <int MODE>
-hipError_t run_mode(const NsGroupRef *refs, int nrefs, int cur_xt, float a, float b, float c,
-                    hipStream_t stream) {
-    hipError_t e = run_product<256, MODE>(refs, nrefs, cur_xt, a, b, c, stream);
-    if (e == hipSuccess) e = run_product<128, MODE>(refs, nrefs, cur_xt, a, b, c, stream);
-    if (e == hipSuccess) e = run_product<64, MODE>(refs, nrefs, cur_xt, a, b, c, stream);
+hipError_t run_mode(const NsGroupRef *refs, int nrefs, int iter, bool last, float a, float b,
+                    float c, hipStream_t stream) {
+    hipError_t e = run_product<256, MODE>(refs, nrefs, iter, last, a, b, c, stream);
+    if (e == hipSuccess) e = run_product<128, MODE>(refs, nrefs, iter, last, a, b, c, stream);
+    if (e == hipSuccess) e = run_product<64, MODE>(refs, nrefs, iter, last, a, b, c, stream);
     return e;
 }
 
@@ -617,8 +700,8 @@ int ns_round_tiles(int tile) {
     }
 }
 
-hipError_t launch_ns_iteration(const NsGroupRef *refs, int nrefs, int cur_xt, float a, float b,
-                               float c, hipStream_t stream) {
+hipError_t launch_ns_iteration(const NsGroupRef *refs, int nrefs, int iter, bool last, float a,
+                               float b, float c, hipStream_t stream) {
     if (nrefs < 1 || nrefs > kMaxCallGroups) return hipErrorInvalidValue;
     for (int i = 0; i < nrefs; ++i) {
         const MuonGeom &g = *refs[i].geom;
@@ -626,9 +709,9 @@ hipError_t launch_ns_iteration(const NsGroupRef *refs, int nrefs, int cur_xt, fl
             if ((t != 64 && t != 128 && t != 256) || g.mp % t != 0 || g.np % t != 0)
                 return hipErrorInvalidValue;
     }
-    hipError_t e = run_mode<kSyrkXXT>(refs, nrefs, cur_xt, a, b, c, stream);
-    if (e == hipSuccess) e = run_mode<kSyrkAA>(refs, nrefs, cur_xt, a, b, c, stream);
-    if (e == hipSuccess) e = run_mode<kGemmBX>(refs, nrefs, cur_xt, a, b, c, stream);
+    hipError_t e = run_mode<kSyrkXXT>(refs, nrefs, iter, last, a, b, c, stream);
+    if (e == hipSuccess) e = run_mode<kSyrkAA>(refs, nrefs, iter, last, a, b, c, stream);
+    if (e == hipSuccess) e = run_mode<kGemmBX>(refs, nrefs, iter, last, a, b, c, stream);
     return e;
 }
 

@@ -239,16 +239,17 @@ zopt_status muon_check_shape(int32_t batch, int64_t rows, int64_t cols) {
     return ZOPT_OK;
 }
 
-// Where the Newton-Schulz result of a call lies: the iteration reads X^T from
-// xt0 at even steps and xt1 at odd ones, so after k steps X holds the result
-// and xt[k % 2] its transpose.  The stored orientation is X when rows <= cols.
+// Where the Newton-Schulz result of a call lies, in the stored orientation:
+// X alternates between the x and xt0 regions (x after an even number of
+// iterations), and matrices stored transposed (rows > cols) find X^T in xt1,
+// which the last iteration (or, with no iterations, the pre-step) writes.
 void muon_output(const MuonGeom &g, const MuonWorkspace &L, int32_t ns_steps, size_t &base,
                  int64_t &ld) {
     if (!g.transposed) {
-        base = L.x;
+        base = (ns_steps % 2) ? L.xt0 : L.x;
         ld = g.np;
     } else {
-        base = (ns_steps % 2) ? L.xt1 : L.xt0;
+        base = L.xt1;
         ld = g.mp;
     }
 }
@@ -368,14 +369,15 @@ hipError_t muon_enqueue(const MuonCallPlan &c, char *ws, float lr, float mu, int
             const int i = c.bins[bi][k];
             brefs[k] = c.refs[i];
             e = launch_muon_pre(c.plans[i].g, c.ptrs[i], mu, nesterov, ns_eps,
-                                ws + c.plans[i].base, c.plans[i].L, dev, s);
+                                ws + c.plans[i].base, c.plans[i].L, ns_steps == 0, dev, s);
         }
         for (int k = 0; k < ns_steps && e == hipSuccess; ++k)
-            e = launch_ns_iteration(brefs, c.bin_size[bi], k & 1, ns_a, ns_b, ns_c, s);
+            e = launch_ns_iteration(brefs, c.bin_size[bi], k, k + 1 == ns_steps, ns_a, ns_b, ns_c,
+                                    s);
         if (health && e == hipSuccess) {
             int bfirst[kMaxCallGroups];
             for (int k = 0; k < c.bin_size[bi]; ++k) bfirst[k] = c.firsts[c.bins[bi][k]];
-            e = launch_ns_health(brefs, bfirst, c.bin_size[bi], guard, health, s);
+            e = launch_ns_health(brefs, bfirst, c.bin_size[bi], ns_steps, guard, health, s);
         }
         for (int k = 0; k < c.bin_size[bi] && e == hipSuccess; ++k) {
             const int i = c.bins[bi][k];

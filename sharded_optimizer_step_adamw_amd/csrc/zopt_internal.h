@@ -110,7 +110,9 @@ struct MuonPtrs {
     uint16_t *weight[kMaxBatch];
 };
 
-// Workspace carve-up (byte offsets; every region 256-byte aligned).
+// Workspace carve-up (byte offsets; every region 256-byte aligned).  x and
+// xt0 hold X (mp x np) in turn, one per Newton-Schulz iteration; xt1 holds
+// the result transposed (np x mp) for matrices stored transposed.
 struct MuonWorkspace {
     size_t x, xt0, xt1, a, b, da, db, partials;
     size_t hsum, hmax, hflag;  // health pass: fp64 / fp32 partials, per-matrix reject flags
@@ -127,9 +129,12 @@ enum : int { kDevLr = 0, kDevMomentum = 1, kDevWeightDecay = 2, kDevScalars = 3 
 
 // dev: device scalars (mu is read there and omm formed from it) or NULL (mu
 // as given).
+// Writes X0 to the x region, and X0^T to xt1 as well when want_xt and the
+// matrices are stored transposed (the result of a call with no iterations).
 hipError_t launch_muon_pre(const MuonGeom &g, const MuonPtrs &ptrs, float mu,
                            int32_t nesterov, float ns_eps, char *ws,
-                           const MuonWorkspace &L, const float *dev, hipStream_t stream);
+                           const MuonWorkspace &L, bool want_xt, const float *dev,
+                           hipStream_t stream);
 
 // reject: per-matrix flags (non-zero: leave that matrix untouched) or NULL.
 // dev: device scalars, from which decay and step_lr = lr * scale are formed
@@ -149,23 +154,25 @@ struct NsGroupRef {
     char *base;
 };
 
-// Health of each matrix's Newton-Schulz result X (in the workspaces) for
-// the nrefs groups, in two launches: writes [ratio, absmax, rejected] for
-// matrix b of group i to health + 2 + 3 * (mat_first[i] + b) and the reject
-// flags to the workspaces.
+// Health of each matrix's Newton-Schulz result X (in the workspaces, after
+// ns_steps iterations) for the nrefs groups, in two launches: writes [ratio,
+// absmax, rejected] for matrix b of group i to health + 2 + 3 * (mat_first[i]
+// + b) and the reject flags to the workspaces.
 hipError_t launch_ns_health(const NsGroupRef *refs, const int *mat_first, int nrefs,
-                            float guard, float *health, hipStream_t stream);
+                            int ns_steps, float guard, float *health, hipStream_t stream);
 
 // health[0] = matrices rejected, health[1] = worst ratio among the others
 // (0 if none), from the nmat triples at health + 2.
 hipError_t launch_ns_health_total(float *health, int32_t nmat, hipStream_t stream);
 
-// One Newton-Schulz iteration of every group of a call: A = X X^T,
-// B = b A + c A A, X = a X + B X, reading X^T from xt[cur_xt] and writing
-// xt[1 - cur_xt].  Three launches per tile size in use (more if over
-// kMaxGroups groups share a tile size).
-hipError_t launch_ns_iteration(const NsGroupRef *refs, int nrefs, int cur_xt, float a, float b,
-                               float c, hipStream_t stream);
+// Iteration `iter` (0-based) of Newton-Schulz for every group of a call:
+// A = X X^T, B = b A + c A A, X' = a X + B X, with X in the workspace's x
+// region at even iterations and in xt0 at odd ones (X' goes to the other);
+// the last iteration also writes X'^T to xt1 for groups stored transposed.
+// Three launches per tile size in use (more if over kMaxGroups groups share
+// a tile size).
+hipError_t launch_ns_iteration(const NsGroupRef *refs, int nrefs, int iter, bool last, float a,
+                               float b, float c, hipStream_t stream);
 
 // Workgroups of the Newton-Schulz kernel with the given tile size that the
 // current device holds at once (one round of tiles).
