@@ -67,6 +67,11 @@ MuonGeom muon_geometry(int32_t batch, int64_t rows, int64_t cols) {
     // B X has 2 m^2 n of the 3 m^2 n + m^3 flops: where the padded sizes allow,
     // it takes the larger tile, which does more work per byte staged
     g.tile_bx = (g.tile == 128 && g.mp % 256 == 0 && g.np % 256 == 0) ? 256 : g.tile;
+    // X X^T and A A touch only the upper-triangle tiles: a group with fewer
+    // than 128 of them at 256 x 256 would leave most of the GPU idle, so it
+    // takes 128 x 128 tiles (four times as many) for those two products
+    const int64_t t256 = g.mp / 256;
+    if (g.tile == 256 && (int64_t)batch * (t256 * (t256 + 1) / 2) < 128) g.tile = 128;
     g.norm_blocks = muon_norm_blocks(rows * cols);
     g.health_blocks = ns_health_blocks((int64_t)g.m * g.np);
     return g;
