@@ -20,7 +20,9 @@ report the other two parts of the metric on their own workloads:
   newton_schulz   rank 0's Muon share of a 32-layer d=4096 decoder (8 x
                   [14336, 4096], 4 x [4096, 14336], 8 x [4096, 4096],
                   8 x [1024, 4096]): bf16 TFLOP/s at 3 m^2 n + m^3
-                  algorithmic flops per iteration, 5 iterations.
+                  algorithmic flops per iteration, 5 iterations (and the same
+                  for the 1B model's rank-0 share);
+  tiny            the tiny configuration's AdamW and Muon step times.
 
 Inputs are seeded and synthetic, generated on the GPU before timing, so the
 timed region starts with everything resident in HBM.  Timing: W untimed
@@ -78,11 +80,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--parts", default="step,adamw,clip,ns,graph",
+    ap.add_argument("--parts", default="step,adamw,clip,ns,graph,tiny",
                     help="comma list of: step (headline), adamw, clip (the clipped step on the "
-                         "adamw shard; needs adamw), ns, graph (eager vs captured Muon calls), "
-                         "copy (a zopt_round_bf16 pass of known size: the calibration for HBM "
-                         "byte counters)")
+                         "adamw shard; needs adamw), ns (8B and 1B rank-0 Muon shares), graph "
+                         "(eager vs captured Muon calls), tiny (the tiny configuration), copy (a "
+                         "zopt_round_bf16 pass of known size: the calibration for HBM byte "
+                         "counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
 
@@ -307,9 +310,9 @@ def bench_clip(torch, z, timer, s, K, W):
                       algorithmic_bytes_per_launch=2 * sl, avg_launch_ms=round(norm_ms, 4)))
 
 
-def bench_ns(torch, z, timer, dev, K, W):
+def bench_ns(torch, z, timer, dev, K, W, w=None):
     import workloads as wl
-    w = wl.LLAMA8B_MUON
+    w = w or wl.LLAMA8B_MUON
     groups, workspace = muon_groups(torch, w, dev)
     total_flops = sum(g["count"] * ns_flops(min(g["rows"], g["cols"]), max(g["rows"], g["cols"]),
                                             w.ns_steps) for g in groups)
@@ -322,7 +325,9 @@ def bench_ns(torch, z, timer, dev, K, W):
     del groups, workspace
     torch.cuda.empty_cache()
     tf = total_flops / ns_ms / 1e9
-    return dict(workload="llama8b rank-0 Muon share (W=8, 32 layers), 5 bf16 NS iterations",
+    names = {"llama8b_rank0_muon": "llama8b rank-0 Muon share (W=8, 32 layers), 5 bf16 NS iterations",
+             "llama1b_rank0_muon": "llama1b rank-0 Muon share (W=8, 16 layers), 5 bf16 NS iterations"}
+    return dict(workload=names.get(w.name, w.name),
                 algorithmic_flops_per_step=total_flops, ns_ms_per_step=round(ns_ms, 3),
                 muon_ms_per_step=round(call_ms, 3), ns_tflops=round(tf, 1),
                 mfma_frac=round(tf / BF16_PEAK_TFLOPS, 4),
@@ -390,6 +395,42 @@ def bench_graph(torch, z, timer, dev, K, W):
         del groups, workspace, graph
         torch.cuda.empty_cache()
     return out
+
+
+def bench_tiny(torch, z, timer, dev, K, W):
+    """The tiny configuration: one AdamW call on rank 0's shard of a
+    1,048,576-element vector (buckets of 262,144, world 4) and one Muon call on
+    2 x [128, 512]; per-step time (both launch-bound: 7 MB of state)."""
+    import workloads as wl
+    wa, wm = wl.TINY_ADAMW, wl.TINY_MUON
+    part = wa.parts[0]
+    sl = z.shard_len(part.n, part.bucket, part.world)
+    master = wl.device_normal(wa.wid, 0, (sl,), wa.master_std, dev)
+    m, v = torch.zeros_like(master), torch.zeros_like(master)
+    grad = wl.device_grad_bf16(wa.wid, 1, (part.n,), wa.grad_std, dev)
+    weight = torch.zeros(part.n, dtype=torch.bfloat16, device=dev)
+    groups, workspace = muon_groups(torch, wm, dev)
+    counter = [0]
+
+    def adamw(_):
+        counter[0] += 1
+        z.adamw_shard_step(master, m, v, grad, weight, part.n, part.bucket, part.world, part.rank,
+                           part.lr, part.beta1, part.beta2, part.eps, part.weight_decay, counter[0])
+
+    def step(i):
+        adamw(i)
+        muon_call(z, wm, groups, workspace, wm.ns_steps)
+
+    timer.run(step, W)
+    step_ms = timer.run(step, K)
+    adamw_ms = timer.run(adamw, K)
+    muon_ms = timer.run(lambda _: muon_call(z, wm, groups, workspace, wm.ns_steps), K)
+    del master, m, v, grad, weight, groups, workspace
+    torch.cuda.empty_cache()
+    return dict(workload="tiny: AdamW rank-0 shard of 1,048,576 (bucket 262,144, world 4) + Muon "
+                         "2 x [128, 512], 5 NS iterations",
+                step_ms=round(step_ms, 4), adamw_ms=round(adamw_ms, 4), muon_ms=round(muon_ms, 4),
+                adamw_gbs=round(28 * sl / adamw_ms / 1e6, 1))
 
 
 def bench_copy(torch, z, timer, dev, K, W):
@@ -475,6 +516,12 @@ def main():
     res_adamw = (bench_adamw(torch, z, timer, dev, max(K, 100), W, clip_leg="clip" in parts)
                  if "adamw" in parts else None)
     res_ns = bench_ns(torch, z, timer, dev, max(2, K // 5), W) if "ns" in parts else None
+    if "ns" in parts:
+        import workloads as wl
+        res_ns1b = bench_ns(torch, z, timer, dev, K, W, wl.LLAMA1B_MUON)
+    else:
+        res_ns1b = None
+    res_tiny = bench_tiny(torch, z, timer, dev, K, W) if "tiny" in parts else None
     res_copy = bench_copy(torch, z, timer, dev, K, W) if "copy" in parts else None
     res_graph = bench_graph(torch, z, timer, dev, K, W) if "graph" in parts else None
     if res_step:
@@ -507,6 +554,10 @@ def main():
         out["adamw_shard"] = res_adamw
     if res_ns:
         out["newton_schulz"] = res_ns
+    if res_ns1b:
+        out["newton_schulz_1b"] = res_ns1b
+    if res_tiny:
+        out["tiny"] = res_tiny
     if res_copy:
         out["round_bf16_calibration"] = res_copy
     if res_graph:
