@@ -54,10 +54,10 @@ MEASURED_TRAFFIC = {
                         bytes_per_launch=7.000e9,
                         profile="profiles/adamw_shard_kernel_zero2_2b_rank3.md"),
     # one Newton-Schulz iteration of the 72 GPT-2-small matrices: the three launches'
-    # FETCH_SIZE + WRITE_SIZE, calibrated (0.6998 GB read, 0.3405 GB written)
+    # FETCH_SIZE + WRITE_SIZE, calibrated (0.7017 GB read, 0.3405 GB written)
     "ns_iteration_gpt2": dict(source="sharded_optimizer_step_adamw_amd/csrc/ns_gemm.hip",
-                              sha256="c4acd49a2c593f69e493d9c0846faf3d00c8d1381ddc8ad3b06aa69d02ce86fe",
-                              bytes_per_launch=1.0403e9,
+                              sha256="6ec693d93f9f137f712755e35c490122ee49142c3a45a617f77b64b6c166ff26",
+                              bytes_per_launch=1.0422e9,
                               profile="profiles/ns_gemm_gpt2_small_step.md"),
     "grad_sq_norm": dict(source="sharded_optimizer_step_adamw_amd/csrc/adamw_shard.hip",
                          sha256="7700ae2a639bcc25367d613767f5358e3cf6fd68c9ed57b1a25e6a6842b9f4a0",
@@ -529,7 +529,8 @@ def main():
         out.update(value=round(res_step["ms"], 4), unit="ms per optimizer step")
         roof = dict(
             kernel=("Newton-Schulz iteration: ns_gemm_kernel X X^T and A A (128 x 128 tiles) "
-                    "+ B X (256 x 256 tiles), one launch each over all 72 matrices"),
+                    "+ ns_bx_kernel B X (256 x 256 tiles, persistent), one launch each over "
+                    "all 72 matrices"),
             bound="mfma", achieved=round(tf, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
             frac=round(tf / BF16_PEAK_TFLOPS, 4), traffic=measured_traffic("ns_iteration_gpt2"),
             traffic_unit="HBM bytes per iteration (3 launches)",

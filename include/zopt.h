@@ -24,7 +24,8 @@
  * --------------------------------
  *  - Every buffer is device memory owned by the caller.  The library
  *    allocates no device memory and keeps no state between calls (a captured
- *    Muon graph is a handle the caller owns); it is reentrant.
+ *    Muon graph is a handle the caller owns; zopt_set_ns_workgroup_limit is
+ *    a process-wide setting); it is reentrant.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *    the call returns without synchronising.  All launch parameters travel
  *    as kernel arguments, so back-to-back calls need no host sync.
@@ -468,6 +469,21 @@ zopt_status zopt_muon_groups_output_view(int32_t ngroups, const int32_t *batch,
  * ZOPT_ERR_DEVICE.
  */
 zopt_status zopt_round_bf16(const float *src, uint16_t *dst, int64_t n, void *stream);
+
+/*
+ * zopt_set_ns_workgroup_limit -- caps the workgroups that the Newton-Schulz
+ * X' = a X + B X launches keep resident.  Those launches are persistent: one
+ * round of workgroups walks all the tiles, each starting its next tile's
+ * loads while it finishes the current one.  n = 0 restores the default, one
+ * full round of the device (one 256 x 256-tile workgroup per compute unit);
+ * n > 0 caps it at max(8, n rounded down to a multiple of 8), which leaves
+ * compute units free for work running beside the optimizer (collectives on
+ * another stream, say) at a cost in Newton-Schulz time.  Process-wide; it
+ * applies to calls enqueued, and graphs captured, after it.  Results do not
+ * depend on it: every tile is computed the same way by whichever workgroup.
+ * Errors: ZOPT_ERR_SIZE (n < 0).
+ */
+zopt_status zopt_set_ns_workgroup_limit(int32_t n);
 
 #ifdef __cplusplus
 }

@@ -78,6 +78,8 @@ def _lib_or_raise() -> ctypes.CDLL:
         L.zopt_shard_len.restype = i64
         L.zopt_round_bf16.argtypes = [vp, vp, i64, vp]
         L.zopt_round_bf16.restype = ctypes.c_int
+        L.zopt_set_ns_workgroup_limit.argtypes = [i32]
+        L.zopt_set_ns_workgroup_limit.restype = ctypes.c_int
         pp = ctypes.POINTER(vp)
         L.zopt_muon_step.argtypes = [i32, i64, i64, pp, pp, pp, pp, f32, f32, i32, f32, i32,
                                      f32, f32, f32, f32, i32, vp,
@@ -244,6 +246,13 @@ def round_bf16(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
     _need(dst, torch.bfloat16, n, "dst", src.device)
     st = lib().zopt_round_bf16(src.data_ptr(), dst.data_ptr(), n, _stream(src.device, stream))
     _check(st, "zopt_round_bf16")
+
+
+def set_ns_workgroup_limit(n: int) -> None:
+    """Caps the workgroups the persistent Newton-Schulz B X launches keep
+    resident (0: a full round of the device); process-wide
+    (zopt_set_ns_workgroup_limit)."""
+    _check(lib().zopt_set_ns_workgroup_limit(int(n)), "zopt_set_ns_workgroup_limit")
 
 
 def _ptr_array(tensors) -> ctypes.Array:

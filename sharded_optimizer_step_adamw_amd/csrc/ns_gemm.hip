@@ -40,6 +40,8 @@
 // together and the launch count per iteration stays at three per tile size.
 // Workgroups are numbered group by group (longest reduction first), matrix by
 // matrix, tile by tile.
+#include <atomic>
+
 #include "zopt_internal.h"
 
 namespace zopt {
@@ -77,10 +79,21 @@ struct NsGroup {
 struct NsLaunch {
     NsGroup g[kMaxGroups];
     int32_t ngroups;
+    int32_t total;  // slots of all groups (B X: the persistent walk's end)
+    int32_t xpf;    // B X: every group's K >= kStages * 32 (pipeline across tiles)
     float a, b, c;
 };
 
 __device__ __forceinline__ uint16_t to_bf16(float x) { return (uint16_t)rne_bf16_bits(x); }
+// lo, hi -> two bf16, round to nearest even, in one gfx950 instruction
+// (v_cvt_pk_bf16_f32).  Equal to rne_bf16_bits for every non-NaN input; a NaN
+// stays a NaN.  Used for Newton-Schulz iterates, which never meet the
+// write-back's NaN convention.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
 __device__ __forceinline__ float from_bf16(uint16_t h) { return bf16_bits_to_float(h); }
 
 // Tile t of a matrix, in bands of kBand tile rows taken column by column, so
@@ -156,13 +169,12 @@ __device__ __forceinline__ int swz(int i, int j) {
     return i * (CHUNKS * 16) + (((j >> 3) ^ (i & (CHUNKS - 1))) << 4) + ((j & 7) << 1);
 }
 
-// Epilogue: the accumulators are completed in place (A A: b Aoff + c (acc +
-// (dA_i + dA_j) Aoff), its diagonal b dA_i + c (acc + dA_i^2), with Aoff
-// staged through LDS; B X needs nothing here, its (a + dB_i) X term was added
-// in the main loop), then leave through the
-// wave's LDS region as coalesced 16-byte row stores: row order to the
-// sub-block itself, transposed to X^T (B X) or to the mirror position (the
-// symmetric products).  A symmetric sub-block that crosses the diagonal is
+// Epilogue of the symmetric products: the accumulators are completed in
+// place (A A: b Aoff + c (acc + (dA_i + dA_j) Aoff), its diagonal
+// b dA_i + c (acc + dA_i^2), with Aoff staged through LDS), then leave
+// through the wave's LDS region as coalesced 16-byte row stores: row order
+// to the sub-block itself, transposed to the mirror position.  A sub-block
+// that crosses the diagonal is
 // stored element by element from its upper triangle, so the mirror of each
 // value is that same bf16 value; below the diagonal nothing is stored; the
 // diagonal goes to the fp32 vector (its bf16 entry is 0).  Every wave passes
@@ -174,10 +186,9 @@ __device__ __forceinline__ void epilogue(const NsGroup &args, float ca, float cb
     constexpr int SR = FM * 16, SC = FN * 16;      // sub-block rows, columns
     constexpr int RCH = SC / 8, TCH = SR / 8;      // chunks per row: row order, transposed
     uint8_t *W = lds_all + wave * (SR * SC * 2);
-    constexpr bool sym = MODE != kGemmBX;
-    const bool below = sym && R0 >= C0 + SC;
-    const bool above = !sym || R0 + SR <= C0;
-    const bool cross = sym && !below && !above;
+    const bool below = R0 >= C0 + SC;
+    const bool above = R0 + SR <= C0;
+    const bool cross = !below && !above;
     const int64_t ldc = args.ldc;
     uint16_t *Cm = args.C + batch * args.c_stride;
     const float *dIn = args.dIn + batch * args.d_stride;
@@ -241,9 +252,8 @@ __device__ __forceinline__ void epilogue(const NsGroup &args, float ca, float cb
             }
     }
     const bool coalesced = !below && !cross;
-    const bool tstore = coalesced && (MODE != kGemmBX || args.CT != nullptr);
     // 2. transposed: T[lj][li], four consecutive rows per 8-byte write
-    if (tstore) {
+    if (coalesced) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -252,14 +262,12 @@ __device__ __forceinline__ void epilogue(const NsGroup &args, float ca, float cb
                     u32x2{pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3])};
     }
     __syncthreads();
-    if (tstore) {
-        uint16_t *dst = MODE == kGemmBX ? args.CT + batch * args.ct_stride : Cm;
-        const int64_t ld = MODE == kGemmBX ? (int64_t)args.ldct : ldc;
+    if (coalesced) {
 #pragma unroll 4
         for (int k = 0; k < TCHUNKS / 64; ++k) {
             const int id = k * 64 + lane, i = id / TCH, c = id % TCH;
             const u32x4 v = *reinterpret_cast<const u32x4 *>(W + i * (TCH * 16) + ((c ^ (i & (TCH - 1))) << 4));
-            *reinterpret_cast<u32x4 *>(dst + (int64_t)(C0 + i) * ld + R0 + c * 8) = v;
+            *reinterpret_cast<u32x4 *>(Cm + (int64_t)(C0 + i) * ldc + R0 + c * 8) = v;
         }
     }
     __syncthreads();
@@ -285,6 +293,19 @@ __device__ __forceinline__ void epilogue(const NsGroup &args, float ca, float cb
     }
 }
 
+
+// Slot rel of a group -> its tile t (false: a padding slot).  Workgroups go
+// to the 8 XCDs round-robin (tile0 and the grid are multiples of 8).  The
+// tiles resident at one time (a round) are consecutive in the banded order, a
+// compact block of the tile grid, and XCD x takes the x-th contiguous eighth
+// of each round: its L2 then serves few operand panels, and the XCDs together
+// stream the round's panels through the shared memory-side cache.
+__device__ __forceinline__ bool round_tile(const NsGroup &G, int rel, int &t) {
+    const int base = rel - rel % G.round_tiles;
+    const int rem = G.padded - base < G.round_tiles ? G.padded - base : G.round_tiles;
+    t = base + (rel & 7) * (rem >> 3) + ((rel - base) >> 3);
+    return t < G.tiles;
+}
 
 // ----------------------------------------------------------------------------
 // The main loop.  K advances in stages of 32 columns through kStages LDS
@@ -312,53 +333,36 @@ constexpr int kBK = 32;
 template <int BM, int MODE>
 __global__ __launch_bounds__(Cfg<BM>::WR * Cfg<BM>::WC * 64)
 __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch L) {
+    static_assert(MODE == kSyrkXXT || MODE == kSyrkAA, "B X has a kernel of its own");
     constexpr int WR = Cfg<BM>::WR, WC = Cfg<BM>::WC, NW = WR * WC;
     constexpr int WTM = BM / WR, WTN = BM / WC, FM = WTM / 16, FN = WTN / 16;
     constexpr int ROW = 64, OPB = BM * ROW, STAGE = 2 * OPB;
     constexpr int LOADS = OPB / 1024 / NW, LPS = 2 * LOADS;
-    constexpr int ND = FM + (MODE == kGemmBX ? 2 : 1) * FN;  // LDS fragment reads per stage
+    constexpr int ND = FM + FN;  // LDS fragment reads per stage
     static_assert(LOADS >= 1 && LOADS * NW * 1024 == OPB, "tile");
     static_assert(kStages * STAGE >= BM * BM * 2, "the epilogue regions fit in the stages");
-    // the stages, then (B X) a + dB_i for the tile's rows
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * STAGE + (MODE == kGemmBX ? BM * 4 : 0)];
-    float *dl = reinterpret_cast<float *>(&lds[kStages * STAGE]);
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * STAGE];
 
     // group, matrix and tile of this workgroup
     const int bid = blockIdx.x;
     int gi = 0;
     while (gi + 1 < L.ngroups && bid >= L.g[gi + 1].tile0) ++gi;
     const NsGroup &G = L.g[gi];
-    // Workgroups go to the 8 XCDs round-robin (tile0 is a multiple of 8).  The
-    // tiles resident at one time (a round) are consecutive in the banded
-    // order, a compact block of the tile grid, and XCD x takes the x-th
-    // contiguous eighth of each round: its L2 then serves few operand panels,
-    // and the XCDs together stream the round's panels through the shared
-    // memory-side cache.  The padding at the end of a group exits at once.
-    const int rel = bid - G.tile0;
-    const int base = rel - rel % G.round_tiles;
-    const int rem = G.padded - base < G.round_tiles ? G.padded - base : G.round_tiles;
-    int t = base + (rel & 7) * (rem >> 3) + ((rel - base) >> 3);
-    if (t >= G.tiles) return;
+    int t;
+    if (!round_tile(G, bid - G.tile0, t)) return;
     const int batch = t / G.tiles_pm;
     t -= batch * G.tiles_pm;
     int ti, tj;
     tile_coords<MODE>(G, t, ti, tj);
     const int m0 = ti * BM, n0 = tj * BM;
     const int ld = G.ld, K = G.K;
-    constexpr bool NN = MODE == kGemmBX;  // Q is X itself, staged k-major
     const uint16_t *Pb = G.P + batch * G.p_stride + (int64_t)m0 * ld;
-    const uint16_t *Qb = NN ? G.Q + batch * G.q_stride + n0
-                            : G.Q + batch * G.q_stride + (int64_t)n0 * ld;
+    const uint16_t *Qb = G.Q + batch * G.q_stride + (int64_t)n0 * ld;
     const int panel_bytes = BM * ld * 2;
-    const int ldq = G.ldq;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wr = wave / WC, wc = wave % WC;
-    if constexpr (MODE == kGemmBX) {
-        const float *dB = G.dIn + batch * G.d_stride + m0;
-        for (int r = tid; r < BM; r += NW * 64) dl[r] = L.a + dB[r];
-    }
 
     f32x4 acc[FM][FN];
 #pragma unroll
@@ -371,46 +375,20 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch 
     // and the chunk that the swizzle places at slot l % 4
     const int lrow = lane >> 2, lchunk = (lane & 3) ^ ((lrow >> 1) & 3);
     const int voff = (lrow * ld + lchunk * 8) * 2;
-    // B X's Q stage: X rows k0 .. k0+31, columns n0 .. n0+BM-1, as rows of
-    // QRB bytes; 32-byte unit u of row r sits at slot u ^ qsw(r).  A
-    // transposing read touches 16 rows (8g + 4h + q, or 16 in a row) x 32
-    // bytes, and qsw spreads them over all eight 32-byte bank groups, two
-    // rows each (rows of 512 or 256 bytes start in the same banks; rows of
-    // 128 bytes alternate halves).  Kilobyte k holds rows k * 1024 / QRB ...;
-    // lane l of its instruction fills slot l % (QRB / 16) (16 bytes) of row
-    // l / (QRB / 16) within it.
-    constexpr int QRB = 2 * BM, QCH = QRB / 16;
-    auto qsw = [](int r) __attribute__((always_inline)) {
-        return BM >= 128 ? (r & 3) | (((r >> 3) & 1) << 2) : ((r >> 1) & 1) | (((r >> 3) & 1) << 1);
-    };
-    int qvoff[LOADS];
-#pragma unroll
-    for (int q = 0; q < LOADS; ++q) {
-        const int r = (q * NW + wave) * (1024 / QRB) + lane / QCH, s16 = lane % QCH;
-        const int col = (((s16 >> 1) ^ qsw(r)) << 4) + ((s16 & 1) << 3);
-        qvoff[q] = (r * ldq + col) * 2;
-    }
     auto gload = [&](int sbase, int k0) {
         const int bytes = k0 < K ? panel_bytes : 0;
         const __amdgpu_buffer_rsrc_t rp =
             __builtin_amdgcn_make_buffer_rsrc((void *)Pb, (short)0, bytes, 0x00020000);
         const __amdgpu_buffer_rsrc_t rq =
-            NN ? __builtin_amdgcn_make_buffer_rsrc((void *)(Qb + (int64_t)k0 * ldq), (short)0,
-                                                   k0 < K ? kBK * ldq * 2 : 0, 0x00020000)
-               : __builtin_amdgcn_make_buffer_rsrc((void *)Qb, (short)0, bytes, 0x00020000);
+            __builtin_amdgcn_make_buffer_rsrc((void *)Qb, (short)0, bytes, 0x00020000);
 #pragma unroll
         for (int q = 0; q < LOADS; ++q) {
             const int k = q * NW + wave;
             const int soff = (16 * k * ld + k0) * 2;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, LDS_ADDR(&lds[sbase + k * 1024]), 16, voff,
                                                      soff, 0, 0);
-            if constexpr (NN) {
-                const int qv = qvoff[q];
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, LDS_ADDR(&lds[sbase + OPB + k * 1024]),
-                                                         16, qv, 0, 0, 0);
-            } else
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, LDS_ADDR(&lds[sbase + OPB + k * 1024]),
-                                                         16, voff, soff, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, LDS_ADDR(&lds[sbase + OPB + k * 1024]), 16,
+                                                     voff, soff, 0, 0);
         }
     };
     // MFMA 16x16x32 operand: lane l holds row l % 16, K-chunk l / 16 of the
@@ -418,44 +396,13 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch 
     const int fr = lane & 15, fh = lane >> 4;
     const int foff = fr * ROW + ((fh ^ ((fr >> 1) & 3)) << 4);
     bf16x8 fa[2][FM], fb[2][FN];
-    const uint32_t lds_base =
-        (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t *)lds);
-    // B X: the B operand of column block j, K-chunk g = lane / 16 is two
-    // transposing reads of 4 x 16 blocks (rows 8g .. 8g+3 and 8g+4 .. 8g+7):
-    // lane 4q + p of a 16-lane group addresses row +q, columns 4p .. 4p+3 of
-    // the block, and lane i then holds rows +0..+3 of column i.
-    const int tg = lane >> 4, tq = (lane >> 2) & 3, tp = lane & 3;
-    const int tpo = ((tp >> 1) << 4) + ((tp & 1) << 3);
-    auto qbyte = [&](int r, int j) __attribute__((always_inline)) {
-        return r * QRB + ((((wc * WTN) / 16 + j) ^ qsw(r)) << 5) + tpo;
-    };
-    int qro[2][FN];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) qro[h][j] = qbyte(8 * tg + 4 * h + tq, j);
     auto read = [&](int buf, int sbase) {
         const uint8_t *pa = &lds[sbase + wr * WTM * ROW + foff];
+        const uint8_t *pb = &lds[sbase + OPB + wc * WTN * ROW + foff];
 #pragma unroll
         for (int i = 0; i < FM; ++i) fa[buf][i] = *reinterpret_cast<const bf16x8 *>(pa + i * 16 * ROW);
-        if constexpr (NN) {
-            // inline assembly, for the reason given at `diag` below; the
-            // values are used only after the next stage's wait (`tie`)
-            const uint32_t qb = lds_base + sbase;
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                u32x2 lo, hi;
-                asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
-                             : "=v"(lo) : "v"(qb + qro[0][j]), "i"(OPB));
-                asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
-                             : "=v"(hi) : "v"(qb + qro[1][j]), "i"(OPB));
-                fb[buf][j] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-            }
-        } else {
-            const uint8_t *pb = &lds[sbase + OPB + wc * WTN * ROW + foff];
-#pragma unroll
-            for (int j = 0; j < FN; ++j) fb[buf][j] = *reinterpret_cast<const bf16x8 *>(pb + j * 16 * ROW);
-        }
+        for (int j = 0; j < FN; ++j) fb[buf][j] = *reinterpret_cast<const bf16x8 *>(pb + j * 16 * ROW);
     };
     auto mma = [&](int buf) {
 #pragma unroll
@@ -466,70 +413,18 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch 
                                                                     0, 0, 0);
     };
 
-    // B X: X' = (a + dB_i) X + Boff X.  The first term needs the tile of X
-    // itself, and the Q operand brings exactly that tile through LDS during
-    // the stages whose K range [k1, k1 + 32) lies inside the tile's rows: its
-    // row k1 + kk is X's row k1 + kk, columns n0 ... So in those stages each
-    // wave adds (a + dB_row) X[row][col] to the accumulators of its rows in
-    // that range (two 16-row blocks), reading X from the stage in LDS (one
-    // transposing read per block: lane i of group g gets rows 4g .. 4g+3 of
-    // column i, the rows its accumulators hold) instead of from memory in the
-    // epilogue.
-    // (The X reads are issued as inline assembly: as ordinary LDS loads the
-    // compiler cannot tell them from the in-flight global->LDS copies into
-    // other stage buffers and would wait for those copies to finish.)
-    const int quad = lane >> 4;
-    auto diag = [&](int sbase, int k1) __attribute__((always_inline)) {
-        if constexpr (MODE == kGemmBX) {
-            const int rw = m0 + wr * WTM;
-            if (k1 < rw || k1 >= rw + WTM) return;
-            const int i0 = (k1 - rw) >> 4;
-#pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                if (i != i0 && i != i0 + 1) continue;
-                const int kk0 = (i - i0) * 16 + quad * 4;
-                const f32x4 d = *reinterpret_cast<const f32x4 *>(&dl[k1 - m0 + kk0]);
-                u32x2 xv[FN];
-#pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const uint32_t addr =
-                        lds_base + sbase + OPB + qbyte((i - i0) * 16 + 4 * tg + tq, j);
-                    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(xv[j]) : "v"(addr));
-                }
-#pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    // the wait is tied to the registers, so no use moves above it
-                    if (j == 0) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(xv[0]));
-                    else asm volatile("" : "+v"(xv[j]));
-                    acc[i][j][0] += d[0] * from_bf16(xv[j].x & 0xFFFFu);
-                    acc[i][j][1] += d[1] * from_bf16(xv[j].x >> 16);
-                    acc[i][j][2] += d[2] * from_bf16(xv[j].y & 0xFFFFu);
-                    acc[i][j][3] += d[3] * from_bf16(xv[j].y >> 16);
-                }
-            }
-        }
-    };
-
     const int KT = K / kBK;
 #pragma unroll
     for (int s = 0; s < kStages; ++s) gload(s * STAGE, s * kBK);
     __builtin_amdgcn_s_waitcnt(WAIT_VM_LGKM0((kStages - 1) * LPS));
     __syncthreads();
-    diag(0, 0);
     read(0, 0);
     int cur = 0;  // buffer of stage kt
     auto body = [&](int kt, auto PAR) __attribute__((always_inline)) {
         constexpr int par = decltype(PAR)::value;
         const int nxt = cur + 1 == kStages ? 0 : cur + 1;
         __builtin_amdgcn_s_waitcnt(WAIT_VM_LGKM0((kStages - 2) * LPS));
-        if constexpr (NN) {
-            // tie: the B operands read by inline assembly in the previous
-            // stage are complete only after the wait above
-#pragma unroll
-            for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(fb[par][j]));
-        }
         __builtin_amdgcn_s_barrier();
-        diag(nxt * STAGE, (kt + 1) * kBK);
         __builtin_amdgcn_sched_barrier(0);
         gload(cur * STAGE, (kt + kStages) * kBK);
         read(par ^ 1, nxt * STAGE);
@@ -560,17 +455,411 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch 
     // the loads past the end still write (zeros) to LDS: drain them before
     // the epilogue reuses the buffers
     __builtin_amdgcn_s_waitcnt(0);
-    if constexpr (NN) {
-        // the last stage's B operands (never used) stay allocated until the
-        // wait above, so their late returns cannot land on other values
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) asm volatile("" : : "v"(fb[b][j]));
-    }
     __syncthreads();
     epilogue<MODE, FM, FN>(G, L.a, L.b, L.c, acc, batch, m0 + wr * WTM, n0 + wc * WTN, wave, lane,
                            lds);
+}
+
+// ----------------------------------------------------------------------------
+// X' = a X + B X: a persistent kernel.  The grid is one round of resident
+// workgroups; workgroup w takes slots w, w + grid, w + 2 grid, ... (the
+// slot -> tile map is the one above, so the tiles in flight at one time are
+// still one compact round).  The stage pipeline runs on across tiles: when a
+// tile's last stages are in flight the loads go on with the next tile's first
+// ones, and the last stage's fragment reads are the next tile's first.  So
+// the next tile's operands arrive while this one computes and stores, and no
+// workgroup idles through a prologue (its stores, which vmcnt counts with the
+// loads, are waited for at the next tile's first stage).
+//
+// P = B (its rows [m0, m0 + BM), K = m); Q = X, staged k-major: rows
+// [k, k + 32) x columns [n0, n0 + BM) as they lie in memory (rows of QRB
+// bytes; 32-byte unit u of row r at slot u ^ qsw(r)).  The MFMA B operand (8
+// consecutive k of one column per lane) is two ds_read_b64_tr_b16 per 16 x 32
+// fragment: lane 4q + p of a 16-lane group addresses row +q, columns
+// 4p .. 4p+3 of a 4 x 16 block, and lane i receives rows +0..+3 of column i.
+// A transposing read touches 16 rows x 32 bytes, and qsw spreads them over
+// all eight 32-byte bank groups, two rows each (rows of 512 or 256 bytes
+// start in the same banks; rows of 128 bytes alternate halves).
+//
+// The MFMA takes X's fragment as its first operand and B's as its second, so
+// it accumulates the tile transposed: lane (c, q) = (l % 16, l / 16) of block
+// (i, j) holds row 16i + c, columns 16j + 4q .. 16j + 4q + 3 of X'.  Four
+// consecutive columns of one row pack into one 8-byte store, so the tile
+// goes from registers straight to memory (no LDS staging, no barrier).
+//
+// (a + dB_i) X_ij: the Q stage of the stages whose K range [k1, k1 + 32)
+// lies inside the wave's rows holds exactly X's rows of that range, so those
+// stages add (a + dB_row) X[row][cols] to the two 16-row blocks there (one
+// 8-byte read per block and lane), instead of reading X again in the
+// epilogue.  dB for a tile's rows is copied into LDS (one of two buffers)
+// while the tile before it runs.
+//
+// A launch whose groups all have K >= kStages * 32 runs the pipeline across
+// tiles; otherwise each tile starts its own (the loads past its end read a
+// zero-size buffer, as in the kernel above).
+//
+// (The LDS reads of X and dB are inline assembly: as ordinary LDS loads the
+// compiler cannot tell them from the in-flight global->LDS copies into other
+// buffers and would wait for those copies to finish.  Their results are tied
+// to the next explicit wait.)
+template <int BM>
+__global__ __launch_bounds__(Cfg<BM>::WR * Cfg<BM>::WC * 64)
+__attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_bx_kernel(NsLaunch L) {
+    constexpr int WR = Cfg<BM>::WR, WC = Cfg<BM>::WC, NW = WR * WC;
+    constexpr int WTM = BM / WR, WTN = BM / WC, FM = WTM / 16, FN = WTN / 16;
+    constexpr int ROW = 64, OPB = BM * ROW, STAGE = 2 * OPB;
+    constexpr int LOADS = OPB / 1024 / NW, LPS = 2 * LOADS;
+    constexpr int QRB = 2 * BM, QCH = QRB / 16;
+    constexpr int DLB = kStages * STAGE;  // two 1 KiB buffers of dB
+    static_assert(LOADS >= 1 && LOADS * NW * 1024 == OPB, "tile");
+    static_assert(BM * 4 <= 1024, "dB rows fit a buffer");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * STAGE + 2048];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wr = wave / WC, wc = wave % WC;
+    const int grid = gridDim.x;
+    const uint32_t lds_base =
+        (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t *)lds);
+
+    // The lane's index, computed afresh where it is used between tiles or
+    // seldom, so that the values derived from it need no register across
+    // the loops.
+    auto lane_id = []() __attribute__((always_inline)) {
+        int l;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+        return l;
+    };
+    struct Tile {
+        int gi, batch, m0, n0;
+    };
+    // slot -> tile (false: a padding slot)
+    auto locate = [&](int slot, Tile &T) __attribute__((always_inline)) -> bool {
+        int gi = 0;
+        while (gi + 1 < L.ngroups && slot >= L.g[gi + 1].tile0) ++gi;
+        const NsGroup &G = L.g[gi];
+        int t;
+        if (!round_tile(G, slot - G.tile0, t)) return false;
+        const int batch = t / G.tiles_pm;
+        t -= batch * G.tiles_pm;
+        int ti, tj;
+        tile_coords<kGemmBX>(G, t, ti, tj);
+        T = Tile{gi, batch, ti * BM, tj * BM};
+        return true;
+    };
+    // this workgroup's first tile at or after `slot`; -1 if none
+    auto seek = [&](int slot, Tile &T) __attribute__((always_inline)) -> int {
+        for (; slot < L.total; slot += grid)
+            if (locate(slot, T)) return slot;
+        return -1;
+    };
+
+    // The load stream: stage ks (counted from the current tile's first)
+    // comes from stage ks - sk of the stream's tile, or is zeros (!live).
+    // Instruction q of this wave fills kilobyte k = q * NW + wave of each
+    // operand's stage.  P: rows 16k .. 16k+15; lane l takes row 16k + l / 4
+    // and the chunk that the swizzle (chunk c of row r at slot c ^ ((r >> 1)
+    // & 3)) places at slot l % 4.  Q: kilobyte k holds stage rows
+    // k * 1024 / QRB ...; lane l fills 16-byte slot l % QCH of row l / QCH.
+    auto qsw = [](int r) __attribute__((always_inline)) {
+        return BM >= 128 ? (r & 3) | (((r >> 3) & 1) << 2) : ((r >> 1) & 1) | (((r >> 3) & 1) << 1);
+    };
+    const uint16_t *sP = nullptr, *sQ = nullptr;
+    int sld = 0, sldq = 0, sk = 0;
+    bool slive = false;
+    int voff = 0, qv[LOADS];
+    auto stream = [&](const Tile &T, int kbase, bool live) __attribute__((always_inline)) {
+        const NsGroup &G = L.g[T.gi];
+        sld = G.ld;
+        sldq = G.ldq;
+        sP = G.P + T.batch * G.p_stride + (int64_t)T.m0 * sld;
+        sQ = G.Q + T.batch * G.q_stride + T.n0;
+        sk = kbase;
+        slive = live;
+        const int ln = lane_id();
+        const int lrow = ln >> 2, lchunk = (ln & 3) ^ ((lrow >> 1) & 3);
+        voff = (lrow * sld + lchunk * 8) * 2;
+#pragma unroll
+        for (int q = 0; q < LOADS; ++q) {
+            const int r = (q * NW + wave) * (1024 / QRB) + ln / QCH, s16 = ln % QCH;
+            qv[q] = (r * sldq + (((s16 >> 1) ^ qsw(r)) << 4) + ((s16 & 1) << 3)) * 2;
+        }
+    };
+    auto gload = [&](int sbase, int ks) __attribute__((always_inline)) {
+        const int k0 = (ks - sk) * kBK;
+        const __amdgpu_buffer_rsrc_t rp =
+            __builtin_amdgcn_make_buffer_rsrc((void *)sP, (short)0, slive ? BM * sld * 2 : 0, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(sQ + (int64_t)k0 * sldq), (short)0, slive ? kBK * sldq * 2 : 0, 0x00020000);
+#pragma unroll
+        for (int q = 0; q < LOADS; ++q) {
+            const int k = q * NW + wave;
+            const int soff = (16 * k * sld + k0) * 2;
+            const int qo = qv[q];
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, LDS_ADDR(&lds[sbase + k * 1024]), 16, voff,
+                                                     soff, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, LDS_ADDR(&lds[sbase + OPB + k * 1024]), 16,
+                                                     qo, 0, 0, 0);
+        }
+    };
+    // dB of tile T's rows into dB buffer `which` (wave 0, one instruction;
+    // lanes past BM / 4 read zeros)
+    auto load_db = [&](int which, const Tile &T) __attribute__((always_inline)) {
+        if (wave == 0) {
+            const NsGroup &G = L.g[T.gi];
+            const float *src = G.dIn + T.batch * G.d_stride + T.m0;
+            const __amdgpu_buffer_rsrc_t rd =
+                __builtin_amdgcn_make_buffer_rsrc((void *)src, (short)0, BM * 4, 0x00020000);
+            // (a plain local as the offset operand: the host pass drops the
+            // kernel's stub for some argument expressions)
+            const int lo16 = lane_id() * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, LDS_ADDR(&lds[DLB + which * 1024]), 16,
+                                                     lo16, 0, 0, 0);
+        }
+    };
+
+    // MFMA 16x16x32 operand of B: lane l holds row l % 16, K-chunk l / 16
+    const int fr = lane & 15, fh = lane >> 4;
+    const int foff = fr * ROW + ((fh ^ ((fr >> 1) & 3)) << 4);
+    bf16x8 fa[2][FM], fb[2][FN];
+    // X's operand of column block j, K-chunk g = lane / 16: two transposing
+    // reads of 4 x 16 blocks, rows 8g + {0..3} and 8g + {4..7} (qsw is the
+    // same for both, so the second is the first plus 4 rows)
+    auto unit = [&](int r, int j) __attribute__((always_inline)) {
+        return r * QRB + ((((wc * WTN) / 16 + j) ^ qsw(r)) << 5);
+    };
+    int qro[FN];
+    {
+        const int tg = lane >> 4, tq = (lane >> 2) & 3, tp = lane & 3;
+        const int tpo = ((tp >> 1) << 4) + ((tp & 1) << 3);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) qro[j] = unit(8 * tg + tq, j) + tpo;
+    }
+    auto read_a = [&](int buf, int sbase, int i) __attribute__((always_inline)) {
+        fa[buf][i] = *reinterpret_cast<const bf16x8 *>(&lds[sbase + wr * WTM * ROW + foff + i * 16 * ROW]);
+    };
+    auto read_b = [&](int buf, int sbase) __attribute__((always_inline)) {
+        const uint32_t qb = lds_base + sbase;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            u32x2 lo, hi;
+            asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(qb + qro[j]), "i"(OPB));
+            asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                         : "=v"(hi) : "v"(qb + qro[j]), "i"(OPB + 4 * QRB));
+            fb[buf][j] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+        }
+    };
+    auto read = [&](int buf, int sbase) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) read_a(buf, sbase, i);
+        read_b(buf, sbase);
+    };
+    f32x4 acc[FM][FN];
+    auto mma = [&](int par) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[par][j], fa[par][i], acc[i][j],
+                                                                    0, 0, 0);
+    };
+    // (a + dB_row) X[row][cols] for the stage at sbase, K range [k1, k1 + 32):
+    // its rows are the wave's 16-row blocks I and I + 1.  Lane (c, q) reads
+    // 8 bytes of stage row 16h + c (h = 0, 1) in 32-byte unit
+    // (wc WTN / 16 + j) ^ qsw(c) = (wc WTN / 16) ^ qsw(c) ^ j (qsw(16 + c) =
+    // qsw(c); the wave's first unit has no bits below j's), i.e. at
+    // xb ^ (j << 5) + sbase, and dB of its row.  The addresses are formed in
+    // the assembly, so that they take no registers between uses.
+    const uint32_t xb = lds_base + OPB + fr * QRB + fh * 8 + ((((wc * WTN) / 16) ^ qsw(fr)) << 5);
+    auto diag_pair = [&](auto I, int sbase, int dbuf) __attribute__((always_inline)) {
+        constexpr int i0 = decltype(I)::value;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            float db;
+            u32x2 xv[FN];
+            const uint32_t da = lds_base + DLB + dbuf * 1024 + (wr * WTM + (lane_id() & 15)) * 4;
+            asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(db) : "v"(da), "i"((i0 + h) * 64));
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                uint32_t t;
+                asm volatile("v_xor_b32 %1, %2, %3\n\tv_add_u32 %1, %4, %1\n\tds_read_b64 %0, %1 offset:%5"
+                             : "=v"(xv[j]), "=&v"(t)
+                             : "i"(j << 5), "v"(xb), "s"(sbase), "i"(h * 16 * QRB));
+            }
+            // the wait is tied to the registers, so no use moves above it
+            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(db));
+            const float d = L.a + db;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                asm volatile("" : "+v"(xv[j]));
+                acc[i0 + h][j][0] += d * from_bf16(xv[j].x & 0xFFFFu);
+                acc[i0 + h][j][1] += d * from_bf16(xv[j].x >> 16);
+                acc[i0 + h][j][2] += d * from_bf16(xv[j].y & 0xFFFFu);
+                acc[i0 + h][j][3] += d * from_bf16(xv[j].y >> 16);
+            }
+        }
+        // (distinct per case, so that the cases' updates are not merged into
+        // one through pointers, which would put acc in scratch memory)
+        asm volatile("; diag %0" : : "n"(i0));
+    };
+    auto diag = [&](int sbase, int k1, const Tile &cu, int dbuf) __attribute__((always_inline)) {
+        const int rel = k1 - (cu.m0 + wr * WTM);
+        if (rel < 0 || rel >= WTM) return;
+        switch (rel >> 5) {
+            case 0: diag_pair(std::integral_constant<int, 0>{}, sbase, dbuf); break;
+            case 1: if constexpr (FM > 2) diag_pair(std::integral_constant<int, 2>{}, sbase, dbuf); break;
+            case 2: if constexpr (FM > 4) diag_pair(std::integral_constant<int, 4>{}, sbase, dbuf); break;
+            case 3: if constexpr (FM > 6) diag_pair(std::integral_constant<int, 6>{}, sbase, dbuf); break;
+        }
+    };
+    // the tile from registers: 8-byte row stores, and for X'^T (when wanted)
+    // 2-byte stores down its columns; buffer stores off the wave's corner of
+    // the tile, so a store needs one lane offset and a scalar one
+    auto store = [&](const Tile &cu) __attribute__((always_inline)) {
+        const NsGroup &G = L.g[cu.gi];
+        const int R0 = cu.m0 + wr * WTM, C0 = cu.n0 + wc * WTN;
+        const int ldc = G.ldc;
+        const int ln = lane_id(), fr = ln & 15, fh = ln >> 4;
+        const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(G.C + cu.batch * G.c_stride + (int64_t)R0 * ldc + C0), (short)0, WTM * ldc * 2,
+            0x00020000);
+        const int vo = (fr * ldc + fh * 4) * 2;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                __builtin_amdgcn_raw_buffer_store_b64(
+                    u32x2{cvt_pk_bf16(acc[i][j][0], acc[i][j][1]), cvt_pk_bf16(acc[i][j][2], acc[i][j][3])},
+                    rc, vo + j * 32, i * 32 * ldc, 0);
+        if (G.CT != nullptr) {
+            const int ldt = G.ldct;
+            const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(G.CT + cu.batch * G.ct_stride + (int64_t)C0 * ldt + R0), (short)0,
+                WTN * ldt * 2, 0x00020000);
+            const int to = (fh * 4 * ldt + fr) * 2;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        __builtin_amdgcn_raw_buffer_store_b16(
+                            (uint16_t)cvt_pk_bf16(acc[i][j][r], 0.0f), rt, to + i * 32,
+                            (j * 16 + r) * ldt * 2, 0);
+        }
+    };
+
+    Tile cu, nx{};
+    int slot = seek(blockIdx.x, cu);
+    if (slot < 0) return;
+    int cur = 0;        // LDS buffer of the current stage
+    int dbuf = 0;       // dB buffer of the current tile
+    bool pref = false;  // the current tile's first stages are in flight
+    load_db(0, cu);
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    for (;;) {
+        const int KT = L.g[cu.gi].K / kBK;  // even: K is a multiple of the tile
+        const int ksw = KT - kStages;       // from stage ksw on, loads fetch the next tile
+        // the next tile, and its dB rows into the other buffer (everyone is
+        // past the previous tile's last reads of that buffer)
+        int nslot = -1;
+        bool more = false, pf = false;
+        auto find_next = [&]() __attribute__((always_inline)) {
+            nslot = seek(slot + grid, nx);
+            more = nslot >= 0;
+            if (!more) nx = cu;
+            pf = more && L.xpf != 0;
+            if (more) load_db(dbuf ^ 1, nx);
+        };
+        find_next();
+        if (!pref) {
+            // this tile's own prologue (everyone is done with the buffers)
+            __syncthreads();
+            stream(cu, 0, true);
+#pragma unroll
+            for (int s = 0; s < kStages; ++s) {
+                if (s == KT) stream(nx, KT, pf);
+                gload(((cur + s) & (kStages - 1)) * STAGE, s);
+            }
+            __builtin_amdgcn_s_waitcnt(WAIT_VM_LGKM0((kStages - 1) * LPS));
+            __syncthreads();
+            read(0, cur * STAGE);
+        }
+        // (zeros made in place: a zero vector kept for this would be one
+        // more register across the loops)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) asm volatile("v_mov_b32 %0, 0" : "=v"(acc[i][j][r]));
+        // Stage kt: its (a + dB) X term, while its buffer still holds it ->
+        // wait until this wave's loads of stage kt+1 have landed -> barrier
+        // (everyone's have; everyone has finished reading stage kt) -> issue
+        // the loads kStages stages ahead into stage kt's buffer -> read the
+        // fragments of stage kt+1, interleaved with the MFMAs of stage kt
+        // (read in the previous stage).
+        // (the last stage reads the fragments of the stage after: the next
+        // tile's first, or zeros)
+        auto body = [&](int kt, auto PAR) __attribute__((always_inline)) {
+            constexpr int par = decltype(PAR)::value;
+            const int nxt = (cur + 1) & (kStages - 1);
+            diag(cur * STAGE, kt * kBK, cu, dbuf);
+            __builtin_amdgcn_s_waitcnt(WAIT_VM_LGKM0((kStages - 2) * LPS));
+            // tie: the X operands read by inline assembly in the previous
+            // stage are complete only after the wait above
+#pragma unroll
+            for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(fb[par][j]));
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            gload(cur * STAGE, kt + kStages);
+            read(par ^ 1, nxt * STAGE);
+            mma(par);
+#pragma unroll
+            for (int x = 0; x < LPS; ++x) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one global load
+            }
+#pragma unroll
+            for (int x = 0; x < FM + 2 * FN; ++x) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            cur = nxt;
+        };
+        // stages whose loads fetch this tile's own stages, then (from ksw on)
+        // the next tile's first ones or zeros
+        int kt = 0;
+#pragma clang loop unroll(disable)
+        for (; kt < ksw; kt += 2) {
+            body(kt, P0{});
+            body(kt + 1, P1{});
+        }
+        if (ksw >= 0) stream(nx, KT, pf);
+#pragma clang loop unroll(disable)
+        for (; kt < KT; kt += 2) {
+            body(kt, P0{});
+            body(kt + 1, P1{});
+        }
+        if (!pf) {
+            // the loads past the end still write (zeros) to LDS: drain them
+            // before the buffers are reused; the last stage's X operands
+            // (zeros, never used) stay allocated until then, so their late
+            // returns cannot land on other values
+            __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) asm volatile("" : : "v"(fb[0][j]));
+        }
+        store(cu);
+        if (!more) break;
+        sk -= KT;
+        cu = nx;
+        slot = nslot;
+        dbuf = __builtin_amdgcn_readfirstlane(dbuf ^ 1);
+        pref = pf;
+    }
 }
 
 template <int T>
@@ -628,10 +917,18 @@ int round_tiles_of() {
     return (cus / 8) * per_cu * 8;
 }
 
+// Process-wide cap on the workgroups a persistent launch keeps resident (0:
+// one full round of the device).
+std::atomic<int> g_workgroup_limit{0};
+
 template <int T, int MODE>
 hipError_t launch_product(const NsGroupRef *refs, const int *idx, int n, int iter, bool last,
                           float a, float b, float c, hipStream_t stream) {
-    const int32_t round_tiles = round_tiles_of<T>();
+    int32_t round_tiles = round_tiles_of<T>();
+    if (MODE == kGemmBX) {
+        const int lim = g_workgroup_limit.load(std::memory_order_relaxed);
+        if (lim > 0 && lim < round_tiles) round_tiles = lim;
+    }
     for (int first = 0; first < n; first += kMaxGroups) {
         const int cnt = n - first < kMaxGroups ? n - first : kMaxGroups;
         NsLaunch L{};
@@ -651,8 +948,17 @@ hipError_t launch_product(const NsGroupRef *refs, const int *idx, int n, int ite
             L.g[k] = s;
         }
         if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((ns_gemm_kernel<T, MODE>), dim3((uint32_t)tiles), dim3(kThreadsOf<T>), 0,
-                           stream, L);
+        L.total = (int32_t)tiles;
+        if constexpr (MODE == kGemmBX) {
+            L.xpf = 1;
+            for (int k = 0; k < cnt; ++k) L.xpf &= L.g[k].K >= kStages * kBK ? 1 : 0;
+            const int64_t grid = tiles < round_tiles ? tiles : round_tiles;
+            hipLaunchKernelGGL((ns_bx_kernel<T>), dim3((uint32_t)grid), dim3(kThreadsOf<T>), 0, stream,
+                               L);
+        } else {
+            hipLaunchKernelGGL((ns_gemm_kernel<T, MODE>), dim3((uint32_t)tiles), dim3(kThreadsOf<T>),
+                               0, stream, L);
+        }
     }
     return hipGetLastError();
 }
@@ -691,6 +997,10 @@ hipError_t run_mode(const NsGroupRef *refs, int nrefs, int iter, bool last, floa
 }
 
 }  // namespace
+
+void ns_set_workgroup_limit(int n) {
+    g_workgroup_limit.store(n > 0 ? (n < 8 ? 8 : n / 8 * 8) : 0, std::memory_order_relaxed);
+}
 
 int ns_round_tiles(int tile) {
     switch (tile) {

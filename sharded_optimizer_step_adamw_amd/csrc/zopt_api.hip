@@ -236,6 +236,12 @@ ZOPT_EXPORT zopt_status zopt_round_bf16(const float *src, uint16_t *dst, int64_t
     return e == hipSuccess ? ZOPT_OK : ZOPT_ERR_DEVICE;
 }
 
+ZOPT_EXPORT zopt_status zopt_set_ns_workgroup_limit(int32_t n) {
+    if (n < 0) return ZOPT_ERR_SIZE;
+    ns_set_workgroup_limit(n);
+    return ZOPT_OK;
+}
+
 namespace {
 
 zopt_status muon_check_shape(int32_t batch, int64_t rows, int64_t cols) {

@@ -178,6 +178,10 @@ hipError_t launch_ns_iteration(const NsGroupRef *refs, int nrefs, int iter, bool
 // current device holds at once (one round of tiles).
 int ns_round_tiles(int tile);
 
+// Caps the workgroups that the persistent B X launches keep resident (n <= 0:
+// a full round; otherwise max(8, n rounded down to a multiple of 8)).
+void ns_set_workgroup_limit(int n);
+
 // Capacity of the memory-side cache (MI355X Infinity Cache).
 constexpr size_t kMemCacheBytes = (size_t)256 << 20;
 

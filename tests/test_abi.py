@@ -46,6 +46,13 @@ def test_shard_len_rejects_bad_sizes():
         assert z.lib().zopt_shard_len(*args) == -1
 
 
+def test_ns_workgroup_limit_checks():
+    L = z.lib()
+    assert L.zopt_set_ns_workgroup_limit(-1) == z.ZOPT_ERR_SIZE
+    assert L.zopt_set_ns_workgroup_limit(16) == z.ZOPT_OK
+    assert L.zopt_set_ns_workgroup_limit(0) == z.ZOPT_OK
+
+
 def adamw(**kw):
     a = dict(master=FAKE, exp_avg=FAKE, exp_avg_sq=FAKE, grad=FAKE, weight=None, N=16,
              bucket=8, world=2, rank=0, shard_len=8, lr=1e-3, beta1=0.9, beta2=0.95,
