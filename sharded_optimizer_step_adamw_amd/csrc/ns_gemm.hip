@@ -84,16 +84,16 @@ struct NsLaunch {
     float a, b, c;
 };
 
-__device__ __forceinline__ uint16_t to_bf16(float x) { return (uint16_t)rne_bf16_bits(x); }
 // lo, hi -> two bf16, round to nearest even, in one gfx950 instruction
 // (v_cvt_pk_bf16_f32).  Equal to rne_bf16_bits for every non-NaN input; a NaN
-// stays a NaN.  Used for Newton-Schulz iterates, which never meet the
-// write-back's NaN convention.
+// stays a NaN.  Used for the Newton-Schulz operands (X, A, B), which never
+// meet the weight write-back's NaN convention.
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
+__device__ __forceinline__ uint16_t cvt_bf16(float x) { return (uint16_t)cvt_pk_bf16(x, 0.0f); }
 __device__ __forceinline__ float from_bf16(uint16_t h) { return bf16_bits_to_float(h); }
 
 // Tile t of a matrix, in bands of kBand tile rows taken column by column, so
@@ -199,7 +199,9 @@ __device__ __forceinline__ void epilogue(const NsGroup &args, float ca, float cb
     // 1. stage the input sub-block (row order) and complete the accumulators
     if (MODE == kSyrkAA && !below) {
         const uint16_t *E = args.E + batch * args.c_stride;
-#pragma unroll 4
+        // (all of the wave's loads in flight at once: the accumulators are the
+        // only other live registers here)
+#pragma unroll
         for (int k = 0; k < RCHUNKS / 64; ++k) {
             const int id = k * 64 + lane, i = id / RCH, c = id % RCH;
             const u32x4 v = *reinterpret_cast<const u32x4 *>(E + (int64_t)(R0 + i) * ldc + C0 + c * 8);
@@ -241,7 +243,7 @@ __device__ __forceinline__ void epilogue(const NsGroup &args, float ca, float cb
                     const int gi = R0 + i * 16 + quad * 4 + r;
                     const float x = acc[i][j][r];
                     if (gi < gj) {
-                        const uint16_t h = to_bf16(x);
+                        const uint16_t h = cvt_bf16(x);
                         Cm[(int64_t)gi * ldc + gj] = h;
                         Cm[(int64_t)gj * ldc + gi] = h;
                     } else if (gi == gj) {
@@ -259,7 +261,7 @@ __device__ __forceinline__ void epilogue(const NsGroup &args, float ca, float cb
 #pragma unroll
             for (int j = 0; j < FN; ++j)
                 *reinterpret_cast<u32x2 *>(W + swz<TCH>(j * 16 + col, i * 16 + quad * 4)) =
-                    u32x2{pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3])};
+                    u32x2{cvt_pk_bf16(acc[i][j][0], acc[i][j][1]), cvt_pk_bf16(acc[i][j][2], acc[i][j][3])};
     }
     __syncthreads();
     if (coalesced) {
@@ -280,7 +282,7 @@ __device__ __forceinline__ void epilogue(const NsGroup &args, float ca, float cb
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     *reinterpret_cast<uint16_t *>(W + swz<RCH>(i * 16 + quad * 4 + r, j * 16 + col)) =
-                        to_bf16(acc[i][j][r]);
+                        cvt_bf16(acc[i][j][r]);
     }
     __syncthreads();
     if (coalesced) {
