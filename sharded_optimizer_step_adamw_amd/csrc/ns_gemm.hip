@@ -171,21 +171,24 @@ __device__ __forceinline__ int swz(int i, int j) {
 
 // Epilogue of the symmetric products: the accumulators are completed in
 // place (A A: b Aoff + c (acc + (dA_i + dA_j) Aoff), its diagonal
-// b dA_i + c (acc + dA_i^2), with Aoff staged through LDS), then leave
-// through the wave's LDS region as coalesced 16-byte row stores: row order
-// to the sub-block itself, transposed to the mirror position.  A sub-block
-// that crosses the diagonal is
-// stored element by element from its upper triangle, so the mirror of each
-// value is that same bf16 value; below the diagonal nothing is stored; the
-// diagonal goes to the fp32 vector (its bf16 entry is 0).  Every wave passes
-// the same barriers.
+// b dA_i + c (acc + dA_i^2), with Aoff staged through LDS), then written
+// once, transposed, to the wave's LDS region, from which the sub-block leaves
+// both as itself (transposing reads give each lane 8 consecutive columns of
+// one row) and as its mirror (plain 16-byte reads of T's rows), in 16-byte
+// stores.  A sub-block that crosses the diagonal is stored element by element
+// from its upper triangle, so the mirror of each value is that same bf16
+// value; below the diagonal nothing is stored; the diagonal goes to the fp32
+// vector (its bf16 entry is 0).  Every wave passes the same barriers.
 template <int MODE, int FM, int FN>
 __device__ __forceinline__ void epilogue(const NsGroup &args, float ca, float cb, float cc,
                                          f32x4 (&acc)[FM][FN], int batch, int R0, int C0, int wave,
                                          int lane, uint8_t *lds_all) {
     constexpr int SR = FM * 16, SC = FN * 16;      // sub-block rows, columns
     constexpr int RCH = SC / 8, TCH = SR / 8;      // chunks per row: row order, transposed
+    static_assert(SC % 32 == 0, "row stores cover 32 columns");
     uint8_t *W = lds_all + wave * (SR * SC * 2);
+    const uint32_t wb =
+        (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t *)W);
     const bool below = R0 >= C0 + SC;
     const bool above = R0 + SR <= C0;
     const bool cross = !below && !above;
@@ -194,40 +197,63 @@ __device__ __forceinline__ void epilogue(const NsGroup &args, float ca, float cb
     const float *dIn = args.dIn + batch * args.d_stride;
     float *dOut = args.dOut + batch * args.d_stride;
     const int col = lane & 15, quad = lane >> 4;
-    constexpr int RCHUNKS = SR * RCH, TCHUNKS = SC * TCH;   // 16-byte chunks per layout
+    // transposing read: lane 4q' + p of a 16-lane group addresses row +q',
+    // columns 4p .. 4p+3 of a 4 x 16 block; lane i gets rows +0..+3 of column i
+    const int tq = (lane >> 2) & 3, tp = lane & 3;
+    auto tr_read = [](uint32_t addr) __attribute__((always_inline)) {
+        u32x2 v;
+        asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr));
+        return v;
+    };
+    constexpr int TCHUNKS = SC * TCH;   // 16-byte chunks of the transposed image
 
-    // 1. stage the input sub-block (row order) and complete the accumulators
+    // 1. A A: stage the input sub-block (row order) and complete the accumulators
+    float da_c[FN], da_r[FM][4];
     if (MODE == kSyrkAA && !below) {
         const uint16_t *E = args.E + batch * args.c_stride;
         // (all of the wave's loads in flight at once: the accumulators are the
         // only other live registers here)
 #pragma unroll
-        for (int k = 0; k < RCHUNKS / 64; ++k) {
+        for (int k = 0; k < SR * RCH / 64; ++k) {
             const int id = k * 64 + lane, i = id / RCH, c = id % RCH;
             const u32x4 v = *reinterpret_cast<const u32x4 *>(E + (int64_t)(R0 + i) * ldc + C0 + c * 8);
             *reinterpret_cast<u32x4 *>(W + i * (RCH * 16) + ((c ^ (i & (RCH - 1))) << 4)) = v;
         }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) da_c[j] = dIn[C0 + j * 16 + col];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) da_r[i][r] = dIn[R0 + i * 16 + quad * 4 + r];
     }
     __syncthreads();
     if (MODE == kSyrkAA && !below) {
+        // the input at the accumulators' positions: one transposing read per
+        // 16 x 16 block gives each lane its 4 rows of one column
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
+            u32x2 e[FN];
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                e[j] = tr_read(wb + swz<RCH>(i * 16 + quad * 4 + tq, j * 16 + 4 * tp));
+            // the wait is tied to the registers, so no use moves above it
+            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(e[0]));
+#pragma unroll
+            for (int j = 1; j < FN; ++j) asm volatile("" : "+v"(e[j]));
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-                const int lj = j * 16 + col, gj = C0 + lj;
-                const float da_j = MODE == kSyrkAA ? dIn[gj] : 0.0f;
+                const int gj = C0 + j * 16 + col;
+                const float in4[4] = {from_bf16(e[j].x & 0xFFFFu), from_bf16(e[j].x >> 16),
+                                      from_bf16(e[j].y & 0xFFFFu), from_bf16(e[j].y >> 16)};
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int li = i * 16 + quad * 4 + r, gi = R0 + li;
-                    const float in = from_bf16(*reinterpret_cast<const uint16_t *>(W + swz<RCH>(li, lj)));
-                    const float v = acc[i][j][r];
-                    const float da_i = dIn[gi];
-                    float x = cb * in + cc * (v + (da_i + da_j) * in);
+                    const int gi = R0 + i * 16 + quad * 4 + r;
+                    const float in = in4[r], v = acc[i][j][r], da_i = da_r[i][r];
+                    float x = cb * in + cc * (v + (da_i + da_c[j]) * in);
                     if (gi == gj) x = cb * da_i + cc * (v + da_i * da_i);
                     acc[i][j][r] = x;
                 }
             }
-            __builtin_amdgcn_sched_barrier(0);
         }
     }
     __syncthreads();
@@ -254,7 +280,8 @@ __device__ __forceinline__ void epilogue(const NsGroup &args, float ca, float cb
             }
     }
     const bool coalesced = !below && !cross;
-    // 2. transposed: T[lj][li], four consecutive rows per 8-byte write
+    // 2. the sub-block transposed, T[lj][li], four consecutive rows per 8-byte
+    // write; it serves both stores
     if (coalesced) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -265,32 +292,27 @@ __device__ __forceinline__ void epilogue(const NsGroup &args, float ca, float cb
     }
     __syncthreads();
     if (coalesced) {
+        // the mirror: T's rows are its rows, 16-byte chunks
 #pragma unroll 4
         for (int k = 0; k < TCHUNKS / 64; ++k) {
             const int id = k * 64 + lane, i = id / TCH, c = id % TCH;
             const u32x4 v = *reinterpret_cast<const u32x4 *>(W + i * (TCH * 16) + ((c ^ (i & (TCH - 1))) << 4));
             *reinterpret_cast<u32x4 *>(Cm + (int64_t)(C0 + i) * ldc + R0 + c * 8) = v;
         }
-    }
-    __syncthreads();
-    // 3. row order
-    if (coalesced) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    *reinterpret_cast<uint16_t *>(W + swz<RCH>(i * 16 + quad * 4 + r, j * 16 + col)) =
-                        cvt_bf16(acc[i][j][r]);
-    }
-    __syncthreads();
-    if (coalesced) {
+        // the sub-block itself, from T by transposing reads: store s covers
+        // rows 16 rb .. +15 and columns 32 ch .. +31; 16-lane group q reads
+        // T rows 32 ch + 8q + {0..3} and + {4..7} at columns 16 rb .. +15, so
+        // lane i holds 8 consecutive columns of row 16 rb + i
 #pragma unroll 4
-        for (int k = 0; k < RCHUNKS / 64; ++k) {
-            const int id = k * 64 + lane, i = id / RCH, c = id % RCH;
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(W + i * (RCH * 16) + ((c ^ (i & (RCH - 1))) << 4));
-            *reinterpret_cast<u32x4 *>(Cm + (int64_t)(R0 + i) * ldc + C0 + c * 8) = v;
+        for (int st = 0; st < (SR / 16) * (SC / 32); ++st) {
+            const int rb = st / (SC / 32), ch = st % (SC / 32);
+            const int t0 = ch * 32 + quad * 8 + tq, c0 = rb * 16 + 4 * tp;
+            const u32x2 lo = tr_read(wb + swz<TCH>(t0, c0));
+            const u32x2 hi = tr_read(wb + swz<TCH>(t0 + 4, c0));
+            u32x4 v = u32x4{lo.x, lo.y, hi.x, hi.y};
+            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v));
+            *reinterpret_cast<u32x4 *>(Cm + (int64_t)(R0 + rb * 16 + col) * ldc + C0 + ch * 32 +
+                                       quad * 8) = v;
         }
     }
 }
