@@ -171,18 +171,18 @@ __device__ __forceinline__ int swz(int i, int j) {
 
 // Epilogue of the symmetric products: the accumulators are completed in
 // place (A A: b Aoff + c (acc + (dA_i + dA_j) Aoff), its diagonal
-// b dA_i + c (acc + dA_i^2), with Aoff staged through LDS), then written
-// once, transposed, to the wave's LDS region, from which the sub-block leaves
-// both as itself (transposing reads give each lane 8 consecutive columns of
-// one row) and as its mirror (plain 16-byte reads of T's rows), in 16-byte
-// stores.  A sub-block that crosses the diagonal is stored element by element
-// from its upper triangle, so the mirror of each value is that same bf16
-// value; below the diagonal nothing is stored; the diagonal goes to the fp32
-// vector (its bf16 entry is 0).  Every wave passes the same barriers.
-template <int MODE, int FM, int FN>
+// b dA_i + c (acc + dA_i^2), with Aoff staged through LDS).  A tile above
+// the diagonal is written once, transposed, to each wave's LDS region, from
+// which the sub-block leaves both as itself (transposing reads give each lane
+// 8 consecutive columns of one row) and as its mirror (plain 16-byte reads of
+// T's rows), in 16-byte stores.  A tile on the diagonal is built symmetric in
+// LDS from its upper triangle and stored once.  The diagonal itself goes to
+// the fp32 vector (its bf16 entry is 0).  Every wave passes the same
+// barriers.
+template <int MODE, int BM, int FM, int FN>
 __device__ __forceinline__ void epilogue(const NsGroup &args, float ca, float cb, float cc,
-                                         f32x4 (&acc)[FM][FN], int batch, int R0, int C0, int wave,
-                                         int lane, uint8_t *lds_all) {
+                                         f32x4 (&acc)[FM][FN], int batch, int m0, int n0, int R0,
+                                         int C0, int wave, int lane, uint8_t *lds_all) {
     constexpr int SR = FM * 16, SC = FN * 16;      // sub-block rows, columns
     constexpr int RCH = SC / 8, TCH = SR / 8;      // chunks per row: row order, transposed
     static_assert(SC % 32 == 0, "row stores cover 32 columns");
@@ -258,27 +258,46 @@ __device__ __forceinline__ void epilogue(const NsGroup &args, float ca, float cb
     }
     __syncthreads();
 
-    if (cross) {
+    if (m0 == n0) {
+        // A tile on the diagonal is its own mirror: every wave puts each
+        // value above the diagonal at both its places in a tile-wide image
+        // (so the mirror of each value is that same bf16 value), 0 on the
+        // diagonal, whose fp32 value goes to the vector; then the workgroup
+        // stores the image once, in 16-byte chunks.
+        constexpr int TB = BM / 8;  // 16-byte chunks per image row
+        if (!below) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int gj = C0 + j * 16 + col;
+                for (int j = 0; j < FN; ++j) {
+                    const int lj = C0 - m0 + j * 16 + col;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int gi = R0 + i * 16 + quad * 4 + r;
-                    const float x = acc[i][j][r];
-                    if (gi < gj) {
-                        const uint16_t h = cvt_bf16(x);
-                        Cm[(int64_t)gi * ldc + gj] = h;
-                        Cm[(int64_t)gj * ldc + gi] = h;
-                    } else if (gi == gj) {
-                        dOut[gi] = x;
-                        Cm[(int64_t)gi * ldc + gi] = 0;
+                    for (int r = 0; r < 4; ++r) {
+                        const int li = R0 - m0 + i * 16 + quad * 4 + r;
+                        const float x = acc[i][j][r];
+                        if (li < lj) {
+                            const uint16_t h = cvt_bf16(x);
+                            *reinterpret_cast<uint16_t *>(lds_all + swz<TB>(li, lj)) = h;
+                            *reinterpret_cast<uint16_t *>(lds_all + swz<TB>(lj, li)) = h;
+                        } else if (li == lj) {
+                            dOut[m0 + li] = x;
+                            *reinterpret_cast<uint16_t *>(lds_all + swz<TB>(li, li)) = 0;
+                        }
                     }
                 }
-            }
+        }
+        __syncthreads();
+        const int tid = wave * 64 + lane;
+        constexpr int NT = BM * BM / (FM * 16 * FN * 16) * 64;  // threads of the workgroup
+#pragma unroll 4
+        for (int k = tid; k < BM * TB; k += NT) {
+            const int i = k / TB, c = k % TB;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(lds_all + i * (TB * 16) + ((c ^ (i & (TB - 1))) << 4));
+            *reinterpret_cast<u32x4 *>(Cm + (int64_t)(m0 + i) * ldc + m0 + c * 8) = v;
+        }
+        return;
     }
+    // off the diagonal every sub-block lies above it
     const bool coalesced = !below && !cross;
     // 2. the sub-block transposed, T[lj][li], four consecutive rows per 8-byte
     // write; it serves both stores
@@ -480,8 +499,8 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch 
     // the epilogue reuses the buffers
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    epilogue<MODE, FM, FN>(G, L.a, L.b, L.c, acc, batch, m0 + wr * WTM, n0 + wc * WTN, wave, lane,
-                           lds);
+    epilogue<MODE, BM, FM, FN>(G, L.a, L.b, L.c, acc, batch, m0, n0, m0 + wr * WTM, n0 + wc * WTN,
+                               wave, lane, lds);
 }
 
 // ----------------------------------------------------------------------------
