@@ -156,11 +156,11 @@ __device__ __forceinline__ void tile_coords(const NsGroup &G, int t, int &ti, in
 template <int BM>
 struct Cfg;
 template <>
-struct Cfg<256> { static constexpr int WR = 2, WC = 4, WPE = 2; };
+struct Cfg<256> { static constexpr int WR = 2, WC = 4, WPE = 2, SYM_STAGES = 4, SYM_WPE = 2; };
 template <>
-struct Cfg<128> { static constexpr int WR = 2, WC = 2, WPE = 2; };
+struct Cfg<128> { static constexpr int WR = 2, WC = 2, WPE = 2, SYM_STAGES = 3, SYM_WPE = 3; };
 template <>
-struct Cfg<64> { static constexpr int WR = 2, WC = 2, WPE = 4; };
+struct Cfg<64> { static constexpr int WR = 2, WC = 2, WPE = 4, SYM_STAGES = 4, SYM_WPE = 4; };
 
 // Swizzled byte offset of element (i, j) in an LDS block whose rows hold
 // `chunks` 16-byte chunks (chunks is a power of two).
@@ -382,9 +382,10 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch 
     constexpr int ROW = 64, OPB = BM * ROW, STAGE = 2 * OPB;
     constexpr int LOADS = OPB / 1024 / NW, LPS = 2 * LOADS;
     constexpr int ND = FM + FN;  // LDS fragment reads per stage
+    constexpr int NSTG = Cfg<BM>::SYM_STAGES;
     static_assert(LOADS >= 1 && LOADS * NW * 1024 == OPB, "tile");
-    static_assert(kStages * STAGE >= BM * BM * 2, "the epilogue regions fit in the stages");
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * STAGE];
+    static_assert(NSTG * STAGE >= BM * BM * 2, "the epilogue regions fit in the stages");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[NSTG * STAGE];
 
     // group, matrix and tile of this workgroup
     const int bid = blockIdx.x;
@@ -458,18 +459,18 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch 
 
     const int KT = K / kBK;
 #pragma unroll
-    for (int s = 0; s < kStages; ++s) gload(s * STAGE, s * kBK);
-    __builtin_amdgcn_s_waitcnt(WAIT_VM_LGKM0((kStages - 1) * LPS));
+    for (int s = 0; s < NSTG; ++s) gload(s * STAGE, s * kBK);
+    __builtin_amdgcn_s_waitcnt(WAIT_VM_LGKM0((NSTG - 1) * LPS));
     __syncthreads();
     read(0, 0);
     int cur = 0;  // buffer of stage kt
     auto body = [&](int kt, auto PAR) __attribute__((always_inline)) {
         constexpr int par = decltype(PAR)::value;
-        const int nxt = cur + 1 == kStages ? 0 : cur + 1;
-        __builtin_amdgcn_s_waitcnt(WAIT_VM_LGKM0((kStages - 2) * LPS));
+        const int nxt = cur + 1 == NSTG ? 0 : cur + 1;
+        __builtin_amdgcn_s_waitcnt(WAIT_VM_LGKM0((NSTG - 2) * LPS));
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        gload(cur * STAGE, (kt + kStages) * kBK);
+        gload(cur * STAGE, (kt + NSTG) * kBK);
         read(par ^ 1, nxt * STAGE);
         mma(par);
 #pragma unroll
@@ -949,14 +950,16 @@ NsGroup product_group(int mode, const NsGroupRef &r, int iter, bool last) {
     return s;
 }
 
+// Workgroups of the T-tile kernel (B X, or the symmetric products) that the
+// device holds at once.
 template <int T>
-int round_tiles_of() {
+int round_tiles_of(bool sym = false) {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus < 8)
         cus = 256;
-    const int per_cu = Cfg<T>::WPE * 4 / (Cfg<T>::WR * Cfg<T>::WC);
+    const int per_cu = (sym ? Cfg<T>::SYM_WPE : Cfg<T>::WPE) * 4 / (Cfg<T>::WR * Cfg<T>::WC);
     return (cus / 8) * per_cu * 8;
 }
 
@@ -967,7 +970,7 @@ std::atomic<int> g_workgroup_limit{0};
 template <int T, int MODE>
 hipError_t launch_product(const NsGroupRef *refs, const int *idx, int n, int iter, bool last,
                           float a, float b, float c, hipStream_t stream) {
-    int32_t round_tiles = round_tiles_of<T>();
+    int32_t round_tiles = round_tiles_of<T>(MODE != kGemmBX);
     if (MODE == kGemmBX) {
         const int lim = g_workgroup_limit.load(std::memory_order_relaxed);
         if (lim > 0 && lim < round_tiles) round_tiles = lim;
