@@ -911,7 +911,12 @@ constexpr int kThreadsOf = Cfg<T>::WR * Cfg<T>::WC * 64;
 
 // The per-group operands of one product of iteration `iter` (X in the x
 // buffer at even iterations, in xt0 at odd ones; the other receives X').
-NsGroup product_group(int mode, const NsGroupRef &r, int iter, bool last) {
+// One launch's share of a group: its matrices [b0, b0 + nb) on tiles of `tile`.
+struct LaunchPart {
+    int ref, b0, nb;
+};
+
+NsGroup product_group(int mode, const NsGroupRef &r, int iter, bool last, int tile, int b0) {
     const MuonGeom &g = *r.geom;
     const MuonWorkspace &L = *r.layout;
     char *ws = r.base;
@@ -924,7 +929,6 @@ NsGroup product_group(int mode, const NsGroupRef &r, int iter, bool last) {
     float *dB = reinterpret_cast<float *>(ws + L.db);
     const int64_t ds = (int64_t)(L.d_stride / 4);
     const int64_t xs = (int64_t)(L.x_stride / 2), as = (int64_t)(L.a_stride / 2);
-    const int tile = mode == kGemmBX ? g.tile_bx : g.tile;
     const int tm = g.mp / tile, tn = g.np / tile;
     NsGroup s{};
     s.d_stride = ds;
@@ -947,6 +951,14 @@ NsGroup product_group(int mode, const NsGroupRef &r, int iter, bool last) {
         s.CT = (last && g.transposed) ? XTout : nullptr; s.ct_stride = xs; s.ldct = g.mp;
         s.dIn = dB; s.dOut = dB;
     }
+    // matrices from b0 on
+    s.P += b0 * s.p_stride;
+    s.Q += b0 * s.q_stride;
+    s.C += b0 * s.c_stride;
+    if (s.E) s.E += b0 * s.c_stride;
+    if (s.CT) s.CT += b0 * s.ct_stride;
+    s.dIn += b0 * s.d_stride;
+    s.dOut += b0 * s.d_stride;
     return s;
 }
 
@@ -967,14 +979,17 @@ int round_tiles_of(bool sym = false) {
 // one full round of the device).
 std::atomic<int> g_workgroup_limit{0};
 
+template <int T>
+int32_t bx_round_tiles() {
+    int32_t r = round_tiles_of<T>();
+    const int lim = g_workgroup_limit.load(std::memory_order_relaxed);
+    return lim > 0 && lim < r ? lim : r;
+}
+
 template <int T, int MODE>
-hipError_t launch_product(const NsGroupRef *refs, const int *idx, int n, int iter, bool last,
-                          float a, float b, float c, hipStream_t stream) {
-    int32_t round_tiles = round_tiles_of<T>(MODE != kGemmBX);
-    if (MODE == kGemmBX) {
-        const int lim = g_workgroup_limit.load(std::memory_order_relaxed);
-        if (lim > 0 && lim < round_tiles) round_tiles = lim;
-    }
+hipError_t launch_product(const NsGroupRef *refs, const LaunchPart *parts, int n, int iter,
+                          bool last, float a, float b, float c, hipStream_t stream) {
+    const int32_t round_tiles = MODE == kGemmBX ? bx_round_tiles<T>() : round_tiles_of<T>(true);
     for (int first = 0; first < n; first += kMaxGroups) {
         const int cnt = n - first < kMaxGroups ? n - first : kMaxGroups;
         NsLaunch L{};
@@ -984,9 +999,9 @@ hipError_t launch_product(const NsGroupRef *refs, const int *idx, int n, int ite
         L.ngroups = cnt;
         int64_t tiles = 0;
         for (int k = 0; k < cnt; ++k) {
-            const NsGroupRef &r = refs[idx[first + k]];
-            NsGroup s = product_group(MODE, r, iter, last);
-            s.tiles = s.tiles_pm * r.geom->batch;
+            const LaunchPart &p = parts[first + k];
+            NsGroup s = product_group(MODE, refs[p.ref], iter, last, T, p.b0);
+            s.tiles = s.tiles_pm * p.nb;
             s.padded = (s.tiles + 7) / 8 * 8;
             s.round_tiles = round_tiles;
             s.tile0 = (int32_t)tiles;
@@ -1009,36 +1024,69 @@ hipError_t launch_product(const NsGroupRef *refs, const int *idx, int n, int ite
     return hipGetLastError();
 }
 
-// One product for every group whose tile size for it is T, longest reduction
-// first so that the short tiles fill the last rounds.
+// The groups whose tile size for the product is T, longest reduction first
+// so that the short tiles fill the last rounds.
 template <int T, int MODE>
-hipError_t run_product(const NsGroupRef *refs, int nrefs, int iter, bool last, float a, float b,
-                       float c, hipStream_t stream) {
-    int idx[kMaxCallGroups];
+int product_parts(const NsGroupRef *refs, int nrefs, LaunchPart *parts) {
     int n = 0;
     for (int i = 0; i < nrefs; ++i) {
         const MuonGeom &g = *refs[i].geom;
-        if ((MODE == kGemmBX ? g.tile_bx : g.tile) == T) idx[n++] = i;
+        if ((MODE == kGemmBX ? g.tile_bx : g.tile) == T) parts[n++] = LaunchPart{i, 0, g.batch};
     }
-    if (n == 0) return hipSuccess;
     for (int i = 1; i < n; ++i)
         for (int j = i; j > 0; --j) {
-            const MuonGeom &p = *refs[idx[j - 1]].geom, &q = *refs[idx[j]].geom;
+            const MuonGeom &p = *refs[parts[j - 1].ref].geom, &q = *refs[parts[j].ref].geom;
             const int kp = MODE == kSyrkXXT ? p.np : p.mp, kq = MODE == kSyrkXXT ? q.np : q.mp;
             if (kp >= kq) break;
-            const int t = idx[j - 1];
-            idx[j - 1] = idx[j];
-            idx[j] = t;
+            const LaunchPart t = parts[j - 1];
+            parts[j - 1] = parts[j];
+            parts[j] = t;
         }
-    return launch_product<T, MODE>(refs, idx, n, iter, last, a, b, c, stream);
+    return n;
 }
 
 template <int MODE>
 hipError_t run_mode(const NsGroupRef *refs, int nrefs, int iter, bool last, float a, float b,
                     float c, hipStream_t stream) {
-    hipError_t e = run_product<256, MODE>(refs, nrefs, iter, last, a, b, c, stream);
-    if (e == hipSuccess) e = run_product<128, MODE>(refs, nrefs, iter, last, a, b, c, stream);
-    if (e == hipSuccess) e = run_product<64, MODE>(refs, nrefs, iter, last, a, b, c, stream);
+    LaunchPart p256[kMaxCallGroups], p128[kMaxCallGroups + 1], p64[kMaxCallGroups];
+    int n256 = product_parts<256, MODE>(refs, nrefs, p256);
+    int n128 = product_parts<128, MODE>(refs, nrefs, p128);
+    const int n64 = product_parts<64, MODE>(refs, nrefs, p64);
+    if (MODE == kGemmBX && n256 > 0) {
+        // The 256-tile launch's last round: when only a few tiles are left for
+        // it, the last group's trailing matrices go to the 128-tile launch
+        // instead (the same arithmetic on smaller tiles: results are the same
+        // bit for bit), if that saves a round of 256 tiles for at most one
+        // round of 128 tiles, which take ~0.6 of the time.
+        auto tiles = [&](const LaunchPart *p, int n, int t) {
+            int64_t s = 0;
+            for (int i = 0; i < n; ++i) {
+                const MuonGeom &g = *refs[p[i].ref].geom;
+                s += (int64_t)(g.mp / t) * (g.np / t) * p[i].nb;
+            }
+            return s;
+        };
+        const int64_t r256 = bx_round_tiles<256>(), r128 = bx_round_tiles<128>();
+        const int64_t t256 = tiles(p256, n256, 256), t128 = tiles(p128, n128, 128);
+        const int64_t rounds = (t256 + r256 - 1) / r256, rem = t256 - (rounds - 1) * r256;
+        LaunchPart &lp = p256[n256 - 1];
+        const MuonGeom &g = *refs[lp.ref].geom;
+        const int64_t q = (int64_t)(g.mp / 256) * (g.np / 256);  // 256-tiles per matrix
+        const int64_t m = (rem + q - 1) / q;                        // matrices to move
+        const int64_t r128_before = (t128 + r128 - 1) / r128;
+        const int64_t r128_after = (t128 + 4 * q * m + r128 - 1) / r128;
+        if (rounds > 1 && rem * 4 <= r256 && m < lp.nb && r128_after - r128_before <= 1 &&
+            n128 <= kMaxCallGroups) {
+            p128[n128++] = LaunchPart{lp.ref, lp.b0 + lp.nb - (int)m, (int)m};
+            lp.nb -= (int)m;
+        }
+    }
+    hipError_t e = hipSuccess;
+    if (n256 > 0) e = launch_product<256, MODE>(refs, p256, n256, iter, last, a, b, c, stream);
+    if (e == hipSuccess && n128 > 0)
+        e = launch_product<128, MODE>(refs, p128, n128, iter, last, a, b, c, stream);
+    if (e == hipSuccess && n64 > 0)
+        e = launch_product<64, MODE>(refs, p64, n64, iter, last, a, b, c, stream);
     return e;
 }
 
