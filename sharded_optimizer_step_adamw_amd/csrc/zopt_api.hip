@@ -126,7 +126,8 @@ zopt_status adamw_prepare(const float *master, const float *exp_avg, const float
                           float eps, float weight_decay, int64_t step, AdamWParams &p) {
     if (!master || !exp_avg || !exp_avg_sq || !grad) return ZOPT_ERR_NULL;
     if (N < 1 || bucket < 1 || world < 1 || rank < 0 || rank >= world) return ZOPT_ERR_SIZE;
-    // the grid holds at most 2^32 - 1 work-items of 8 elements each
+    // sizes the index arithmetic is written for (a step is issued as
+    // launches of at most 2^30 shard elements each)
     if (N > ((int64_t)1 << 40)) return ZOPT_ERR_SIZE;
     if (!finite(lr) || lr < 0.0f || !(beta1 >= 0.0f && beta1 < 1.0f) ||
         !(beta2 >= 0.0f && beta2 < 1.0f) || !finite(eps) || eps <= 0.0f ||

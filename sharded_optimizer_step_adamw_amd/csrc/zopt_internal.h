@@ -53,8 +53,14 @@ struct AdamWParams {
     float beta1, beta2, eps;
     float step_size, bc2_sqrt, decay, omb1, omb2;
     float grad_scale;
-    int32_t vec;         // fp32 bases 16-byte and bf16 bases 8-byte aligned
+    int32_t vec;         // gradient base 16-byte aligned (the norm pass's vector loads)
     double inv_piece;    // 1 / piece, for the bucket index
+    // When a piece holds a whole number of AdamW tiles (tpp tiles, tpp > 0),
+    // no tile of [0, full_len) straddles a bucket edge and the bucket of such
+    // a tile is tile / tpp (tiles [0, full_tiles)); tpp = 0 otherwise.
+    uint32_t tpp;
+    uint32_t full_tiles;
+    double inv_tpp;      // 1 / tpp
     const float *stats;  // clip statistics in device memory: grad_scale read there (or NULL)
     int32_t skip_nonfinite;  // with stats: a found_inf there skips the step
 };

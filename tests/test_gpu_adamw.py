@@ -234,6 +234,40 @@ def test_zero2_full_size_sampled():
     assert not gw[other.to(DEV)].float().any()
 
 
+def test_shard_longer_than_one_launch_sampled():
+    """world 1, N = 2^30 + 300,001 in buckets of 1 << 25: the step is issued as
+    two launches (a launch covers at most 2^30 elements), so the elements on
+    both sides of the launch boundary, the ragged tail and a seeded sample are
+    stepped by the oracle one by one and compared bitwise."""
+    n, bucket = (1 << 30) + 300_001, 1 << 25
+    sl = z.shard_len(n, bucket, 1)
+    assert sl == n
+    rng = np.random.default_rng(77)
+    edge = 1 << 30
+    j = np.unique(np.concatenate([rng.integers(0, sl, 1 << 18), np.arange(edge - 600, edge + 600),
+                                  np.arange(sl - 600, sl)])).astype(np.int64)
+    flat, real = oracle.shard_index_map(n, bucket, 1, 0, j)
+    assert real.all() and np.array_equal(flat, j)
+    gp = wl.device_normal(90, 0, (sl,), 0.02, DEV)
+    gm, gv = torch.zeros_like(gp), torch.zeros_like(gp)
+    gw = torch.zeros((n,), dtype=torch.bfloat16, device=DEV)
+    jt = torch.from_numpy(j).to(DEV)
+    p = gp[jt].cpu().numpy()
+    m, v = np.zeros_like(p), np.zeros_like(p)
+    hps = [f32(x) for x in (3e-4, 0.9, 0.95, 1e-8, 0.1)]
+    for t in range(1, 3):
+        gg = wl.device_grad_bf16(90, 1, (n,), 1e-3, DEV, step=t)
+        gs = oracle.bf16_bits_to_f32(u16(gg[jt]))
+        z.adamw_shard_step(gp, gm, gv, gg, gw, n, bucket, 1, 0, *hps, t)
+        w = oracle.adamw_points(p, m, v, gs.copy(), *hps, t)
+        del gg
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(gp[jt].cpu().numpy().view(np.uint32), p.view(np.uint32))
+    np.testing.assert_array_equal(gm[jt].cpu().numpy().view(np.uint32), m.view(np.uint32))
+    np.testing.assert_array_equal(gv[jt].cpu().numpy().view(np.uint32), v.view(np.uint32))
+    np.testing.assert_array_equal(u16(gw[jt]), w)
+
+
 # ------------------------------------------------------------ round_bf16
 
 def test_round_bf16_exhaustive():
@@ -263,3 +297,19 @@ def test_round_bf16_sizes_and_alignment(n, off):
     dst = torch.full((n + off,), 7.0, dtype=torch.bfloat16, device=DEV)[off:]
     z.round_bf16(src, dst)
     assert np.array_equal(u16(dst), oracle.rne_bf16(x))
+
+
+def test_round_bf16_longer_than_one_launch_sampled():
+    """n = 2^33 + 1001 (two launches: a launch covers at most 2^33 elements):
+    both sides of the launch boundary, the tail and a seeded sample against
+    the oracle's rounding."""
+    n = (1 << 33) + 1001
+    src = wl.device_normal(91, 0, (n,), 1.0, DEV)
+    dst = torch.full((n,), 7.0, dtype=torch.bfloat16, device=DEV)
+    z.round_bf16(src, dst)
+    rng = np.random.default_rng(91)
+    edge = 1 << 33
+    j = np.unique(np.concatenate([rng.integers(0, n, 1 << 18), np.arange(edge - 600, edge + 600),
+                                  np.arange(n - 600, n)])).astype(np.int64)
+    jt = torch.from_numpy(j).to(DEV)
+    assert np.array_equal(u16(dst[jt]), oracle.rne_bf16(src[jt].cpu().numpy()))
