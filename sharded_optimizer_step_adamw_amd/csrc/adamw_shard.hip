@@ -39,6 +39,7 @@ constexpr int kTile = kThreads;          // shard elements per workgroup: one pe
 // Workgroups per launch: a dispatch's grid counts work-items in 32 bits, so
 // longer shards are stepped by several launches, each from a tile offset.
 constexpr int64_t kMaxLaunchTiles = int64_t(1) << 22;
+constexpr int64_t kMaxGridY = 65535;     // buckets per bucket-grid launch
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -149,6 +150,49 @@ __global__ __launch_bounds__(kThreads) void adamw_shard_kernel(
     st_stream(exp_avg + j, m);
     st_stream(exp_avg_sq + j, v);
     if (real && weight) st_stream(weight + f, (uint16_t)rne_bf16_bits(p));
+}
+
+// The per-step scalars of the AdamW update, alone (the bucket-grid kernel's
+// small argument block).
+struct AdamWScalars {
+    float beta1, beta2, eps, step_size, bc2_sqrt, decay, omb1, omb2, grad_scale;
+    int32_t skip_nonfinite;
+    const float *stats;
+};
+
+// The full buckets of the shard as a grid of (tiles per piece) x (buckets):
+// blockIdx.y is the bucket, blockIdx.x the tile within this rank's piece of
+// it.  grad_r and weight_r are the flat arrays advanced to this rank's piece
+// of bucket 0, so the flat index of a tile is blockIdx.y * bstride +
+// blockIdx.x * kTile from them, with bstride the adjusted bucket length:
+// scalar arithmetic on the launch indices, and all four loads leave at once.
+template <bool kDevScale>
+__global__ __launch_bounds__(kThreads) void adamw_bucket_grid_kernel(
+    float *__restrict__ master, float *__restrict__ exp_avg, float *__restrict__ exp_avg_sq,
+    const uint16_t *__restrict__ grad_r, uint16_t *__restrict__ weight_r, int64_t bstride,
+    uint32_t tpp, AdamWScalars s) {
+    const int64_t j = ((int64_t)blockIdx.y * tpp + blockIdx.x) * kTile + threadIdx.x;
+    const int64_t f = (int64_t)blockIdx.y * bstride + (int64_t)blockIdx.x * kTile + threadIdx.x;
+    float p = ld_stream(master + j), m = ld_stream(exp_avg + j), v = ld_stream(exp_avg_sq + j);
+    const float gb = bf16_bits_to_float(ld_stream(grad_r + f));
+    if constexpr (kDevScale) {
+        if (s.skip_nonfinite && s.stats[kClipFoundInf] != 0.0f) return;
+        s.grad_scale = s.stats[kClipGradScale];
+    }
+    AdamWParams a;
+    a.beta1 = s.beta1;
+    a.beta2 = s.beta2;
+    a.eps = s.eps;
+    a.step_size = s.step_size;
+    a.bc2_sqrt = s.bc2_sqrt;
+    a.decay = s.decay;
+    a.omb1 = s.omb1;
+    a.omb2 = s.omb2;
+    adamw_update(p, m, v, gb * s.grad_scale, a);
+    st_stream(master + j, p);
+    st_stream(exp_avg + j, m);
+    st_stream(exp_avg_sq + j, v);
+    if (weight_r) st_stream(weight_r + f, (uint16_t)rne_bf16_bits(p));
 }
 
 // ------------------------------------------------------------------ norm
@@ -303,7 +347,26 @@ hipError_t launch_adamw_shard(float *master, float *exp_avg, float *exp_avg_sq,
         p.full_tiles = (uint32_t)(p.full_len / kTile);
         p.inv_tpp = 1.0 / (double)p.tpp;
     }
-    for (int64_t t = 0; t < tiles; t += kMaxLaunchTiles) {
+    int64_t t = 0;
+    if (p.tpp && p.full_tiles > 0 && p.tpp <= kMaxLaunchTiles &&
+        p.full_tiles / p.tpp <= kMaxGridY) {
+        // the full buckets as one (tiles per piece) x (buckets) grid
+        const dim3 grid(p.tpp, p.full_tiles / p.tpp);
+        const AdamWScalars sc{p.beta1, p.beta2,    p.eps,  p.step_size, p.bc2_sqrt,
+                              p.decay, p.omb1,     p.omb2, p.grad_scale, p.skip_nonfinite,
+                              p.stats};
+        const int64_t bstride = p.gap + p.piece;
+        const uint16_t *grad_r = grad + p.rank_off;
+        uint16_t *weight_r = weight ? weight + p.rank_off : nullptr;
+        if (p.stats)
+            hipLaunchKernelGGL(adamw_bucket_grid_kernel<true>, grid, dim3(kThreads), 0, stream,
+                               master, exp_avg, exp_avg_sq, grad_r, weight_r, bstride, p.tpp, sc);
+        else
+            hipLaunchKernelGGL(adamw_bucket_grid_kernel<false>, grid, dim3(kThreads), 0, stream,
+                               master, exp_avg, exp_avg_sq, grad_r, weight_r, bstride, p.tpp, sc);
+        t = p.full_tiles;
+    }
+    for (; t < tiles; t += kMaxLaunchTiles) {
         const uint32_t blocks = (uint32_t)(tiles - t < kMaxLaunchTiles ? tiles - t : kMaxLaunchTiles);
         if (p.stats)
             hipLaunchKernelGGL(adamw_shard_kernel<true>, dim3(blocks), dim3(kThreads), 0, stream,

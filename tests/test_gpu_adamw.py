@@ -234,12 +234,16 @@ def test_zero2_full_size_sampled():
     assert not gw[other.to(DEV)].float().any()
 
 
-def test_shard_longer_than_one_launch_sampled():
-    """world 1, N = 2^30 + 300,001 in buckets of 1 << 25: the step is issued as
-    two launches (a launch covers at most 2^30 elements), so the elements on
-    both sides of the launch boundary, the ragged tail and a seeded sample are
-    stepped by the oracle one by one and compared bitwise."""
-    n, bucket = (1 << 30) + 300_001, 1 << 25
+@pytest.mark.parametrize("bucket", [1 << 25, (1 << 25) + 1])
+def test_shard_longer_than_one_launch_sampled(bucket):
+    """world 1, N = 2^30 + 300,001.  Buckets of 1 << 25 (a whole number of
+    256-element tiles): the 32 full buckets as one bucket-grid launch, the
+    short last bucket as a launch of its own.  Buckets of (1 << 25) + 1: tiles
+    straddle bucket edges, and the step is issued as two launches (a launch
+    covers at most 2^30 elements).  The elements on both sides of 2^30, the
+    ragged tail and a seeded sample are stepped by the oracle one by one and
+    compared bitwise."""
+    n = (1 << 30) + 300_001
     sl = z.shard_len(n, bucket, 1)
     assert sl == n
     rng = np.random.default_rng(77)
