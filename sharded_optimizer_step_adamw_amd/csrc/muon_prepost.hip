@@ -29,14 +29,80 @@
 namespace zopt {
 namespace {
 
+// Elements per thread and sweeps per workgroup of the streaming passes.
+// Measured on MI355X (GPT-2-small and 8B-share Muon calls): one sweep of 8
+// per thread in pass 1 and 4 per thread in the post-step beat four sweeps of
+// 8 and 8 (pre/post 4% faster) and one element per thread (34% slower).
 constexpr int kThreads = 256;
-constexpr int kPerThread = 8;       // elements per thread per sweep
-constexpr int kSweeps = 4;          // sweeps per workgroup in pass 1
-constexpr int kChunk = kThreads * kPerThread * kSweeps;  // elements / workgroup
+constexpr int kPreEPT = 8;          // pass 1 of a call with no iterations: elements per thread per sweep
+constexpr int kSweeps = 1;          // sweeps per workgroup in that pass
+constexpr int kChunk = kThreads * kPreEPT * kSweeps;  // elements / workgroup
+constexpr int kPostEPT = 4;         // post-step: elements per thread (1, 4 or 8)
 constexpr int kTile = 64;           // pass-2 transpose tile
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// E consecutive fp32 (E = 1, 4 or 8; 16-byte aligned for E > 1).
+template <int E, bool NT>
+__device__ __forceinline__ void ld_f32(const float *p, float (&x)[E]) {
+    if constexpr (E == 1) {
+        x[0] = NT ? __builtin_nontemporal_load(p) : *p;
+    } else {
+#pragma unroll
+        for (int h = 0; h < E / 4; ++h) {
+            const f32x4 *q = reinterpret_cast<const f32x4 *>(p) + h;
+            const f32x4 v = NT ? __builtin_nontemporal_load(q) : *q;
+            x[4 * h] = v.x; x[4 * h + 1] = v.y; x[4 * h + 2] = v.z; x[4 * h + 3] = v.w;
+        }
+    }
+}
+template <int E, bool NT>
+__device__ __forceinline__ void st_f32(float *p, const float (&x)[E]) {
+    if constexpr (E == 1) {
+        if (NT) __builtin_nontemporal_store(x[0], p); else *p = x[0];
+    } else {
+#pragma unroll
+        for (int h = 0; h < E / 4; ++h) {
+            f32x4 *q = reinterpret_cast<f32x4 *>(p) + h;
+            const f32x4 v{x[4 * h], x[4 * h + 1], x[4 * h + 2], x[4 * h + 3]};
+            if (NT) __builtin_nontemporal_store(v, q); else *q = v;
+        }
+    }
+}
+// E consecutive bf16 as fp32 (8 / 16-byte aligned for E = 4 / 8).
+template <int E>
+__device__ __forceinline__ void ld_bf16(const uint16_t *p, float (&x)[E]) {
+    if constexpr (E == 1) {
+        x[0] = bf16_bits_to_float(__builtin_nontemporal_load(p));
+    } else {
+        uint32_t w[E / 2];
+        if constexpr (E == 4) {
+            const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+            w[0] = v.x; w[1] = v.y;
+        } else {
+            const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+            w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) x[e] = bf16_bits_to_float((w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
+    }
+}
+// E values rounded to bf16 and stored (8 / 16-byte aligned for E = 4 / 8).
+template <int E>
+__device__ __forceinline__ void st_bf16(uint16_t *p, const float (&x)[E]) {
+    if constexpr (E == 1) {
+        __builtin_nontemporal_store((uint16_t)rne_bf16_bits(x[0]), p);
+    } else if constexpr (E == 4) {
+        __builtin_nontemporal_store(u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])},
+                                    reinterpret_cast<u32x2 *>(p));
+    } else {
+        __builtin_nontemporal_store(u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                          pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])},
+                                    reinterpret_cast<u32x4 *>(p));
+    }
+}
 
 // Fixed-order sum over the workgroup: butterfly within each 64-wide wave,
 // then the four wave sums in order.
@@ -84,25 +150,21 @@ __global__ __launch_bounds__(kThreads) void muon_momentum_kernel(
     float sumsq = 0.0f;
     const int64_t base = (int64_t)blockIdx.x * kChunk;
     for (int s = 0; s < kSweeps; ++s) {
-        const int64_t i0 = base + ((int64_t)s * kThreads + threadIdx.x) * kPerThread;
+        const int64_t i0 = base + ((int64_t)s * kThreads + threadIdx.x) * kPreEPT;
         if (i0 >= a.count) break;
-        if (a.vec && i0 + kPerThread <= a.count) {
-            f32x4 *M = reinterpret_cast<f32x4 *>(mom + i0);
-            u32x4 gw = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(grad + i0));
-            f32x4 m0 = M[0], m1 = M[1];
-            float m[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-            uint32_t gb[4] = {gw.x, gw.y, gw.z, gw.w};
+        if (a.vec && i0 + kPreEPT <= a.count) {
+            float m[kPreEPT], g[kPreEPT];
+            ld_f32<kPreEPT, false>(mom + i0, m);
+            ld_bf16<kPreEPT>(grad + i0, g);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float g = bf16_bits_to_float((gb[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
+            for (int e = 0; e < kPreEPT; ++e) {
                 float u;
-                momentum_update(m[e], g, u, a);
+                momentum_update(m[e], g[e], u, a);
                 sumsq += u * u;
             }
-            M[0] = f32x4{m[0], m[1], m[2], m[3]};
-            M[1] = f32x4{m[4], m[5], m[6], m[7]};
+            st_f32<kPreEPT, false>(mom + i0, m);
         } else {
-            for (int e = 0; e < kPerThread && i0 + e < a.count; ++e) {
+            for (int e = 0; e < kPreEPT && i0 + e < a.count; ++e) {
                 float g = bf16_bits_to_float(grad[i0 + e]);
                 float m = mom[i0 + e], u;
                 momentum_update(m, g, u, a);
@@ -117,13 +179,13 @@ __global__ __launch_bounds__(kThreads) void muon_momentum_kernel(
 
 // One workgroup per matrix: s = 1 / (||U||_F + eps) from the partials.
 __global__ __launch_bounds__(kThreads) void muon_norm_kernel(
-    float *__restrict__ partials, int32_t norm_blocks, float *__restrict__ scale,
+    float *__restrict__ partials, int32_t norm_blocks, int32_t count, float *__restrict__ scale,
     float ns_eps) {
     __shared__ float lds4[4];
     const int b = blockIdx.x;
     const float *p = partials + (int64_t)b * norm_blocks;
     float s = 0.0f;
-    for (int i = threadIdx.x; i < norm_blocks; i += kThreads) s += p[i];
+    for (int i = threadIdx.x; i < count; i += kThreads) s += p[i];
     float total = block_sum(s, lds4);
     if (threadIdx.x == 0) scale[b] = 1.0f / (__builtin_sqrtf(total) + ns_eps);
 }
@@ -232,6 +294,88 @@ __global__ __launch_bounds__(kThreads) void muon_scale_kernel(
     }
 }
 
+// Pass 1 of a call that runs Newton-Schulz iterations, fused with the write
+// of its input: one workgroup per 64 x 64 tile of the padded
+// stored-orientation matrix updates M there, writes bf16(U) (not yet scaled)
+// in the Newton-Schulz orientation -- straight out, or through the LDS tile
+// when the matrix is stored transposed -- with zeros in the padding, and
+// leaves the tile's sum of U^2 (a fixed order: each thread's 16 elements,
+// then the workgroup sum) as a partial.  The first iteration applies
+// s = 1 / (||U||_F + eps) to the products it forms from this X (s^2 to X X^T,
+// s to B X), so X0 = s U is never stored: 12 bytes per element in all,
+// against 10 + 8 for pass 1 and a separate scaling pass.
+__global__ __launch_bounds__(kThreads) void muon_momentum_x_kernel(
+    MuonPtrs ptrs, ScaleArgs a, float *__restrict__ partials, int32_t norm_blocks,
+    uint16_t *__restrict__ x_base, int64_t x_stride) {
+    __shared__ uint16_t tile[kTile][kTile + 2];
+    __shared__ float lds4[4];
+    const int b = blockIdx.y;
+    const int tr = blockIdx.x / a.tiles_c, tc = blockIdx.x % a.tiles_c;
+    float *__restrict__ mom = ptrs.momentum[b];
+    const uint16_t *__restrict__ grad = ptrs.grad[b];
+    uint16_t *x = x_base + (int64_t)b * x_stride;
+    PreArgs pa{0, 0, a.mu, a.omm, a.nesterov, nullptr};
+    device_momentum(a.dev, pa.mu, pa.omm);
+    float sumsq = 0.0f;
+
+    // 64 rows x 8 groups of 8 columns = 512 groups; two per thread
+    for (int q = 0; q < 2; ++q) {
+        const int grp = threadIdx.x + q * kThreads;
+        const int lr = grp >> 3, lc = (grp & 7) * 8;
+        const int r = tr * kTile + lr, c0 = tc * kTile + lc;
+        float us[8];
+        if (a.vec && r < a.rows && c0 + 8 <= a.cols) {
+            const int64_t i = (int64_t)r * a.cols + c0;
+            float m[8], g[8];
+            ld_f32<8, true>(mom + i, m);  // read once, next by the next step
+            ld_bf16<8>(grad + i, g);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) momentum_update(m[e], g[e], us[e], pa);
+            st_f32<8, true>(mom + i, m);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int c = c0 + e;
+                float u = 0.0f;
+                if (r < a.rows && c < a.cols) {
+                    const int64_t i = (int64_t)r * a.cols + c;
+                    float m = mom[i];
+                    momentum_update(m, bf16_bits_to_float(grad[i]), u, pa);
+                    mom[i] = m;
+                }
+                us[e] = u;
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sumsq += us[e] * us[e];
+        const uint32_t packed[4] = {pack_bf16x2(us[0], us[1]), pack_bf16x2(us[2], us[3]),
+                                    pack_bf16x2(us[4], us[5]), pack_bf16x2(us[6], us[7])};
+        if (!a.transposed)
+            *reinterpret_cast<u32x4 *>(x + (int64_t)r * a.np + c0) =
+                u32x4{packed[0], packed[1], packed[2], packed[3]};
+        else
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                tile[lr][lc + e] = (uint16_t)((packed[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
+    }
+    const float total = block_sum(sumsq, lds4);  // its barriers also order the tile writes
+    if (threadIdx.x == 0) partials[(int64_t)b * norm_blocks + blockIdx.x] = total;
+    if (!a.transposed) return;  // uniform
+    // transposed: X row = stored column, X columns = stored rows
+    for (int q = 0; q < 2; ++q) {
+        const int grp = threadIdx.x + q * kThreads;
+        const int lc = grp >> 3, lr0 = (grp & 7) * 8;
+        uint32_t packed[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2)
+            packed[e >> 1] = (uint32_t)tile[lr0 + e][lc] | ((uint32_t)tile[lr0 + e + 1][lc] << 16);
+        const int64_t orow = (int64_t)tc * kTile + lc;
+        const int64_t ocol = (int64_t)tr * kTile + lr0;
+        *reinterpret_cast<u32x4 *>(x + orow * a.np + ocol) =
+            u32x4{packed[0], packed[1], packed[2], packed[3]};
+    }
+}
+
 struct PostArgs {
     int32_t rows, cols;
     int32_t vec;
@@ -254,38 +398,28 @@ __global__ __launch_bounds__(kThreads) void muon_post_kernel(
         a.decay = (float)(1.0 - lr * wd);
         a.step_lr = (float)(lr * a.scale);
     }
-    const int64_t count = (int64_t)a.rows * a.cols;
-    const int64_t i0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * kPerThread;
+    const uint32_t count = (uint32_t)a.rows * (uint32_t)a.cols;  // < 2^31
+    const uint32_t i0 = (blockIdx.x * kThreads + threadIdx.x) * kPostEPT;
     if (i0 >= count) return;
     float *__restrict__ P = ptrs.master[b];
     uint16_t *__restrict__ W = ptrs.weight[b];
     const uint16_t *__restrict__ O = o_base + (int64_t)b * a.o_stride;
-    if (a.vec && i0 + kPerThread <= count) {
-        // cols % 8 == 0: the 8 elements share one row
-        const int64_t r = i0 / a.cols, c = i0 - r * a.cols;
-        u32x4 ow = *reinterpret_cast<const u32x4 *>(O + r * a.o_ld + c);
-        f32x4 *Pv = reinterpret_cast<f32x4 *>(P + i0);
-        f32x4 p0 = __builtin_nontemporal_load(Pv), p1 = __builtin_nontemporal_load(Pv + 1);
-        float p[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-        uint32_t ob[4] = {ow.x, ow.y, ow.z, ow.w};
+    if (a.vec && i0 + kPostEPT <= count) {
+        // cols % 8 == 0: the elements share one row
+        float p[kPostEPT], o[kPostEPT];
+        ld_f32<kPostEPT, true>(P + i0, p);
+        const uint32_t r = i0 / (uint32_t)a.cols, c = i0 - r * (uint32_t)a.cols;
+        ld_bf16<kPostEPT>(O + (int64_t)r * a.o_ld + c, o);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float o = bf16_bits_to_float((ob[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
-            p[e] = p[e] * a.decay - a.step_lr * o;
-        }
-        __builtin_nontemporal_store(f32x4{p[0], p[1], p[2], p[3]}, Pv);
-        __builtin_nontemporal_store(f32x4{p[4], p[5], p[6], p[7]}, Pv + 1);
-        if (W) {
-            u32x4 w{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                    pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-            __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(W + i0));
-        }
+        for (int e = 0; e < kPostEPT; ++e) p[e] = p[e] * a.decay - a.step_lr * o[e];
+        st_f32<kPostEPT, true>(P + i0, p);
+        if (W) st_bf16<kPostEPT>(W + i0, p);
         return;
     }
-    for (int e = 0; e < kPerThread && i0 + e < count; ++e) {
-        const int64_t i = i0 + e;
-        const int64_t r = i / a.cols, c = i - r * a.cols;
-        float o = bf16_bits_to_float(O[r * a.o_ld + c]);
+    for (uint32_t e = 0; e < (uint32_t)kPostEPT && i0 + e < count; ++e) {
+        const uint32_t i = i0 + e;
+        const uint32_t r = i / (uint32_t)a.cols, c = i - r * (uint32_t)a.cols;
+        float o = bf16_bits_to_float(O[(int64_t)r * a.o_ld + c]);
         float p = P[i] * a.decay - a.step_lr * o;
         P[i] = p;
         if (W) W[i] = (uint16_t)rne_bf16_bits(p);
@@ -487,28 +621,42 @@ hipError_t launch_ns_health_total(float *health, int32_t nmat, hipStream_t strea
 
 int32_t muon_norm_blocks(int64_t count) { return (int32_t)((count + kChunk - 1) / kChunk); }
 
+int32_t muon_pre_tiles(const MuonGeom &g) {
+    const int srows = g.transposed ? g.np : g.mp;
+    const int scols = g.transposed ? g.mp : g.np;
+    return (srows / kTile) * (scols / kTile);
+}
+
 hipError_t launch_muon_pre(const MuonGeom &g, const MuonPtrs &ptrs, float mu,
                            int32_t nesterov, float ns_eps, char *ws,
-                           const MuonWorkspace &L, bool want_xt, const float *dev,
+                           const MuonWorkspace &L, bool no_iterations, const float *dev,
                            hipStream_t stream) {
     const int64_t count = (int64_t)g.rows * g.cols;
     const float omm = (float)(1.0 - (double)mu);
     bool vec = (count % 8) == 0;
     for (int b = 0; b < g.batch; ++b)
         vec = vec && aligned16(ptrs.momentum[b]) && aligned16(ptrs.grad[b]);
-    PreArgs pa{(int32_t)count, vec ? 1 : 0, mu, omm, nesterov, dev};
     float *partials = reinterpret_cast<float *>(ws + L.partials);
-    float *scale = partials + (int64_t)g.batch * g.norm_blocks;
-    hipLaunchKernelGGL(muon_momentum_kernel, dim3(g.norm_blocks, g.batch), dim3(kThreads),
+    float *scale = muon_scale_ptr(ws, g, L);
+    // stored-orientation padded extent
+    const int scols = g.transposed ? g.mp : g.np;
+    const int tiles = muon_pre_tiles(g);
+    ScaleArgs sa{g.rows, g.cols, g.transposed, g.mp, g.np, scols / kTile, mu, omm, nesterov,
+                 (vec && g.cols % 8 == 0) ? 1 : 0, dev, (no_iterations && g.transposed) ? 1 : 0};
+    if (!no_iterations) {
+        hipLaunchKernelGGL(muon_momentum_x_kernel, dim3(tiles, g.batch), dim3(kThreads), 0,
+                           stream, ptrs, sa, partials, g.norm_blocks,
+                           reinterpret_cast<uint16_t *>(ws + L.x), (int64_t)(L.x_stride / 2));
+        hipLaunchKernelGGL(muon_norm_kernel, dim3(g.batch), dim3(kThreads), 0, stream, partials,
+                           g.norm_blocks, tiles, scale, ns_eps);
+        return hipGetLastError();
+    }
+    const int32_t chunks = muon_norm_blocks(count);
+    PreArgs pa{(int32_t)count, vec ? 1 : 0, mu, omm, nesterov, dev};
+    hipLaunchKernelGGL(muon_momentum_kernel, dim3(chunks, g.batch), dim3(kThreads),
                        0, stream, ptrs, pa, partials, g.norm_blocks);
     hipLaunchKernelGGL(muon_norm_kernel, dim3(g.batch), dim3(kThreads), 0, stream, partials,
-                       g.norm_blocks, scale, ns_eps);
-    // stored-orientation padded extent
-    const int srows = g.transposed ? g.np : g.mp;
-    const int scols = g.transposed ? g.mp : g.np;
-    ScaleArgs sa{g.rows, g.cols, g.transposed, g.mp, g.np, scols / kTile, mu, omm, nesterov,
-                 (vec && g.cols % 8 == 0) ? 1 : 0, dev, (want_xt && g.transposed) ? 1 : 0};
-    const int tiles = (srows / kTile) * (scols / kTile);
+                       g.norm_blocks, chunks, scale, ns_eps);
     hipLaunchKernelGGL(muon_scale_kernel, dim3(tiles, g.batch), dim3(kThreads), 0, stream,
                        ptrs, sa, scale, reinterpret_cast<uint16_t *>(ws + L.x),
                        reinterpret_cast<uint16_t *>(ws + L.xt1),
@@ -527,7 +675,7 @@ hipError_t launch_muon_post(const MuonGeom &g, const MuonPtrs &ptrs,
               (ptrs.weight[b] == nullptr || aligned16(ptrs.weight[b]));
     PostArgs pa{g.rows, g.cols, vec ? 1 : 0, decay, step_lr, o_ld, (int64_t)(o_stride / 2),
                 reject, dev, scale};
-    const int64_t units = (count + kPerThread - 1) / kPerThread;
+    const int64_t units = (count + kPostEPT - 1) / kPostEPT;
     const int64_t blocks = (units + kThreads - 1) / kThreads;
     hipLaunchKernelGGL(muon_post_kernel, dim3((uint32_t)blocks, g.batch), dim3(kThreads), 0,
                        stream, ptrs, pa, o_base);

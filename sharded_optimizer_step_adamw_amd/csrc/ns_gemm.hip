@@ -74,6 +74,10 @@ struct NsGroup {
     int64_t d_stride;            // floats between matrices of dA / dB
     uint16_t *CT;                // GEMM_BX: X'^T, or NULL (not wanted)
     int64_t ct_stride;
+    // First iteration: X holds bf16(U) and the matrix's pre-scale s is
+    // applied here, s^2 to X X^T and s to B X (one float per matrix); NULL
+    // otherwise.
+    const float *xs;
 };
 
 struct NsLaunch {
@@ -197,6 +201,16 @@ __device__ __forceinline__ void epilogue(const NsGroup &args, float ca, float cb
     const float *dIn = args.dIn + batch * args.d_stride;
     float *dOut = args.dOut + batch * args.d_stride;
     const int col = lane & 15, quad = lane >> 4;
+    if (MODE == kSyrkXXT && args.xs != nullptr) {
+        // first iteration: A = (s U)(s U)^T from the products of U
+        const float s = args.xs[batch], s2 = s * s;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[i][j][r] *= s2;
+    }
     // transposing read: lane 4q' + p of a 16-lane group addresses row +q',
     // columns 4p .. 4p+3 of a 4 x 16 block; lane i gets rows +0..+3 of column i
     const int tq = (lane >> 2) & 3, tp = lane & 3;
@@ -768,6 +782,16 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_bx_kernel(NsLaunch L)
             (void *)(G.C + cu.batch * G.c_stride + (int64_t)R0 * ldc + C0), (short)0, WTM * ldc * 2,
             0x00020000);
         const int vo = (fr * ldc + fh * 4) * 2;
+        if (G.xs != nullptr) {
+            // first iteration: X' = (a + dB) (s U) + Boff (s U) from the products of U
+            const float s = G.xs[cu.batch];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[i][j][r] *= s;
+        }
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -951,6 +975,7 @@ NsGroup product_group(int mode, const NsGroupRef &r, int iter, bool last, int ti
         s.CT = (last && g.transposed) ? XTout : nullptr; s.ct_stride = xs; s.ldct = g.mp;
         s.dIn = dB; s.dOut = dB;
     }
+    if (iter == 0 && mode != kSyrkAA) s.xs = muon_scale_ptr(ws, g, L) + b0;
     // matrices from b0 on
     s.P += b0 * s.p_stride;
     s.Q += b0 * s.q_stride;

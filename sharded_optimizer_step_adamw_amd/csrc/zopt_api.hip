@@ -72,7 +72,8 @@ MuonGeom muon_geometry(int32_t batch, int64_t rows, int64_t cols) {
     // takes 128 x 128 tiles (four times as many) for those two products
     const int64_t t256 = g.mp / 256;
     if (g.tile == 256 && (int64_t)batch * (t256 * (t256 + 1) / 2) < 128) g.tile = 128;
-    g.norm_blocks = muon_norm_blocks(rows * cols);
+    const int32_t chunks = muon_norm_blocks(rows * cols), tiles = muon_pre_tiles(g);
+    g.norm_blocks = chunks > tiles ? chunks : tiles;
     g.health_blocks = ns_health_blocks((int64_t)g.m * g.np);
     return g;
 }

@@ -105,7 +105,7 @@ struct MuonGeom {
     int32_t mp, np;
     int32_t tile;        // square output tile of the Newton-Schulz products X X^T and A A
     int32_t tile_bx;     // and of B X
-    int32_t norm_blocks; // workgroups (and norm partials) per matrix, pre-pass 1
+    int32_t norm_blocks; // norm partials per matrix (room for either form of pass 1)
     int32_t health_blocks;  // workgroups (and partials) per matrix of the health pass
 };
 
@@ -135,12 +135,24 @@ enum : int { kDevLr = 0, kDevMomentum = 1, kDevWeightDecay = 2, kDevScalars = 3 
 
 // dev: device scalars (mu is read there and omm formed from it) or NULL (mu
 // as given).
-// Writes X0 to the x region, and X0^T to xt1 as well when want_xt and the
-// matrices are stored transposed (the result of a call with no iterations).
+// Steps the momentum and forms s = 1 / (||U||_F + eps) per matrix (at
+// muon_scale_ptr).  With iterations to follow, the x region receives
+// bf16(U) in the Newton-Schulz orientation and the first iteration applies
+// s; with no_iterations, X0 = bf16(U s) itself (the call's result), and X0^T
+// in xt1 as well for matrices stored transposed.
 hipError_t launch_muon_pre(const MuonGeom &g, const MuonPtrs &ptrs, float mu,
                            int32_t nesterov, float ns_eps, char *ws,
-                           const MuonWorkspace &L, bool want_xt, const float *dev,
+                           const MuonWorkspace &L, bool no_iterations, const float *dev,
                            hipStream_t stream);
+
+// 64 x 64 tiles of the padded stored-orientation matrix (the fused pass 1's
+// workgroups and norm partials per matrix).
+int32_t muon_pre_tiles(const MuonGeom &g);
+
+// The per-matrix pre-scale s of a group, after its norm partials.
+inline float *muon_scale_ptr(char *ws, const MuonGeom &g, const MuonWorkspace &L) {
+    return reinterpret_cast<float *>(ws + L.partials) + (int64_t)g.batch * g.norm_blocks;
+}
 
 // reject: per-matrix flags (non-zero: leave that matrix untouched) or NULL.
 // dev: device scalars, from which decay and step_lr = lr * scale are formed
