@@ -49,18 +49,19 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 # recorded in profiles/.  Reported only while the kernel source is the one the
 # counters were taken on.
 MEASURED_TRAFFIC = {
+    # the full buckets (bucket-grid launch) and the last bucket: 3.500 GB read, 3.500 GB written
     "adamw_shard": dict(source="sharded_optimizer_step_adamw_amd/csrc/adamw_shard.hip",
-                        sha256="7700ae2a639bcc25367d613767f5358e3cf6fd68c9ed57b1a25e6a6842b9f4a0",
+                        sha256="eb634639dcc4f5fb057abadb322544f78356e888bfa3d815b4dd1ac93d32ea9d",
                         bytes_per_launch=7.000e9,
-                        profile="profiles/adamw_shard_kernel_zero2_2b_rank3.md"),
-    # one Newton-Schulz iteration of the 72 GPT-2-small matrices: the three launches'
-    # FETCH_SIZE + WRITE_SIZE, calibrated (0.7017 GB read, 0.3405 GB written)
+                        profile="profiles/adamw_bucket_grid_kernel_zero2_2b_rank3.md"),
+    # one Newton-Schulz iteration of the 72 GPT-2-small matrices: the four launches'
+    # FETCH_SIZE + WRITE_SIZE, calibrated (0.7145 GB read, 0.3403 GB written)
     "ns_iteration_gpt2": dict(source="sharded_optimizer_step_adamw_amd/csrc/ns_gemm.hip",
-                              sha256="6ec693d93f9f137f712755e35c490122ee49142c3a45a617f77b64b6c166ff26",
-                              bytes_per_launch=1.0422e9,
+                              sha256="01666720cdd0cbb5b49cfdb132387ed64e374f3ff78b48c660c346babc0f755b",
+                              bytes_per_launch=1.0548e9,
                               profile="profiles/ns_gemm_gpt2_small_step.md"),
     "grad_sq_norm": dict(source="sharded_optimizer_step_adamw_amd/csrc/adamw_shard.hip",
-                         sha256="7700ae2a639bcc25367d613767f5358e3cf6fd68c9ed57b1a25e6a6842b9f4a0",
+                         sha256="eb634639dcc4f5fb057abadb322544f78356e888bfa3d815b4dd1ac93d32ea9d",
                          bytes_per_launch=0.5004e9,
                          profile="profiles/grad_sq_norm_kernel_zero2_2b_rank3.md"),
 }
@@ -215,15 +216,18 @@ def bench_step(torch, z, timer, dev, K, W):
     ms = timer.run(step, K)
 
     # the dominant kernels: one Newton-Schulz iteration of all 72 matrices is
-    # three launches (X X^T, A A with its epilogue, B X with its epilogue, each
-    # over every group); its time is the difference of the Muon call with 5
-    # and with 0 iterations, over 5
+    # four launches (X X^T and A A with its epilogue over every group, B X with
+    # its epilogue on 256-tiles and its short tail on 128-tiles); its time is
+    # the difference of the Muon call with 5 and with 1 iteration, over 4 (the
+    # two calls take the same pre/post path)
     t5 = timer.run(lambda _: muon_call(z, wm, groups, workspace, 5), K)
+    t1 = timer.run(lambda _: muon_call(z, wm, groups, workspace, 1), K)
     t0 = timer.run(lambda _: muon_call(z, wm, groups, workspace, 0), K)
-    iter_ms = (t5 - t0) / 5
+    iter_ms = (t5 - t1) / 4
     iter_flops = sum(g["count"] * ns_flops(min(g["rows"], g["cols"]), max(g["rows"], g["cols"]), 1)
                      for g in groups)
-    per_group = dict(muon_call_ms=round(t5, 4), pre_post_ms=round(t0, 4),
+    per_group = dict(muon_call_ms=round(t5, 4), one_iteration_call_ms=round(t1, 4),
+                     pre_post_ms=round(t1 - iter_ms, 4), zero_iteration_call_ms=round(t0, 4),
                      groups=[dict(shape=[g["rows"], g["cols"]], count=g["count"]) for g in groups],
                      ns_health=ns_health_check(torch, z, timer, wm, groups, workspace, K, t5))
     adamw_bytes = 28 * n
@@ -255,10 +259,13 @@ def bench_adamw(torch, z, timer, dev, K, W, clip_leg=False):
     del s
     torch.cuda.empty_cache()
     gbs = 28 * sl / ms / 1e6
-    roof = dict(kernel="adamw_shard_kernel (one launch per step)", bound="hbm",
+    roof = dict(kernel=("zopt_adamw_shard_step: adamw_bucket_grid_kernel over the 59 full "
+                        "buckets + adamw_shard_kernel over the short last one (two launches "
+                        "per step, timed together)"), bound="hbm",
                 achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=round(gbs / HBM_PEAK_GBS, 4), traffic=measured_traffic("adamw_shard"),
-                algorithmic_bytes_per_launch=28 * sl, avg_launch_ms=round(ms, 4))
+                algorithmic_bytes_per_launch=28 * sl, avg_launch_ms=round(ms, 4),
+                launches_per_step=2)
     out = dict(workload="zero2 flat AdamW shard: N=2.0e9, bucket 1<<25, world 8, rank 3",
                shard_len=sl, algorithmic_bytes_per_step=28 * sl, ms_per_step=round(ms, 4),
                gbs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4), steps=K,
@@ -318,8 +325,11 @@ def bench_ns(torch, z, timer, dev, K, W, w=None):
                                             w.ns_steps) for g in groups)
     timer.run(lambda _: muon_call(z, w, groups, workspace, w.ns_steps), max(1, W))
     t5 = timer.run(lambda _: muon_call(z, w, groups, workspace, w.ns_steps), K)
-    t0 = timer.run(lambda _: muon_call(z, w, groups, workspace, 0), K)
-    ns_ms, call_ms = t5 - t0, t5
+    t1 = timer.run(lambda _: muon_call(z, w, groups, workspace, 1), K)
+    # a 1-iteration call takes the same pre/post path as the 5-iteration one
+    # (a call with no iterations takes another: it writes X0 itself), so
+    # their difference is 4 iterations
+    ns_ms, call_ms = (t5 - t1) * w.ns_steps / (w.ns_steps - 1), t5
     rows = [dict(shape=[g["rows"], g["cols"]], count=g["count"]) for g in groups]
     health = ns_health_check(torch, z, timer, w, groups, workspace, K, t5)
     del groups, workspace
@@ -528,12 +538,12 @@ def main():
         tf = res_step["ns_iter_flops"] / res_step["ns_iter_ms"] / 1e9
         out.update(value=round(res_step["ms"], 4), unit="ms per optimizer step")
         roof = dict(
-            kernel=("Newton-Schulz iteration: ns_gemm_kernel X X^T and A A (128 x 128 tiles) "
-                    "+ ns_bx_kernel B X (256 x 256 tiles, persistent), one launch each over "
-                    "all 72 matrices"),
+            kernel=("Newton-Schulz iteration: ns_gemm_kernel X X^T and A A (128 x 128 tiles, "
+                    "one launch each over all 72 matrices) + ns_bx_kernel B X (persistent: "
+                    "256 x 256 tiles over 71 matrices, 128 x 128 tiles over the last one)"),
             bound="mfma", achieved=round(tf, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
             frac=round(tf / BF16_PEAK_TFLOPS, 4), traffic=measured_traffic("ns_iteration_gpt2"),
-            traffic_unit="HBM bytes per iteration (3 launches)",
+            traffic_unit="HBM bytes per iteration (4 launches)",
             algorithmic_flops_per_unit=res_step["ns_iter_flops"],
             avg_unit_ms=round(res_step["ns_iter_ms"], 4))
     else:
