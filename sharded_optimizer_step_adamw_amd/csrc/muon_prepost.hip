@@ -376,6 +376,71 @@ __global__ __launch_bounds__(kThreads) void muon_momentum_x_kernel(
     }
 }
 
+// The same pass for a matrix stored in the Newton-Schulz orientation (rows
+// <= cols): a flat stream of 2048 consecutive stored elements per workgroup,
+// 8 per thread, M updated in place and bf16(U) written to X's row at the
+// padded stride np, one fixed-order partial of U^2 per workgroup.  (The
+// 64 x 64 tiles above read 64 row pieces of 256 bytes per workgroup; this
+// reads whole 8 KiB runs.)  The padding of X is zeroed by muon_x_pad_kernel.
+__global__ __launch_bounds__(kThreads) void muon_momentum_xflat_kernel(
+    MuonPtrs ptrs, ScaleArgs a, float *__restrict__ partials, int32_t norm_blocks,
+    uint16_t *__restrict__ x_base, int64_t x_stride) {
+    __shared__ float lds4[4];
+    const int b = blockIdx.y;
+    float *__restrict__ mom = ptrs.momentum[b];
+    const uint16_t *__restrict__ grad = ptrs.grad[b];
+    uint16_t *x = x_base + (int64_t)b * x_stride;
+    PreArgs pa{0, 0, a.mu, a.omm, a.nesterov, nullptr};
+    device_momentum(a.dev, pa.mu, pa.omm);
+    const uint32_t count = (uint32_t)a.rows * (uint32_t)a.cols;  // < 2^31
+    const uint32_t i0 = (blockIdx.x * kThreads + threadIdx.x) * 8;
+    float sumsq = 0.0f;
+    if (a.vec && i0 + 8 <= count) {
+        // cols % 8 == 0: the 8 elements share one row
+        float m[8], g[8], us[8];
+        ld_f32<8, true>(mom + i0, m);
+        ld_bf16<8>(grad + i0, g);
+        const uint32_t r = i0 / (uint32_t)a.cols, c = i0 - r * (uint32_t)a.cols;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) momentum_update(m[e], g[e], us[e], pa);
+        st_f32<8, true>(mom + i0, m);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sumsq += us[e] * us[e];
+        __builtin_nontemporal_store(
+            u32x4{pack_bf16x2(us[0], us[1]), pack_bf16x2(us[2], us[3]), pack_bf16x2(us[4], us[5]),
+                  pack_bf16x2(us[6], us[7])},
+            reinterpret_cast<u32x4 *>(x + (int64_t)r * a.np + c));
+    } else {
+        for (uint32_t e = 0; e < 8 && i0 + e < count; ++e) {
+            const uint32_t i = i0 + e, r = i / (uint32_t)a.cols, c = i - r * (uint32_t)a.cols;
+            float m = mom[i], u;
+            momentum_update(m, bf16_bits_to_float(grad[i]), u, pa);
+            mom[i] = m;
+            sumsq += u * u;
+            x[(int64_t)r * a.np + c] = (uint16_t)rne_bf16_bits(u);
+        }
+    }
+    const float total = block_sum(sumsq, lds4);
+    if (threadIdx.x == 0) partials[(int64_t)b * norm_blocks + blockIdx.x] = total;
+}
+
+// Zeros of X's padding for the flat pass: columns [cols, np) of rows
+// [0, rows), then rows [rows, mp) whole; `pad` elements per matrix.
+__global__ __launch_bounds__(kThreads) void muon_x_pad_kernel(
+    int32_t rows, int32_t cols, int32_t np, int64_t pad, uint16_t *__restrict__ x_base,
+    int64_t x_stride) {
+    const int64_t k = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (k >= pad) return;
+    uint16_t *x = x_base + (int64_t)blockIdx.y * x_stride;
+    const int64_t wpad = np - cols, side = (int64_t)rows * wpad;
+    if (k < side) {
+        const int64_t r = k / wpad;
+        x[r * np + cols + (k - r * wpad)] = 0;
+    } else {
+        x[(int64_t)rows * np + (k - side)] = 0;
+    }
+}
+
 struct PostArgs {
     int32_t rows, cols;
     int32_t vec;
@@ -643,15 +708,28 @@ hipError_t launch_muon_pre(const MuonGeom &g, const MuonPtrs &ptrs, float mu,
     const int tiles = muon_pre_tiles(g);
     ScaleArgs sa{g.rows, g.cols, g.transposed, g.mp, g.np, scols / kTile, mu, omm, nesterov,
                  (vec && g.cols % 8 == 0) ? 1 : 0, dev, (no_iterations && g.transposed) ? 1 : 0};
+    const int32_t chunks = muon_norm_blocks(count);
     if (!no_iterations) {
-        hipLaunchKernelGGL(muon_momentum_x_kernel, dim3(tiles, g.batch), dim3(kThreads), 0,
-                           stream, ptrs, sa, partials, g.norm_blocks,
-                           reinterpret_cast<uint16_t *>(ws + L.x), (int64_t)(L.x_stride / 2));
+        uint16_t *x = reinterpret_cast<uint16_t *>(ws + L.x);
+        const int64_t xs = (int64_t)(L.x_stride / 2);
+        int32_t parts = tiles;
+        if (g.transposed) {
+            hipLaunchKernelGGL(muon_momentum_x_kernel, dim3(tiles, g.batch), dim3(kThreads), 0,
+                               stream, ptrs, sa, partials, g.norm_blocks, x, xs);
+        } else {
+            hipLaunchKernelGGL(muon_momentum_xflat_kernel, dim3(chunks, g.batch), dim3(kThreads),
+                               0, stream, ptrs, sa, partials, g.norm_blocks, x, xs);
+            parts = chunks;
+            const int64_t pad = (int64_t)g.rows * (g.np - g.cols) + (int64_t)(g.mp - g.rows) * g.np;
+            if (pad > 0)
+                hipLaunchKernelGGL(muon_x_pad_kernel,
+                                   dim3((uint32_t)((pad + kThreads - 1) / kThreads), g.batch),
+                                   dim3(kThreads), 0, stream, g.rows, g.cols, g.np, pad, x, xs);
+        }
         hipLaunchKernelGGL(muon_norm_kernel, dim3(g.batch), dim3(kThreads), 0, stream, partials,
-                           g.norm_blocks, tiles, scale, ns_eps);
+                           g.norm_blocks, parts, scale, ns_eps);
         return hipGetLastError();
     }
-    const int32_t chunks = muon_norm_blocks(count);
     PreArgs pa{(int32_t)count, vec ? 1 : 0, mu, omm, nesterov, dev};
     hipLaunchKernelGGL(muon_momentum_kernel, dim3(chunks, g.batch), dim3(kThreads),
                        0, stream, ptrs, pa, partials, g.norm_blocks);
