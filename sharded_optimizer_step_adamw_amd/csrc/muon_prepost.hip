@@ -295,22 +295,26 @@ __global__ __launch_bounds__(kThreads) void muon_scale_kernel(
 }
 
 // Pass 1 of a call that runs Newton-Schulz iterations, fused with the write
-// of its input: one workgroup per 64 x 64 tile of the padded
-// stored-orientation matrix updates M there, writes bf16(U) (not yet scaled)
-// in the Newton-Schulz orientation -- straight out, or through the LDS tile
-// when the matrix is stored transposed -- with zeros in the padding, and
-// leaves the tile's sum of U^2 (a fixed order: each thread's 16 elements,
+// of its input, for a matrix stored transposed: one workgroup per T x T tile
+// of the padded stored-orientation matrix (T = 128 where both padded sides
+// allow, else 64) updates M there, writes bf16(U) (not yet scaled) in the
+// Newton-Schulz orientation through the LDS tile, with zeros in the padding,
+// and leaves the tile's sum of U^2 (a fixed order: each thread's elements,
 // then the workgroup sum) as a partial.  The first iteration applies
 // s = 1 / (||U||_F + eps) to the products it forms from this X (s^2 to X X^T,
 // s to B X), so X0 = s U is never stored: 12 bytes per element in all,
 // against 10 + 8 for pass 1 and a separate scaling pass.
+template <int T>
 __global__ __launch_bounds__(kThreads) void muon_momentum_x_kernel(
     MuonPtrs ptrs, ScaleArgs a, float *__restrict__ partials, int32_t norm_blocks,
     uint16_t *__restrict__ x_base, int64_t x_stride) {
-    __shared__ uint16_t tile[kTile][kTile + 2];
+    constexpr int GPR = T / 8;                  // 8-element groups per tile row
+    constexpr int PER = T * GPR / kThreads;     // groups per thread
+    __shared__ uint16_t tile[T][T + 2];
     __shared__ float lds4[4];
     const int b = blockIdx.y;
-    const int tr = blockIdx.x / a.tiles_c, tc = blockIdx.x % a.tiles_c;
+    const int tiles_c = a.transposed ? a.mp / T : a.np / T;  // tiles along the stored columns
+    const int tr = blockIdx.x / tiles_c, tc = blockIdx.x % tiles_c;
     float *__restrict__ mom = ptrs.momentum[b];
     const uint16_t *__restrict__ grad = ptrs.grad[b];
     uint16_t *x = x_base + (int64_t)b * x_stride;
@@ -318,11 +322,11 @@ __global__ __launch_bounds__(kThreads) void muon_momentum_x_kernel(
     device_momentum(a.dev, pa.mu, pa.omm);
     float sumsq = 0.0f;
 
-    // 64 rows x 8 groups of 8 columns = 512 groups; two per thread
-    for (int q = 0; q < 2; ++q) {
+    // T rows x GPR groups of 8 columns; PER per thread
+    for (int q = 0; q < PER; ++q) {
         const int grp = threadIdx.x + q * kThreads;
-        const int lr = grp >> 3, lc = (grp & 7) * 8;
-        const int r = tr * kTile + lr, c0 = tc * kTile + lc;
+        const int lr = grp / GPR, lc = (grp % GPR) * 8;
+        const int r = tr * T + lr, c0 = tc * T + lc;
         float us[8];
         if (a.vec && r < a.rows && c0 + 8 <= a.cols) {
             const int64_t i = (int64_t)r * a.cols + c0;
@@ -362,15 +366,15 @@ __global__ __launch_bounds__(kThreads) void muon_momentum_x_kernel(
     if (threadIdx.x == 0) partials[(int64_t)b * norm_blocks + blockIdx.x] = total;
     if (!a.transposed) return;  // uniform
     // transposed: X row = stored column, X columns = stored rows
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < PER; ++q) {
         const int grp = threadIdx.x + q * kThreads;
-        const int lc = grp >> 3, lr0 = (grp & 7) * 8;
+        const int lc = grp / GPR, lr0 = (grp % GPR) * 8;
         uint32_t packed[4];
 #pragma unroll
         for (int e = 0; e < 8; e += 2)
             packed[e >> 1] = (uint32_t)tile[lr0 + e][lc] | ((uint32_t)tile[lr0 + e + 1][lc] << 16);
-        const int64_t orow = (int64_t)tc * kTile + lc;
-        const int64_t ocol = (int64_t)tr * kTile + lr0;
+        const int64_t orow = (int64_t)tc * T + lc;
+        const int64_t ocol = (int64_t)tr * T + lr0;
         *reinterpret_cast<u32x4 *>(x + orow * a.np + ocol) =
             u32x4{packed[0], packed[1], packed[2], packed[3]};
     }
@@ -713,9 +717,14 @@ hipError_t launch_muon_pre(const MuonGeom &g, const MuonPtrs &ptrs, float mu,
         uint16_t *x = reinterpret_cast<uint16_t *>(ws + L.x);
         const int64_t xs = (int64_t)(L.x_stride / 2);
         int32_t parts = tiles;
-        if (g.transposed) {
-            hipLaunchKernelGGL(muon_momentum_x_kernel, dim3(tiles, g.batch), dim3(kThreads), 0,
-                               stream, ptrs, sa, partials, g.norm_blocks, x, xs);
+        if (g.transposed && g.mp % 128 == 0 && g.np % 128 == 0) {
+            // 128 x 128 tiles: 512-byte runs of M read and 256-byte runs of X written
+            parts = (g.np / 128) * (g.mp / 128);
+            hipLaunchKernelGGL(muon_momentum_x_kernel<128>, dim3(parts, g.batch), dim3(kThreads),
+                               0, stream, ptrs, sa, partials, g.norm_blocks, x, xs);
+        } else if (g.transposed) {
+            hipLaunchKernelGGL(muon_momentum_x_kernel<kTile>, dim3(tiles, g.batch), dim3(kThreads),
+                               0, stream, ptrs, sa, partials, g.norm_blocks, x, xs);
         } else {
             hipLaunchKernelGGL(muon_momentum_xflat_kernel, dim3(chunks, g.batch), dim3(kThreads),
                                0, stream, ptrs, sa, partials, g.norm_blocks, x, xs);
