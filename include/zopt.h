@@ -256,9 +256,12 @@ int64_t zopt_shard_len(int64_t N, int64_t bucket, int32_t world);
  *        g = fp32(grad);  M = mu * M + omm * g;
  *        U = omm * g + mu * M  (nesterov)   or   U = M   (otherwise)
  *      with mu = momentum_beta and omm = fp32(1 - mu) formed in double.
- *   2. Pre-scale: X0 = bf16(U * s), s = 1 / (||U||_F + ns_eps), the norm a
+ *   2. Pre-scale: X0 = s U, s = 1 / (||U||_F + ns_eps), the norm a
  *      fixed-order (run-to-run deterministic) reduction in fp32; X0 is taken
  *      transposed when rows > cols, so X is m x n with m = min(rows, cols).
+ *      With ns_steps = 0, X0 = bf16(U * s) is the result.  Otherwise X0 is
+ *      never stored: the first iteration reads bf16(U) and applies s in fp32
+ *      to its products (s^2 to X X^T, s to B X).
  *   3. ns_steps Newton-Schulz iterations [BluScript trainer source, ShardedMuon
  *      comment block: X <- aX + (bXX' + c(XX')^2)X]:
  *        A = X X^T;  B = b A + c A A;  X = a X + B X

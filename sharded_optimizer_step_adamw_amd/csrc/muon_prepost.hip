@@ -5,13 +5,17 @@
 // gradient; dmuon PR #16, commit "NS CUDA-graph replay": momentum, lr and wd
 // stay in the eager pre/post steps around the fixed-shape Newton-Schulz]:
 //   pass 1  M = mu M + (1-mu) g, U = (1-mu) g + mu M (or U = M); write M,
-//           one fp32 partial sum of U^2 per workgroup            (10 B/elem)
+//           bf16(U) in the Newton-Schulz orientation (zero padding), and
+//           fixed-order partial sums of U^2                      (12 B/elem)
 //   final   per matrix, s = 1 / (sqrt(sum of partials) + eps), the partials
-//           summed in a fixed order (deterministic)
+//           summed in a fixed order (deterministic); the first Newton-Schulz
+//           iteration applies s to its products
+// A call with no iterations returns X0 = bf16(U s) itself, so it runs
+//   pass 1  M and the partials only                              (10 B/elem)
 //   pass 2  recompute U from the new M (bitwise the same U), write
-//           X0 = bf16(U s) in the Newton-Schulz orientation (and its
-//           transpose only when a call with no iterations needs it as the
-//           result), zero-filling the tile padding               (8 B/elem)
+//           X0 = bf16(U s) in the Newton-Schulz orientation and, for a
+//           matrix stored transposed, X0^T, zero-filling the tile padding
+//                                                                 (8 B/elem)
 // Health [BluScript trainer source, per-step report: nsratio, the update's
 // ||O||_F / sqrt(min(rows, cols)), about 1 when healthy, and nsrej, the
 // updates the divergence guard refused for an element above 1000]:
