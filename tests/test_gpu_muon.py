@@ -382,3 +382,56 @@ def test_gpt2_small_one_call():
             wref = oracle.muon_post(P[i], o, f32(w.lr), f32(w.weight_decay), 1)
             np.testing.assert_array_equal(gP[i].cpu().numpy().view(np.uint32), P[i].view(np.uint32))
             np.testing.assert_array_equal(u16(gW[i]), wref)
+
+
+@pytest.mark.parametrize("batch,rows,cols,ns_steps", [
+    (2, 200, 520, 5), (2, 520, 200, 5), (1, 300, 1030, 5), (1, 1030, 300, 5),
+    (1, 1100, 1300, 5), (2, 130, 65, 0), (1, 65, 130, 1),
+])
+def test_workspace_needs_no_initialisation(batch, rows, cols, ns_steps):
+    """The workspace's prior contents do not matter: one filled with 0xFF
+    bytes (NaN in every bf16 and fp32 slot, the Newton-Schulz padding
+    included) gives bit for bit the outputs of a zero-filled one, on ragged
+    shapes of both orientations and all three tile sizes, with and without
+    iterations."""
+    P, M, G = make_inputs(batch, rows, cols, seed=rows + 3 * cols, momentum_nonzero=True)
+    outs = []
+    for fill in (0x00, 0xFF):
+        gP, gM, gG = [dev_f32(p) for p in P], [dev_f32(m) for m in M], [dev_bf16(g) for g in G]
+        gW = [torch.empty((rows, cols), dtype=torch.bfloat16, device=DEV) for _ in range(batch)]
+        ws = torch.full((z.muon_workspace_bytes(batch, rows, cols),), fill, dtype=torch.uint8,
+                        device=DEV)
+        z.muon_step(gP, gM, gG, gW, f32(8e-4), f32(0.95), True, f32(0.1), ns_steps, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append([u16(z.muon_output_view(ws, batch, rows, cols, ns_steps, i))
+                     for i in range(batch)] + [u16(w) for w in gW] +
+                    [t.cpu().numpy().view(np.uint32) for t in gP + gM])
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+    for o in outs[1][:batch]:
+        assert not np.isnan(oracle.bf16_bits_to_f32(o)).any()
+
+
+def test_grouped_workspace_needs_no_initialisation():
+    """The same for a grouped call over both pass-1 forms (a flat stream with
+    padding, a transposed matrix on 128 x 128 tiles) and a 64-tile group."""
+    specs = [(2, 300, 1030), (1, 1030, 300), (2, 1536, 768), (3, 100, 300)]
+    inputs = [make_inputs(b, r, c, seed=11 + r + c, momentum_nonzero=True) for b, r, c in specs]
+    need = z.muon_groups_workspace_bytes(specs)
+    outs = []
+    for fill in (0x00, 0xFF):
+        groups, flat = [], []
+        for (b, r, c), (P, M, G) in zip(specs, inputs):
+            gP, gM, gG = [dev_f32(p) for p in P], [dev_f32(m) for m in M], [dev_bf16(g) for g in G]
+            gW = [torch.empty((r, c), dtype=torch.bfloat16, device=DEV) for _ in range(b)]
+            groups.append((gP, gM, gG, gW))
+            flat += gP + gM
+        ws = torch.full((need,), fill, dtype=torch.uint8, device=DEV)
+        z.muon_step_groups(groups, f32(8e-4), f32(0.95), True, f32(0.1), 5, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append([t.cpu().numpy().view(np.uint32) for t in flat] +
+                    [u16(w) for g in groups for w in g[3]])
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+    for w in outs[1][-sum(b for b, _, _ in specs):]:
+        assert not np.isnan(oracle.bf16_bits_to_f32(w)).any()
