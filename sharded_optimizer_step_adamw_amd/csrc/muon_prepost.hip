@@ -433,19 +433,22 @@ __global__ __launch_bounds__(kThreads) void muon_momentum_xflat_kernel(
 }
 
 // Zeros of X's padding for the flat pass: columns [cols, np) of rows
-// [0, rows), then rows [rows, mp) whole; `pad` elements per matrix.
+// [0, rows), then rows [rows, mp) whole; `pad` elements per matrix, walked by
+// a grid of at most kPadBlocks workgroups per matrix.
+constexpr int64_t kPadBlocks = 4096;
 __global__ __launch_bounds__(kThreads) void muon_x_pad_kernel(
     int32_t rows, int32_t cols, int32_t np, int64_t pad, uint16_t *__restrict__ x_base,
     int64_t x_stride) {
-    const int64_t k = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (k >= pad) return;
     uint16_t *x = x_base + (int64_t)blockIdx.y * x_stride;
     const int64_t wpad = np - cols, side = (int64_t)rows * wpad;
-    if (k < side) {
-        const int64_t r = k / wpad;
-        x[r * np + cols + (k - r * wpad)] = 0;
-    } else {
-        x[(int64_t)rows * np + (k - side)] = 0;
+    for (int64_t k = (int64_t)blockIdx.x * kThreads + threadIdx.x; k < pad;
+         k += (int64_t)gridDim.x * kThreads) {
+        if (k < side) {
+            const int64_t r = k / wpad;
+            x[r * np + cols + (k - r * wpad)] = 0;
+        } else {
+            x[(int64_t)rows * np + (k - side)] = 0;
+        }
     }
 }
 
@@ -734,10 +737,13 @@ hipError_t launch_muon_pre(const MuonGeom &g, const MuonPtrs &ptrs, float mu,
                                0, stream, ptrs, sa, partials, g.norm_blocks, x, xs);
             parts = chunks;
             const int64_t pad = (int64_t)g.rows * (g.np - g.cols) + (int64_t)(g.mp - g.rows) * g.np;
-            if (pad > 0)
+            if (pad > 0) {
+                const int64_t blocks = (pad + kThreads - 1) / kThreads;
                 hipLaunchKernelGGL(muon_x_pad_kernel,
-                                   dim3((uint32_t)((pad + kThreads - 1) / kThreads), g.batch),
+                                   dim3((uint32_t)(blocks < kPadBlocks ? blocks : kPadBlocks),
+                                        g.batch),
                                    dim3(kThreads), 0, stream, g.rows, g.cols, g.np, pad, x, xs);
+            }
         }
         hipLaunchKernelGGL(muon_norm_kernel, dim3(g.batch), dim3(kThreads), 0, stream, partials,
                            g.norm_blocks, parts, scale, ns_eps);
