@@ -327,12 +327,16 @@ bool muon_fixed_hypers_ok(int32_t nesterov, int32_t ns_steps, float ns_a, float 
 }
 
 // Pointer tables and launch bins of a planned call whose workspace starts at
-// ws.  A group whose workspace fits in the memory-side cache and whose B X
-// product alone fills two rounds of the GPU's workgroup slots gets a bin of
-// its own, all its iterations back to back, so its operands stay cached from
-// one product to the next.  The other groups -- too small to fill the GPU, or
-// too large to stay cached anyway -- share one bin, so that their tiles fill
-// each other's partial rounds.
+// ws.  All groups share one bin, so that their tiles fill each other's
+// partial rounds.  A group whose symmetric products were given 128 x 128
+// tiles for having too few 256 x 256 upper-triangle tiles to fill the GPU on
+// its own goes back to 256 x 256 tiles when the bin holds groups on those:
+// its short tiles then run in the partial last rounds of their launches
+// instead of in launches of their own (the results are the same bit for bit:
+// every element is accumulated over K in the same order on either tile).
+// Measured on the 8B rank-0 share (8 x [1024, 4096] beside 4096-row groups):
+// 52.95 ms per call against 53.40 ms with that group in a bin of its own on
+// 128-tiles.
 void muon_bin_call(MuonCallPlan &c, char *ws, float *const *master, float *const *momentum,
                    const uint16_t *const *grad, uint16_t *const *weight, const int32_t *batch) {
     for (int i = 0, first = 0; i < c.ngroups; first += batch[i], ++i) {
@@ -346,23 +350,16 @@ void muon_bin_call(MuonCallPlan &c, char *ws, float *const *master, float *const
         }
         c.refs[i] = NsGroupRef{&c.plans[i].g, &c.plans[i].L, ws + c.plans[i].base};
     }
-    c.nbins = 0;
-    int shared = -1;
+    c.nbins = 1;
+    c.bin_size[0] = c.ngroups;
+    bool any256 = false;
     for (int i = 0; i < c.ngroups; ++i) {
-        const MuonGeom &g = c.plans[i].g;
-        const int64_t bx_tiles = (int64_t)(g.mp / g.tile_bx) * (g.np / g.tile_bx) * g.batch;
-        const bool alone = c.plans[i].L.total <= kMemCacheBytes &&
-                           bx_tiles >= 2 * (int64_t)ns_round_tiles(g.tile_bx);
-        if (alone) {
-            c.bins[c.nbins][0] = i;
-            c.bin_size[c.nbins++] = 1;
-        } else {
-            if (shared < 0) {
-                shared = c.nbins++;
-                c.bin_size[shared] = 0;
-            }
-            c.bins[shared][c.bin_size[shared]++] = i;
-        }
+        c.bins[0][i] = i;
+        any256 = any256 || c.plans[i].g.tile == 256;
+    }
+    for (int i = 0; any256 && i < c.ngroups; ++i) {
+        MuonGeom &g = c.plans[i].g;
+        if (g.tile == 128 && g.m >= 1024 && g.mp % 256 == 0) g.tile = 256;
     }
 }
 

@@ -200,7 +200,4 @@ int ns_round_tiles(int tile);
 // a full round; otherwise max(8, n rounded down to a multiple of 8)).
 void ns_set_workgroup_limit(int n);
 
-// Capacity of the memory-side cache (MI355X Infinity Cache).
-constexpr size_t kMemCacheBytes = (size_t)256 << 20;
-
 }  // namespace zopt
