@@ -51,7 +51,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 MEASURED_TRAFFIC = {
     # the full buckets (bucket-grid launch) and the last bucket: 3.500 GB read, 3.500 GB written
     "adamw_shard": dict(source="sharded_optimizer_step_adamw_amd/csrc/adamw_shard.hip",
-                        sha256="eb634639dcc4f5fb057abadb322544f78356e888bfa3d815b4dd1ac93d32ea9d",
+                        sha256="673b6ee27b692f43da0cb776f129120c95304617a7117f995f9273186f2e9bca",
                         bytes_per_launch=7.000e9,
                         profile="profiles/adamw_bucket_grid_kernel_zero2_2b_rank3.md"),
     # one Newton-Schulz iteration of the 72 GPT-2-small matrices: the four launches'
@@ -61,7 +61,7 @@ MEASURED_TRAFFIC = {
                               bytes_per_launch=1.0548e9,
                               profile="profiles/ns_gemm_gpt2_small_step.md"),
     "grad_sq_norm": dict(source="sharded_optimizer_step_adamw_amd/csrc/adamw_shard.hip",
-                         sha256="eb634639dcc4f5fb057abadb322544f78356e888bfa3d815b4dd1ac93d32ea9d",
+                         sha256="673b6ee27b692f43da0cb776f129120c95304617a7117f995f9273186f2e9bca",
                          bytes_per_launch=0.5004e9,
                          profile="profiles/grad_sq_norm_kernel_zero2_2b_rank3.md"),
 }

@@ -12,12 +12,16 @@
 // gradient and 12 B of fp32 state and writes 12 B of state and 2 B of bf16
 // weight (28 B).  A workgroup of 256 threads streams one tile of 256 shard
 // elements, one element per thread, so a wave-wide instruction covers 256
-// contiguous bytes of a state array.  Measured on MI355X at 2.5e8 elements,
-// this small per-workgroup footprint streams the eight arrays at 81% of the
-// HBM peak, against 71% for 2048-element tiles of 16-byte vectors and 76-79%
-// for 512-1024-element tiles: the smaller each workgroup's span of every
-// array, the more compact the window of addresses in flight.  Nothing is
-// re-read, so every access is a streaming (non-temporal) one.
+// contiguous bytes of a state array.  When the buckets' pieces hold whole
+// tiles, the full buckets are one launch of a (tiles per piece) x (buckets)
+// grid whose flat index needs no division, so all four loads of a thread
+// leave at once (adamw_bucket_grid_kernel); the rest of the shard is mapped
+// through the bucket layout tile by tile (adamw_shard_kernel).  Measured on
+// MI355X at 2.5e8 elements: 81% of the HBM peak, against 70% for
+// 2048-element tiles of 16-byte vectors and 76-79% for 512-1024-element
+// tiles -- on this part the many-stream step runs faster the smaller each
+// workgroup's span of every array.  Nothing is re-read, so every access is a
+// streaming (non-temporal) one.
 //
 // Also here: the squared gradient norm of the same shard (2 B read per
 // element) and the clip statistics derived from it [DEG zero.py:
