@@ -86,6 +86,8 @@ def test_tiny_workload_all_ranks_bitwise():
     (1, 1, 1, 0),
     (100_003, 4096, 1, 0),       # world 1, ragged tail
     (1 << 20, 1 << 17, 8, 5),    # all 16-byte aligned: the vector path
+    ((1 << 14) + 3, 1 << 12, 8, 7),  # bucket grid, then a last piece of padding only
+    ((1 << 20) + 100, 1 << 17, 8, 6),  # bucket grid, then a padded last bucket
 ])
 def test_layouts_bitwise(n, bucket, world, rank):
     run_both(n, bucket, world, rank, 3, seed=n + bucket + world + rank)
@@ -270,6 +272,42 @@ def test_shard_longer_than_one_launch_sampled(bucket):
     np.testing.assert_array_equal(gm[jt].cpu().numpy().view(np.uint32), m.view(np.uint32))
     np.testing.assert_array_equal(gv[jt].cpu().numpy().view(np.uint32), v.view(np.uint32))
     np.testing.assert_array_equal(u16(gw[jt]), w)
+
+
+def test_more_buckets_than_one_grid_holds_sampled():
+    """World 2, rank 1, buckets of 512 (pieces of one 256-element tile): 65,536
+    full buckets are past the bucket grid's y range, so the step takes the
+    1-D launch with its 32-bit tile-to-bucket index.  The oracle maps and
+    steps a seeded sample of shard indices (its map walks every bucket per
+    element) plus both ends of the last pieces, compared bitwise; the other
+    rank's weights are left alone."""
+    n, bucket, world, rank = 65536 * 512 + 300, 512, 2, 1
+    sl = z.shard_len(n, bucket, world)
+    assert sl == oracle.shard_len(n, bucket, world) == 65536 * 256 + 150
+    rng = np.random.default_rng(65)
+    j = np.unique(np.concatenate([rng.integers(0, sl, 1 << 12), np.arange(sl - 700, sl),
+                                  np.arange(0, 300)])).astype(np.int64)
+    flat, real = oracle.shard_index_map(n, bucket, world, rank, j)
+    assert real.all()
+    gp = wl.device_normal(92, 0, (sl,), 0.02, DEV)
+    gm, gv = torch.zeros_like(gp), torch.zeros_like(gp)
+    gw = torch.zeros((n,), dtype=torch.bfloat16, device=DEV)
+    jt, ft = torch.from_numpy(j).to(DEV), torch.from_numpy(flat).to(DEV)
+    p = gp[jt].cpu().numpy()
+    m, v = np.zeros_like(p), np.zeros_like(p)
+    hps = [f32(x) for x in (1e-3, 0.9, 0.95, 1e-8, 0.1)]
+    for t in range(1, 3):
+        gg = wl.device_grad_bf16(92, 1, (n,), 1e-3, DEV, step=t)
+        gs = oracle.bf16_bits_to_f32(u16(gg[ft]))
+        z.adamw_shard_step(gp, gm, gv, gg, gw, n, bucket, world, rank, *hps, t)
+        w = oracle.adamw_points(p, m, v, gs.copy(), *hps, t)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(gp[jt].cpu().numpy().view(np.uint32), p.view(np.uint32))
+    np.testing.assert_array_equal(gm[jt].cpu().numpy().view(np.uint32), m.view(np.uint32))
+    np.testing.assert_array_equal(gv[jt].cpu().numpy().view(np.uint32), v.view(np.uint32))
+    np.testing.assert_array_equal(u16(gw[ft]), w)
+    other = torch.tensor([0, 255, 512 * 1000 + 17, 65536 * 512 + 149], device=DEV)
+    assert not gw[other].float().any()
 
 
 # ------------------------------------------------------------ round_bf16
