@@ -78,6 +78,11 @@ struct NsGroup {
     // applied here, s^2 to X X^T and s to B X (one float per matrix); NULL
     // otherwise.
     const float *xs;
+    // X X^T split along K: this entry's fp32 partial product (mp x mp per
+    // matrix, row stride ldc), written whole for every computed tile; the
+    // fix-up kernel forms A from the parts.  NULL: the normal epilogue.
+    float *part;
+    int64_t part_stride;
 };
 
 struct NsLaunch {
@@ -201,6 +206,19 @@ __device__ __forceinline__ void epilogue(const NsGroup &args, float ca, float cb
     const float *dIn = args.dIn + batch * args.d_stride;
     float *dOut = args.dOut + batch * args.d_stride;
     const int col = lane & 15, quad = lane >> 4;
+    if (MODE == kSyrkXXT && args.part != nullptr) {
+        // one part of a split reduction: the raw fp32 sums (every workgroup
+        // of the group takes this branch, so no barrier is skipped by some)
+        float *Pm = args.part + batch * args.part_stride;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    Pm[(int64_t)(R0 + i * 16 + quad * 4 + r) * ldc + C0 + j * 16 + col] = acc[i][j][r];
+        return;
+    }
     if (MODE == kSyrkXXT && args.xs != nullptr) {
         // first iteration: A = (s U)(s U)^T from the products of U
         const float s = args.xs[batch], s2 = s * s;
@@ -938,9 +956,11 @@ constexpr int kThreadsOf = Cfg<T>::WR * Cfg<T>::WC * 64;
 // One launch's share of a group: its matrices [b0, b0 + nb) on tiles of `tile`.
 struct LaunchPart {
     int ref, b0, nb;
+    int split = 0, nsplit = 1;  // X X^T: part `split` of the group's K split in nsplit
 };
 
-NsGroup product_group(int mode, const NsGroupRef &r, int iter, bool last, int tile, int b0) {
+NsGroup product_group(int mode, const NsGroupRef &r, int iter, bool last, int tile, int b0,
+                      int split = 0, int nsplit = 1) {
     const MuonGeom &g = *r.geom;
     const MuonWorkspace &L = *r.layout;
     char *ws = r.base;
@@ -976,6 +996,18 @@ NsGroup product_group(int mode, const NsGroupRef &r, int iter, bool last, int ti
         s.dIn = dB; s.dOut = dB;
     }
     if (iter == 0 && mode != kSyrkAA) s.xs = muon_scale_ptr(ws, g, L) + b0;
+    if (mode == kSyrkXXT && nsplit > 1) {
+        // K range [split K / nsplit, (split + 1) K / nsplit) of X's columns;
+        // s is applied by the fix-up, to the sum of the parts
+        const int kp = g.np / nsplit;
+        s.P += (int64_t)split * kp;
+        s.Q += (int64_t)split * kp;
+        s.K = kp;
+        s.part_stride = (int64_t)g.mp * g.mp;
+        s.part = reinterpret_cast<float *>(ws + L.part) +
+                 (int64_t)split * g.batch * s.part_stride + b0 * s.part_stride;
+        s.xs = nullptr;
+    }
     // matrices from b0 on
     s.P += b0 * s.p_stride;
     s.Q += b0 * s.q_stride;
@@ -1025,7 +1057,7 @@ hipError_t launch_product(const NsGroupRef *refs, const LaunchPart *parts, int n
         int64_t tiles = 0;
         for (int k = 0; k < cnt; ++k) {
             const LaunchPart &p = parts[first + k];
-            NsGroup s = product_group(MODE, refs[p.ref], iter, last, T, p.b0);
+            NsGroup s = product_group(MODE, refs[p.ref], iter, last, T, p.b0, p.split, p.nsplit);
             s.tiles = s.tiles_pm * p.nb;
             s.padded = (s.tiles + 7) / 8 * 8;
             s.round_tiles = round_tiles;
@@ -1056,12 +1088,15 @@ int product_parts(const NsGroupRef *refs, int nrefs, LaunchPart *parts) {
     int n = 0;
     for (int i = 0; i < nrefs; ++i) {
         const MuonGeom &g = *refs[i].geom;
-        if ((MODE == kGemmBX ? g.tile_bx : g.tile) == T) parts[n++] = LaunchPart{i, 0, g.batch};
+        if ((MODE == kGemmBX ? g.tile_bx : g.tile) != T) continue;
+        const int ns = MODE == kSyrkXXT ? g.ksplit : 1;
+        for (int k = 0; k < ns; ++k) parts[n++] = LaunchPart{i, 0, g.batch, k, ns};
     }
     for (int i = 1; i < n; ++i)
         for (int j = i; j > 0; --j) {
             const MuonGeom &p = *refs[parts[j - 1].ref].geom, &q = *refs[parts[j].ref].geom;
-            const int kp = MODE == kSyrkXXT ? p.np : p.mp, kq = MODE == kSyrkXXT ? q.np : q.mp;
+            const int kp = MODE == kSyrkXXT ? p.np / parts[j - 1].nsplit : p.mp,
+                      kq = MODE == kSyrkXXT ? q.np / parts[j].nsplit : q.mp;
             if (kp >= kq) break;
             const LaunchPart t = parts[j - 1];
             parts[j - 1] = parts[j];
@@ -1073,7 +1108,7 @@ int product_parts(const NsGroupRef *refs, int nrefs, LaunchPart *parts) {
 template <int MODE>
 hipError_t run_mode(const NsGroupRef *refs, int nrefs, int iter, bool last, float a, float b,
                     float c, hipStream_t stream) {
-    LaunchPart p256[kMaxCallGroups], p128[kMaxCallGroups + 1], p64[kMaxCallGroups];
+    LaunchPart p256[2 * kMaxCallGroups], p128[2 * kMaxCallGroups + 1], p64[2 * kMaxCallGroups];
     int n256 = product_parts<256, MODE>(refs, nrefs, p256);
     int n128 = product_parts<128, MODE>(refs, nrefs, p128);
     const int n64 = product_parts<64, MODE>(refs, nrefs, p64);
@@ -1101,7 +1136,7 @@ hipError_t run_mode(const NsGroupRef *refs, int nrefs, int iter, bool last, floa
         const int64_t r128_before = (t128 + r128 - 1) / r128;
         const int64_t r128_after = (t128 + 4 * q * m + r128 - 1) / r128;
         if (rounds > 1 && rem * 4 <= r256 && m < lp.nb && r128_after - r128_before <= 1 &&
-            n128 <= kMaxCallGroups) {
+            n128 < 2 * kMaxCallGroups + 1) {
             p128[n128++] = LaunchPart{lp.ref, lp.b0 + lp.nb - (int)m, (int)m};
             lp.nb -= (int)m;
         }
@@ -1113,6 +1148,77 @@ hipError_t run_mode(const NsGroupRef *refs, int nrefs, int iter, bool last, floa
     if (e == hipSuccess && n64 > 0)
         e = launch_product<64, MODE>(refs, p64, n64, iter, last, a, b, c, stream);
     return e;
+}
+
+// X X^T of a group split along K: A from the ksplit fp32 parts, summed in
+// part order, times s^2 in the first iteration -- the same values the
+// unsplit epilogue forms from its accumulators -- with A's off-diagonal
+// entries in bf16 on both sides of the diagonal, its diagonal 0 and the
+// diagonal's fp32 values in dA.  One workgroup per 64 x 64 block on or above
+// the diagonal (blockIdx.y: matrix); the mirror goes through LDS so that both
+// stores are row runs.
+__global__ __launch_bounds__(256) void ns_xxt_fixup_kernel(const float *__restrict__ part,
+                                                           int64_t part_stride, int nsplit,
+                                                           int mp, int batch,
+                                                           const float *__restrict__ xs,
+                                                           uint16_t *__restrict__ A,
+                                                           int64_t a_stride, float *__restrict__ dA,
+                                                           int64_t d_stride) {
+    __shared__ uint16_t tt[64][64 + 2];
+    const int nb = mp / 64;
+    int t = blockIdx.x, bi = 0;
+    while (t >= nb - bi) {
+        t -= nb - bi;
+        ++bi;
+    }
+    const int bj = bi + t;
+    const int b = blockIdx.y;
+    const float s = xs ? xs[b] : 1.0f, s2 = s * s;
+    const int c = threadIdx.x & 63, rq = threadIdx.x >> 6;
+    uint16_t *Am = A + b * a_stride;
+    float *dm = dA + b * d_stride;
+#pragma unroll 4
+    for (int k = 0; k < 16; ++k) {
+        const int r = rq * 16 + k;
+        const int gi = bi * 64 + r, gj = bj * 64 + c;
+        const int64_t o = (int64_t)b * part_stride + (int64_t)gi * mp + gj;
+        float v = part[o];
+        for (int p = 1; p < nsplit; ++p) v += part[o + (int64_t)p * batch * part_stride];
+        if (xs) v *= s2;
+        if (gi < gj) {
+            const uint16_t h = cvt_bf16(v);
+            Am[(int64_t)gi * mp + gj] = h;
+            tt[c][r] = h;
+        } else if (gi == gj) {
+            dm[gi] = v;
+            Am[(int64_t)gi * mp + gi] = 0;
+        }
+    }
+    __syncthreads();
+    // the mirror: row gj of A, columns gi < gj of this block
+    const int mr = threadIdx.x >> 2, c0 = (threadIdx.x & 3) * 16;
+#pragma unroll 4
+    for (int k = 0; k < 16; ++k) {
+        const int gi = bi * 64 + c0 + k, gj = bj * 64 + mr;
+        if (gi < gj) Am[(int64_t)gj * mp + gi] = tt[mr][c0 + k];
+    }
+}
+
+hipError_t launch_xxt_fixups(const NsGroupRef *refs, int nrefs, int iter, hipStream_t stream) {
+    for (int i = 0; i < nrefs; ++i) {
+        const MuonGeom &g = *refs[i].geom;
+        if (g.ksplit < 2) continue;
+        const MuonWorkspace &L = *refs[i].layout;
+        char *ws = refs[i].base;
+        const int nb = g.mp / 64;
+        const float *xs = iter == 0 ? muon_scale_ptr(ws, g, L) : nullptr;
+        hipLaunchKernelGGL(ns_xxt_fixup_kernel, dim3(nb * (nb + 1) / 2, g.batch), dim3(256), 0,
+                           stream, reinterpret_cast<const float *>(ws + L.part),
+                           (int64_t)g.mp * g.mp, g.ksplit, g.mp, g.batch, xs,
+                           reinterpret_cast<uint16_t *>(ws + L.a), (int64_t)(L.a_stride / 2),
+                           reinterpret_cast<float *>(ws + L.da), (int64_t)(L.d_stride / 4));
+    }
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -1139,6 +1245,7 @@ hipError_t launch_ns_iteration(const NsGroupRef *refs, int nrefs, int iter, bool
                 return hipErrorInvalidValue;
     }
     hipError_t e = run_mode<kSyrkXXT>(refs, nrefs, iter, last, a, b, c, stream);
+    if (e == hipSuccess) e = launch_xxt_fixups(refs, nrefs, iter, stream);
     if (e == hipSuccess) e = run_mode<kSyrkAA>(refs, nrefs, iter, last, a, b, c, stream);
     if (e == hipSuccess) e = run_mode<kGemmBX>(refs, nrefs, iter, last, a, b, c, stream);
     return e;

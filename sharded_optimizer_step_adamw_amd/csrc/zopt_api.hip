@@ -74,6 +74,12 @@ MuonGeom muon_geometry(int32_t batch, int64_t rows, int64_t cols) {
     if (g.tile == 256 && (int64_t)batch * (t256 * (t256 + 1) / 2) < 128) g.tile = 128;
     const int32_t chunks = muon_norm_blocks(rows * cols), tiles = muon_pre_tiles(g);
     g.norm_blocks = chunks > tiles ? chunks : tiles;
+    // X X^T of a group with a long reduction and fewer upper-triangle tiles of
+    // 256 than the GPU has compute units is split along K in two: its tiles
+    // would otherwise set the length of the launch.  The rule depends on the
+    // group alone, so a group's result is the same in any call.
+    const int64_t u256 = (g.mp + 255) / 256;
+    g.ksplit = (g.np >= 8192 && (int64_t)batch * (u256 * (u256 + 1) / 2) < 256) ? 2 : 1;
     g.health_blocks = ns_health_blocks((int64_t)g.m * g.np);
     return g;
 }
@@ -91,6 +97,8 @@ MuonWorkspace muon_workspace_layout(const MuonGeom &g) {
     L.b = off;   off += L.a_stride * g.batch;
     L.da = off;  off += L.d_stride * g.batch;
     L.db = off;  off += L.d_stride * g.batch;
+    L.part = off;
+    if (g.ksplit > 1) off += round_up((size_t)g.ksplit * g.batch * g.mp * g.mp * 4, 256);
     L.partials = off;
     off += round_up(((size_t)g.batch * g.norm_blocks + g.batch) * sizeof(float), 256);
     const size_t hparts = (size_t)g.batch * g.health_blocks;

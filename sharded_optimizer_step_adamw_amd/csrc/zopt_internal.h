@@ -106,6 +106,7 @@ struct MuonGeom {
     int32_t tile;        // square output tile of the Newton-Schulz products X X^T and A A
     int32_t tile_bx;     // and of B X
     int32_t norm_blocks; // norm partials per matrix (room for either form of pass 1)
+    int32_t ksplit;      // X X^T reduction split in this many parts (1: none)
     int32_t health_blocks;  // workgroups (and partials) per matrix of the health pass
 };
 
@@ -121,6 +122,7 @@ struct MuonPtrs {
 // the result transposed (np x mp) for matrices stored transposed.
 struct MuonWorkspace {
     size_t x, xt0, xt1, a, b, da, db, partials;
+    size_t part;       // X X^T split: ksplit fp32 mp x mp partial products per matrix
     size_t hsum, hmax, hflag;  // health pass: fp64 / fp32 partials, per-matrix reject flags
     size_t total;
     size_t x_stride, a_stride, d_stride;  // bytes per matrix of each region kind

@@ -435,3 +435,15 @@ def test_grouped_workspace_needs_no_initialisation():
         assert np.array_equal(a, b)
     for w in outs[1][-sum(b for b, _, _ in specs):]:
         assert not np.isnan(oracle.bf16_bits_to_f32(w)).any()
+
+
+@pytest.mark.parametrize("ns_steps", [1, 5])
+def test_split_reduction_groups(ns_steps):
+    """X X^T split along K (a group whose reduction is at least 8192 long and
+    whose upper-triangle tiles of 256 are too few to fill the GPU): ragged
+    shapes of both orientations, on 256 tiles beside a 4096^2 group in the
+    grouped call and on 128 tiles in the separate ones -- each split matrix
+    against the oracle, every matrix against the separate calls bit for bit;
+    one iteration puts the pre-scale in the fix-up."""
+    specs = [(1, 1100, 8300), (2, 8200, 1030), (1, 4096, 4096)]
+    grouped_vs_separate(specs, seed=77, ns_steps=ns_steps, ns_check=lambda b, r, c, i: r != c)
