@@ -55,10 +55,10 @@ MEASURED_TRAFFIC = {
                         bytes_per_launch=7.000e9,
                         profile="profiles/adamw_bucket_grid_kernel_zero2_2b_rank3.md"),
     # one Newton-Schulz iteration of the 72 GPT-2-small matrices: the four launches'
-    # FETCH_SIZE + WRITE_SIZE, calibrated (0.7145 GB read, 0.3403 GB written)
+    # FETCH_SIZE + WRITE_SIZE, calibrated (0.7137 GB read, 0.3403 GB written)
     "ns_iteration_gpt2": dict(source="sharded_optimizer_step_adamw_amd/csrc/ns_gemm.hip",
-                              sha256="01666720cdd0cbb5b49cfdb132387ed64e374f3ff78b48c660c346babc0f755b",
-                              bytes_per_launch=1.0548e9,
+                              sha256="965e58691b738e401f317e77d17b076850545fc21cdec095ae904a100f60aa14",
+                              bytes_per_launch=1.0540e9,
                               profile="profiles/ns_gemm_gpt2_small_step.md"),
     "grad_sq_norm": dict(source="sharded_optimizer_step_adamw_amd/csrc/adamw_shard.hip",
                          sha256="673b6ee27b692f43da0cb776f129120c95304617a7117f995f9273186f2e9bca",
