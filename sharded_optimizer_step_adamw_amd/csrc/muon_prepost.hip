@@ -385,14 +385,18 @@ __global__ __launch_bounds__(kThreads) void muon_momentum_x_kernel(
 }
 
 // The same pass for a matrix stored in the Newton-Schulz orientation (rows
-// <= cols): a flat stream of 2048 consecutive stored elements per workgroup,
-// 8 per thread, M updated in place and bf16(U) written to X's row at the
-// padded stride np, one fixed-order partial of U^2 per workgroup.  (The
-// 64 x 64 tiles above read 64 row pieces of 256 bytes per workgroup; this
-// reads whole 8 KiB runs.)  The padding of X is zeroed by muon_x_pad_kernel.
+// <= cols): a flat stream of consecutive stored elements (kFlatEPT per
+// thread), M updated in place and bf16(U) written to X's row at the padded
+// stride np, one fixed-order partial of U^2 per workgroup.  (LDS-transpose
+// tiles read 64-128 row pieces of 256-512 bytes per workgroup; this reads
+// whole runs.)  The padding of X is zeroed by muon_x_pad_kernel.
+// elements per thread of the flat pass: 4 (1024 per workgroup) measured ~1% faster than 8 on
+// a one-iteration GPT-2-small call, like the post-step's 4
+constexpr int kFlatEPT = 4;
 __global__ __launch_bounds__(kThreads) void muon_momentum_xflat_kernel(
     MuonPtrs ptrs, ScaleArgs a, float *__restrict__ partials, int32_t norm_blocks,
     uint16_t *__restrict__ x_base, int64_t x_stride) {
+    constexpr int E = kFlatEPT;
     __shared__ float lds4[4];
     const int b = blockIdx.y;
     float *__restrict__ mom = ptrs.momentum[b];
@@ -401,25 +405,22 @@ __global__ __launch_bounds__(kThreads) void muon_momentum_xflat_kernel(
     PreArgs pa{0, 0, a.mu, a.omm, a.nesterov, nullptr};
     device_momentum(a.dev, pa.mu, pa.omm);
     const uint32_t count = (uint32_t)a.rows * (uint32_t)a.cols;  // < 2^31
-    const uint32_t i0 = (blockIdx.x * kThreads + threadIdx.x) * 8;
+    const uint32_t i0 = (blockIdx.x * kThreads + threadIdx.x) * E;
     float sumsq = 0.0f;
-    if (a.vec && i0 + 8 <= count) {
-        // cols % 8 == 0: the 8 elements share one row
-        float m[8], g[8], us[8];
-        ld_f32<8, true>(mom + i0, m);
-        ld_bf16<8>(grad + i0, g);
+    if (a.vec && i0 + E <= count) {
+        // cols % 8 == 0: the elements share one row
+        float m[E], g[E], us[E];
+        ld_f32<E, true>(mom + i0, m);
+        ld_bf16<E>(grad + i0, g);
         const uint32_t r = i0 / (uint32_t)a.cols, c = i0 - r * (uint32_t)a.cols;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) momentum_update(m[e], g[e], us[e], pa);
-        st_f32<8, true>(mom + i0, m);
+        for (int e = 0; e < E; ++e) momentum_update(m[e], g[e], us[e], pa);
+        st_f32<E, true>(mom + i0, m);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sumsq += us[e] * us[e];
-        __builtin_nontemporal_store(
-            u32x4{pack_bf16x2(us[0], us[1]), pack_bf16x2(us[2], us[3]), pack_bf16x2(us[4], us[5]),
-                  pack_bf16x2(us[6], us[7])},
-            reinterpret_cast<u32x4 *>(x + (int64_t)r * a.np + c));
+        for (int e = 0; e < E; ++e) sumsq += us[e] * us[e];
+        st_bf16<E>(x + (int64_t)r * a.np + c, us);
     } else {
-        for (uint32_t e = 0; e < 8 && i0 + e < count; ++e) {
+        for (uint32_t e = 0; e < (uint32_t)E && i0 + e < count; ++e) {
             const uint32_t i = i0 + e, r = i / (uint32_t)a.cols, c = i - r * (uint32_t)a.cols;
             float m = mom[i], u;
             momentum_update(m, bf16_bits_to_float(grad[i]), u, pa);
@@ -695,7 +696,12 @@ hipError_t launch_ns_health_total(float *health, int32_t nmat, hipStream_t strea
     return hipGetLastError();
 }
 
-int32_t muon_norm_blocks(int64_t count) { return (int32_t)((count + kChunk - 1) / kChunk); }
+int32_t muon_norm_blocks(int64_t count) {
+    // room for the partials of either pass-1 form
+    const int64_t a = (count + kChunk - 1) / kChunk;
+    const int64_t b = (count + kThreads * kFlatEPT - 1) / (kThreads * kFlatEPT);
+    return (int32_t)(a > b ? a : b);
+}
 
 int32_t muon_pre_tiles(const MuonGeom &g) {
     const int srows = g.transposed ? g.np : g.mp;
@@ -719,7 +725,7 @@ hipError_t launch_muon_pre(const MuonGeom &g, const MuonPtrs &ptrs, float mu,
     const int tiles = muon_pre_tiles(g);
     ScaleArgs sa{g.rows, g.cols, g.transposed, g.mp, g.np, scols / kTile, mu, omm, nesterov,
                  (vec && g.cols % 8 == 0) ? 1 : 0, dev, (no_iterations && g.transposed) ? 1 : 0};
-    const int32_t chunks = muon_norm_blocks(count);
+    const int32_t chunks = (int32_t)((count + kChunk - 1) / kChunk);  // the separate pass 1
     if (!no_iterations) {
         uint16_t *x = reinterpret_cast<uint16_t *>(ws + L.x);
         const int64_t xs = (int64_t)(L.x_stride / 2);
@@ -733,9 +739,10 @@ hipError_t launch_muon_pre(const MuonGeom &g, const MuonPtrs &ptrs, float mu,
             hipLaunchKernelGGL(muon_momentum_x_kernel<kTile>, dim3(tiles, g.batch), dim3(kThreads),
                                0, stream, ptrs, sa, partials, g.norm_blocks, x, xs);
         } else {
-            hipLaunchKernelGGL(muon_momentum_xflat_kernel, dim3(chunks, g.batch), dim3(kThreads),
+            const int32_t fchunks = (int32_t)((count + kThreads * kFlatEPT - 1) / (kThreads * kFlatEPT));
+            hipLaunchKernelGGL(muon_momentum_xflat_kernel, dim3(fchunks, g.batch), dim3(kThreads),
                                0, stream, ptrs, sa, partials, g.norm_blocks, x, xs);
-            parts = chunks;
+            parts = fchunks;
             const int64_t pad = (int64_t)g.rows * (g.np - g.cols) + (int64_t)(g.mp - g.rows) * g.np;
             if (pad > 0) {
                 const int64_t blocks = (pad + kThreads - 1) / kThreads;
