@@ -23,9 +23,12 @@
  * Conventions common to every call
  * --------------------------------
  *  - Every buffer is device memory owned by the caller.  The library
- *    allocates no device memory and keeps no state between calls (a captured
- *    Muon graph is a handle the caller owns; zopt_set_ns_workgroup_limit is
- *    a process-wide setting); it is reentrant.
+ *    allocates no device memory and keeps no state between calls, with two
+ *    exceptions: a captured Muon graph is a handle the caller owns; and
+ *    zopt_set_ns_workgroup_limit is a process-wide setting that every later
+ *    call in the process uses (one thread's setting changes the launch plan,
+ *    never the results, of another's calls).  Every other call is
+ *    reentrant.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *    the call returns without synchronising.  All launch parameters travel
  *    as kernel arguments, so back-to-back calls need no host sync.
@@ -256,12 +259,16 @@ int64_t zopt_shard_len(int64_t N, int64_t bucket, int32_t world);
  *        g = fp32(grad);  M = mu * M + omm * g;
  *        U = omm * g + mu * M  (nesterov)   or   U = M   (otherwise)
  *      with mu = momentum_beta and omm = fp32(1 - mu) formed in double.
- *   2. Pre-scale: X0 = s U, s = 1 / (||U||_F + ns_eps), the norm a
- *      fixed-order (run-to-run deterministic) reduction in fp32; X0 is taken
- *      transposed when rows > cols, so X is m x n with m = min(rows, cols).
- *      With ns_steps = 0, X0 = bf16(U * s) is the result.  Otherwise X0 is
- *      never stored: the first iteration reads bf16(U) and applies s in fp32
- *      to its products (s^2 to X X^T, s to B X).
+ *   2. Pre-scale: X0 = s U, s = 1 / (||U||_F + ns_eps), ||U||_F^2 a
+ *      fixed-order (run-to-run deterministic) fp64 sum of the exact squares
+ *      and s formed in double; X0 is taken transposed when rows > cols, so X
+ *      is m x n with m = min(rows, cols).  With ns_steps = 0,
+ *      X0 = bf16(U * s) (the product in double) is the result.  Otherwise,
+ *      when 2^-60 <= ||U||_F^2 <= 2^100, X0 is never stored: the first
+ *      iteration reads bf16(U) and applies s in fp32 to its products (s^2 to
+ *      X X^T, s to B X), which in that range can neither overflow nor lose
+ *      precision to underflow; outside it (huge or tiny gradients, Inf, NaN)
+ *      X0 = bf16(U * s) is written first and the iteration reads that.
  *   3. ns_steps Newton-Schulz iterations [BluScript trainer source, ShardedMuon
  *      comment block: X <- aX + (bXX' + c(XX')^2)X]:
  *        A = X X^T;  B = b A + c A A;  X = a X + B X
@@ -279,7 +286,9 @@ int64_t zopt_shard_len(int64_t N, int64_t bucket, int32_t world);
  *
  * Arguments
  *   batch        1 .. 64 matrices.
- *   rows, cols   the stored shape, >= 1, rows * cols < 2^31.
+ *   rows, cols   the stored shape, >= 1, rows * cols < 2^31 and
+ *                max(rows, cols) <= 2^21 (2,097,152: the kernels address a
+ *                row panel of the padded matrix with 32-bit byte offsets).
  *   master, momentum   host arrays of `batch` device pointers, fp32
  *                [rows * cols] each, read and written.
  *   grad         host array of `batch` device pointers, bf16 [rows * cols].

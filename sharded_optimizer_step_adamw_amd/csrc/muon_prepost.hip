@@ -6,16 +6,20 @@
 // stay in the eager pre/post steps around the fixed-shape Newton-Schulz]:
 //   pass 1  M = mu M + (1-mu) g, U = (1-mu) g + mu M (or U = M); write M,
 //           bf16(U) in the Newton-Schulz orientation (zero padding), and
-//           fixed-order partial sums of U^2                      (12 B/elem)
-//   final   per matrix, s = 1 / (sqrt(sum of partials) + eps), the partials
-//           summed in a fixed order (deterministic); the first Newton-Schulz
-//           iteration applies s to its products
+//           fixed-order fp64 partial sums of U^2 (exact squares)  (12 B/elem)
+//   final   per matrix, s = 1 / (sqrt(sum of partials) + eps) in double, the
+//           partials summed in a fixed order (deterministic); the first
+//           Newton-Schulz iteration applies s to its products when ||U||_F^2
+//           lies in [2^-60, 2^100], where those fp32 products of bf16(U)
+//           neither overflow nor lose precision to underflow; outside that
+//           range (huge or tiny gradients, Inf, NaN) this kernel rewrites X
+//           as X0 = bf16(U s) itself and the iteration applies 1
 // A call with no iterations returns X0 = bf16(U s) itself, so it runs
 //   pass 1  M and the partials only                              (10 B/elem)
 //   pass 2  recompute U from the new M (bitwise the same U), write
-//           X0 = bf16(U s) in the Newton-Schulz orientation and, for a
-//           matrix stored transposed, X0^T, zero-filling the tile padding
-//                                                                 (8 B/elem)
+//           X0 = bf16(U s) (U s formed in double) in the Newton-Schulz
+//           orientation and, for a matrix stored transposed, X0^T,
+//           zero-filling the tile padding                        (8 B/elem)
 // Health [BluScript trainer source, per-step report: nsratio, the update's
 // ||O||_F / sqrt(min(rows, cols)), about 1 when healthy, and nsrej, the
 // updates the divergence guard refused for an element above 1000]:
@@ -43,6 +47,7 @@ constexpr int kSweeps = 1;          // sweeps per workgroup in that pass
 constexpr int kChunk = kThreads * kPreEPT * kSweeps;  // elements / workgroup
 constexpr int kPostEPT = 4;         // post-step: elements per thread (1, 4 or 8)
 constexpr int kTile = 64;           // pass-2 transpose tile
+constexpr int kFallbackBlocks = 32; // workgroups per matrix of the norm launch (X0 rewrite)
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -108,18 +113,34 @@ __device__ __forceinline__ void st_bf16(uint16_t *p, const float (&x)[E]) {
     }
 }
 
-// Fixed-order sum over the workgroup: butterfly within each 64-wide wave,
-// then the four wave sums in order.
-__device__ float block_sum(float x, float *lds4) {
+// Fixed-order sum of fp64 values over the workgroup: butterfly within each
+// 64-wide wave, then the four wave sums in order.
+__device__ double block_sum_d(double x, double *lds4) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
     const int wave = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) lds4[wave] = x;
     __syncthreads();
-    float s = ((lds4[0] + lds4[1]) + lds4[2]) + lds4[3];
+    double s = ((lds4[0] + lds4[1]) + lds4[2]) + lds4[3];
     __syncthreads();
     return s;
 }
+
+// u^2 added to an fp64 sum: the square of a binary32 value is exact in
+// binary64, so the fused form rounds once, as a separate add would.
+__device__ __forceinline__ void add_sq(double &acc, float u) {
+    const double d = (double)u;
+    acc = __builtin_fma(d, d, acc);
+}
+
+// The range of ||U||_F^2 over which the first Newton-Schulz iteration applies
+// the pre-scale s to its fp32 products of bf16(U): every entry of U U^T is at
+// most ||U||_F^2 <= 2^100 and every accumulator of B U at most ~10 ||U||_F, far
+// inside binary32; s and s^2 stay normal; and with ||U||_F^2 >= 2^-60 a
+// typical product of two entries (about ||U||_F^2 / (m n) >= 2^-91 for
+// m n < 2^31) is a normal binary32, so only entries ~1e-9 of the typical one
+// or smaller could underflow.
+constexpr double kFoldMin = 0x1p-60, kFoldMax = 0x1p100;
 
 struct PreArgs {
     int32_t count;        // rows * cols
@@ -145,13 +166,13 @@ __device__ __forceinline__ void momentum_update(float &m, float g, float &u,
 }
 
 __global__ __launch_bounds__(kThreads) void muon_momentum_kernel(
-    MuonPtrs ptrs, PreArgs a, float *__restrict__ partials, int32_t norm_blocks) {
-    __shared__ float lds4[4];
+    MuonPtrs ptrs, PreArgs a, double *__restrict__ partials, int32_t norm_blocks) {
+    __shared__ double lds4[4];
     device_momentum(a.dev, a.mu, a.omm);
     const int b = blockIdx.y;
     float *__restrict__ mom = ptrs.momentum[b];
     const uint16_t *__restrict__ grad = ptrs.grad[b];
-    float sumsq = 0.0f;
+    double sumsq = 0.0;
     const int64_t base = (int64_t)blockIdx.x * kChunk;
     for (int s = 0; s < kSweeps; ++s) {
         const int64_t i0 = base + ((int64_t)s * kThreads + threadIdx.x) * kPreEPT;
@@ -164,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void muon_momentum_kernel(
             for (int e = 0; e < kPreEPT; ++e) {
                 float u;
                 momentum_update(m[e], g[e], u, a);
-                sumsq += u * u;
+                add_sq(sumsq, u);
             }
             st_f32<kPreEPT, false>(mom + i0, m);
         } else {
@@ -173,25 +194,12 @@ __global__ __launch_bounds__(kThreads) void muon_momentum_kernel(
                 float m = mom[i0 + e], u;
                 momentum_update(m, g, u, a);
                 mom[i0 + e] = m;
-                sumsq += u * u;
+                add_sq(sumsq, u);
             }
         }
     }
-    float total = block_sum(sumsq, lds4);
+    const double total = block_sum_d(sumsq, lds4);
     if (threadIdx.x == 0) partials[(int64_t)b * norm_blocks + blockIdx.x] = total;
-}
-
-// One workgroup per matrix: s = 1 / (||U||_F + eps) from the partials.
-__global__ __launch_bounds__(kThreads) void muon_norm_kernel(
-    float *__restrict__ partials, int32_t norm_blocks, int32_t count, float *__restrict__ scale,
-    float ns_eps) {
-    __shared__ float lds4[4];
-    const int b = blockIdx.x;
-    const float *p = partials + (int64_t)b * norm_blocks;
-    float s = 0.0f;
-    for (int i = threadIdx.x; i < count; i += kThreads) s += p[i];
-    float total = block_sum(s, lds4);
-    if (threadIdx.x == 0) scale[b] = 1.0f / (__builtin_sqrtf(total) + ns_eps);
 }
 
 struct ScaleArgs {
@@ -206,17 +214,18 @@ struct ScaleArgs {
     int32_t want_t;         // also write X0^T
 };
 
-// Pass 2.  One workgroup per 64 x 64 tile of the padded stored-orientation
-// matrix.  The stored orientation is X when rows <= cols and X^T otherwise;
-// it is written straight out, and the LDS-transposed tile goes to the other.
-__global__ __launch_bounds__(kThreads) void muon_scale_kernel(
-    MuonPtrs ptrs, ScaleArgs a, const float *__restrict__ scale,
-    uint16_t *__restrict__ x_base, uint16_t *__restrict__ xt_base,
-    int64_t x_stride, int64_t xt_stride) {
-    __shared__ uint16_t tile[kTile][kTile + 2];
-    const int b = blockIdx.y;
-    const int tr = blockIdx.x / a.tiles_c, tc = blockIdx.x % a.tiles_c;
-    const float s = scale[b];
+// X0 = bf16(U sd) on one 64 x 64 tile (index t) of the padded
+// stored-orientation matrix b, U recomputed from the momentum pass 1 wrote
+// (bitwise the U pass 1 formed) and U sd formed in double.  The stored
+// orientation is X when rows <= cols and X^T otherwise; it is written straight
+// out (for X^T only when a.want_t), and the LDS-transposed tile goes to the
+// other.  Zeros in the padding.  Every thread of the workgroup calls it.
+__device__ __forceinline__ void x0_tile(const MuonPtrs &ptrs, const ScaleArgs &a,
+                                        const PreArgs &pa, int b, int t, double sd,
+                                        uint16_t *__restrict__ x_base,
+                                        uint16_t *__restrict__ xt_base, int64_t x_stride,
+                                        int64_t xt_stride, uint16_t (*tile)[kTile + 2]) {
+    const int tr = t / a.tiles_c, tc = t % a.tiles_c;
     const float *__restrict__ mom = ptrs.momentum[b];
     const uint16_t *__restrict__ grad = ptrs.grad[b];
     // the stored-orientation output and its padded leading dimension
@@ -226,8 +235,6 @@ __global__ __launch_bounds__(kThreads) void muon_scale_kernel(
                                    : xt_base + (int64_t)b * xt_stride;
     const int64_t ld_direct = a.transposed ? a.mp : a.np;
     const int64_t ld_other = a.transposed ? a.np : a.mp;
-    PreArgs pa{0, 0, a.mu, a.omm, a.nesterov, nullptr};
-    device_momentum(a.dev, pa.mu, pa.omm);
 
     // 64 rows x 8 groups of 8 columns = 512 groups; two per thread
     for (int q = 0; q < 2; ++q) {
@@ -247,8 +254,8 @@ __global__ __launch_bounds__(kThreads) void muon_scale_kernel(
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float g = bf16_bits_to_float((gb[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
-                const float u = a.nesterov ? pa.omm * g + pa.mu * mv[e] : mv[e];
-                xs[e] = u * s;
+                const float u = pa.nesterov ? pa.omm * g + pa.mu * mv[e] : mv[e];
+                xs[e] = (float)((double)u * sd);
             }
 #pragma unroll
             for (int e = 0; e < 8; e += 2) packed[e >> 1] = pack_bf16x2(xs[e], xs[e + 1]);
@@ -264,8 +271,8 @@ __global__ __launch_bounds__(kThreads) void muon_scale_kernel(
                         const int64_t i = (int64_t)r * a.cols + c;
                         float g = bf16_bits_to_float(grad[i]);
                         float m = mom[i];  // already updated by pass 1
-                        float u = a.nesterov ? pa.omm * g + pa.mu * m : m;
-                        x = u * s;
+                        float u = pa.nesterov ? pa.omm * g + pa.mu * m : m;
+                        x = (float)((double)u * sd);
                     }
                     x2[h] = x;
                 }
@@ -296,6 +303,53 @@ __global__ __launch_bounds__(kThreads) void muon_scale_kernel(
         *reinterpret_cast<u32x4 *>(other + orow * ld_other + ocol) =
             u32x4{packed[0], packed[1], packed[2], packed[3]};
     }
+    __syncthreads();  // the tile is free for the caller's next one
+}
+
+// Per matrix b = blockIdx.y: s = 1 / (||U||_F + eps) in double from the fp64
+// partials, summed in a fixed order (every workgroup of the matrix forms the
+// same value), stored as sd[b]; xs[b] is the factor the first Newton-Schulz
+// iteration applies to its products of X.  With fold (iterations follow and
+// pass 1 left bf16(U) in X): xs[b] = s when ||U||_F^2 lies in [kFoldMin,
+// kFoldMax]; otherwise xs[b] = 1 and the workgroups of the matrix rewrite X
+// as X0 = bf16(U s), tiles blockIdx.x, blockIdx.x + gridDim.x, ...  Without
+// fold one workgroup per matrix only forms s (pass 2 writes X0).
+__global__ __launch_bounds__(kThreads) void muon_norm_kernel(
+    MuonPtrs ptrs, ScaleArgs a, const double *__restrict__ partials, int32_t norm_blocks,
+    int32_t count, double *__restrict__ sd, float *__restrict__ xs, float ns_eps, int32_t fold,
+    int32_t tiles, uint16_t *__restrict__ x_base, int64_t x_stride) {
+    __shared__ double lds4[4];
+    __shared__ uint16_t tile[kTile][kTile + 2];
+    const int b = blockIdx.y;
+    const double *p = partials + (int64_t)b * norm_blocks;
+    double acc = 0.0;
+    for (int i = threadIdx.x; i < count; i += kThreads) acc += p[i];
+    const double total = block_sum_d(acc, lds4);
+    const double s = 1.0 / (__builtin_sqrt(total) + (double)ns_eps);
+    // (NaN and infinity compare false: such a matrix takes the rewrite)
+    const bool folded = total >= kFoldMin && total <= kFoldMax;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        sd[b] = s;
+        xs[b] = (fold && folded) ? (float)s : 1.0f;
+    }
+    if (!fold || folded) return;  // uniform
+    PreArgs pa{0, 0, a.mu, a.omm, a.nesterov, nullptr};
+    device_momentum(a.dev, pa.mu, pa.omm);
+    for (int t = blockIdx.x; t < tiles; t += gridDim.x)
+        x0_tile(ptrs, a, pa, b, t, s, x_base, x_base, x_stride, x_stride, tile);
+}
+
+// Pass 2 of a call with no iterations.  One workgroup per 64 x 64 tile of
+// the padded stored-orientation matrix: X0 = bf16(U s), and X0^T where wanted.
+__global__ __launch_bounds__(kThreads) void muon_scale_kernel(
+    MuonPtrs ptrs, ScaleArgs a, const double *__restrict__ sd,
+    uint16_t *__restrict__ x_base, uint16_t *__restrict__ xt_base,
+    int64_t x_stride, int64_t xt_stride) {
+    __shared__ uint16_t tile[kTile][kTile + 2];
+    const int b = blockIdx.y;
+    PreArgs pa{0, 0, a.mu, a.omm, a.nesterov, nullptr};
+    device_momentum(a.dev, pa.mu, pa.omm);
+    x0_tile(ptrs, a, pa, b, blockIdx.x, sd[b], x_base, xt_base, x_stride, xt_stride, tile);
 }
 
 // Pass 1 of a call that runs Newton-Schulz iterations, fused with the write
@@ -310,12 +364,12 @@ __global__ __launch_bounds__(kThreads) void muon_scale_kernel(
 // against 10 + 8 for pass 1 and a separate scaling pass.
 template <int T>
 __global__ __launch_bounds__(kThreads) void muon_momentum_x_kernel(
-    MuonPtrs ptrs, ScaleArgs a, float *__restrict__ partials, int32_t norm_blocks,
+    MuonPtrs ptrs, ScaleArgs a, double *__restrict__ partials, int32_t norm_blocks,
     uint16_t *__restrict__ x_base, int64_t x_stride) {
     constexpr int GPR = T / 8;                  // 8-element groups per tile row
     constexpr int PER = T * GPR / kThreads;     // groups per thread
     __shared__ uint16_t tile[T][T + 2];
-    __shared__ float lds4[4];
+    __shared__ double lds4[4];
     const int b = blockIdx.y;
     const int tiles_c = a.transposed ? a.mp / T : a.np / T;  // tiles along the stored columns
     const int tr = blockIdx.x / tiles_c, tc = blockIdx.x % tiles_c;
@@ -324,7 +378,7 @@ __global__ __launch_bounds__(kThreads) void muon_momentum_x_kernel(
     uint16_t *x = x_base + (int64_t)b * x_stride;
     PreArgs pa{0, 0, a.mu, a.omm, a.nesterov, nullptr};
     device_momentum(a.dev, pa.mu, pa.omm);
-    float sumsq = 0.0f;
+    double sumsq = 0.0;
 
     // T rows x GPR groups of 8 columns; PER per thread
     for (int q = 0; q < PER; ++q) {
@@ -355,7 +409,7 @@ __global__ __launch_bounds__(kThreads) void muon_momentum_x_kernel(
             }
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sumsq += us[e] * us[e];
+        for (int e = 0; e < 8; ++e) add_sq(sumsq, us[e]);
         const uint32_t packed[4] = {pack_bf16x2(us[0], us[1]), pack_bf16x2(us[2], us[3]),
                                     pack_bf16x2(us[4], us[5]), pack_bf16x2(us[6], us[7])};
         if (!a.transposed)
@@ -366,7 +420,7 @@ __global__ __launch_bounds__(kThreads) void muon_momentum_x_kernel(
             for (int e = 0; e < 8; ++e)
                 tile[lr][lc + e] = (uint16_t)((packed[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
     }
-    const float total = block_sum(sumsq, lds4);  // its barriers also order the tile writes
+    const double total = block_sum_d(sumsq, lds4);  // its barriers also order the tile writes
     if (threadIdx.x == 0) partials[(int64_t)b * norm_blocks + blockIdx.x] = total;
     if (!a.transposed) return;  // uniform
     // transposed: X row = stored column, X columns = stored rows
@@ -394,10 +448,10 @@ __global__ __launch_bounds__(kThreads) void muon_momentum_x_kernel(
 // a one-iteration GPT-2-small call, like the post-step's 4
 constexpr int kFlatEPT = 4;
 __global__ __launch_bounds__(kThreads) void muon_momentum_xflat_kernel(
-    MuonPtrs ptrs, ScaleArgs a, float *__restrict__ partials, int32_t norm_blocks,
+    MuonPtrs ptrs, ScaleArgs a, double *__restrict__ partials, int32_t norm_blocks,
     uint16_t *__restrict__ x_base, int64_t x_stride) {
     constexpr int E = kFlatEPT;
-    __shared__ float lds4[4];
+    __shared__ double lds4[4];
     const int b = blockIdx.y;
     float *__restrict__ mom = ptrs.momentum[b];
     const uint16_t *__restrict__ grad = ptrs.grad[b];
@@ -406,7 +460,7 @@ __global__ __launch_bounds__(kThreads) void muon_momentum_xflat_kernel(
     device_momentum(a.dev, pa.mu, pa.omm);
     const uint32_t count = (uint32_t)a.rows * (uint32_t)a.cols;  // < 2^31
     const uint32_t i0 = (blockIdx.x * kThreads + threadIdx.x) * E;
-    float sumsq = 0.0f;
+    double sumsq = 0.0;
     if (a.vec && i0 + E <= count) {
         // cols % 8 == 0: the elements share one row
         float m[E], g[E], us[E];
@@ -417,7 +471,7 @@ __global__ __launch_bounds__(kThreads) void muon_momentum_xflat_kernel(
         for (int e = 0; e < E; ++e) momentum_update(m[e], g[e], us[e], pa);
         st_f32<E, true>(mom + i0, m);
 #pragma unroll
-        for (int e = 0; e < E; ++e) sumsq += us[e] * us[e];
+        for (int e = 0; e < E; ++e) add_sq(sumsq, us[e]);
         st_bf16<E>(x + (int64_t)r * a.np + c, us);
     } else {
         for (uint32_t e = 0; e < (uint32_t)E && i0 + e < count; ++e) {
@@ -425,11 +479,11 @@ __global__ __launch_bounds__(kThreads) void muon_momentum_xflat_kernel(
             float m = mom[i], u;
             momentum_update(m, bf16_bits_to_float(grad[i]), u, pa);
             mom[i] = m;
-            sumsq += u * u;
+            add_sq(sumsq, u);
             x[(int64_t)r * a.np + c] = (uint16_t)rne_bf16_bits(u);
         }
     }
-    const float total = block_sum(sumsq, lds4);
+    const double total = block_sum_d(sumsq, lds4);
     if (threadIdx.x == 0) partials[(int64_t)b * norm_blocks + blockIdx.x] = total;
 }
 
@@ -718,8 +772,11 @@ hipError_t launch_muon_pre(const MuonGeom &g, const MuonPtrs &ptrs, float mu,
     bool vec = (count % 8) == 0;
     for (int b = 0; b < g.batch; ++b)
         vec = vec && aligned16(ptrs.momentum[b]) && aligned16(ptrs.grad[b]);
-    float *partials = reinterpret_cast<float *>(ws + L.partials);
-    float *scale = muon_scale_ptr(ws, g, L);
+    double *partials = reinterpret_cast<double *>(ws + L.partials);
+    double *sd = muon_sd_ptr(ws, g, L);
+    float *xs = muon_scale_ptr(ws, g, L);
+    uint16_t *x = reinterpret_cast<uint16_t *>(ws + L.x);
+    const int64_t xstr = (int64_t)(L.x_stride / 2);
     // stored-orientation padded extent
     const int scols = g.transposed ? g.mp : g.np;
     const int tiles = muon_pre_tiles(g);
@@ -727,21 +784,19 @@ hipError_t launch_muon_pre(const MuonGeom &g, const MuonPtrs &ptrs, float mu,
                  (vec && g.cols % 8 == 0) ? 1 : 0, dev, (no_iterations && g.transposed) ? 1 : 0};
     const int32_t chunks = (int32_t)((count + kChunk - 1) / kChunk);  // the separate pass 1
     if (!no_iterations) {
-        uint16_t *x = reinterpret_cast<uint16_t *>(ws + L.x);
-        const int64_t xs = (int64_t)(L.x_stride / 2);
         int32_t parts = tiles;
         if (g.transposed && g.mp % 128 == 0 && g.np % 128 == 0) {
             // 128 x 128 tiles: 512-byte runs of M read and 256-byte runs of X written
             parts = (g.np / 128) * (g.mp / 128);
             hipLaunchKernelGGL(muon_momentum_x_kernel<128>, dim3(parts, g.batch), dim3(kThreads),
-                               0, stream, ptrs, sa, partials, g.norm_blocks, x, xs);
+                               0, stream, ptrs, sa, partials, g.norm_blocks, x, xstr);
         } else if (g.transposed) {
             hipLaunchKernelGGL(muon_momentum_x_kernel<kTile>, dim3(tiles, g.batch), dim3(kThreads),
-                               0, stream, ptrs, sa, partials, g.norm_blocks, x, xs);
+                               0, stream, ptrs, sa, partials, g.norm_blocks, x, xstr);
         } else {
             const int32_t fchunks = (int32_t)((count + kThreads * kFlatEPT - 1) / (kThreads * kFlatEPT));
             hipLaunchKernelGGL(muon_momentum_xflat_kernel, dim3(fchunks, g.batch), dim3(kThreads),
-                               0, stream, ptrs, sa, partials, g.norm_blocks, x, xs);
+                               0, stream, ptrs, sa, partials, g.norm_blocks, x, xstr);
             parts = fchunks;
             const int64_t pad = (int64_t)g.rows * (g.np - g.cols) + (int64_t)(g.mp - g.rows) * g.np;
             if (pad > 0) {
@@ -749,22 +804,24 @@ hipError_t launch_muon_pre(const MuonGeom &g, const MuonPtrs &ptrs, float mu,
                 hipLaunchKernelGGL(muon_x_pad_kernel,
                                    dim3((uint32_t)(blocks < kPadBlocks ? blocks : kPadBlocks),
                                         g.batch),
-                                   dim3(kThreads), 0, stream, g.rows, g.cols, g.np, pad, x, xs);
+                                   dim3(kThreads), 0, stream, g.rows, g.cols, g.np, pad, x, xstr);
             }
         }
-        hipLaunchKernelGGL(muon_norm_kernel, dim3(g.batch), dim3(kThreads), 0, stream, partials,
-                           g.norm_blocks, parts, scale, ns_eps);
+        // the norm, and the rewrite of X for a matrix whose ||U||_F^2 is out of
+        // the first iteration's range (the other workgroups leave at once)
+        const int fb = tiles < kFallbackBlocks ? tiles : kFallbackBlocks;
+        hipLaunchKernelGGL(muon_norm_kernel, dim3(fb, g.batch), dim3(kThreads), 0, stream, ptrs,
+                           sa, partials, g.norm_blocks, parts, sd, xs, ns_eps, 1, tiles, x, xstr);
         return hipGetLastError();
     }
     PreArgs pa{(int32_t)count, vec ? 1 : 0, mu, omm, nesterov, dev};
     hipLaunchKernelGGL(muon_momentum_kernel, dim3(chunks, g.batch), dim3(kThreads),
                        0, stream, ptrs, pa, partials, g.norm_blocks);
-    hipLaunchKernelGGL(muon_norm_kernel, dim3(g.batch), dim3(kThreads), 0, stream, partials,
-                       g.norm_blocks, chunks, scale, ns_eps);
+    hipLaunchKernelGGL(muon_norm_kernel, dim3(1, g.batch), dim3(kThreads), 0, stream, ptrs, sa,
+                       partials, g.norm_blocks, chunks, sd, xs, ns_eps, 0, tiles, x, xstr);
     hipLaunchKernelGGL(muon_scale_kernel, dim3(tiles, g.batch), dim3(kThreads), 0, stream,
-                       ptrs, sa, scale, reinterpret_cast<uint16_t *>(ws + L.x),
-                       reinterpret_cast<uint16_t *>(ws + L.xt1),
-                       (int64_t)(L.x_stride / 2), (int64_t)(L.x_stride / 2));
+                       ptrs, sa, sd, x, reinterpret_cast<uint16_t *>(ws + L.xt1), xstr,
+                       (int64_t)(L.x_stride / 2));
     return hipGetLastError();
 }
 

@@ -100,7 +100,8 @@ MuonWorkspace muon_workspace_layout(const MuonGeom &g) {
     L.part = off;
     if (g.ksplit > 1) off += round_up((size_t)g.ksplit * g.batch * g.mp * g.mp * 4, 256);
     L.partials = off;
-    off += round_up(((size_t)g.batch * g.norm_blocks + g.batch) * sizeof(float), 256);
+    off += round_up(((size_t)g.batch * g.norm_blocks + g.batch) * sizeof(double) +
+                        (size_t)g.batch * sizeof(float), 256);
     const size_t hparts = (size_t)g.batch * g.health_blocks;
     L.hsum = off;  off += round_up(hparts * sizeof(double), 256);
     L.hmax = off;  off += round_up(hparts * sizeof(float), 256);
@@ -254,8 +255,16 @@ ZOPT_EXPORT zopt_status zopt_set_ns_workgroup_limit(int32_t n) {
 
 namespace {
 
+// The Newton-Schulz kernels address a panel of up to 256 rows of the padded
+// m x np matrix, and a 32-row stage of its columns, with 32-bit byte offsets
+// (256 * np * 2 < 2^31 needs np < 2^22); the longer side is held to 2^21,
+// which leaves every such offset below 2^30, and the element count to
+// below 2^31 (the streaming passes index a matrix in 32 bits).
+constexpr int64_t kMuonMaxSide = (int64_t)1 << 21;
+
 zopt_status muon_check_shape(int32_t batch, int64_t rows, int64_t cols) {
     if (batch < 1 || batch > kMaxBatch || rows < 1 || cols < 1) return ZOPT_ERR_SIZE;
+    if (rows > kMuonMaxSide || cols > kMuonMaxSide) return ZOPT_ERR_SIZE;
     if (rows * cols >= ((int64_t)1 << 31)) return ZOPT_ERR_SIZE;
     return ZOPT_OK;
 }

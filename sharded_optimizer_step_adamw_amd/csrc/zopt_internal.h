@@ -138,10 +138,12 @@ enum : int { kDevLr = 0, kDevMomentum = 1, kDevWeightDecay = 2, kDevScalars = 3 
 // dev: device scalars (mu is read there and omm formed from it) or NULL (mu
 // as given).
 // Steps the momentum and forms s = 1 / (||U||_F + eps) per matrix (at
-// muon_scale_ptr).  With iterations to follow, the x region receives
-// bf16(U) in the Newton-Schulz orientation and the first iteration applies
-// s; with no_iterations, X0 = bf16(U s) itself (the call's result), and X0^T
-// in xt1 as well for matrices stored transposed.
+// muon_sd_ptr).  With iterations to follow, the x region receives bf16(U) in
+// the Newton-Schulz orientation and the first iteration applies s (the factor
+// at muon_scale_ptr), or, for a matrix whose ||U||_F^2 is too large or too
+// small for that, X0 = bf16(U s) and the factor is 1; with no_iterations,
+// X0 = bf16(U s) itself (the call's result), and X0^T in xt1 as well for
+// matrices stored transposed.
 hipError_t launch_muon_pre(const MuonGeom &g, const MuonPtrs &ptrs, float mu,
                            int32_t nesterov, float ns_eps, char *ws,
                            const MuonWorkspace &L, bool no_iterations, const float *dev,
@@ -151,9 +153,15 @@ hipError_t launch_muon_pre(const MuonGeom &g, const MuonPtrs &ptrs, float mu,
 // workgroups and norm partials per matrix).
 int32_t muon_pre_tiles(const MuonGeom &g);
 
-// The per-matrix pre-scale s of a group, after its norm partials.
+// The partials region of a group: batch * norm_blocks fp64 partial sums of
+// U^2, then per matrix the pre-scale s = 1 / (||U||_F + eps) in fp64, then
+// per matrix the binary32 factor the first Newton-Schulz iteration applies to
+// its products of X (s, or 1 where the pre-step wrote X0 = bf16(U s) itself).
+inline double *muon_sd_ptr(char *ws, const MuonGeom &g, const MuonWorkspace &L) {
+    return reinterpret_cast<double *>(ws + L.partials) + (int64_t)g.batch * g.norm_blocks;
+}
 inline float *muon_scale_ptr(char *ws, const MuonGeom &g, const MuonWorkspace &L) {
-    return reinterpret_cast<float *>(ws + L.partials) + (int64_t)g.batch * g.norm_blocks;
+    return reinterpret_cast<float *>(muon_sd_ptr(ws, g, L) + g.batch);
 }
 
 // reject: per-matrix flags (non-zero: leave that matrix untouched) or NULL.

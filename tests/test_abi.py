@@ -173,6 +173,12 @@ def muon(**kw):
     (dict(batch=0), z.ZOPT_ERR_SIZE), (dict(batch=65), z.ZOPT_ERR_SIZE),
     (dict(rows=0), z.ZOPT_ERR_SIZE), (dict(cols=-3), z.ZOPT_ERR_SIZE),
     (dict(rows=1 << 16, cols=1 << 15), z.ZOPT_ERR_SIZE),
+    # thin, long matrices past the 2^21 side limit (element count below 2^31):
+    # 32-bit panel offsets of the Newton-Schulz kernels would wrap
+    (dict(rows=8, cols=250_000_000), z.ZOPT_ERR_SIZE),
+    (dict(rows=30_000_000, cols=64), z.ZOPT_ERR_SIZE),
+    (dict(rows=1, cols=(1 << 31) - 1), z.ZOPT_ERR_SIZE),
+    (dict(rows=(1 << 21) + 1, cols=1), z.ZOPT_ERR_SIZE),
     (dict(master=None), z.ZOPT_ERR_NULL), (dict(grad=ptrs(2, null_at=1)), z.ZOPT_ERR_NULL),
     (dict(weight=ptrs(2, null_at=0)), z.ZOPT_ERR_NULL), (dict(ws_bytes=None), z.ZOPT_ERR_NULL),
     (dict(lr=-1.0), z.ZOPT_ERR_HYPER), (dict(mu=1.0), z.ZOPT_ERR_HYPER),
@@ -184,6 +190,12 @@ def muon(**kw):
 ])
 def test_muon_rejects(kw, status):
     assert muon(**kw) == status
+
+
+def test_muon_side_limit_is_inclusive():
+    # 2^21 on the longer side is accepted (the workspace query answers)
+    for rows, cols in ((1, 1 << 21), (1 << 21, 512), (1023, 1 << 21)):
+        assert z.muon_workspace_bytes(1, rows, cols) > 0
 
 
 def test_muon_workspace_query_and_too_small():

@@ -188,20 +188,113 @@ def test_ns_closed_form_on_singular_values(m, n, spectrum):
     assert rel_fro(o, closed) <= NS_TOL
 
 
+# Singular values spanning two decades are the one input class measured
+# outside 2e-2: the smallest directions grow by ~3.44 per iteration and so
+# does the bf16 rounding noise in them, so any bf16 Newton-Schulz ends
+# ~2.5-3e-2 from float64 there.  The bar for it is stated here, against the
+# float64 oracle.
+NS_TOL_TWO_DECADE = 3e-2
+
+
 @pytest.mark.parametrize("m,n", [(64, 192), (384, 128)])
 def test_ns_two_decade_spectrum_is_bf16_limited(m, n):
-    """Singular values spanning 1 .. 1e-2: the smallest directions grow by
-    ~3.44 per iteration and so does the bf16 noise injected into them; any
-    bf16 Newton-Schulz ends ~2.5-3e-2 from float64 here.  The GPU must not
-    add error beyond the bf16 rounding model of the same input."""
+    """Singular values 1 .. 1e-2 (geometric): within NS_TOL_TWO_DECADE of the
+    float64 oracle.  The bf16 rounding model's error on the same input is
+    printed beside it as a diagnostic only."""
     from ns_bf16_model import newton_schulz_bf16_model
     sigma = np.geomspace(1.0, 1e-2, min(m, n))
     o, gf, _, _ = ns_on_spectrum(m, n, sigma, seed=m + n)
     ref = oracle.newton_schulz(gf)
     model_err = rel_fro(newton_schulz_bf16_model(gf), ref)
     gpu_err = rel_fro(o, ref)
-    print(f"two-decade spectrum {m}x{n}: GPU {gpu_err:.3e}, bf16 model {model_err:.3e}")
-    assert gpu_err <= 1.25 * model_err
+    print(f"two-decade spectrum {m}x{n}: GPU {gpu_err:.3e} (bf16 model {model_err:.3e})")
+    assert gpu_err <= NS_TOL_TWO_DECADE
+
+
+def extreme_grads(rows, cols, kind, seed):
+    """bf16 gradients of a magnitude far from the usual: a Gaussian times
+    `kind` (a float), or 'bf16max': N(0, 1e-3) with 1% of the entries set to
+    +-0x7F7F, the largest finite bf16."""
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal((rows, cols))
+    if kind == "bf16max":
+        g = (g * 1e-3).astype(np.float32)
+        mask = rng.random((rows, cols)) < 0.01
+        bits = wl.to_bf16_bits(g)
+        bits[mask] = np.where(rng.random(int(mask.sum())) < 0.5, 0x7F7F, 0xFF7F)
+        return bits
+    return wl.to_bf16_bits((g * kind).astype(np.float32))
+
+
+@pytest.mark.parametrize("rows,cols,kinds,ns_steps", [
+    (768, 3072, (1e17, 1e30, "bf16max", 1e12, 1e-30, 1e-10), 5),
+    (3072, 768, (1e17, "bf16max"), 5),
+    (768, 3072, (1e17, 1e30, "bf16max", 1e-30), 0),
+    (4096, 4096, (1e17, "bf16max"), 5),
+    (4096, 4096, (1e30,), 0),
+])
+def test_extreme_gradient_magnitudes(rows, cols, kinds, ns_steps):
+    """Huge and tiny finite gradients (||U||_F^2 from ~2^-190 to ~2^270,
+    inside and outside the range where the first iteration applies the
+    pre-scale to products of bf16(U)), each in one group beside a matrix of
+    ordinary gradients: the update is NaN-free and within 2e-2 of float64,
+    the momentum and the teacher-forced post-step bit for bit."""
+    k = len(kinds) + 1
+    P, M, G = make_inputs(k, rows, cols, seed=rows + cols + ns_steps, momentum_nonzero=False)
+    for i, kind in enumerate(kinds):
+        G[i + 1] = extreme_grads(rows, cols, kind, seed=17 + i)
+    gP, gM, gG = [dev_f32(p) for p in P], [dev_f32(m) for m in M], [dev_bf16(g) for g in G]
+    gW = [torch.empty((rows, cols), dtype=torch.bfloat16, device=DEV) for _ in range(k)]
+    lr, mu, wd = f32(8e-4), f32(0.95), f32(0.1)
+    ws = z.muon_step(gP, gM, gG, gW, lr, mu, True, wd, ns_steps)
+    torch.cuda.synchronize()
+    for i in range(k):
+        kind = "normal" if i == 0 else kinds[i - 1]
+        m = M[i].copy()
+        u = oracle.muon_pre(m, G[i], mu, True)
+        np.testing.assert_array_equal(gM[i].cpu().numpy().view(np.uint32), m.view(np.uint32))
+        o = oracle.bf16_bits_to_f32(u16(z.muon_output_view(ws, k, rows, cols, ns_steps, i)))
+        assert not np.isnan(o).any(), kind
+        err = rel_fro(o.astype(np.float64), oracle.newton_schulz(u, ns_steps))
+        print(f"{rows}x{cols} ns_steps={ns_steps} grads {kind}: NS rel err {err:.3e}", flush=True)
+        assert err <= NS_TOL, (kind, err)
+        p = P[i].copy()
+        w = oracle.muon_post(p, o, lr, wd, 1)
+        np.testing.assert_array_equal(gP[i].cpu().numpy().view(np.uint32), p.view(np.uint32))
+        np.testing.assert_array_equal(u16(gW[i]), w)
+
+
+@pytest.mark.parametrize("rows,cols,ns_steps", [(200, 520, 5), (520, 200, 5), (200, 520, 0)])
+def test_infinite_gradient_gives_nan_update_like_the_oracle(rows, cols, ns_steps):
+    """An infinite gradient entry: ||U||_F is infinite, so the oracle's
+    pre-scaled matrix holds NaN at that entry and 0 elsewhere, and Newton-
+    Schulz spreads the NaN over the whole update -- the GPU's update is NaN
+    wherever the oracle's is, the matrix beside it in the group is unaffected,
+    momentum and the teacher-forced post-step are bit for bit (NaN where the
+    oracle's is NaN)."""
+    P, M, G = make_inputs(2, rows, cols, seed=23, momentum_nonzero=True)
+    G[1] = G[1].copy()
+    G[1][rows // 3, cols // 5] = 0x7F80  # +Inf
+    gP, gM, gG = [dev_f32(p) for p in P], [dev_f32(m) for m in M], [dev_bf16(g) for g in G]
+    lr, mu, wd = f32(8e-4), f32(0.95), f32(0.1)
+    ws = z.muon_step(gP, gM, gG, None, lr, mu, True, wd, ns_steps)
+    torch.cuda.synchronize()
+    for i in range(2):
+        m = M[i].copy()
+        u = oracle.muon_pre(m, G[i], mu, True)
+        np.testing.assert_array_equal(gM[i].cpu().numpy().view(np.uint32), m.view(np.uint32))
+        o = oracle.bf16_bits_to_f32(u16(z.muon_output_view(ws, 2, rows, cols, ns_steps, i)))
+        with np.errstate(invalid="ignore"):
+            ref = oracle.newton_schulz(u, ns_steps)
+        np.testing.assert_array_equal(np.isnan(o), np.isnan(ref))
+        if i == 0:
+            assert rel_fro(o.astype(np.float64), ref) <= NS_TOL
+        p = P[i].copy()
+        oracle.muon_post(p, o, lr, wd, 1, want_weight=False)
+        got = gP[i].cpu().numpy()
+        nan = np.isnan(p)
+        assert np.array_equal(np.isnan(got), nan)  # NaN payloads may differ
+        np.testing.assert_array_equal(got[~nan].view(np.uint32), p[~nan].view(np.uint32))
 
 
 def test_deterministic_run_to_run():
@@ -241,12 +334,29 @@ def test_gpt2_small_shapes():
             np.testing.assert_array_equal(gP[i].cpu().numpy().view(np.uint32), P[i].view(np.uint32))
 
 
+NS_BLOCK = 128
+NS_TOL_BLOCK = 5e-2
+
+
+def blockwise_rel_fro(o, ref, blk=NS_BLOCK):
+    """The largest relative Frobenius error over the blk x blk blocks of the
+    update (ragged edge blocks included).  A wrong 16 x 16 MFMA block inside a
+    128 x 128 block is 1/8 of its norm: ~0.12 there, while on the whole of a
+    4096 x 14336 matrix it would add well under the 2e-2 bar."""
+    worst = 0.0
+    for r in range(0, o.shape[0], blk):
+        for c in range(0, o.shape[1], blk):
+            worst = max(worst, rel_fro(o[r:r + blk, c:c + blk], ref[r:r + blk, c:c + blk]))
+    return worst
+
+
 @pytest.mark.parametrize("workload", ["llama1b_rank0_muon", "llama8b_rank0_muon"])
 def test_full_size_groups_one_matrix_each(workload):
     """The full 1B and 8B rank-0 shares in the launch configuration the
     benchmark times (one zopt_muon_step_groups call over all groups);
-    momentum and post-step are checked on every matrix, NS against fp64 on one
-    matrix per group."""
+    momentum and post-step are checked on every matrix, NS against fp64 on the
+    first and the last matrix of every group: within 2e-2 on the whole matrix
+    and within NS_TOL_BLOCK on every 128 x 128 block."""
     w = wl.MUON_WORKLOADS[workload]
     calls, inputs = [], []
     for gi, grp in enumerate(w.groups):
@@ -270,10 +380,14 @@ def test_full_size_groups_one_matrix_each(workload):
             u = oracle.muon_pre(m, G[i], f32(w.momentum), True)
             np.testing.assert_array_equal(gM[i].cpu().numpy().view(np.uint32), m.view(np.uint32))
             o = oracle.bf16_bits_to_f32(u16(z.muon_groups_output_view(ws, shapes, 5, gi, i)))
-            if i == 0:
-                err = rel_fro(o.astype(np.float64), oracle.newton_schulz(u))
-                print(f"{workload} group {shape} x{grp.count}: NS rel err {err:.3e}", flush=True)
+            if i in (0, grp.count - 1):
+                ref = oracle.newton_schulz(u)
+                o64 = o.astype(np.float64)
+                err, berr = rel_fro(o64, ref), blockwise_rel_fro(o64, ref)
+                print(f"{workload} group {shape} x{grp.count} matrix {i}: NS rel err {err:.3e}, "
+                      f"worst {NS_BLOCK}-block {berr:.3e}", flush=True)
                 assert err <= NS_TOL
+                assert berr <= NS_TOL_BLOCK
             p = P0[i]
             oracle.muon_post(p, o, f32(w.lr), f32(w.weight_decay), 1, want_weight=False)
             np.testing.assert_array_equal(gP[i].cpu().numpy().view(np.uint32), p.view(np.uint32))
