@@ -23,12 +23,13 @@
  * Conventions common to every call
  * --------------------------------
  *  - Every buffer is device memory owned by the caller.  The library
- *    allocates no device memory and keeps no state between calls, with two
- *    exceptions: a captured Muon graph is a handle the caller owns; and
+ *    allocates no device memory at run time and keeps no state between calls,
+ *    with three exceptions: a captured Muon graph is a handle the caller owns;
  *    zopt_set_ns_workgroup_limit is a process-wide setting that every later
  *    call in the process uses (one thread's setting changes the launch plan,
- *    never the results, of another's calls).  Every other call is
- *    reentrant.
+ *    never the results, of another's calls); and zopt_grad_sq_norm_noalloc
+ *    uses a 16 KiB array per GPU that the library holds for the life of the
+ *    process.  Every other call is reentrant.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *    the call returns without synchronising.  All launch parameters travel
  *    as kernel arguments, so back-to-back calls need no host sync.
@@ -190,6 +191,31 @@ enum {
 zopt_status zopt_grad_sq_norm(const uint16_t *grad, int64_t N, int64_t bucket, int32_t world,
                               int32_t rank, int64_t shard_len, double *sq, void *workspace,
                               size_t *workspace_bytes, void *stream);
+
+/*
+ * zopt_grad_sq_norm_noalloc -- zopt_grad_sq_norm for callers that cannot
+ * allocate device memory (code under stream capture, tight training loops,
+ * harnesses that forbid allocation): the same sum, bit for bit, with the
+ * partial sums kept in a scratch array inside the library instead of a
+ * caller's workspace.  The array is 16 KiB per GPU (2048 doubles, the most
+ * partials any shard length needs), allocated when the library is loaded and
+ * held until the process ends; the call itself allocates nothing.  Every
+ * call on one GPU uses that GPU's one array, so calls that may overlap on a
+ * GPU (different streams, or different host threads without ordering) race
+ * and must not be issued; calls in one stream are ordered and safe.  The
+ * array needs no clearing: each call writes every partial it reads.
+ *
+ * Arguments as zopt_grad_sq_norm, without workspace and workspace_bytes.
+ *
+ * Errors: ZOPT_ERR_NULL (grad or sq NULL); ZOPT_ERR_SIZE (the layout
+ * arguments as for zopt_adamw_shard_step); ZOPT_ERR_WORKSPACE (the partials
+ * would exceed the array -- no valid layout does); ZOPT_ERR_DEVICE (the
+ * array's address could not be found on the current device, or a launch
+ * failed).
+ */
+zopt_status zopt_grad_sq_norm_noalloc(const uint16_t *grad, int64_t N, int64_t bucket,
+                                      int32_t world, int32_t rank, int64_t shard_len,
+                                      double *sq, void *stream);
 
 /*
  * zopt_grad_clip_stats -- the clip statistics (layout above) from `count`

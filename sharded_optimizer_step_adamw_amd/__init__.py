@@ -20,6 +20,7 @@ Entry points (same names as the C ABI in include/zopt.h):
   round_bf16         fp32 -> bf16 round-to-nearest-even
   shard_len          the shard length the layout derives (zopt_shard_len)
   grad_sq_norm       sum of squares of a rank's real gradient elements
+  grad_sq_norm_noalloc  the same with the library's own scratch (allocates nothing)
   grad_clip_stats    clip statistics (device scalars) from summed squares
   adamw_shard_step_clipped   AdamW taking grad_scale from the clip statistics
 """
@@ -72,6 +73,8 @@ def _lib_or_raise() -> ctypes.CDLL:
         L.zopt_grad_sq_norm.argtypes = [vp, i64, i64, i32, i32, i64, vp, vp,
                                         ctypes.POINTER(ctypes.c_size_t), vp]
         L.zopt_grad_sq_norm.restype = ctypes.c_int
+        L.zopt_grad_sq_norm_noalloc.argtypes = [vp, i64, i64, i32, i32, i64, vp, vp]
+        L.zopt_grad_sq_norm_noalloc.restype = ctypes.c_int
         L.zopt_grad_clip_stats.argtypes = [vp, i32, f32, f32, vp, vp]
         L.zopt_grad_clip_stats.restype = ctypes.c_int
         L.zopt_shard_len.argtypes = [i64, i64, i32]
@@ -220,6 +223,21 @@ def grad_sq_norm(grad, n, bucket, world, rank, out: Optional[torch.Tensor] = Non
                                  shard_len(n, bucket, world), out.data_ptr(),
                                  workspace.data_ptr(), ctypes.byref(size), _stream(dev, stream))
     _check(st, "zopt_grad_sq_norm")
+    return out
+
+
+def grad_sq_norm_noalloc(grad, n, bucket, world, rank, out: torch.Tensor,
+                         stream=None) -> torch.Tensor:
+    """grad_sq_norm with the library's own 16 KiB scratch per GPU instead of
+    a workspace (zopt_grad_sq_norm_noalloc): `out` is a float64 [1] device
+    tensor the caller provides, and the call allocates nothing.  Calls that
+    overlap on one GPU race on the scratch."""
+    _need(grad, torch.bfloat16, n, "grad")
+    _need(out, torch.float64, 1, "out", grad.device)
+    st = lib().zopt_grad_sq_norm_noalloc(grad.data_ptr(), n, bucket, world, rank,
+                                         shard_len(n, bucket, world), out.data_ptr(),
+                                         _stream(grad.device, stream))
+    _check(st, "zopt_grad_sq_norm_noalloc")
     return out
 
 

@@ -7,6 +7,7 @@
 // passes.
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "zopt.h"
 #include "zopt_internal.h"
@@ -220,6 +221,57 @@ ZOPT_EXPORT zopt_status zopt_grad_sq_norm(const uint16_t *grad, int64_t N, int64
     if (!grad || !sq) return ZOPT_ERR_NULL;
     if (*workspace_bytes < need || ((uintptr_t)workspace & 255u)) return ZOPT_ERR_WORKSPACE;
     hipError_t e = launch_grad_sq_norm(grad, p, (double *)workspace, sq, (hipStream_t)stream);
+    return e == hipSuccess ? ZOPT_OK : ZOPT_ERR_DEVICE;
+}
+
+// The scratch of zopt_grad_sq_norm_noalloc: the fp64 partials of the norm
+// pass (at most kNormBlocksMax, 16 KiB).  Each GPU the library runs on holds
+// its own copy until the process ends.  In host code `scratch` names a host
+// stand-in, never the device memory: host code uses the address
+// hipGetSymbolAddress gives for the current device (scratch_address).
+static __device__ __align__(256) double scratch[kNormBlocksMax];
+
+namespace {
+
+constexpr int kScratchDevices = 256;
+std::mutex g_scratch_mutex;
+void *g_scratch_addr[kScratchDevices];  // per device, set at its first call
+
+// The device address of `scratch` on the current device, looked up once per
+// device with that device current.
+hipError_t scratch_address(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_addr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_addr[dev] = p;
+    }
+    *out = g_scratch_addr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+ZOPT_EXPORT zopt_status zopt_grad_sq_norm_noalloc(const uint16_t *grad, int64_t N,
+                                                  int64_t bucket, int32_t world, int32_t rank,
+                                                  int64_t shard_len, double *sq, void *stream) {
+    if (!grad || !sq) return ZOPT_ERR_NULL;
+    if (N < 1 || bucket < 1 || world < 1 || rank < 0 || rank >= world) return ZOPT_ERR_SIZE;
+    if (N > ((int64_t)1 << 40)) return ZOPT_ERR_SIZE;
+    AdamWParams p{};
+    if (shard_len != adamw_layout(N, bucket, world, rank, p)) return ZOPT_ERR_SIZE;
+    p.shard_len = shard_len;
+    const size_t need = (size_t)grad_sq_norm_blocks(shard_len) * sizeof(double);
+    if (need > sizeof(scratch)) return ZOPT_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (scratch_address(&ws) != hipSuccess) return ZOPT_ERR_DEVICE;
+    hipError_t e = launch_grad_sq_norm(grad, p, (double *)ws, sq, (hipStream_t)stream);
     return e == hipSuccess ? ZOPT_OK : ZOPT_ERR_DEVICE;
 }
 
