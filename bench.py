@@ -28,7 +28,8 @@ Inputs are seeded and synthetic, generated on the GPU before timing, so the
 timed region starts with everything resident in HBM.  Timing: W untimed
 warm-up steps, then K steps bracketed by torch.cuda.synchronize() and HIP
 events on the stream the library launches on.  `cpu_baseline` times the CPU
-oracle (test infrastructure) on the same headline step on the host.
+oracle (test infrastructure) on the host: the same headline step in full, and
+the other workloads on stated samples.
 """
 from __future__ import annotations
 
@@ -457,24 +458,149 @@ def bench_copy(torch, z, timer, dev, K, W):
                 gbs=round(6 * n / ms / 1e6, 1))
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def _cpu_threads():
+    """The threads the all-cores legs use: the process's CPU share, capped by
+    OMP_NUM_THREADS where it is set (the BLAS behind numpy follows it too)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    return max(1, min(n, int(cap))) if cap.isdigit() and int(cap) > 0 else n
+
+
+def _blas_limit(n):
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(limits=n)
+    except Exception:  # no control over BLAS threads: leave them as they are
+        import contextlib
+        return contextlib.nullcontext()
+
+
+def _adamw_points_timed(oracle, arrays, hp, steps, threads, step0=1):
+    """The oracle's element-wise AdamW (binary32, scalar C) over `steps`
+    steps of the given elements, split into `threads` contiguous chunks run
+    concurrently (ctypes releases the GIL during the call).  Seconds."""
+    from concurrent.futures import ThreadPoolExecutor
+    p, m, v, g = arrays
+    n = p.size
+    bounds = [(k * n // threads, (k + 1) * n // threads) for k in range(threads)]
+
+    def run(b, t):
+        lo, hi = b
+        oracle.adamw_points(p[lo:hi], m[lo:hi], v[lo:hi], g[lo:hi], *hp, t)
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(threads) as ex:
+        for t in range(step0, step0 + steps):
+            list(ex.map(run, bounds, [t] * threads))
+    return time.perf_counter() - t0
+
+
+def _gathered_grads(oracle, part, rng_grad):
+    """binary32 gradients of rank part.rank's shard elements (the flat
+    gradient gathered through the oracle's index map; padding 0)."""
+    import numpy as np
+    sl = oracle.shard_len(part.n, part.bucket, part.world)
+    flat, real = oracle.shard_index_map(part.n, part.bucket, part.world, part.rank,
+                                        np.arange(sl))
+    g = np.zeros(sl, np.float32)
+    g[real] = oracle.bf16_bits_to_f32(rng_grad[flat[real]])
+    return g
+
+
+def _muon_one_per_shape(oracle, wl, w, threads):
+    """One matrix per distinct stored shape through the oracle's whole Muon
+    step with no iteration (binary32 pre- and post-step in C, the float64
+    pre-scale), plus the cost of one float64 Newton-Schulz iteration through
+    numpy's BLAS on `threads` threads, timed once per distinct Newton-Schulz
+    shape (min x max: both orientations of a shape iterate on the same
+    product sizes) as ns(U, 1) - ns(U, 0).  Per matrix: t0 + 5 iterations;
+    then times the group's matrix count.  Seconds, and the per-shape rows."""
+    import numpy as np
+    per_shape, total, iter_s = [], 0.0, {}
+    with _blas_limit(threads):
+        for gi, grp in enumerate(w.groups):
+            shape = (grp.rows, grp.cols)
+            r = wl.rng(w.wid, 700 + gi)
+            p = r.standard_normal(shape, dtype=np.float32) * np.float32(w.master_std)
+            if w.grad_dist == "student_t3":
+                gx = r.standard_t(3, size=shape) * w.grad_std
+            else:
+                gx = r.standard_normal(shape, dtype=np.float32) * np.float32(w.grad_std)
+            g = wl.to_bf16_bits(np.asarray(gx, np.float32))
+            del gx
+            mm = np.zeros(shape, np.float32)
+            t = time.perf_counter()
+            oracle.muon_step(p, mm, g, w.lr, w.momentum, w.nesterov, w.weight_decay, 0,
+                             w.ns_coeffs, w.ns_eps, w.adjust_lr)
+            t0 = time.perf_counter() - t
+            key = (min(shape), max(shape))
+            if key not in iter_s:
+                u = oracle.muon_pre(np.zeros(shape, np.float32), g, w.momentum, w.nesterov)
+                ts = []
+                for steps in (0, 1):
+                    t = time.perf_counter()
+                    oracle.newton_schulz(u, steps, w.ns_coeffs, w.ns_eps)
+                    ts.append(time.perf_counter() - t)
+                iter_s[key] = max(ts[1] - ts[0], 0.0)
+                del u
+            one = t0 + w.ns_steps * iter_s[key]
+            total += one * grp.count
+            per_shape.append(dict(shape=list(shape), count=grp.count,
+                                  s_step_no_iteration=round(t0, 3),
+                                  s_per_iteration=round(iter_s[key], 3),
+                                  s_per_matrix_extrapolated=round(one, 3)))
+            del p, g, mm
+    return total, per_shape
+
+
 def cpu_baseline():
-    """The CPU oracle (test infrastructure, untuned) on the same headline step:
-    the two AdamW calls over all 38,652,672 elements (scalar C, one thread)
-    and all 72 Muon matrices (binary32 pre/post in C, float64 Newton-Schulz
-    through numpy's BLAS)."""
+    """The CPU oracle (test infrastructure, untuned) on the host cores.
+
+    `value` is the headline GPT-2-small step in full (not extrapolated) on all
+    the threads the process may use: the two AdamW calls over 38,652,672
+    elements split into one contiguous chunk per thread, and all 72 Muon
+    matrices with float64 Newton-Schulz through numpy's BLAS.  `configs`
+    times the other workloads the same way, each with its sample stated:
+    the tiny one in full on 1 thread and on all; the ZeRO-2 shard on a
+    seeded sample of 1,048,576 shard indices over 100 steps, extrapolated to
+    the whole shard, plus the whole shard's step 1; the 1B and 8B Muon shares
+    on one matrix per shape, extrapolated by iteration and matrix count."""
     import numpy as np
     import oracle
     import workloads as wl
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        blas_threads = os.cpu_count() or 1
+    T = _cpu_threads()
+    configs = {}
+
+    # --- headline: the GPT-2-small step, whole
     wa, wm = wl.GPT2_ADAMW, wl.GPT2_MUON
     n = wa.n_total
-    p = wl.host_normal(wa.wid, 0, n, wa.master_std)
-    g = wl.host_grad_bf16(wa.wid, 1, n, wa.grad_std, "normal_outliers")
-    m, v, w = np.zeros_like(p), np.zeros_like(p), np.zeros(n, np.uint16)
+    p0 = wl.host_normal(wa.wid, 0, n, wa.master_std)
+    gb = wl.host_grad_bf16(wa.wid, 1, n, wa.grad_std, "normal_outliers")
+    g32 = oracle.bf16_bits_to_f32(gb)
+    adamw_s = {}
+    for threads in (1, T):
+        secs = 0.0
+        for part in wa.parts:
+            s = slice(part.offset, part.offset + part.n)
+            arrays = (p0[s].copy(), np.zeros(part.n, np.float32), np.zeros(part.n, np.float32),
+                      g32[s].copy())
+            hp = (part.lr, part.beta1, part.beta2, part.eps, part.weight_decay)
+            secs += _adamw_points_timed(oracle, arrays, hp, 1, threads)
+        adamw_s[threads] = secs
     mats = []
     for gi, grp in enumerate(wm.groups):
         for i in range(grp.count):
@@ -483,25 +609,95 @@ def cpu_baseline():
                          np.zeros(shape, np.float32),
                          wl.host_grad_bf16(wm.wid, 5000 + 100 * gi + i, shape, wm.grad_std,
                                            "normal_outliers")))
-    t0 = time.perf_counter()
-    for part in wa.parts:
-        s = slice(part.offset, part.offset + part.n)
-        pv, mv, vv, wv = p[s].copy(), m[s].copy(), v[s].copy(), w[s].copy()
-        oracle.adamw_shard_step(pv, mv, vv, g[s].copy(), wv, part.n, part.bucket, part.world,
-                                part.rank, part.lr, part.beta1, part.beta2, part.eps,
-                                part.weight_decay, 1)
-    t1 = time.perf_counter()
-    for master, mom, grad in mats:
-        oracle.muon_step(master, mom, grad, wm.lr, wm.momentum, wm.nesterov, wm.weight_decay,
-                         wm.ns_steps, wm.ns_coeffs, wm.ns_eps, wm.adjust_lr)
-    t2 = time.perf_counter()
-    return dict(value=round((t2 - t0) * 1e3, 1), unit="ms per optimizer step",
-                cores=int(blas_threads), kind="oracle",
+    with _blas_limit(T):
+        t0 = time.perf_counter()
+        for master, mom, grad in mats:
+            oracle.muon_step(master, mom, grad, wm.lr, wm.momentum, wm.nesterov,
+                             wm.weight_decay, wm.ns_steps, wm.ns_coeffs, wm.ns_eps, wm.adjust_lr)
+        muon_s = time.perf_counter() - t0
+    head_ms = (adamw_s[T] + muon_s) * 1e3
+    configs["gpt2_small_step"] = dict(
+        ms_per_step=round(head_ms, 1), threads=T, extrapolated=False,
+        adamw_ms_1_thread=round(adamw_s[1] * 1e3, 1), adamw_ms_all_threads=round(adamw_s[T] * 1e3, 1),
+        muon_ms=round(muon_s * 1e3, 1),
+        sample="whole step: AdamW over 38,652,672 elements, 72 Muon matrices, float64 NS")
+    del p0, gb, g32, mats
+
+    # --- tiny: whole, 10 steps, 1 thread and all
+    ta, tm = wl.TINY_ADAMW, wl.TINY_MUON
+    part = ta.parts[0]
+    sl = oracle.shard_len(part.n, part.bucket, part.world)
+    flat_g = wl.host_grad_bf16(ta.wid, 1, part.n, ta.grad_std)
+    g = _gathered_grads(oracle, part, flat_g)
+    p_t = wl.host_normal(ta.wid, 0, sl, ta.master_std)
+    hp = (part.lr, part.beta1, part.beta2, part.eps, part.weight_decay)
+    tiny = dict(sample="whole: AdamW rank-0 shard of 262,144 elements x 10 steps (one gradient "
+                       "reused) + Muon 2 x [128, 512] x 10 steps, float64 NS",
+                extrapolated=False, threads=T)
+    mats = [(wl.host_normal(tm.wid, 10 + i, (128, 512), tm.master_std),
+             wl.host_grad_bf16(tm.wid, 20 + i, (128, 512), tm.grad_std)) for i in range(2)]
+    for threads, key in ((1, "ms_per_step_1_thread"), (T, "ms_per_step_all_threads")):
+        arrays = (p_t.copy(), np.zeros(sl, np.float32), np.zeros(sl, np.float32), g)
+        a_s = _adamw_points_timed(oracle, arrays, hp, ta.steps, threads)
+        with _blas_limit(threads):
+            ms = [(p.copy(), np.zeros((128, 512), np.float32), gg) for p, gg in mats]
+            t0 = time.perf_counter()
+            for _ in range(tm.steps):
+                for master, mom, gg in ms:
+                    oracle.muon_step(master, mom, gg, tm.lr, tm.momentum, tm.nesterov,
+                                     tm.weight_decay, tm.ns_steps, tm.ns_coeffs, tm.ns_eps,
+                                     tm.adjust_lr)
+            m_s = time.perf_counter() - t0
+        tiny[key] = round((a_s / ta.steps + m_s / tm.steps) * 1e3, 2)
+    configs["tiny"] = tiny
+
+    # --- ZeRO-2 shard: a seeded sample of shard indices over 100 steps,
+    # extrapolated; and the whole shard's first step
+    wz = wl.ZERO2_ADAMW
+    part = wz.parts[0]
+    sl = oracle.shard_len(part.n, part.bucket, part.world)
+    k = 1_048_576
+    r = wl.rng(wz.wid, 900)
+    hp = (part.lr, part.beta1, part.beta2, part.eps, part.weight_decay)
+    sample_p = r.standard_normal(k, dtype=np.float32) * np.float32(wz.master_std)
+    sample_g = oracle.bf16_bits_to_f32(wl.to_bf16_bits(
+        r.standard_normal(k, dtype=np.float32) * np.float32(wz.grad_std)))
+    z2 = dict(sample=(f"a seeded sample of {k:,} shard elements over {wz.steps} steps (element-"
+                      f"wise: exact for those elements), per-step time extrapolated linearly to "
+                      f"the {sl:,}-element shard; plus the whole shard's step 1 (the sample's "
+                      f"values repeated over it)"),
+              extrapolated=True, threads=T)
+    for threads, key in ((1, "ms_per_step_extrapolated_1_thread"),
+                         (T, "ms_per_step_extrapolated_all_threads")):
+        arrays = (sample_p.copy(), np.zeros(k, np.float32), np.zeros(k, np.float32), sample_g)
+        secs = _adamw_points_timed(oracle, arrays, hp, wz.steps, threads)
+        z2[key] = round(secs / wz.steps * (sl / k) * 1e3, 1)
+    # the whole shard's step 1 (its values: the seeded sample repeated)
+    full = (np.resize(sample_p, sl), np.zeros(sl, np.float32), np.zeros(sl, np.float32),
+            np.resize(sample_g, sl))
+    z2["whole_shard_step1_ms_all_threads"] = round(
+        _adamw_points_timed(oracle, full, hp, 1, T) * 1e3, 1)
+    del full
+    configs["zero2_adamw_shard"] = z2
+
+    # --- Muon shares: one matrix per shape
+    for w, key in ((wl.LLAMA1B_MUON, "llama1b_rank0_muon"), (wl.LLAMA8B_MUON, "llama8b_rank0_muon")):
+        total, per_shape = _muon_one_per_shape(oracle, wl, w, T)
+        configs[key] = dict(
+            ms_per_step_extrapolated=round(total * 1e3, 1), threads=T, extrapolated=True,
+            sample=("one matrix per distinct stored shape through the whole Muon step with no "
+                    "iteration (t0), and one float64 Newton-Schulz iteration (t_it) per distinct "
+                    "Newton-Schulz shape; per matrix t0 + 5 t_it, times the group's matrix "
+                    "count"),
+            per_shape=per_shape)
+
+    return dict(value=round(head_ms, 1), unit="ms per optimizer step", cores=T, kind="oracle",
                 sample=("the whole headline step, not extrapolated: AdamW over 38,652,672 "
-                        f"elements in scalar C on 1 thread ({(t1 - t0) * 1e3:.0f} ms), 72 Muon "
-                        "matrices with float64 Newton-Schulz through numpy BLAS on "
-                        f"{blas_threads} threads ({(t2 - t1) * 1e3:.0f} ms)"),
-                host_cpus=os.cpu_count(), host=platform.processor() or platform.machine())
+                        f"elements in scalar C split over {T} threads "
+                        f"({adamw_s[T] * 1e3:.0f} ms; {adamw_s[1] * 1e3:.0f} ms on 1 thread), "
+                        f"72 Muon matrices with float64 Newton-Schulz through numpy BLAS on {T} "
+                        f"threads ({muon_s * 1e3:.0f} ms)"),
+                cpu_model=_cpu_model(), host_cpus=os.cpu_count(), configs=configs)
 
 
 def main():
