@@ -133,6 +133,21 @@ __device__ __forceinline__ void add_sq(double &acc, float u) {
     acc = __builtin_fma(d, d, acc);
 }
 
+// The sum of the exact squares of E (4 or 8) binary32 values in fp64, added
+// pairwise (a short dependency chain: the streaming passes that use it keep
+// several groups of loads in flight per thread).
+template <int E>
+__device__ __forceinline__ double sum_sq(const float (&u)[E]) {
+    double s[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) s[e] = (double)u[e] * (double)u[e];
+#pragma unroll
+    for (int w = 1; w < E; w *= 2)
+#pragma unroll
+        for (int e = 0; e < E; e += 2 * w) s[e] += s[e + w];
+    return s[0];
+}
+
 // The range of ||U||_F^2 over which the first Newton-Schulz iteration applies
 // the pre-scale s to its fp32 products of bf16(U): every entry of U U^T is at
 // most ||U||_F^2 <= 2^100 and every accumulator of B U at most ~10 ||U||_F, far
@@ -181,12 +196,10 @@ __global__ __launch_bounds__(kThreads) void muon_momentum_kernel(
             float m[kPreEPT], g[kPreEPT];
             ld_f32<kPreEPT, false>(mom + i0, m);
             ld_bf16<kPreEPT>(grad + i0, g);
+            float us[kPreEPT];
 #pragma unroll
-            for (int e = 0; e < kPreEPT; ++e) {
-                float u;
-                momentum_update(m[e], g[e], u, a);
-                add_sq(sumsq, u);
-            }
+            for (int e = 0; e < kPreEPT; ++e) momentum_update(m[e], g[e], us[e], a);
+            sumsq += sum_sq(us);
             st_f32<kPreEPT, false>(mom + i0, m);
         } else {
             for (int e = 0; e < kPreEPT && i0 + e < a.count; ++e) {
@@ -379,7 +392,49 @@ __global__ __launch_bounds__(kThreads) void muon_momentum_x_kernel(
     PreArgs pa{0, 0, a.mu, a.omm, a.nesterov, nullptr};
     device_momentum(a.dev, pa.mu, pa.omm);
     double sumsq = 0.0;
+    // bf16(U) of the group of 8 at tile row lr, column lc: to X (rows <= cols)
+    // or to the LDS tile (transposed)
+    auto put = [&](int lr, int lc, int r, int c0, const float (&us)[8]) __attribute__((always_inline)) {
+        const uint32_t packed[4] = {pack_bf16x2(us[0], us[1]), pack_bf16x2(us[2], us[3]),
+                                    pack_bf16x2(us[4], us[5]), pack_bf16x2(us[6], us[7])};
+        if (!a.transposed)
+            *reinterpret_cast<u32x4 *>(x + (int64_t)r * a.np + c0) =
+                u32x4{packed[0], packed[1], packed[2], packed[3]};
+        else
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                tile[lr][lc + e] = (uint16_t)((packed[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
+    };
 
+    if (a.vec && (tr + 1) * T <= a.rows && (tc + 1) * T <= a.cols) {
+        // a tile inside the matrix (uniform): the loads of LB groups leave
+        // together, before any of them is used (the pass is latency-bound
+        // with one group in flight per thread)
+        constexpr int LB = PER < 4 ? PER : 4;
+        for (int q0 = 0; q0 < PER; q0 += LB) {
+            float m[LB][8], g[LB][8];
+#pragma unroll
+            for (int k = 0; k < LB; ++k) {
+                const int grp = threadIdx.x + (q0 + k) * kThreads;
+                const int r = tr * T + grp / GPR, c0 = tc * T + (grp % GPR) * 8;
+                const int64_t i = (int64_t)r * a.cols + c0;
+                ld_f32<8, true>(mom + i, m[k]);  // read once, next by the next step
+                ld_bf16<8>(grad + i, g[k]);
+            }
+#pragma unroll
+            for (int k = 0; k < LB; ++k) {
+                const int grp = threadIdx.x + (q0 + k) * kThreads;
+                const int lr = grp / GPR, lc = (grp % GPR) * 8;
+                const int r = tr * T + lr, c0 = tc * T + lc;
+                float us[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) momentum_update(m[k][e], g[k][e], us[e], pa);
+                st_f32<8, true>(mom + (int64_t)r * a.cols + c0, m[k]);
+                sumsq += sum_sq(us);
+                put(lr, lc, r, c0, us);
+            }
+        }
+    } else {
     // T rows x GPR groups of 8 columns; PER per thread
     for (int q = 0; q < PER; ++q) {
         const int grp = threadIdx.x + q * kThreads;
@@ -408,17 +463,9 @@ __global__ __launch_bounds__(kThreads) void muon_momentum_x_kernel(
                 us[e] = u;
             }
         }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) add_sq(sumsq, us[e]);
-        const uint32_t packed[4] = {pack_bf16x2(us[0], us[1]), pack_bf16x2(us[2], us[3]),
-                                    pack_bf16x2(us[4], us[5]), pack_bf16x2(us[6], us[7])};
-        if (!a.transposed)
-            *reinterpret_cast<u32x4 *>(x + (int64_t)r * a.np + c0) =
-                u32x4{packed[0], packed[1], packed[2], packed[3]};
-        else
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                tile[lr][lc + e] = (uint16_t)((packed[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
+        sumsq += sum_sq(us);
+        put(lr, lc, r, c0, us);
+    }
     }
     const double total = block_sum_d(sumsq, lds4);  // its barriers also order the tile writes
     if (threadIdx.x == 0) partials[(int64_t)b * norm_blocks + blockIdx.x] = total;
@@ -470,8 +517,7 @@ __global__ __launch_bounds__(kThreads) void muon_momentum_xflat_kernel(
 #pragma unroll
         for (int e = 0; e < E; ++e) momentum_update(m[e], g[e], us[e], pa);
         st_f32<E, true>(mom + i0, m);
-#pragma unroll
-        for (int e = 0; e < E; ++e) add_sq(sumsq, us[e]);
+        sumsq += sum_sq(us);
         st_bf16<E>(x + (int64_t)r * a.np + c, us);
     } else {
         for (uint32_t e = 0; e < (uint32_t)E && i0 + e < count; ++e) {

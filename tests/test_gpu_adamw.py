@@ -85,6 +85,11 @@ def test_tiny_workload_all_ranks_bitwise():
     (3, 8, 4, 3),                # a shard of padding only for the last rank
     (1, 1, 1, 0),
     (100_003, 4096, 1, 0),       # world 1, ragged tail
+    # pieces of whole tiles with a short last bucket: the bucket grid over the
+    # full buckets, the last one (a partial last tile, padding for rank 3) on
+    # its own
+    (100_003, 8192, 4, 0), (100_003, 8192, 4, 3),
+    ((1 << 14) + 3, 1 << 12, 8, 7),  # the last bucket's piece is padding only for rank 7
     (1 << 20, 1 << 17, 8, 5),    # all 16-byte aligned: the vector path
     ((1 << 14) + 3, 1 << 12, 8, 7),  # bucket grid, then a last piece of padding only
     ((1 << 20) + 100, 1 << 17, 8, 6),  # bucket grid, then a padded last bucket
