@@ -496,15 +496,17 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch 
     __syncthreads();
     read(0, 0);
     int cur = 0;  // buffer of stage kt
-    auto body = [&](int kt, auto PAR) __attribute__((always_inline)) {
+    auto body = [&](int kt, auto PAR, auto LIVE) __attribute__((always_inline)) {
         constexpr int par = decltype(PAR)::value;
         const int nxt = cur + 1 == NSTG ? 0 : cur + 1;
         __builtin_amdgcn_s_waitcnt(WAIT_VM_LGKM0((NSTG - 2) * LPS));
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         gload(cur * STAGE, (kt + NSTG) * kBK);
+        if constexpr (decltype(LIVE)::value) {
         read(par ^ 1, nxt * STAGE);
         mma(par);
+        }
 #pragma unroll
         for (int x = 0; x < LPS; ++x) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
@@ -520,14 +522,23 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch 
     };
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
-    int kt = 0;
-    // two stages per trip, so that the fragment buffer of each is static
+    // a wave whose sub-tile of a diagonal tile lies wholly below the diagonal
+    // computes nothing the epilogue stores: it only loads and synchronises
+    const bool dead = m0 == n0 && wr * WTM >= wc * WTN + WTN;
+    auto kloop = [&](auto LIVE) __attribute__((always_inline)) {
+        int kt = 0;
+        // two stages per trip, so that the fragment buffer of each is static
 #pragma clang loop unroll(disable)
-    for (; kt + 2 <= KT; kt += 2) {
-        body(kt, P0{});
-        body(kt + 1, P1{});
-    }
-    if (kt < KT) body(kt, P0{});
+        for (; kt + 2 <= KT; kt += 2) {
+            body(kt, P0{}, LIVE);
+            body(kt + 1, P1{}, LIVE);
+        }
+        if (kt < KT) body(kt, P0{}, LIVE);
+    };
+    if (dead)
+        kloop(std::false_type{});
+    else
+        kloop(std::true_type{});
     // the loads past the end still write (zeros) to LDS: drain them before
     // the epilogue reuses the buffers
     __builtin_amdgcn_s_waitcnt(0);
