@@ -56,11 +56,24 @@ MEASURED_TRAFFIC = {
                         bytes_per_launch=7.000e9,
                         profile="profiles/adamw_bucket_grid_kernel_zero2_2b_rank3.md"),
     # one Newton-Schulz iteration of the 72 GPT-2-small matrices: the four launches'
-    # FETCH_SIZE + WRITE_SIZE, calibrated (0.7137 GB read, 0.3403 GB written)
+    # FETCH_SIZE + WRITE_SIZE, calibrated (0.7146 GB read, 0.3403 GB written)
     "ns_iteration_gpt2": dict(source="sharded_optimizer_step_adamw_amd/csrc/ns_gemm.hip",
-                              sha256="965e58691b738e401f317e77d17b076850545fc21cdec095ae904a100f60aa14",
-                              bytes_per_launch=1.0540e9,
+                              sha256="9ffa0d63cd33de9c690957c7b35591a6c0c34117cde93707535152bdb377218c",
+                              bytes_per_launch=1.0549e9,
                               profile="profiles/ns_gemm_gpt2_small_step.md"),
+    # one Newton-Schulz iteration of the 8B rank-0 share (28 matrices): X X^T, A A and
+    # B X, calibrated (23.590 GB read, 3.121 GB written)
+    "ns_iteration_llama8b": dict(source="sharded_optimizer_step_adamw_amd/csrc/ns_gemm.hip",
+                                 sha256="9ffa0d63cd33de9c690957c7b35591a6c0c34117cde93707535152bdb377218c",
+                                 bytes_per_launch=26.712e9,
+                                 profile="profiles/ns_gemm_llama8b_rank0.md"),
+    # one Newton-Schulz iteration of the 1B rank-0 share (12 matrices): X X^T on 256 and
+    # 128 tiles, the split-K fix-up, A A on 256 and 128 tiles, B X, calibrated (1.4529 GB
+    # read, 0.3569 GB written)
+    "ns_iteration_llama1b": dict(source="sharded_optimizer_step_adamw_amd/csrc/ns_gemm.hip",
+                                 sha256="9ffa0d63cd33de9c690957c7b35591a6c0c34117cde93707535152bdb377218c",
+                                 bytes_per_launch=1.8098e9,
+                                 profile="profiles/ns_gemm_llama1b_rank0.md"),
     "grad_sq_norm": dict(source="sharded_optimizer_step_adamw_amd/csrc/adamw_shard.hip",
                          sha256="673b6ee27b692f43da0cb776f129120c95304617a7117f995f9273186f2e9bca",
                          bytes_per_launch=0.5004e9,
@@ -338,12 +351,28 @@ def bench_ns(torch, z, timer, dev, K, W, w=None):
     tf = total_flops / ns_ms / 1e9
     names = {"llama8b_rank0_muon": "llama8b rank-0 Muon share (W=8, 32 layers), 5 bf16 NS iterations",
              "llama1b_rank0_muon": "llama1b rank-0 Muon share (W=8, 16 layers), 5 bf16 NS iterations"}
+    # the dominant kernels: one Newton-Schulz iteration of every matrix of the
+    # share (the unit), timed as (5-iteration call - 1-iteration call) / 4
+    if w.name == "llama8b_rank0_muon":
+        kernel = ("Newton-Schulz iteration of the 28 matrices: ns_gemm_kernel<256,0> X X^T and "
+                  "ns_gemm_kernel<256,1> A A (one launch each over all four groups), "
+                  "ns_bx_kernel<256> B X (persistent, 256 workgroups)")
+        traffic, tunit = measured_traffic("ns_iteration_llama8b"), "HBM bytes per iteration (3 launches)"
+    else:
+        kernel = ("Newton-Schulz iteration of the 12 matrices: X X^T (256 tiles, and 128 tiles for "
+                  "the 512-row group; the 11264 x 2048 pair split along K plus its fix-up), A A, "
+                  "ns_bx_kernel<256> B X")
+        traffic, tunit = measured_traffic("ns_iteration_llama1b"), "HBM bytes per iteration (6 launches)"
+    roof = dict(kernel=kernel, bound="mfma", achieved=round(tf, 1), peak=BF16_PEAK_TFLOPS,
+                unit="TFLOP/s", frac=round(tf / BF16_PEAK_TFLOPS, 4), traffic=traffic,
+                traffic_unit=tunit, algorithmic_flops_per_unit=total_flops // w.ns_steps,
+                avg_unit_ms=round(ns_ms / w.ns_steps, 4))
     return dict(workload=names.get(w.name, w.name),
                 algorithmic_flops_per_step=total_flops, ns_ms_per_step=round(ns_ms, 3),
                 muon_ms_per_step=round(call_ms, 3), ns_tflops=round(tf, 1),
                 mfma_frac=round(tf / BF16_PEAK_TFLOPS, 4),
                 muon_step_tflops=round(total_flops / call_ms / 1e9, 1), groups=rows, steps=K,
-                ns_health=health)
+                ns_health=health, roofline=roof)
 
 
 def bench_graph(torch, z, timer, dev, K, W):

@@ -335,9 +335,18 @@ __global__ __launch_bounds__(kThreads) void muon_norm_kernel(
     __shared__ uint16_t tile[kTile][kTile + 2];
     const int b = blockIdx.y;
     const double *p = partials + (int64_t)b * norm_blocks;
-    double acc = 0.0;
-    for (int i = threadIdx.x; i < count; i += kThreads) acc += p[i];
-    const double total = block_sum_d(acc, lds4);
+    // four loads in flight per thread (tens of thousands of partials for the
+    // largest matrices); the same fixed order in every workgroup
+    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+    int i = threadIdx.x;
+    for (; i + 3 * kThreads < count; i += 4 * kThreads) {
+        a0 += p[i];
+        a1 += p[i + kThreads];
+        a2 += p[i + 2 * kThreads];
+        a3 += p[i + 3 * kThreads];
+    }
+    for (; i < count; i += kThreads) a0 += p[i];
+    const double total = block_sum_d((a0 + a1) + (a2 + a3), lds4);
     const double s = 1.0 / (__builtin_sqrt(total) + (double)ns_eps);
     // (NaN and infinity compare false: such a matrix takes the rewrite)
     const bool folded = total >= kFoldMin && total <= kFoldMax;
@@ -854,8 +863,12 @@ hipError_t launch_muon_pre(const MuonGeom &g, const MuonPtrs &ptrs, float mu,
             }
         }
         // the norm, and the rewrite of X for a matrix whose ||U||_F^2 is out of
-        // the first iteration's range (the other workgroups leave at once)
-        const int fb = tiles < kFallbackBlocks ? tiles : kFallbackBlocks;
+        // the first iteration's range (the other workgroups leave at once).
+        // Every workgroup of a matrix sums all its partials, so matrices with
+        // many get fewer workgroups (at least 4 for the rewrite)
+        int fb = 16384 / (parts > 0 ? parts : 1);
+        fb = fb < 4 ? 4 : fb > kFallbackBlocks ? kFallbackBlocks : fb;
+        if (fb > tiles) fb = tiles;
         hipLaunchKernelGGL(muon_norm_kernel, dim3(fb, g.batch), dim3(kThreads), 0, stream, ptrs,
                            sa, partials, g.norm_blocks, parts, sd, xs, ns_eps, 1, tiles, x, xstr);
         return hipGetLastError();
