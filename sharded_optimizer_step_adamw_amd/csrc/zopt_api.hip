@@ -5,6 +5,7 @@
 // binary32, workspace carve-up), and enqueues its kernels on the caller's
 // stream without synchronising.  Nothing is enqueued unless every check
 // passes.
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -432,6 +433,115 @@ void muon_bin_call(MuonCallPlan &c, char *ws, float *const *master, float *const
     }
 }
 
+}  // namespace
+
+bool zopt::ns_split_streams(const NsGroupRef *refs, int nrefs) {
+    if (nrefs < 2) return false;
+    int64_t wg = 0;
+    for (int i = 0; i < nrefs; ++i) {
+        const MuonGeom &g = *refs[i].geom;
+        if (g.tile != 256) continue;
+        const int64_t tm = g.mp / 256;
+        wg += (int64_t)g.batch * (tm * (tm + 1) / 2) * g.ksplit;
+    }
+    return wg > 0 && wg < 2 * (int64_t)ns_round_tiles(256);
+}
+
+namespace {
+
+// The second stream of Muon calls whose Newton-Schulz iterations are split
+// over two streams (ns_split_streams): one per device, default priority,
+// created at the first such call on that device that is not being captured
+// (creating a stream inside a capture is not done), with the two events that
+// fork it from the caller's stream and join it back.  g_aux_mutex is held
+// while a call enqueues its fork ... join, so that calls from several host
+// threads take the events one at a time; the work of those calls on the
+// second stream is then ordered as their enqueues were.
+struct AuxStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    bool failed = false;  // creation failed once: calls run on one stream
+};
+std::mutex g_aux_mutex;
+AuxStream g_aux[kScratchDevices];
+
+// The current device's second stream (g_aux_mutex held), or nullptr: not
+// created yet and `caller` is capturing, or creation failed.
+AuxStream *aux_stream(hipStream_t caller) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return nullptr;
+    AuxStream &a = g_aux[dev];
+    if (a.s != nullptr) return &a;
+    if (a.failed) return nullptr;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+        return nullptr;
+    if (hipStreamCreateWithFlags(&a.s, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&a.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&a.join, hipEventDisableTiming) != hipSuccess) {
+        if (a.s) (void)hipStreamDestroy(a.s);
+        if (a.fork) (void)hipEventDestroy(a.fork);
+        a = AuxStream{};
+        a.failed = true;
+        return nullptr;
+    }
+    return &a;
+}
+
+// The Newton-Schulz iterations of one bin (nb groups at refs), on stream s
+// alone or, when ns_split_streams says so and the second stream is there,
+// on s and the second stream: groups in order of work, each to the stream
+// with less so far; s waits for the second stream's last launch before it
+// returns.
+hipError_t ns_iterations(const NsGroupRef *refs, int nb, int ns_steps, float ns_a, float ns_b,
+                         float ns_c, hipStream_t s) {
+    hipError_t e = hipSuccess;
+    if (ns_steps > 0 && ns_split_streams(refs, nb)) {
+        std::lock_guard<std::mutex> lock(g_aux_mutex);
+        AuxStream *aux = aux_stream(s);
+        if (aux != nullptr) {
+            double work[kMaxCallGroups];
+            int order[kMaxCallGroups];
+            for (int k = 0; k < nb; ++k) {
+                const MuonGeom &g = *refs[k].geom;
+                const double m = g.m, n = g.n;
+                work[k] = g.batch * (3.0 * m * m * n + m * m * m);
+                order[k] = k;
+            }
+            std::stable_sort(order, order + nb, [&](int x, int y) { return work[x] > work[y]; });
+            NsGroupRef ra[kMaxCallGroups], rb[kMaxCallGroups];
+            int na = 0, nbb = 0;
+            double wa = 0.0, wb = 0.0;
+            for (int t = 0; t < nb; ++t) {
+                const int k = order[t];
+                if (wa <= wb) {
+                    ra[na++] = refs[k];
+                    wa += work[k];
+                } else {
+                    rb[nbb++] = refs[k];
+                    wb += work[k];
+                }
+            }
+            e = hipEventRecord(aux->fork, s);
+            if (e == hipSuccess) e = hipStreamWaitEvent(aux->s, aux->fork, 0);
+            for (int k = 0; k < ns_steps && e == hipSuccess; ++k) {
+                e = launch_ns_iteration(ra, na, k, k + 1 == ns_steps, ns_a, ns_b, ns_c, s);
+                if (e == hipSuccess)
+                    e = launch_ns_iteration(rb, nbb, k, k + 1 == ns_steps, ns_a, ns_b, ns_c,
+                                            aux->s);
+            }
+            // the join is enqueued whatever happened above, so that s never
+            // runs ahead of work already on the second stream
+            const hipError_t ej = hipEventRecord(aux->join, aux->s);
+            const hipError_t ew = ej == hipSuccess ? hipStreamWaitEvent(s, aux->join, 0) : ej;
+            return e != hipSuccess ? e : ew;
+        }
+    }
+    for (int k = 0; k < ns_steps && e == hipSuccess; ++k)
+        e = launch_ns_iteration(refs, nb, k, k + 1 == ns_steps, ns_a, ns_b, ns_c, s);
+    return e;
+}
+
 // Enqueues a planned call on stream s.  With dev (device scalars [lr,
 // momentum_beta, weight_decay]) the kernels read those when they run and
 // lr / mu / wd here are unused; with health the Newton-Schulz health pass
@@ -450,9 +560,8 @@ hipError_t muon_enqueue(const MuonCallPlan &c, char *ws, float lr, float mu, int
             e = launch_muon_pre(c.plans[i].g, c.ptrs[i], mu, nesterov, ns_eps,
                                 ws + c.plans[i].base, c.plans[i].L, ns_steps == 0, dev, s);
         }
-        for (int k = 0; k < ns_steps && e == hipSuccess; ++k)
-            e = launch_ns_iteration(brefs, c.bin_size[bi], k, k + 1 == ns_steps, ns_a, ns_b, ns_c,
-                                    s);
+        if (e == hipSuccess)
+            e = ns_iterations(brefs, c.bin_size[bi], ns_steps, ns_a, ns_b, ns_c, s);
         if (health && e == hipSuccess) {
             int bfirst[kMaxCallGroups];
             for (int k = 0; k < c.bin_size[bi]; ++k) bfirst[k] = c.firsts[c.bins[bi][k]];
@@ -614,6 +723,18 @@ ZOPT_EXPORT zopt_status zopt_muon_graph_create(
     // `scalars` when they run, so one capture serves every step
     hipStream_t cs = nullptr;
     if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) return ZOPT_ERR_DEVICE;
+    if (ns_steps > 0) {
+        // a call split over two streams: the second stream exists before the
+        // capture begins (none is created inside it)
+        for (int bi = 0; bi < c.nbins; ++bi) {
+            NsGroupRef brefs[kMaxCallGroups];
+            for (int k = 0; k < c.bin_size[bi]; ++k) brefs[k] = c.refs[c.bins[bi][k]];
+            if (ns_split_streams(brefs, c.bin_size[bi])) {
+                std::lock_guard<std::mutex> lock(g_aux_mutex);
+                (void)aux_stream(cs);
+            }
+        }
+    }
     hipGraph_t g = nullptr;
     hipGraphExec_t ex = nullptr;
     hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);

@@ -206,6 +206,14 @@ hipError_t launch_ns_iteration(const NsGroupRef *refs, int nrefs, int iter, bool
 // current device holds at once (one round of tiles).
 int ns_round_tiles(int tile);
 
+// Whether the Newton-Schulz iterations of these groups (one launch bin) run
+// on two streams, the groups divided between them by work: when the bin's
+// 256-tile X X^T launch (split parts included) holds fewer than two rounds of
+// workgroups, so that each product's launch leaves much of the GPU idle in
+// its last round and the other stream's launches fill it.  Per-matrix
+// arithmetic is the same either way (results equal bit for bit).
+bool ns_split_streams(const NsGroupRef *refs, int nrefs);
+
 // Caps the workgroups that the persistent B X launches keep resident (n <= 0:
 // a full round; otherwise max(8, n rounded down to a multiple of 8)).
 void ns_set_workgroup_limit(int n);

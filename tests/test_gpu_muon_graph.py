@@ -145,6 +145,16 @@ def test_guarded_replays():
                     steps=3)
 
 
+def test_two_stream_call_replays():
+    """A call whose Newton-Schulz iterations are divided over two streams
+    (three 256-tile groups with 280 X X^T workgroups in all): the captured
+    fork and join replay to the eager call's results, with and without the
+    health pass."""
+    specs = [(1, 4096, 4096), (2, 2048, 2048), (2, 2048, 5632)]
+    replay_vs_eager(specs, seed=6, steps=3)
+    replay_vs_eager(specs, seed=7, steps=2, guard=1000.0)
+
+
 def test_gpt2_small_replays():
     """The headline's 72 matrices in one captured call, three replays."""
     specs = [(g.count, g.rows, g.cols) for g in wl.GPT2_MUON.groups]
