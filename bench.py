@@ -67,12 +67,15 @@ MEASURED_TRAFFIC = {
                                  sha256="9ffa0d63cd33de9c690957c7b35591a6c0c34117cde93707535152bdb377218c",
                                  bytes_per_launch=26.712e9,
                                  profile="profiles/ns_gemm_llama8b_rank0.md"),
-    # one Newton-Schulz iteration of the 1B rank-0 share (12 matrices): X X^T on 256 and
-    # 128 tiles, the split-K fix-up, A A on 256 and 128 tiles, B X, calibrated (1.4529 GB
-    # read, 0.3569 GB written)
+    # one Newton-Schulz iteration of the 1B rank-0 share (12 matrices) on two streams:
+    # the 2 x [11264, 2048] group (split X X^T, fix-up, A A, B X) on one, the other three
+    # groups (X X^T and A A on 256 and 128 tiles, B X) on the other, calibrated (1.2536 GB
+    # read, 0.3568 GB written); the launch plan (which launches exist) is in zopt_api.hip
     "ns_iteration_llama1b": dict(source="sharded_optimizer_step_adamw_amd/csrc/ns_gemm.hip",
                                  sha256="9ffa0d63cd33de9c690957c7b35591a6c0c34117cde93707535152bdb377218c",
-                                 bytes_per_launch=1.8098e9,
+                                 also=[("sharded_optimizer_step_adamw_amd/csrc/zopt_api.hip",
+                                        "d4c9bfd78af04acbfdb288990240c3c51766e2a5ac54abae0f4533de1d456b60")],
+                                 bytes_per_launch=1.6104e9,
                                  profile="profiles/ns_gemm_llama1b_rank0.md"),
     "grad_sq_norm": dict(source="sharded_optimizer_step_adamw_amd/csrc/adamw_shard.hip",
                          sha256="673b6ee27b692f43da0cb776f129120c95304617a7117f995f9273186f2e9bca",
@@ -84,9 +87,10 @@ MEASURED_TRAFFIC = {
 def measured_traffic(key):
     import hashlib
     t = MEASURED_TRAFFIC[key]
-    with open(os.path.join(ROOT, t["source"]), "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != t["sha256"]:
-            return None
+    for src, sha in [(t["source"], t["sha256"])] + list(t.get("also", [])):
+        with open(os.path.join(ROOT, src), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != sha:
+                return None
     return t["bytes_per_launch"]
 
 
@@ -359,10 +363,11 @@ def bench_ns(torch, z, timer, dev, K, W, w=None):
                   "ns_bx_kernel<256> B X (persistent, 256 workgroups)")
         traffic, tunit = measured_traffic("ns_iteration_llama8b"), "HBM bytes per iteration (3 launches)"
     else:
-        kernel = ("Newton-Schulz iteration of the 12 matrices: X X^T (256 tiles, and 128 tiles for "
-                  "the 512-row group; the 11264 x 2048 pair split along K plus its fix-up), A A, "
-                  "ns_bx_kernel<256> B X")
-        traffic, tunit = measured_traffic("ns_iteration_llama1b"), "HBM bytes per iteration (6 launches)"
+        kernel = ("Newton-Schulz iteration of the 12 matrices on two streams: the 11264 x 2048 pair "
+                  "(X X^T split along K plus its fix-up, A A, ns_bx_kernel<256> B X) on one, the "
+                  "other three groups (X X^T and A A on 256 tiles, and 128 tiles for the 512-row "
+                  "group, ns_bx_kernel<256> B X) on the other")
+        traffic, tunit = measured_traffic("ns_iteration_llama1b"), "HBM bytes per iteration (9 launches)"
     roof = dict(kernel=kernel, bound="mfma", achieved=round(tf, 1), peak=BF16_PEAK_TFLOPS,
                 unit="TFLOP/s", frac=round(tf / BF16_PEAK_TFLOPS, 4), traffic=traffic,
                 traffic_unit=tunit, algorithmic_flops_per_unit=total_flops // w.ns_steps,
