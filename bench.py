@@ -55,11 +55,14 @@ MEASURED_TRAFFIC = {
                         sha256="673b6ee27b692f43da0cb776f129120c95304617a7117f995f9273186f2e9bca",
                         bytes_per_launch=7.000e9,
                         profile="profiles/adamw_bucket_grid_kernel_zero2_2b_rank3.md"),
-    # one Newton-Schulz iteration of the 72 GPT-2-small matrices: the four launches'
-    # FETCH_SIZE + WRITE_SIZE, calibrated (0.7146 GB read, 0.3403 GB written)
+    # one Newton-Schulz iteration of the 72 GPT-2-small matrices on two streams: the
+    # six launches' FETCH_SIZE + WRITE_SIZE, calibrated (0.4842 GB read, 0.2553 GB
+    # written); the launch plan (tiles, streams) is in zopt_api.hip
     "ns_iteration_gpt2": dict(source="sharded_optimizer_step_adamw_amd/csrc/ns_gemm.hip",
                               sha256="9ffa0d63cd33de9c690957c7b35591a6c0c34117cde93707535152bdb377218c",
-                              bytes_per_launch=1.0549e9,
+                              also=[("sharded_optimizer_step_adamw_amd/csrc/zopt_api.hip",
+                                     "d462e3b0e464bbdef991a0467d2eb84a0d3fdc94e8c2d35be4fcf6a4c1390209")],
+                              bytes_per_launch=0.7394e9,
                               profile="profiles/ns_gemm_gpt2_small_step.md"),
     # one Newton-Schulz iteration of the 8B rank-0 share (28 matrices): X X^T, A A and
     # B X, calibrated (23.590 GB read, 3.121 GB written)
@@ -74,7 +77,7 @@ MEASURED_TRAFFIC = {
     "ns_iteration_llama1b": dict(source="sharded_optimizer_step_adamw_amd/csrc/ns_gemm.hip",
                                  sha256="9ffa0d63cd33de9c690957c7b35591a6c0c34117cde93707535152bdb377218c",
                                  also=[("sharded_optimizer_step_adamw_amd/csrc/zopt_api.hip",
-                                        "d4c9bfd78af04acbfdb288990240c3c51766e2a5ac54abae0f4533de1d456b60")],
+                                        "d462e3b0e464bbdef991a0467d2eb84a0d3fdc94e8c2d35be4fcf6a4c1390209")],
                                  bytes_per_launch=1.6104e9,
                                  profile="profiles/ns_gemm_llama1b_rank0.md"),
     "grad_sq_norm": dict(source="sharded_optimizer_step_adamw_amd/csrc/adamw_shard.hip",
@@ -234,10 +237,9 @@ def bench_step(torch, z, timer, dev, K, W):
     ms = timer.run(step, K)
 
     # the dominant kernels: one Newton-Schulz iteration of all 72 matrices is
-    # four launches (X X^T and A A with its epilogue over every group, B X with
-    # its epilogue on 256-tiles and its short tail on 128-tiles); its time is
-    # the difference of the Muon call with 5 and with 1 iteration, over 4 (the
-    # two calls take the same pre/post path)
+    # six launches on two streams (on each, X X^T and A A over its groups and
+    # B X); its time is the difference of the Muon call with 5 and with 1
+    # iteration, over 4 (the two calls take the same pre/post path)
     t5 = timer.run(lambda _: muon_call(z, wm, groups, workspace, 5), K)
     t1 = timer.run(lambda _: muon_call(z, wm, groups, workspace, 1), K)
     t0 = timer.run(lambda _: muon_call(z, wm, groups, workspace, 0), K)
@@ -768,12 +770,12 @@ def main():
         tf = res_step["ns_iter_flops"] / res_step["ns_iter_ms"] / 1e9
         out.update(value=round(res_step["ms"], 4), unit="ms per optimizer step")
         roof = dict(
-            kernel=("Newton-Schulz iteration: ns_gemm_kernel X X^T and A A (128 x 128 tiles, "
-                    "one launch each over all 72 matrices) + ns_bx_kernel B X (persistent: "
-                    "256 x 256 tiles over 71 matrices, 128 x 128 tiles over the last one)"),
+            kernel=("Newton-Schulz iteration on two streams: the 48 x [768, 768] group on one, "
+                    "the 3072 x 768 and 768 x 3072 groups on the other, each stream "
+                    "ns_gemm_kernel<256> X X^T and A A + ns_bx_kernel<256> B X (persistent)"),
             bound="mfma", achieved=round(tf, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
             frac=round(tf / BF16_PEAK_TFLOPS, 4), traffic=measured_traffic("ns_iteration_gpt2"),
-            traffic_unit="HBM bytes per iteration (4 launches)",
+            traffic_unit="HBM bytes per iteration (6 launches)",
             algorithmic_flops_per_unit=res_step["ns_iter_flops"],
             avg_unit_ms=round(res_step["ns_iter_ms"], 4))
     else:

@@ -64,10 +64,11 @@ MuonGeom muon_geometry(int32_t batch, int64_t rows, int64_t cols) {
     g.m = (int32_t)(rows < cols ? rows : cols);
     g.n = (int32_t)(rows < cols ? cols : rows);
     // 256 x 256 tiles from m = 1024 on, and from m = 768 on where they pad m
-    // no further than 128 x 128 tiles would (m = 768, or 897 .. 1023):
-    // measured on GPT-2-small's 768-row groups, Newton-Schulz 1.739 -> 1.640 ms
-    // per call (6 upper-triangle tiles per matrix instead of 21, each with four
-    // times the work)
+    // no further than 128 x 128 tiles would (m = 768, or 897 .. 1023): 6
+    // upper-triangle tiles per 768-row matrix instead of 21.  On GPT-2-small's
+    // three 768-row groups (432 X X^T workgroups, under two rounds, so the
+    // iterations run on two streams) Newton-Schulz took 1.630 ms per call
+    // against 1.718 on 128 tiles; on one stream the 256 tiles alone took 1.743.
     const bool big = g.m >= 1024 || (g.m >= 768 && round_up64(g.m, 256) == round_up64(g.m, 128));
     g.tile = big ? 256 : g.m >= 256 ? 128 : 64;
     g.mp = (int32_t)round_up64(g.m, g.tile);
