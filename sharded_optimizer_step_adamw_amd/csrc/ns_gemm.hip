@@ -244,9 +244,10 @@ __device__ __forceinline__ void epilogue(const NsGroup &args, float ca, float cb
     if (MODE == kSyrkAA && !below) {
         const uint16_t *E = args.E + batch * args.c_stride;
         // (all of the wave's loads in flight at once: the accumulators are the
-        // only other live registers here)
+        // only other live registers here; on 256 tiles the main loop's last
+        // stages have put the sub-block there already)
 #pragma unroll
-        for (int k = 0; k < SR * RCH / 64; ++k) {
+        for (int k = 0; k < (BM == 256 ? 0 : SR * RCH / 64); ++k) {
             const int id = k * 64 + lane, i = id / RCH, c = id % RCH;
             const u32x4 v = *reinterpret_cast<const u32x4 *>(E + (int64_t)(R0 + i) * ldc + C0 + c * 8);
             *reinterpret_cast<u32x4 *>(W + i * (RCH * 16) + ((c ^ (i & (RCH - 1))) << 4)) = v;
@@ -451,6 +452,18 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch 
     // and the chunk that the swizzle places at slot l % 4
     const int lrow = lane >> 2, lchunk = (lane & 3) ^ ((lrow >> 1) & 3);
     const int voff = (lrow * ld + lchunk * 8) * 2;
+    // A A on 256 tiles: the stages past the end of K (the last four
+    // iterations' loads, into the four buffers as they free up) fetch the
+    // input tile Aoff[m0.., n0..] that the epilogue needs, straight into the
+    // per-wave regions it reads it from (wave w's 128 x 64 sub-block, rows of
+    // 128 bytes, chunk c of row i at slot c ^ (i % 8), at w x 16 KiB: the
+    // buffer of stage s holds the regions of waves 2s and 2s + 1).  Kilobyte k
+    // of a region is its rows 8k .. 8k+7; lane l takes row l / 8 of it and the
+    // chunk the swizzle puts at slot l % 8.
+    constexpr bool kEpre = MODE == kSyrkAA && BM == 256;
+    static_assert(!kEpre || (NSTG == 4 && NSTG * STAGE == BM * BM * 2), "four buffers hold the input tile");
+    const uint16_t *Eb = kEpre ? G.E + batch * G.c_stride + (int64_t)m0 * G.ldc + n0 : nullptr;
+    const int evoff = ((lane >> 3) * G.ldc + (((lane & 7) ^ (lane >> 3)) << 3)) * 2;
     auto gload = [&](int sbase, int k0) {
         const int bytes = k0 < K ? panel_bytes : 0;
         const __amdgpu_buffer_rsrc_t rp =
@@ -465,6 +478,22 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch 
                                                      soff, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, LDS_ADDR(&lds[sbase + OPB + k * 1024]), 16,
                                                      voff, soff, 0, 0);
+        }
+    };
+    // the input tile's regions of waves 2B and 2B + 1 into stage buffer B
+    auto egload = [&](auto B) __attribute__((always_inline)) {
+        constexpr int ow = 2 * decltype(B)::value;
+        const __amdgpu_buffer_rsrc_t re =
+            __builtin_amdgcn_make_buffer_rsrc((void *)Eb, (short)0, BM * G.ldc * 2, 0x00020000);
+#pragma unroll
+        for (int q = 0; q < LOADS; ++q) {
+            const int k = q * NW + wave;
+            const int sp = (((ow / WC) * WTM + 8 * k) * G.ldc + (ow % WC) * WTN) * 2;
+            const int sq = ((((ow + 1) / WC) * WTM + 8 * k) * G.ldc + ((ow + 1) % WC) * WTN) * 2;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                re, LDS_ADDR(&lds[decltype(B)::value * STAGE + k * 1024]), 16, evoff, sp, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                re, LDS_ADDR(&lds[decltype(B)::value * STAGE + OPB + k * 1024]), 16, evoff, sq, 0, 0);
         }
     };
     // MFMA 16x16x32 operand: lane l holds row l % 16, K-chunk l / 16 of the
@@ -496,13 +525,18 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch 
     __syncthreads();
     read(0, 0);
     int cur = 0;  // buffer of stage kt
-    auto body = [&](int kt, auto PAR, auto LIVE) __attribute__((always_inline)) {
+    // (TAIL >= 0: one of the last NSTG stages of a 256-tile A A, whose
+    // buffer TAIL receives the input tile's regions instead of zeros)
+    auto body = [&](int kt, auto PAR, auto LIVE, auto TAIL) __attribute__((always_inline)) {
         constexpr int par = decltype(PAR)::value;
         const int nxt = cur + 1 == NSTG ? 0 : cur + 1;
         __builtin_amdgcn_s_waitcnt(WAIT_VM_LGKM0((NSTG - 2) * LPS));
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        gload(cur * STAGE, (kt + NSTG) * kBK);
+        if constexpr (decltype(TAIL)::value >= 0)
+            egload(TAIL);
+        else
+            gload(cur * STAGE, (kt + NSTG) * kBK);
         if constexpr (decltype(LIVE)::value) {
         read(par ^ 1, nxt * STAGE);
         mma(par);
@@ -525,15 +559,30 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch 
     // a wave whose sub-tile of a diagonal tile lies wholly below the diagonal
     // computes nothing the epilogue stores: it only loads and synchronises
     const bool dead = m0 == n0 && wr * WTM >= wc * WTN + WTN;
+    using NT = std::integral_constant<int, -1>;
     auto kloop = [&](auto LIVE) __attribute__((always_inline)) {
         int kt = 0;
-        // two stages per trip, so that the fragment buffer of each is static
+        if constexpr (kEpre) {
+            // K is a multiple of 256: the last four stages are stages 0 .. 3
+            // of the buffers (cur = kt % 4)
 #pragma clang loop unroll(disable)
-        for (; kt + 2 <= KT; kt += 2) {
-            body(kt, P0{}, LIVE);
-            body(kt + 1, P1{}, LIVE);
+            for (; kt + NSTG < KT; kt += 2) {
+                body(kt, P0{}, LIVE, NT{});
+                body(kt + 1, P1{}, LIVE, NT{});
+            }
+            body(kt, P0{}, LIVE, std::integral_constant<int, 0>{});
+            body(kt + 1, P1{}, LIVE, std::integral_constant<int, 1>{});
+            body(kt + 2, P0{}, LIVE, std::integral_constant<int, 2>{});
+            body(kt + 3, P1{}, LIVE, std::integral_constant<int, 3>{});
+        } else {
+            // two stages per trip, so that the fragment buffer of each is static
+#pragma clang loop unroll(disable)
+            for (; kt + 2 <= KT; kt += 2) {
+                body(kt, P0{}, LIVE, NT{});
+                body(kt + 1, P1{}, LIVE, NT{});
+            }
+            if (kt < KT) body(kt, P0{}, LIVE, NT{});
         }
-        if (kt < KT) body(kt, P0{}, LIVE);
     };
     if (dead)
         kloop(std::false_type{});
