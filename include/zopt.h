@@ -380,13 +380,14 @@ zopt_status zopt_muon_output_view(int32_t batch, int64_t rows, int64_t cols,
  * Short launches on two streams: when the groups on 256 x 256 output tiles
  * give the X X^T launch fewer than two rounds of workgroups (2 x 256 on a
  * 256-CU GPU), each product's launch would leave much of the GPU idle in its
- * last round.  The groups' Newton-Schulz iterations then run on `stream` and
- * on a second stream of the library's, the groups divided between the two by
- * work (largest first, each to the stream with less): the second stream
- * waits for everything enqueued on `stream` before the call (an event), and
- * `stream` waits for the second stream's last launch before the call's
- * remaining work (another event), so the call is ordered on `stream` as any
- * other.  The results are the same bit for bit.  The second stream is
+ * last round.  The groups then run on `stream` and on a second stream of the
+ * library's, divided between the two by Newton-Schulz work (largest first,
+ * each to the stream with less), each group's momentum pass, iterations and
+ * (with no health pass) post-step on its stream: the second stream waits for
+ * everything enqueued on `stream` before the call (an event), and `stream`
+ * waits for the second stream's last launch (another event) before the
+ * health pass, or at the end of the call, so the call is ordered on `stream`
+ * as any other.  The results are the same bit for bit.  The second stream is
  * created at the first such call on the GPU that is not under stream capture
  * (a call under capture before that runs on one stream) and by
  * zopt_muon_graph_create before its capture; calls from several host threads

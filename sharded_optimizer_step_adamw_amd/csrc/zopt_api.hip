@@ -495,58 +495,25 @@ AuxStream *aux_stream(hipStream_t caller) {
     return &a;
 }
 
-// The Newton-Schulz iterations of one bin (nb groups at refs), on stream s
-// alone or, when ns_split_streams says so and the second stream is there,
-// on s and the second stream: groups in order of work, each to the stream
-// with less so far; s waits for the second stream's last launch before it
-// returns.
-hipError_t ns_iterations(const NsGroupRef *refs, int nb, int ns_steps, float ns_a, float ns_b,
-                         float ns_c, hipStream_t s) {
-    hipError_t e = hipSuccess;
-    if (ns_steps > 0 && ns_split_streams(refs, nb)) {
-        std::lock_guard<std::mutex> lock(g_aux_mutex);
-        AuxStream *aux = aux_stream(s);
-        if (aux != nullptr) {
-            double work[kMaxCallGroups];
-            int order[kMaxCallGroups];
-            for (int k = 0; k < nb; ++k) {
-                const MuonGeom &g = *refs[k].geom;
-                const double m = g.m, n = g.n;
-                work[k] = g.batch * (3.0 * m * m * n + m * m * m);
-                order[k] = k;
-            }
-            std::stable_sort(order, order + nb, [&](int x, int y) { return work[x] > work[y]; });
-            NsGroupRef ra[kMaxCallGroups], rb[kMaxCallGroups];
-            int na = 0, nbb = 0;
-            double wa = 0.0, wb = 0.0;
-            for (int t = 0; t < nb; ++t) {
-                const int k = order[t];
-                if (wa <= wb) {
-                    ra[na++] = refs[k];
-                    wa += work[k];
-                } else {
-                    rb[nbb++] = refs[k];
-                    wb += work[k];
-                }
-            }
-            e = hipEventRecord(aux->fork, s);
-            if (e == hipSuccess) e = hipStreamWaitEvent(aux->s, aux->fork, 0);
-            for (int k = 0; k < ns_steps && e == hipSuccess; ++k) {
-                e = launch_ns_iteration(ra, na, k, k + 1 == ns_steps, ns_a, ns_b, ns_c, s);
-                if (e == hipSuccess)
-                    e = launch_ns_iteration(rb, nbb, k, k + 1 == ns_steps, ns_a, ns_b, ns_c,
-                                            aux->s);
-            }
-            // the join is enqueued whatever happened above, so that s never
-            // runs ahead of work already on the second stream
-            const hipError_t ej = hipEventRecord(aux->join, aux->s);
-            const hipError_t ew = ej == hipSuccess ? hipStreamWaitEvent(s, aux->join, 0) : ej;
-            return e != hipSuccess ? e : ew;
-        }
+// The sides of a bin whose Newton-Schulz launches run on two streams: side[k]
+// is 0 (the caller's stream) or 1 (the second); the groups in order of
+// Newton-Schulz work, each to the side with less so far.
+void split_sides(const NsGroupRef *refs, int nb, int *side) {
+    double work[kMaxCallGroups];
+    int order[kMaxCallGroups];
+    for (int k = 0; k < nb; ++k) {
+        const MuonGeom &g = *refs[k].geom;
+        const double m = g.m, n = g.n;
+        work[k] = g.batch * (3.0 * m * m * n + m * m * m);
+        order[k] = k;
     }
-    for (int k = 0; k < ns_steps && e == hipSuccess; ++k)
-        e = launch_ns_iteration(refs, nb, k, k + 1 == ns_steps, ns_a, ns_b, ns_c, s);
-    return e;
+    std::stable_sort(order, order + nb, [&](int x, int y) { return work[x] > work[y]; });
+    double w[2] = {0.0, 0.0};
+    for (int t = 0; t < nb; ++t) {
+        const int k = order[t], d = w[0] <= w[1] ? 0 : 1;
+        side[k] = d;
+        w[d] += work[k];
+    }
 }
 
 // Enqueues a planned call on stream s.  With dev (device scalars [lr,
@@ -560,21 +527,68 @@ hipError_t muon_enqueue(const MuonCallPlan &c, char *ws, float lr, float mu, int
     const double lr_d = (double)lr, wd_d = (double)wd;
     hipError_t e = hipSuccess;
     for (int bi = 0; bi < c.nbins && e == hipSuccess; ++bi) {
+        const int nb = c.bin_size[bi];
         NsGroupRef brefs[kMaxCallGroups];
-        for (int k = 0; k < c.bin_size[bi] && e == hipSuccess; ++k) {
+        for (int k = 0; k < nb; ++k) brefs[k] = c.refs[c.bins[bi][k]];
+        // A bin whose Newton-Schulz launches are short runs on two streams:
+        // each group's pre-pass, iterations and (with no health pass) post-step
+        // on its side's stream; the second stream forks from the caller's
+        // before the pre-passes and joins it before the health pass, or at the
+        // end.  The lock makes the fork ... join enqueue of one call atomic.
+        std::unique_lock<std::mutex> lock(g_aux_mutex, std::defer_lock);
+        AuxStream *aux = nullptr;
+        int side[kMaxCallGroups] = {};
+        if (ns_steps > 0 && ns_split_streams(brefs, nb)) {
+            lock.lock();
+            aux = aux_stream(s);
+            if (aux != nullptr)
+                split_sides(brefs, nb, side);
+            else
+                lock.unlock();
+        }
+        auto on = [&](int k) { return aux != nullptr && side[k] ? aux->s : s; };
+        bool joined = aux == nullptr;
+        auto join = [&]() {
+            // (enqueued whatever happened before, so that s never runs ahead
+            // of work already on the second stream)
+            if (joined) return;
+            joined = true;
+            const hipError_t ej = hipEventRecord(aux->join, aux->s);
+            const hipError_t ew = ej == hipSuccess ? hipStreamWaitEvent(s, aux->join, 0) : ej;
+            if (e == hipSuccess) e = ew;
+        };
+        if (aux != nullptr) {
+            e = hipEventRecord(aux->fork, s);
+            if (e == hipSuccess) e = hipStreamWaitEvent(aux->s, aux->fork, 0);
+        }
+        for (int k = 0; k < nb && e == hipSuccess; ++k) {
             const int i = c.bins[bi][k];
-            brefs[k] = c.refs[i];
             e = launch_muon_pre(c.plans[i].g, c.ptrs[i], mu, nesterov, ns_eps,
-                                ws + c.plans[i].base, c.plans[i].L, ns_steps == 0, dev, s);
+                                ws + c.plans[i].base, c.plans[i].L, ns_steps == 0, dev, on(k));
         }
-        if (e == hipSuccess)
-            e = ns_iterations(brefs, c.bin_size[bi], ns_steps, ns_a, ns_b, ns_c, s);
-        if (health && e == hipSuccess) {
-            int bfirst[kMaxCallGroups];
-            for (int k = 0; k < c.bin_size[bi]; ++k) bfirst[k] = c.firsts[c.bins[bi][k]];
-            e = launch_ns_health(brefs, bfirst, c.bin_size[bi], ns_steps, guard, health, s);
+        if (aux != nullptr) {
+            NsGroupRef r[2][kMaxCallGroups];
+            int n[2] = {0, 0};
+            for (int k = 0; k < nb; ++k) r[side[k]][n[side[k]]++] = brefs[k];
+            for (int it = 0; it < ns_steps && e == hipSuccess; ++it) {
+                e = launch_ns_iteration(r[0], n[0], it, it + 1 == ns_steps, ns_a, ns_b, ns_c, s);
+                if (e == hipSuccess)
+                    e = launch_ns_iteration(r[1], n[1], it, it + 1 == ns_steps, ns_a, ns_b, ns_c,
+                                            aux->s);
+            }
+        } else {
+            for (int it = 0; it < ns_steps && e == hipSuccess; ++it)
+                e = launch_ns_iteration(brefs, nb, it, it + 1 == ns_steps, ns_a, ns_b, ns_c, s);
         }
-        for (int k = 0; k < c.bin_size[bi] && e == hipSuccess; ++k) {
+        if (health) {
+            join();
+            if (e == hipSuccess) {
+                int bfirst[kMaxCallGroups];
+                for (int k = 0; k < nb; ++k) bfirst[k] = c.firsts[c.bins[bi][k]];
+                e = launch_ns_health(brefs, bfirst, nb, ns_steps, guard, health, s);
+            }
+        }
+        for (int k = 0; k < nb && e == hipSuccess; ++k) {
             const int i = c.bins[bi][k];
             const MuonGeom &g = c.plans[i].g;
             const double big = (double)(g.rows > g.cols ? g.rows : g.cols);
@@ -592,8 +606,9 @@ hipError_t muon_enqueue(const MuonCallPlan &c, char *ws, float lr, float mu, int
             e = launch_muon_post(g, c.ptrs[i],
                                  reinterpret_cast<const uint16_t *>(ws + c.plans[i].base + obase),
                                  old, c.plans[i].L.x_stride, decay, step_lr, reject, dev, scale,
-                                 s);
+                                 health ? s : on(k));
         }
+        join();
     }
     if (health && e == hipSuccess) e = launch_ns_health_total(health, c.nmat, s);
     return e;
