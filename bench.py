@@ -56,29 +56,31 @@ MEASURED_TRAFFIC = {
                         bytes_per_launch=7.000e9,
                         profile="profiles/adamw_bucket_grid_kernel_zero2_2b_rank3.md"),
     # one Newton-Schulz iteration of the 72 GPT-2-small matrices on two streams: the
-    # six launches' FETCH_SIZE + WRITE_SIZE, calibrated (0.4842 GB read, 0.2553 GB
+    # six launches' FETCH_SIZE + WRITE_SIZE, calibrated (0.6574 GB read, 0.3403 GB
     # written); the launch plan (tiles, streams) is in zopt_api.hip
     "ns_iteration_gpt2": dict(source="sharded_optimizer_step_adamw_amd/csrc/ns_gemm.hip",
-                              sha256="9ffa0d63cd33de9c690957c7b35591a6c0c34117cde93707535152bdb377218c",
+                              sha256="73657686043fc53c8ee1957cbd619d62e3d05e6317ce7a8681b3f4d1f29fac04",
                               also=[("sharded_optimizer_step_adamw_amd/csrc/zopt_api.hip",
-                                     "d462e3b0e464bbdef991a0467d2eb84a0d3fdc94e8c2d35be4fcf6a4c1390209")],
-                              bytes_per_launch=0.7394e9,
+                                     "0a3448ca28c6d321a16ae4639d1ea27ee2277297164932076ab05749a27dd2db")],
+                              bytes_per_launch=0.9977e9,
                               profile="profiles/ns_gemm_gpt2_small_step.md"),
     # one Newton-Schulz iteration of the 8B rank-0 share (28 matrices): X X^T, A A and
-    # B X, calibrated (23.590 GB read, 3.121 GB written)
+    # B X, calibrated (23.788 GB read, 3.122 GB written)
     "ns_iteration_llama8b": dict(source="sharded_optimizer_step_adamw_amd/csrc/ns_gemm.hip",
-                                 sha256="9ffa0d63cd33de9c690957c7b35591a6c0c34117cde93707535152bdb377218c",
-                                 bytes_per_launch=26.712e9,
+                                 sha256="73657686043fc53c8ee1957cbd619d62e3d05e6317ce7a8681b3f4d1f29fac04",
+                                 also=[("sharded_optimizer_step_adamw_amd/csrc/zopt_api.hip",
+                                        "0a3448ca28c6d321a16ae4639d1ea27ee2277297164932076ab05749a27dd2db")],
+                                 bytes_per_launch=26.909e9,
                                  profile="profiles/ns_gemm_llama8b_rank0.md"),
     # one Newton-Schulz iteration of the 1B rank-0 share (12 matrices) on two streams:
     # the 2 x [11264, 2048] group (split X X^T, fix-up, A A, B X) on one, the other three
-    # groups (X X^T and A A on 256 and 128 tiles, B X) on the other, calibrated (1.2536 GB
+    # groups (X X^T and A A on 256 and 128 tiles, B X) on the other, calibrated (1.2547 GB
     # read, 0.3568 GB written); the launch plan (which launches exist) is in zopt_api.hip
     "ns_iteration_llama1b": dict(source="sharded_optimizer_step_adamw_amd/csrc/ns_gemm.hip",
-                                 sha256="9ffa0d63cd33de9c690957c7b35591a6c0c34117cde93707535152bdb377218c",
+                                 sha256="73657686043fc53c8ee1957cbd619d62e3d05e6317ce7a8681b3f4d1f29fac04",
                                  also=[("sharded_optimizer_step_adamw_amd/csrc/zopt_api.hip",
-                                        "d462e3b0e464bbdef991a0467d2eb84a0d3fdc94e8c2d35be4fcf6a4c1390209")],
-                                 bytes_per_launch=1.6104e9,
+                                        "0a3448ca28c6d321a16ae4639d1ea27ee2277297164932076ab05749a27dd2db")],
+                                 bytes_per_launch=1.6115e9,
                                  profile="profiles/ns_gemm_llama1b_rank0.md"),
     "grad_sq_norm": dict(source="sharded_optimizer_step_adamw_amd/csrc/adamw_shard.hip",
                          sha256="673b6ee27b692f43da0cb776f129120c95304617a7117f995f9273186f2e9bca",
