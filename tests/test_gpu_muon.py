@@ -565,6 +565,17 @@ def test_two_stream_groups(ns_steps):
                         ns_check=lambda b, r, c, i: r == 2048 and i == 0)
 
 
+def test_groups_of_768_to_1023_rows_on_256_tiles():
+    """Groups whose short side is 768 or 897..1023 take 256 x 256 tiles when
+    those pad it no further than 128 x 128 would: beside a 4096^2 group the
+    3 x [768, 2000] and 2 x [960, 1500] groups run their symmetric products on
+    256 tiles (174 X X^T workgroups in all, so on two streams), alone on 128
+    tiles (too few 256-tiles of their own).  Every matrix equals the separate
+    calls' bit for bit; the 768- and 960-row matrices against the oracle."""
+    specs = [(3, 768, 2000), (2, 960, 1500), (1, 4096, 4096)]
+    grouped_vs_separate(specs, seed=555, ns_check=lambda b, r, c, i: r < 4096)
+
+
 @pytest.mark.parametrize("ns_steps", [1, 5])
 def test_split_reduction_groups(ns_steps):
     """X X^T split along K (a group whose reduction is at least 8192 long and
