@@ -55,33 +55,16 @@ MEASURED_TRAFFIC = {
                         sha256="673b6ee27b692f43da0cb776f129120c95304617a7117f995f9273186f2e9bca",
                         bytes_per_launch=7.000e9,
                         profile="profiles/adamw_bucket_grid_kernel_zero2_2b_rank3.md"),
-    # one Newton-Schulz iteration of the 72 GPT-2-small matrices on two streams: the
-    # six launches' FETCH_SIZE + WRITE_SIZE, calibrated (0.6574 GB read, 0.3403 GB
-    # written); the launch plan (tiles, streams) is in zopt_api.hip
-    "ns_iteration_gpt2": dict(source="sharded_optimizer_step_adamw_amd/csrc/ns_gemm.hip",
-                              sha256="73657686043fc53c8ee1957cbd619d62e3d05e6317ce7a8681b3f4d1f29fac04",
-                              also=[("sharded_optimizer_step_adamw_amd/csrc/zopt_api.hip",
-                                     "0a3448ca28c6d321a16ae4639d1ea27ee2277297164932076ab05749a27dd2db")],
-                              bytes_per_launch=0.9977e9,
-                              profile="profiles/ns_gemm_gpt2_small_step.md"),
-    # one Newton-Schulz iteration of the 8B rank-0 share (28 matrices): X X^T, A A and
-    # B X, calibrated (23.788 GB read, 3.122 GB written)
-    "ns_iteration_llama8b": dict(source="sharded_optimizer_step_adamw_amd/csrc/ns_gemm.hip",
-                                 sha256="73657686043fc53c8ee1957cbd619d62e3d05e6317ce7a8681b3f4d1f29fac04",
-                                 also=[("sharded_optimizer_step_adamw_amd/csrc/zopt_api.hip",
-                                        "0a3448ca28c6d321a16ae4639d1ea27ee2277297164932076ab05749a27dd2db")],
-                                 bytes_per_launch=26.909e9,
-                                 profile="profiles/ns_gemm_llama8b_rank0.md"),
-    # one Newton-Schulz iteration of the 1B rank-0 share (12 matrices) on two streams:
-    # the 2 x [11264, 2048] group (split X X^T, fix-up, A A, B X) on one, the other three
-    # groups (X X^T and A A on 256 and 128 tiles, B X) on the other, calibrated (1.2547 GB
-    # read, 0.3568 GB written); the launch plan (which launches exist) is in zopt_api.hip
-    "ns_iteration_llama1b": dict(source="sharded_optimizer_step_adamw_amd/csrc/ns_gemm.hip",
-                                 sha256="73657686043fc53c8ee1957cbd619d62e3d05e6317ce7a8681b3f4d1f29fac04",
-                                 also=[("sharded_optimizer_step_adamw_amd/csrc/zopt_api.hip",
-                                        "0a3448ca28c6d321a16ae4639d1ea27ee2277297164932076ab05749a27dd2db")],
-                                 bytes_per_launch=1.6115e9,
-                                 profile="profiles/ns_gemm_llama1b_rank0.md"),
+    # the Newton-Schulz of one 5-step Muon call (every NS launch: the symmetric
+    # products, the fix-ups of split X X^T, P X / Q X), FETCH_SIZE + WRITE_SIZE summed
+    # over the call's dispatches and calibrated; the launch plan (which launches
+    # exist, on which stream) is in zopt_api.hip.  Not yet measured on this source.
+    "ns_call_gpt2": dict(source="sharded_optimizer_step_adamw_amd/csrc/ns_gemm.hip", sha256=None,
+                         bytes_per_launch=None, profile="profiles/ns_gemm_gpt2_small_step.md"),
+    "ns_call_llama8b": dict(source="sharded_optimizer_step_adamw_amd/csrc/ns_gemm.hip", sha256=None,
+                            bytes_per_launch=None, profile="profiles/ns_gemm_llama8b_rank0.md"),
+    "ns_call_llama1b": dict(source="sharded_optimizer_step_adamw_amd/csrc/ns_gemm.hip", sha256=None,
+                            bytes_per_launch=None, profile="profiles/ns_gemm_llama1b_rank0.md"),
     "grad_sq_norm": dict(source="sharded_optimizer_step_adamw_amd/csrc/adamw_shard.hip",
                          sha256="673b6ee27b692f43da0cb776f129120c95304617a7117f995f9273186f2e9bca",
                          bytes_per_launch=0.5004e9,
@@ -92,6 +75,8 @@ MEASURED_TRAFFIC = {
 def measured_traffic(key):
     import hashlib
     t = MEASURED_TRAFFIC[key]
+    if t["sha256"] is None:
+        return None
     for src, sha in [(t["source"], t["sha256"])] + list(t.get("also", [])):
         with open(os.path.join(ROOT, src), "rb") as f:
             if hashlib.sha256(f.read()).hexdigest() != sha:
@@ -114,10 +99,43 @@ def parse():
     return ap.parse_args()
 
 
-def ns_flops(m, n, steps):
-    """Algorithmic flops of `steps` iterations on an m x n input (m <= n):
-    upper-triangle X X^T (m^2 n), upper-triangle A A (m^3), B X (2 m^2 n)."""
-    return steps * (3 * m * m * n + m ** 3)
+def gram_segments(steps, per=3):
+    """Segment lengths of the Gram form (the library's rule): ceil(steps / 3)
+    segments as even as possible, longer ones first."""
+    if steps <= 0:
+        return []
+    nseg = (steps + per - 1) // per
+    base, extra = divmod(steps, nseg)
+    return [base + (1 if i < extra else 0) for i in range(nseg)]
+
+
+def ns_flops(m, n, steps, form=0):
+    """Algorithmic flops of `steps` Newton-Schulz steps on an m x n input
+    (m <= n) as the library computes them.  Plain iterations (form 1, or
+    n < 2 m): per step upper-triangle X X^T (m^2 n), upper-triangle A A
+    (m^3), B X (2 m^2 n).  Gram form (forms 0 and 2 with n >= 2 m): per
+    segment of L steps X X^T (m^2 n), L upper-triangle A_j A_j, 3 (L - 1)
+    upper-triangle products of two symmetric m x m matrices (m^3 each),
+    Q X (2 m^2 n)."""
+    if form == 1 or n < 2 * m:
+        return steps * (3 * m * m * n + m ** 3)
+    return sum(3 * m * m * n + (4 * L - 3) * m ** 3 for L in gram_segments(steps))
+
+
+def group_flops(groups, steps, form=0):
+    return sum(g["count"] * ns_flops(min(g["rows"], g["cols"]), max(g["rows"], g["cols"]), steps,
+                                     form) for g in groups)
+
+
+def timed_forms(z, timer, fn, K):
+    """fn timed K times in the plain form (A/B against the default, on the
+    same buffers); the default form restored after."""
+    z.set_ns_form(z.NS_FORM_PLAIN)
+    try:
+        fn(0)
+        return timer.run(fn, K)
+    finally:
+        z.set_ns_form(z.NS_FORM_AUTO)
 
 
 class Timer:
@@ -238,18 +256,20 @@ def bench_step(torch, z, timer, dev, K, W):
     timer.run(step, W)
     ms = timer.run(step, K)
 
-    # the dominant kernels: one Newton-Schulz iteration of all 72 matrices is
-    # six launches on two streams (on each, X X^T and A A over its groups and
-    # B X); its time is the difference of the Muon call with 5 and with 1
-    # iteration, over 4 (the two calls take the same pre/post path)
+    # the dominant kernels: the Newton-Schulz of the Muon call (72 matrices,
+    # 5 steps) on two streams -- the 48 x [768, 768] group in plain
+    # iterations on one, the 768 x 3072 groups in Gram segments of 3 and 2
+    # steps on the other; its time is the 5-step call less the call with no
+    # steps (momentum, pre-scale and post-step only)
     t5 = timer.run(lambda _: muon_call(z, wm, groups, workspace, 5), K)
-    t1 = timer.run(lambda _: muon_call(z, wm, groups, workspace, 1), K)
     t0 = timer.run(lambda _: muon_call(z, wm, groups, workspace, 0), K)
-    iter_ms = (t5 - t1) / 4
-    iter_flops = sum(g["count"] * ns_flops(min(g["rows"], g["cols"]), max(g["rows"], g["cols"]), 1)
-                     for g in groups)
-    per_group = dict(muon_call_ms=round(t5, 4), one_iteration_call_ms=round(t1, 4),
-                     pre_post_ms=round(t1 - iter_ms, 4), zero_iteration_call_ms=round(t0, 4),
+    ns_ms = t5 - t0
+    ns_fl = group_flops(groups, 5)
+    t5p = timed_forms(z, timer, lambda _: muon_call(z, wm, groups, workspace, 5), K)
+    per_group = dict(muon_call_ms=round(t5, 4), zero_step_call_ms=round(t0, 4),
+                     ns_ms=round(ns_ms, 4),
+                     plain_form=dict(muon_call_ms=round(t5p, 4), ns_ms=round(t5p - t0, 4),
+                                     algorithmic_flops=group_flops(groups, 5, form=1)),
                      groups=[dict(shape=[g["rows"], g["cols"]], count=g["count"]) for g in groups],
                      ns_health=ns_health_check(torch, z, timer, wm, groups, workspace, K, t5))
     adamw_bytes = 28 * n
@@ -260,7 +280,7 @@ def bench_step(torch, z, timer, dev, K, W):
         p.beta2, p.eps, p.weight_decay, 1000 + i) for p in wa.parts], K)
     del a, groups, workspace
     torch.cuda.empty_cache()
-    return dict(ms=ms, ns_iter_ms=iter_ms, ns_iter_flops=iter_flops, muon=per_group,
+    return dict(ms=ms, ns_ms=ns_ms, ns_flops=ns_fl, muon=per_group,
                 adamw_ms=ta, adamw_gbs=adamw_bytes / ta / 1e6)
 
 
@@ -343,15 +363,18 @@ def bench_ns(torch, z, timer, dev, K, W, w=None):
     import workloads as wl
     w = w or wl.LLAMA8B_MUON
     groups, workspace = muon_groups(torch, w, dev)
-    total_flops = sum(g["count"] * ns_flops(min(g["rows"], g["cols"]), max(g["rows"], g["cols"]),
-                                            w.ns_steps) for g in groups)
+    total_flops = group_flops(groups, w.ns_steps)
     timer.run(lambda _: muon_call(z, w, groups, workspace, w.ns_steps), max(1, W))
     t5 = timer.run(lambda _: muon_call(z, w, groups, workspace, w.ns_steps), K)
-    t1 = timer.run(lambda _: muon_call(z, w, groups, workspace, 1), K)
-    # a 1-iteration call takes the same pre/post path as the 5-iteration one
-    # (a call with no iterations takes another: it writes X0 itself), so
-    # their difference is 4 iterations
-    ns_ms, call_ms = (t5 - t1) * w.ns_steps / (w.ns_steps - 1), t5
+    t0 = timer.run(lambda _: muon_call(z, w, groups, workspace, 0), K)
+    # the Newton-Schulz of the call: the 5-step call less the call with no
+    # steps (momentum, pre-scale and post-step; with no steps the pre-scale
+    # writes X0 = bf16(U s), and X0^T for matrices stored transposed, where a
+    # call with steps writes bf16(U): the same bytes but for that transpose)
+    ns_ms, call_ms = t5 - t0, t5
+    t5p = timed_forms(z, timer, lambda _: muon_call(z, w, groups, workspace, w.ns_steps), K)
+    plain = dict(muon_ms_per_step=round(t5p, 3), ns_ms_per_step=round(t5p - t0, 3),
+                 algorithmic_flops_per_step=group_flops(groups, w.ns_steps, form=1))
     rows = [dict(shape=[g["rows"], g["cols"]], count=g["count"]) for g in groups]
     health = ns_health_check(torch, z, timer, w, groups, workspace, K, t5)
     del groups, workspace
@@ -359,29 +382,32 @@ def bench_ns(torch, z, timer, dev, K, W, w=None):
     tf = total_flops / ns_ms / 1e9
     names = {"llama8b_rank0_muon": "llama8b rank-0 Muon share (W=8, 32 layers), 5 bf16 NS iterations",
              "llama1b_rank0_muon": "llama1b rank-0 Muon share (W=8, 16 layers), 5 bf16 NS iterations"}
-    # the dominant kernels: one Newton-Schulz iteration of every matrix of the
-    # share (the unit), timed as (5-iteration call - 1-iteration call) / 4
+    # the dominant kernels: the Newton-Schulz products of one 5-step call over
+    # every matrix of the share (the unit), timed as the 5-step call less the
+    # call with no steps
     if w.name == "llama8b_rank0_muon":
-        kernel = ("Newton-Schulz iteration of the 28 matrices: ns_gemm_kernel<256,0> X X^T and "
-                  "ns_gemm_kernel<256,1> A A (one launch each over all four groups), "
-                  "ns_bx_kernel<256> B X (persistent, 256 workgroups)")
-        traffic, tunit = measured_traffic("ns_iteration_llama8b"), "HBM bytes per iteration (3 launches)"
+        kernel = ("Newton-Schulz of the 28 matrices, one stream, 23 merged steps: the 8 x [4096, "
+                  "4096] group in plain iterations (ns_gemm_kernel<256,0,bf16> X X^T, "
+                  "ns_gemm_kernel<256,1,bf16> P, ns_bx_kernel<256> P X), the three groups with "
+                  "n >= 2m in Gram segments of 3 and 2 steps (X X^T, ns_gemm_kernel<256,1,fp16> "
+                  "and ns_gemm_kernel<256,3,fp16> on the m x m chain, ns_bx_kernel<256> Q X)")
+        traffic, tunit = measured_traffic("ns_call_llama8b"), "HBM bytes per 5-step call (all NS launches)"
     else:
-        kernel = ("Newton-Schulz iteration of the 12 matrices on two streams: the 11264 x 2048 pair "
-                  "(X X^T split along K plus its fix-up, A A, ns_bx_kernel<256> B X) on one, the "
-                  "other three groups (X X^T and A A on 256 tiles, and 128 tiles for the 512-row "
-                  "group, ns_bx_kernel<256> B X) on the other")
-        traffic, tunit = measured_traffic("ns_iteration_llama1b"), "HBM bytes per iteration (9 launches)"
+        kernel = ("Newton-Schulz of the 12 matrices on two streams: the 11264 x 2048 pair (Gram "
+                  "segments; X X^T split along K plus its fix-up) on one, the other three groups "
+                  "(2048 x 5632 and 512 x 2048 in Gram segments, 2048 x 2048 in plain "
+                  "iterations) on the other")
+        traffic, tunit = measured_traffic("ns_call_llama1b"), "HBM bytes per 5-step call (all NS launches)"
     roof = dict(kernel=kernel, bound="mfma", achieved=round(tf, 1), peak=BF16_PEAK_TFLOPS,
                 unit="TFLOP/s", frac=round(tf / BF16_PEAK_TFLOPS, 4), traffic=traffic,
-                traffic_unit=tunit, algorithmic_flops_per_unit=total_flops // w.ns_steps,
-                avg_unit_ms=round(ns_ms / w.ns_steps, 4))
+                traffic_unit=tunit, algorithmic_flops_per_unit=total_flops,
+                avg_unit_ms=round(ns_ms, 4))
     return dict(workload=names.get(w.name, w.name),
                 algorithmic_flops_per_step=total_flops, ns_ms_per_step=round(ns_ms, 3),
                 muon_ms_per_step=round(call_ms, 3), ns_tflops=round(tf, 1),
                 mfma_frac=round(tf / BF16_PEAK_TFLOPS, 4),
-                muon_step_tflops=round(total_flops / call_ms / 1e9, 1), groups=rows, steps=K,
-                ns_health=health, roofline=roof)
+                muon_step_tflops=round(total_flops / call_ms / 1e9, 1), zero_step_call_ms=round(t0, 3),
+                plain_form=plain, groups=rows, steps=K, ns_health=health, roofline=roof)
 
 
 def bench_graph(torch, z, timer, dev, K, W):
@@ -769,17 +795,19 @@ def main():
     res_copy = bench_copy(torch, z, timer, dev, K, W) if "copy" in parts else None
     res_graph = bench_graph(torch, z, timer, dev, K, W) if "graph" in parts else None
     if res_step:
-        tf = res_step["ns_iter_flops"] / res_step["ns_iter_ms"] / 1e9
+        tf = res_step["ns_flops"] / res_step["ns_ms"] / 1e9
         out.update(value=round(res_step["ms"], 4), unit="ms per optimizer step")
         roof = dict(
-            kernel=("Newton-Schulz iteration on two streams: the 48 x [768, 768] group on one, "
-                    "the 3072 x 768 and 768 x 3072 groups on the other, each stream "
-                    "ns_gemm_kernel<256> X X^T and A A + ns_bx_kernel<256> B X (persistent)"),
+            kernel=("Newton-Schulz of the Muon call (72 matrices, 5 steps) on two streams: the "
+                    "48 x [768, 768] group in plain iterations (ns_gemm_kernel<256> X X^T and P, "
+                    "ns_bx_kernel<256> P X) on one, the 3072 x 768 and 768 x 3072 groups in Gram "
+                    "segments of 3 and 2 steps (X X^T, fp16 m x m chain on ns_gemm_kernel<256>, "
+                    "ns_bx_kernel<256> Q X) on the other"),
             bound="mfma", achieved=round(tf, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-            frac=round(tf / BF16_PEAK_TFLOPS, 4), traffic=measured_traffic("ns_iteration_gpt2"),
-            traffic_unit="HBM bytes per iteration (6 launches)",
-            algorithmic_flops_per_unit=res_step["ns_iter_flops"],
-            avg_unit_ms=round(res_step["ns_iter_ms"], 4))
+            frac=round(tf / BF16_PEAK_TFLOPS, 4), traffic=measured_traffic("ns_call_gpt2"),
+            traffic_unit="HBM bytes per 5-step call (all NS launches)",
+            algorithmic_flops_per_unit=res_step["ns_flops"],
+            avg_unit_ms=round(res_step["ns_ms"], 4))
     else:
         roof = None
     out.update(n_gpus=1, steps=K, warmup=W,

@@ -24,10 +24,12 @@
  * --------------------------------
  *  - Every buffer is device memory owned by the caller.  The library
  *    allocates no device memory at run time and keeps no state between calls,
- *    with four exceptions: a captured Muon graph is a handle the caller owns;
+ *    with five exceptions: a captured Muon graph is a handle the caller owns;
  *    zopt_set_ns_workgroup_limit is a process-wide setting that every later
  *    call in the process uses (one thread's setting changes the launch plan,
- *    never the results, of another's calls); zopt_grad_sq_norm_noalloc
+ *    never the results, of another's calls); zopt_set_ns_form is another,
+ *    which selects how Newton-Schulz is computed (and so changes results
+ *    within bf16 rounding, and the workspace size); zopt_grad_sq_norm_noalloc
  *    uses a 16 KiB array per GPU that the library holds for the life of the
  *    process; and a grouped Muon call whose Newton-Schulz launches are short
  *    (see zopt_muon_step_groups) uses a second stream per GPU, with two
@@ -303,7 +305,21 @@ int64_t zopt_shard_len(int64_t N, int64_t bucket, int32_t world);
  *        A = X X^T;  B = b A + c A A;  X = a X + B X
  *      on bf16 matrix cores with fp32 accumulation; A, B and X are rounded to
  *      bf16 after each product; only the upper triangle of the symmetric A
- *      and B is computed and mirrored.
+ *      and B is computed and mirrored.  Where the long side is at least twice
+ *      the short one (n >= 2 m) the same polynomial map runs in segments of
+ *      up to three steps on the m x m Gram matrix: with A_j = X_j X_j^T and
+ *      P_j = a I + b A_j + c A_j^2, X_{j+1} = P_j X_j gives A_{j+1} =
+ *      P_j^2 A_j and X_L = (P_{L-1} ... P_0) X_0, so a segment forms X X^T
+ *      once and multiplies X by one m x m matrix; every other product is of
+ *      two commuting symmetric m x m matrices (upper triangle computed), and
+ *      the chain of them is held in fp16 where the coefficients allow
+ *      (zopt_set_ns_form), with the final m x m factor rounded to bf16.  Five
+ *      steps are segments of 3 and 2: 6 m^2 n + 14 m^3 flops against
+ *      15 m^2 n + 5 m^3.  Each segment restarts from its X, which keeps the
+ *      bf16 rounding of the m x m chain from compounding.  The two forms
+ *      agree to within bf16 rounding, not bit for bit; zopt_set_ns_form
+ *      selects plain iterations for every matrix.  Every symmetric m x m
+ *      matrix is held as a bf16 off-diagonal part and an fp32 diagonal.
  *   4. Post-step [BluScript trainer source, Muon config block (weight decay
  *      pinned to AdamW's) and the note beside the MuonAdjustLr choice]:
  *        P = P * decay - step_lr * fp32(O),  weight = bf16(P)
@@ -544,6 +560,26 @@ zopt_status zopt_round_bf16(const float *src, uint16_t *dst, int64_t n, void *st
  * Errors: ZOPT_ERR_SIZE (n < 0).
  */
 zopt_status zopt_set_ns_workgroup_limit(int32_t n);
+
+/*
+ * zopt_set_ns_form -- the Newton-Schulz form of later calls:
+ *   0 (the default) runs matrices whose long side is at least twice the
+ *     short one in segments on the Gram matrix (zopt_muon_step, step 3),
+ *     holding a segment's m x m chain in fp16 (3 more mantissa bits than
+ *     bf16, the same matrix-core rate) when the coefficients keep every
+ *     matrix of the chain below 2^13 in magnitude (checked on the scalar
+ *     map over singular values in [0, 1.05]; true for the usual quintic and
+ *     cubic coefficients), else in bf16;
+ *   1 runs plain iterations for every matrix;
+ *   2 is form 0 with the chain always in bf16 (for comparison: less
+ *     accurate than both others on some inputs).
+ * Process-wide; it applies to workspace queries, calls and graph captures
+ * made after it.  Forms 0 and 2 need more workspace for those shapes (three
+ * more m x m 16-bit matrices and fp32 diagonals per matrix), so a workspace
+ * sized under form 1 fails their size check (ZOPT_ERR_WORKSPACE).
+ * Errors: ZOPT_ERR_HYPER (form not 0, 1 or 2).
+ */
+zopt_status zopt_set_ns_form(int32_t form);
 
 #ifdef __cplusplus
 }

@@ -83,6 +83,8 @@ def _lib_or_raise() -> ctypes.CDLL:
         L.zopt_round_bf16.restype = ctypes.c_int
         L.zopt_set_ns_workgroup_limit.argtypes = [i32]
         L.zopt_set_ns_workgroup_limit.restype = ctypes.c_int
+        L.zopt_set_ns_form.argtypes = [i32]
+        L.zopt_set_ns_form.restype = ctypes.c_int
         pp = ctypes.POINTER(vp)
         L.zopt_muon_step.argtypes = [i32, i64, i64, pp, pp, pp, pp, f32, f32, i32, f32, i32,
                                      f32, f32, f32, f32, i32, vp,
@@ -271,6 +273,18 @@ def set_ns_workgroup_limit(n: int) -> None:
     resident (0: a full round of the device); process-wide
     (zopt_set_ns_workgroup_limit)."""
     _check(lib().zopt_set_ns_workgroup_limit(int(n)), "zopt_set_ns_workgroup_limit")
+
+
+NS_FORM_AUTO, NS_FORM_PLAIN, NS_FORM_GRAM_BF16 = 0, 1, 2
+
+
+def set_ns_form(form: int) -> None:
+    """Newton-Schulz form of later calls: NS_FORM_AUTO (segments on the Gram
+    matrix for matrices whose long side is at least twice the short one, the
+    m x m chain in fp16 where the coefficients allow), NS_FORM_PLAIN (plain
+    iterations throughout) or NS_FORM_GRAM_BF16 (as AUTO, chain in bf16)
+    (zopt_set_ns_form)."""
+    _check(lib().zopt_set_ns_form(int(form)), "zopt_set_ns_form")
 
 
 def _ptr_array(tensors) -> ctypes.Array:

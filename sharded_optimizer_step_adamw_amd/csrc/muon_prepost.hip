@@ -781,7 +781,7 @@ hipError_t launch_ns_health(const NsGroupRef *refs, const int *mat_first, int nr
         const MuonWorkspace &L = *refs[i].layout;
         char *ws = refs[i].base;
         HealthGroup &G = h.g[i];
-        G.x = reinterpret_cast<const uint16_t *>(ws + ((ns_steps & 1) ? L.xt0 : L.x));
+        G.x = reinterpret_cast<const uint16_t *>(ws + ((ns_segments(g, ns_steps) & 1) ? L.xt0 : L.x));
         G.x_stride = (int64_t)(L.x_stride / 2);
         G.count = (int64_t)g.m * g.np;  // a multiple of 8: np is a multiple of 64
         G.psum = reinterpret_cast<double *>(ws + L.hsum);

@@ -40,7 +40,11 @@
 // together and the launch count per iteration stays at three per tile size.
 // Workgroups are numbered group by group (longest reduction first), matrix by
 // matrix, tile by tile.
+#include <algorithm>
 #include <atomic>
+#include <cmath>
+#include <mutex>
+#include <vector>
 
 #include "zopt_internal.h"
 
@@ -52,7 +56,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-enum Mode : int { kSyrkXXT = 0, kSyrkAA = 1, kGemmBX = 2 };
+enum Mode : int { kSyrkXXT = 0, kSyrkAA = 1, kGemmBX = 2, kSymLR = 3 };
 
 // One group of same-shape matrices in a launch.
 struct NsGroup {
@@ -69,8 +73,9 @@ struct NsGroup {
     uint16_t *C;                 // A or B (SYRK) / X, updated in place (GEMM)
     int64_t c_stride;
     const uint16_t *E;           // SYRK_AA: Aoff (for b*A); unused otherwise
-    const float *dIn;            // SYRK_AA: dA; GEMM_BX: dB
-    float *dOut;                 // SYRK_XXT: dA; SYRK_AA: dB
+    const float *dIn;            // SYRK_AA: dA; GEMM_BX: dP; SYM_LR: the left operand's diagonal
+    const float *dIn2;           // SYM_LR: the right operand's diagonal
+    float *dOut;                 // SYRK_XXT: dA; SYRK_AA: dP; SYM_LR: the product's diagonal
     int64_t d_stride;            // floats between matrices of dA / dB
     uint16_t *CT;                // GEMM_BX: X'^T, or NULL (not wanted)
     int64_t ct_stride;
@@ -83,6 +88,8 @@ struct NsGroup {
     // fix-up kernel forms A from the parts.  NULL: the normal epilogue.
     float *part;
     int64_t part_stride;
+    // Symmetric products: the output's 16-bit element type (0 bf16, 1 fp16)
+    int32_t out_f16;
 };
 
 struct NsLaunch {
@@ -104,6 +111,23 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
 }
 __device__ __forceinline__ uint16_t cvt_bf16(float x) { return (uint16_t)cvt_pk_bf16(x, 0.0f); }
 __device__ __forceinline__ float from_bf16(uint16_t h) { return bf16_bits_to_float(h); }
+
+// The same for fp16 (v_cvt_pk_f16_f32, round to nearest even), the element
+// type of a Gram segment's m x m chain.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_pk_f16(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
+}
+__device__ __forceinline__ float from_f16(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+template <bool F16>
+__device__ __forceinline__ float from_el(uint16_t h) {
+    return F16 ? from_f16(h) : from_bf16(h);
+}
+// two values of a symmetric product's output, in its element type
+__device__ __forceinline__ uint32_t pack_el(float lo, float hi, bool f16) {
+    return f16 ? cvt_pk_f16(lo, hi) : cvt_pk_bf16(lo, hi);
+}
 
 // Tile t of a matrix, in bands of kBand tile rows taken column by column, so
 // that the tiles an XCD runs at the same time share few operand row panels
@@ -188,7 +212,7 @@ __device__ __forceinline__ int swz(int i, int j) {
 // LDS from its upper triangle and stored once.  The diagonal itself goes to
 // the fp32 vector (its bf16 entry is 0).  Every wave passes the same
 // barriers.
-template <int MODE, int BM, int FM, int FN>
+template <int MODE, int BM, int FM, int FN, bool F16>
 __device__ __forceinline__ void epilogue(const NsGroup &args, float ca, float cb, float cc,
                                          f32x4 (&acc)[FM][FN], int batch, int m0, int n0, int R0,
                                          int C0, int wave, int lane, uint8_t *lds_all) {
@@ -202,6 +226,7 @@ __device__ __forceinline__ void epilogue(const NsGroup &args, float ca, float cb
     const bool above = R0 + SR <= C0;
     const bool cross = !below && !above;
     const int64_t ldc = args.ldc;
+    const bool of16 = args.out_f16 != 0;
     uint16_t *Cm = args.C + batch * args.c_stride;
     const float *dIn = args.dIn + batch * args.d_stride;
     float *dOut = args.dOut + batch * args.d_stride;
@@ -276,15 +301,69 @@ __device__ __forceinline__ void epilogue(const NsGroup &args, float ca, float cb
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
                 const int gj = C0 + j * 16 + col;
-                const float in4[4] = {from_bf16(e[j].x & 0xFFFFu), from_bf16(e[j].x >> 16),
-                                      from_bf16(e[j].y & 0xFFFFu), from_bf16(e[j].y >> 16)};
+                const float in4[4] = {from_el<F16>(e[j].x & 0xFFFFu), from_el<F16>(e[j].x >> 16),
+                                      from_el<F16>(e[j].y & 0xFFFFu), from_el<F16>(e[j].y >> 16)};
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int gi = R0 + i * 16 + quad * 4 + r;
                     const float in = in4[r], v = acc[i][j][r], da_i = da_r[i][r];
                     float x = cb * in + cc * (v + (da_i + da_c[j]) * in);
-                    if (gi == gj) x = cb * da_i + cc * (v + da_i * da_i);
+                    if (gi == gj) x = ca + (cb * da_i + cc * (v + da_i * da_i));
                     acc[i][j][r] = x;
+                }
+            }
+        }
+    }
+    if (MODE == kSymLR && !below) {
+        // C = L R of two symmetric matrices held as off-diagonal parts and
+        // diagonals: the accumulators hold Loff Roff; add dL_i Roff_ij +
+        // Loff_ij dR_j (both off-diagonal parts are 0 on the diagonal, where
+        // dL_i dR_i is added instead).  By symmetry Loff_ij = Loff_ji, so the
+        // lane's four rows of column j are four consecutive entries of row j:
+        // one 8-byte load per 16 x 16 block and operand, in NH rounds of the
+        // row blocks to bound the registers in flight.
+        const uint16_t *Lm = args.P + batch * args.p_stride;
+        const uint16_t *Rm = args.Q + batch * args.q_stride;
+        const float *dL = args.dIn + batch * args.d_stride;
+        const float *dR = args.dIn2 + batch * args.d_stride;
+        const int64_t ld = args.ld;
+        float dr[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) dr[j] = dR[C0 + j * 16 + col];
+        constexpr int NH = FM >= 8 ? 4 : 2, FH = FM / NH;
+        static_assert(FM % NH == 0, "rounds of the row blocks");
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            u32x2 lv[FH][FN], rv[FH][FN];
+            f32x4 dl[FH];
+#pragma unroll
+            for (int ii = 0; ii < FH; ++ii) {
+                const int r0 = R0 + (h * FH + ii) * 16 + quad * 4;
+                dl[ii] = *reinterpret_cast<const f32x4 *>(dL + r0);
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int64_t o = (int64_t)(C0 + j * 16 + col) * ld + r0;
+                    lv[ii][j] = *reinterpret_cast<const u32x2 *>(Lm + o);
+                    rv[ii][j] = *reinterpret_cast<const u32x2 *>(Rm + o);
+                }
+            }
+#pragma unroll
+            for (int ii = 0; ii < FH; ++ii) {
+                const int i = h * FH + ii;
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int gj = C0 + j * 16 + col;
+                    const float lo4[4] = {from_el<F16>(lv[ii][j].x & 0xFFFFu), from_el<F16>(lv[ii][j].x >> 16),
+                                          from_el<F16>(lv[ii][j].y & 0xFFFFu), from_el<F16>(lv[ii][j].y >> 16)};
+                    const float ro4[4] = {from_el<F16>(rv[ii][j].x & 0xFFFFu), from_el<F16>(rv[ii][j].x >> 16),
+                                          from_el<F16>(rv[ii][j].y & 0xFFFFu), from_el<F16>(rv[ii][j].y >> 16)};
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int gi = R0 + i * 16 + quad * 4 + r;
+                        const float v = acc[i][j][r];
+                        acc[i][j][r] = gi == gj ? v + dl[ii][r] * dr[j]
+                                                : v + dl[ii][r] * ro4[r] + lo4[r] * dr[j];
+                    }
                 }
             }
         }
@@ -309,7 +388,7 @@ __device__ __forceinline__ void epilogue(const NsGroup &args, float ca, float cb
                         const int li = R0 - m0 + i * 16 + quad * 4 + r;
                         const float x = acc[i][j][r];
                         if (li < lj) {
-                            const uint16_t h = cvt_bf16(x);
+                            const uint16_t h = (uint16_t)pack_el(x, 0.0f, of16);
                             *reinterpret_cast<uint16_t *>(lds_all + swz<TB>(li, lj)) = h;
                             *reinterpret_cast<uint16_t *>(lds_all + swz<TB>(lj, li)) = h;
                         } else if (li == lj) {
@@ -340,7 +419,7 @@ __device__ __forceinline__ void epilogue(const NsGroup &args, float ca, float cb
 #pragma unroll
             for (int j = 0; j < FN; ++j)
                 *reinterpret_cast<u32x2 *>(W + swz<TCH>(j * 16 + col, i * 16 + quad * 4)) =
-                    u32x2{cvt_pk_bf16(acc[i][j][0], acc[i][j][1]), cvt_pk_bf16(acc[i][j][2], acc[i][j][3])};
+                    u32x2{pack_el(acc[i][j][0], acc[i][j][1], of16), pack_el(acc[i][j][2], acc[i][j][3], of16)};
     }
     __syncthreads();
     if (coalesced) {
@@ -406,10 +485,11 @@ constexpr int kBK = 32;
 // expcnt[6:4], lgkmcnt[11:8], vmcnt high bits[15:14])
 #define WAIT_VM_LGKM0(n) ((((n) & 15) | (((n) >> 4) << 14) | (7 << 4)))
 
-template <int BM, int MODE>
+template <int BM, int MODE, bool F16>
 __global__ __launch_bounds__(Cfg<BM>::WR * Cfg<BM>::WC * 64)
 __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch L) {
-    static_assert(MODE == kSyrkXXT || MODE == kSyrkAA, "B X has a kernel of its own");
+    static_assert(MODE == kSyrkXXT || MODE == kSyrkAA || MODE == kSymLR, "B X has a kernel of its own");
+    static_assert(!(F16 && MODE == kSyrkXXT), "X is bf16");
     constexpr int WR = Cfg<BM>::WR, WC = Cfg<BM>::WC, NW = WR * WC;
     constexpr int WTM = BM / WR, WTN = BM / WC, FM = WTM / 16, FN = WTN / 16;
     constexpr int ROW = 64, OPB = BM * ROW, STAGE = 2 * OPB;
@@ -514,8 +594,13 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch 
         for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[buf][i], fb[buf][j], acc[i][j],
-                                                                    0, 0, 0);
+                if constexpr (F16)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        __builtin_bit_cast(f16x8, fa[buf][i]), __builtin_bit_cast(f16x8, fb[buf][j]),
+                        acc[i][j], 0, 0, 0);
+                else
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[buf][i], fb[buf][j],
+                                                                        acc[i][j], 0, 0, 0);
     };
 
     const int KT = K / kBK;
@@ -592,7 +677,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch 
     // the epilogue reuses the buffers
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    epilogue<MODE, BM, FM, FN>(G, L.a, L.b, L.c, acc, batch, m0, n0, m0 + wr * WTM, n0 + wc * WTN,
+    epilogue<MODE, BM, FM, FN, F16>(G, L.a, L.b, L.c, acc, batch, m0, n0, m0 + wr * WTM, n0 + wc * WTN,
                                wave, lane, lds);
 }
 
@@ -824,7 +909,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_bx_kernel(NsLaunch L)
             }
             // the wait is tied to the registers, so no use moves above it
             asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(db));
-            const float d = L.a + db;
+            const float d = db;
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
                 asm volatile("" : "+v"(xv[j]));
@@ -1011,26 +1096,29 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_bx_kernel(NsLaunch L)
 template <int T>
 constexpr int kThreadsOf = Cfg<T>::WR * Cfg<T>::WC * 64;
 
-// The per-group operands of one product of iteration `iter` (X in the x
-// buffer at even iterations, in xt0 at odd ones; the other receives X').
-// One launch's share of a group: its matrices [b0, b0 + nb) on tiles of `tile`.
+// One launch's share of a group: its matrices [b0, b0 + nb), one product of
+// a program step (pool slots in1, in2 -> out) in segment seg.
 struct LaunchPart {
     int ref, b0, nb;
     int split = 0, nsplit = 1;  // X X^T: part `split` of the group's K split in nsplit
+    int in1 = 0, in2 = 0, out = 0;
+    int seg = 0;
+    bool last = false;  // the step is in the group's last segment
+    bool in_f16 = false, out_f16 = false;  // symmetric operands / output in fp16
 };
 
-NsGroup product_group(int mode, const NsGroupRef &r, int iter, bool last, int tile, int b0,
-                      int split = 0, int nsplit = 1) {
+// The operands of a part (X in the x buffer in even segments, in xt0 in odd
+// ones; the other receives X').
+NsGroup product_group(int mode, const NsGroupRef &r, const LaunchPart &p, int tile) {
     const MuonGeom &g = *r.geom;
     const MuonWorkspace &L = *r.layout;
     char *ws = r.base;
-    uint16_t *X = reinterpret_cast<uint16_t *>(ws + ((iter & 1) ? L.xt0 : L.x));
-    uint16_t *Xn = reinterpret_cast<uint16_t *>(ws + ((iter & 1) ? L.x : L.xt0));
+    const int b0 = p.b0;
+    uint16_t *X = reinterpret_cast<uint16_t *>(ws + ((p.seg & 1) ? L.xt0 : L.x));
+    uint16_t *Xn = reinterpret_cast<uint16_t *>(ws + ((p.seg & 1) ? L.x : L.xt0));
     uint16_t *XTout = reinterpret_cast<uint16_t *>(ws + L.xt1);
-    uint16_t *A = reinterpret_cast<uint16_t *>(ws + L.a);
-    uint16_t *B = reinterpret_cast<uint16_t *>(ws + L.b);
-    float *dA = reinterpret_cast<float *>(ws + L.da);
-    float *dB = reinterpret_cast<float *>(ws + L.db);
+    auto sm = [&](int k) { return reinterpret_cast<uint16_t *>(ws + L.sm[k]); };
+    auto sd = [&](int k) { return reinterpret_cast<float *>(ws + L.sd[k]); };
     const int64_t ds = (int64_t)(L.d_stride / 4);
     const int64_t xs = (int64_t)(L.x_stride / 2), as = (int64_t)(L.a_stride / 2);
     const int tm = g.mp / tile, tn = g.np / tile;
@@ -1040,32 +1128,36 @@ NsGroup product_group(int mode, const NsGroupRef &r, int iter, bool last, int ti
     if (mode == kSyrkXXT) {
         s.P = X; s.Q = X; s.p_stride = xs; s.q_stride = xs; s.ld = g.np; s.K = g.np;
         s.tiles_n = tm; s.tiles_pm = tm * (tm + 1) / 2;
-        s.C = A; s.c_stride = as; s.ldc = g.mp;
-        s.dIn = dA; s.dOut = dA;
-    } else if (mode == kSyrkAA) {
-        s.P = A; s.Q = A; s.p_stride = as; s.q_stride = as; s.ld = g.mp; s.K = g.mp;
+        s.C = sm(p.out); s.c_stride = as; s.ldc = g.mp;
+        s.dIn = sd(p.out); s.dOut = sd(p.out);
+    } else if (mode == kSyrkAA || mode == kSymLR) {
+        s.P = sm(p.in1); s.Q = sm(mode == kSyrkAA ? p.in1 : p.in2);
+        s.p_stride = as; s.q_stride = as; s.ld = g.mp; s.K = g.mp;
         s.tiles_n = tm; s.tiles_pm = tm * (tm + 1) / 2;
-        s.C = B; s.c_stride = as; s.ldc = g.mp; s.E = A;
-        s.dIn = dA; s.dOut = dB;
+        s.C = sm(p.out); s.c_stride = as; s.ldc = g.mp;
+        if (mode == kSyrkAA) s.E = sm(p.in1);
+        s.dIn = sd(p.in1); s.dOut = sd(p.out);
+        if (mode == kSymLR) s.dIn2 = sd(p.in2);
     } else {
-        s.P = B; s.Q = X; s.p_stride = as; s.q_stride = xs; s.ld = g.mp; s.K = g.mp;
+        s.P = sm(p.in1); s.Q = X; s.p_stride = as; s.q_stride = xs; s.ld = g.mp; s.K = g.mp;
         s.ldq = g.np;
         s.tiles_n = tn; s.tiles_pm = tm * tn;
         s.C = Xn; s.c_stride = xs; s.ldc = g.np;
-        s.CT = (last && g.transposed) ? XTout : nullptr; s.ct_stride = xs; s.ldct = g.mp;
-        s.dIn = dB; s.dOut = dB;
+        s.CT = (p.last && g.transposed) ? XTout : nullptr; s.ct_stride = xs; s.ldct = g.mp;
+        s.dIn = sd(p.in1); s.dOut = sd(p.in1);
     }
-    if (iter == 0 && mode != kSyrkAA) s.xs = muon_scale_ptr(ws, g, L) + b0;
-    if (mode == kSyrkXXT && nsplit > 1) {
+    if (p.seg == 0 && (mode == kSyrkXXT || mode == kGemmBX)) s.xs = muon_scale_ptr(ws, g, L) + b0;
+    s.out_f16 = p.out_f16 ? 1 : 0;
+    if (mode == kSyrkXXT && p.nsplit > 1) {
         // K range [split K / nsplit, (split + 1) K / nsplit) of X's columns;
         // s is applied by the fix-up, to the sum of the parts
-        const int kp = g.np / nsplit;
-        s.P += (int64_t)split * kp;
-        s.Q += (int64_t)split * kp;
+        const int kp = g.np / p.nsplit;
+        s.P += (int64_t)p.split * kp;
+        s.Q += (int64_t)p.split * kp;
         s.K = kp;
         s.part_stride = (int64_t)g.mp * g.mp;
         s.part = reinterpret_cast<float *>(ws + L.part) +
-                 (int64_t)split * g.batch * s.part_stride + b0 * s.part_stride;
+                 (int64_t)p.split * g.batch * s.part_stride + b0 * s.part_stride;
         s.xs = nullptr;
     }
     // matrices from b0 on
@@ -1075,6 +1167,7 @@ NsGroup product_group(int mode, const NsGroupRef &r, int iter, bool last, int ti
     if (s.E) s.E += b0 * s.c_stride;
     if (s.CT) s.CT += b0 * s.ct_stride;
     s.dIn += b0 * s.d_stride;
+    if (s.dIn2) s.dIn2 += b0 * s.d_stride;
     s.dOut += b0 * s.d_stride;
     return s;
 }
@@ -1103,9 +1196,9 @@ int32_t bx_round_tiles() {
     return lim > 0 && lim < r ? lim : r;
 }
 
-template <int T, int MODE>
-hipError_t launch_product(const NsGroupRef *refs, const LaunchPart *parts, int n, int iter,
-                          bool last, float a, float b, float c, hipStream_t stream) {
+template <int T, int MODE, bool F16>
+hipError_t launch_product(const NsGroupRef *refs, const LaunchPart *parts, int n, float a,
+                          float b, float c, hipStream_t stream) {
     const int32_t round_tiles = MODE == kGemmBX ? bx_round_tiles<T>() : round_tiles_of<T>(true);
     for (int first = 0; first < n; first += kMaxGroups) {
         const int cnt = n - first < kMaxGroups ? n - first : kMaxGroups;
@@ -1117,7 +1210,7 @@ hipError_t launch_product(const NsGroupRef *refs, const LaunchPart *parts, int n
         int64_t tiles = 0;
         for (int k = 0; k < cnt; ++k) {
             const LaunchPart &p = parts[first + k];
-            NsGroup s = product_group(MODE, refs[p.ref], iter, last, T, p.b0, p.split, p.nsplit);
+            NsGroup s = product_group(MODE, refs[p.ref], p, T);
             s.tiles = s.tiles_pm * p.nb;
             s.padded = (s.tiles + 7) / 8 * 8;
             s.round_tiles = round_tiles;
@@ -1134,23 +1227,21 @@ hipError_t launch_product(const NsGroupRef *refs, const LaunchPart *parts, int n
             hipLaunchKernelGGL((ns_bx_kernel<T>), dim3((uint32_t)grid), dim3(kThreadsOf<T>), 0, stream,
                                L);
         } else {
-            hipLaunchKernelGGL((ns_gemm_kernel<T, MODE>), dim3((uint32_t)tiles), dim3(kThreadsOf<T>),
-                               0, stream, L);
+            hipLaunchKernelGGL((ns_gemm_kernel<T, MODE, F16>), dim3((uint32_t)tiles),
+                               dim3(kThreadsOf<T>), 0, stream, L);
         }
     }
     return hipGetLastError();
 }
 
-// The groups whose tile size for the product is T, longest reduction first
+// The parts whose tile size for the product is T, longest reduction first
 // so that the short tiles fill the last rounds.
 template <int T, int MODE>
-int product_parts(const NsGroupRef *refs, int nrefs, LaunchPart *parts) {
+int product_parts(const NsGroupRef *refs, const LaunchPart *all, int nall, LaunchPart *parts) {
     int n = 0;
-    for (int i = 0; i < nrefs; ++i) {
-        const MuonGeom &g = *refs[i].geom;
-        if ((MODE == kGemmBX ? g.tile_bx : g.tile) != T) continue;
-        const int ns = MODE == kSyrkXXT ? g.ksplit : 1;
-        for (int k = 0; k < ns; ++k) parts[n++] = LaunchPart{i, 0, g.batch, k, ns};
+    for (int i = 0; i < nall; ++i) {
+        const MuonGeom &g = *refs[all[i].ref].geom;
+        if ((MODE == kGemmBX ? g.tile_bx : g.tile) == T) parts[n++] = all[i];
     }
     for (int i = 1; i < n; ++i)
         for (int j = i; j > 0; --j) {
@@ -1165,13 +1256,13 @@ int product_parts(const NsGroupRef *refs, int nrefs, LaunchPart *parts) {
     return n;
 }
 
-template <int MODE>
-hipError_t run_mode(const NsGroupRef *refs, int nrefs, int iter, bool last, float a, float b,
+template <int MODE, bool F16 = false>
+hipError_t run_mode(const NsGroupRef *refs, const LaunchPart *all, int nall, float a, float b,
                     float c, hipStream_t stream) {
     LaunchPart p256[2 * kMaxCallGroups], p128[2 * kMaxCallGroups + 1], p64[2 * kMaxCallGroups];
-    int n256 = product_parts<256, MODE>(refs, nrefs, p256);
-    int n128 = product_parts<128, MODE>(refs, nrefs, p128);
-    const int n64 = product_parts<64, MODE>(refs, nrefs, p64);
+    int n256 = product_parts<256, MODE>(refs, all, nall, p256);
+    int n128 = product_parts<128, MODE>(refs, all, nall, p128);
+    const int n64 = product_parts<64, MODE>(refs, all, nall, p64);
     if (MODE == kGemmBX && n256 > 0) {
         // The 256-tile launch's last round: when only a few tiles are left for
         // it, the last group's trailing matrices go to the 128-tile launch
@@ -1197,16 +1288,19 @@ hipError_t run_mode(const NsGroupRef *refs, int nrefs, int iter, bool last, floa
         const int64_t r128_after = (t128 + 4 * q * m + r128 - 1) / r128;
         if (rounds > 1 && rem * 4 <= r256 && m < lp.nb && r128_after - r128_before <= 1 &&
             n128 < 2 * kMaxCallGroups + 1) {
-            p128[n128++] = LaunchPart{lp.ref, lp.b0 + lp.nb - (int)m, (int)m};
+            LaunchPart mv = lp;
+            mv.b0 = lp.b0 + lp.nb - (int)m;
+            mv.nb = (int)m;
+            p128[n128++] = mv;
             lp.nb -= (int)m;
         }
     }
     hipError_t e = hipSuccess;
-    if (n256 > 0) e = launch_product<256, MODE>(refs, p256, n256, iter, last, a, b, c, stream);
+    if (n256 > 0) e = launch_product<256, MODE, F16>(refs, p256, n256, a, b, c, stream);
     if (e == hipSuccess && n128 > 0)
-        e = launch_product<128, MODE>(refs, p128, n128, iter, last, a, b, c, stream);
+        e = launch_product<128, MODE, F16>(refs, p128, n128, a, b, c, stream);
     if (e == hipSuccess && n64 > 0)
-        e = launch_product<64, MODE>(refs, p64, n64, iter, last, a, b, c, stream);
+        e = launch_product<64, MODE, F16>(refs, p64, n64, a, b, c, stream);
     return e;
 }
 
@@ -1223,7 +1317,7 @@ __global__ __launch_bounds__(256) void ns_xxt_fixup_kernel(const float *__restri
                                                            const float *__restrict__ xs,
                                                            uint16_t *__restrict__ A,
                                                            int64_t a_stride, float *__restrict__ dA,
-                                                           int64_t d_stride) {
+                                                           int64_t d_stride, int out_f16) {
     __shared__ uint16_t tt[64][64 + 2];
     const int nb = mp / 64;
     int t = blockIdx.x, bi = 0;
@@ -1246,7 +1340,7 @@ __global__ __launch_bounds__(256) void ns_xxt_fixup_kernel(const float *__restri
         for (int p = 1; p < nsplit; ++p) v += part[o + (int64_t)p * batch * part_stride];
         if (xs) v *= s2;
         if (gi < gj) {
-            const uint16_t h = cvt_bf16(v);
+            const uint16_t h = (uint16_t)pack_el(v, 0.0f, out_f16 != 0);
             Am[(int64_t)gi * mp + gj] = h;
             tt[c][r] = h;
         } else if (gi == gj) {
@@ -1264,21 +1358,111 @@ __global__ __launch_bounds__(256) void ns_xxt_fixup_kernel(const float *__restri
     }
 }
 
-hipError_t launch_xxt_fixups(const NsGroupRef *refs, int nrefs, int iter, hipStream_t stream) {
-    for (int i = 0; i < nrefs; ++i) {
-        const MuonGeom &g = *refs[i].geom;
-        if (g.ksplit < 2) continue;
-        const MuonWorkspace &L = *refs[i].layout;
-        char *ws = refs[i].base;
+hipError_t launch_xxt_fixups(const NsGroupRef *refs, const LaunchPart *all, int nall,
+                             hipStream_t stream) {
+    for (int i = 0; i < nall; ++i) {
+        const LaunchPart &p = all[i];
+        if (p.nsplit < 2 || p.split != 0) continue;
+        const MuonGeom &g = *refs[p.ref].geom;
+        const MuonWorkspace &L = *refs[p.ref].layout;
+        char *ws = refs[p.ref].base;
         const int nb = g.mp / 64;
-        const float *xs = iter == 0 ? muon_scale_ptr(ws, g, L) : nullptr;
+        const float *xs = p.seg == 0 ? muon_scale_ptr(ws, g, L) : nullptr;
         hipLaunchKernelGGL(ns_xxt_fixup_kernel, dim3(nb * (nb + 1) / 2, g.batch), dim3(256), 0,
                            stream, reinterpret_cast<const float *>(ws + L.part),
                            (int64_t)g.mp * g.mp, g.ksplit, g.mp, g.batch, xs,
-                           reinterpret_cast<uint16_t *>(ws + L.a), (int64_t)(L.a_stride / 2),
-                           reinterpret_cast<float *>(ws + L.da), (int64_t)(L.d_stride / 4));
+                           reinterpret_cast<uint16_t *>(ws + L.sm[p.out]), (int64_t)(L.a_stride / 2),
+                           reinterpret_cast<float *>(ws + L.sd[p.out]), (int64_t)(L.d_stride / 4),
+                           p.out_f16 ? 1 : 0);
     }
     return hipGetLastError();
+}
+
+// The program of ns_steps steps in segments (ns_segments).  A segment of
+// length L from X (= X_0 of the segment) [the Gram-matrix identities: with
+// A_j = X_j X_j^T and P_j = a I + b A_j + c A_j^2, X_{j+1} = P_j X_j, so
+// A_{j+1} = P_j A_j P_j = P_j^2 A_j (P_j is a polynomial in A_j) and
+// X_L = P_{L-1} ... P_0 X_0]:
+//   A_0 = X X^T
+//   for j < L:  P_j = a I + b A_j + c A_j^2
+//               Q_j = P_j Q_{j-1}            (Q_0 = P_0)
+//               S_j = P_j P_j,  A_{j+1} = S_j A_j     (j < L - 1)
+//   X' = Q_{L-1} X
+// Every matrix on the way is a polynomial in A_0, so every product is of two
+// commuting symmetric matrices and is itself symmetric.  With L = 1 this is
+// the plain iteration (X X^T, P, P X).  Slots go lowest free first; five
+// suffice for any L.  In a segment of L > 1 steps the chain A_0 ... Q_{L-1}
+// is held in fp16 (f16 set) except Q_{L-1}, which X' = Q X reads beside the
+// bf16 X; with f16 clear, or L = 1, everything is bf16.
+void build_program(bool gram, int ns_steps, bool f16, NsProgram &pr) {
+    MuonGeom g{};
+    g.gram = gram ? 1 : 0;
+    int len[100];
+    const int nseg = ns_segments(g, ns_steps, len);
+    pr.len = 0;
+    auto emit = [&](int kind, int seg, bool last) -> NsStep & {
+        NsStep &st = pr.step[pr.len++];
+        st = NsStep{};
+        st.kind = (int8_t)kind;
+        st.seg = (int16_t)seg;
+        st.last_seg = last ? 1 : 0;
+        return st;
+    };
+    bool h = false;  // this segment's chain in fp16
+    auto add = [&](NsStep &st, int in1, int in2, int out, bool out16 = true) {
+        st.in1[st.nprod] = (int8_t)in1;
+        st.in2[st.nprod] = (int8_t)in2;
+        st.out[st.nprod] = (int8_t)out;
+        st.f16in = (st.kind == kSyrkAA || st.kind == kSymLR) && h ? 1 : 0;
+        st.f16out[st.nprod] = st.kind != kGemmBX && h && out16 ? 1 : 0;
+        ++st.nprod;
+    };
+    for (int sg = 0; sg < nseg; ++sg) {
+        const bool last = sg + 1 == nseg;
+        const int L = len[sg];
+        h = f16 && L > 1;
+        bool busy[kNsSlots] = {};
+        auto alloc = [&]() {
+            int k = 0;
+            while (busy[k]) ++k;
+            busy[k] = true;
+            return k;
+        };
+        int A = alloc();
+        add(emit(kSyrkXXT, sg, last), A, A, A);
+        int Q = -1;
+        for (int j = 0; j < L; ++j) {
+            const int P = alloc();
+            add(emit(kSyrkAA, sg, last), A, A, P);
+            int S = -1, Qn = -1;
+            if (j > 0 || j + 1 < L) {
+                NsStep &st = emit(kSymLR, sg, last);
+                if (j > 0) {
+                    Qn = alloc();
+                    add(st, P, Q, Qn, j + 1 < L);  // Q_{L-1} in bf16
+                }
+                if (j + 1 < L) {
+                    S = alloc();
+                    add(st, P, P, S);
+                }
+            }
+            if (j > 0) {
+                busy[Q] = false;  // Q_{j-1} (P_0 for j = 1)
+                busy[P] = false;
+                Q = Qn;
+            } else {
+                Q = P;
+            }
+            if (j + 1 < L) {
+                const int An = alloc();
+                add(emit(kSymLR, sg, last), S, A, An);
+                busy[S] = false;
+                busy[A] = false;
+                A = An;
+            }
+        }
+        add(emit(kGemmBX, sg, last), Q, Q, Q);
+    }
 }
 
 }  // namespace
@@ -1295,20 +1479,159 @@ int ns_round_tiles(int tile) {
     }
 }
 
-hipError_t launch_ns_iteration(const NsGroupRef *refs, int nrefs, int iter, bool last, float a,
-                               float b, float c, hipStream_t stream) {
-    if (nrefs < 1 || nrefs > kMaxCallGroups) return hipErrorInvalidValue;
+int ns_segments(const MuonGeom &g, int ns_steps, int *len) {
+    if (ns_steps <= 0) return 0;
+    const int per = g.gram ? kNsMaxSegment : 1;
+    const int nseg = (ns_steps + per - 1) / per;
+    if (len != nullptr) {
+        const int base = ns_steps / nseg, extra = ns_steps % nseg;
+        for (int i = 0; i < nseg; ++i) len[i] = base + (i < extra ? 1 : 0);
+    }
+    return nseg;
+}
+
+// fp16's largest finite value is 65504.  Every m x m matrix of a segment is a
+// polynomial in its A_0 and symmetric, so no entry exceeds its largest
+// |eigenvalue|: the polynomial's value on A_0's spectrum.  The first
+// segment's X_0 has ||X_0||_F <= 1 (the pre-scale), so its singular values
+// lie in [0, 1]; a step maps a singular value s to s p(s^2), a segment to
+// s |q(s^2)| with q = p_{L-1} ... p_0 on the way.  The bound is the largest
+// |value| of A_j, P_j, S_j = P_j^2, Q_j over a grid of s in [0, 1.05] (5% for
+// rounding) carried through every segment; fp16 when twice it is below 2^14.
+// (The last call's answer is kept: the check is a few thousand steps of
+// scalar arithmetic per Newton-Schulz step.)
+bool ns_gram_f16_safe(int ns_steps, float a, float b, float c) {
+    static std::mutex mu;
+    static int k_steps = -1;
+    static float k_a = 0.0f, k_b = 0.0f, k_c = 0.0f;
+    static bool k_ok = false;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        if (k_steps == ns_steps && k_a == a && k_b == b && k_c == c) return k_ok;
+    }
+    MuonGeom g{};
+    g.gram = 1;
+    int len[100];
+    const int nseg = ns_segments(g, ns_steps, len);
+    const double A = a, B = b, C = c;
+    constexpr int kGrid = 2048;
+    double worst = 0.0;
+    for (int i = 0; i <= kGrid && std::isfinite(worst); ++i) {
+        double sig = 1.05 * i / kGrid;
+        for (int sg = 0; sg < nseg; ++sg) {
+            double lam = sig * sig, q = 1.0;
+            worst = std::max(worst, lam);
+            for (int j = 0; j < len[sg]; ++j) {
+                const double pv = A + B * lam + C * lam * lam;
+                q *= pv;
+                worst = std::max(worst, std::max(std::fabs(pv), std::fabs(q)));
+                if (j + 1 < len[sg]) {
+                    worst = std::max(worst, pv * pv);
+                    lam *= pv * pv;
+                    worst = std::max(worst, lam);
+                }
+            }
+            sig *= std::fabs(q);
+        }
+    }
+    const bool ok = std::isfinite(worst) && 2.0 * worst < 16384.0;
+    std::lock_guard<std::mutex> lock(mu);
+    k_steps = ns_steps;
+    k_a = a;
+    k_b = b;
+    k_c = c;
+    k_ok = ok;
+    return ok;
+}
+
+void ns_schedule(const NsGroupRef *refs, int nrefs, int ns_steps, bool f16, NsSchedule &s) {
+    s.used[0] = s.used[1] = 0;
+    for (int i = 0; i < nrefs; ++i) s.used[refs[i].geom->gram ? 1 : 0] = 1;
+    for (int p = 0; p < 2; ++p) {
+        s.prog[p].len = 0;
+        if (s.used[p] && ns_steps > 0) build_program(p == 1, ns_steps, f16, s.prog[p]);
+    }
+    const int n0 = s.prog[0].len, n1 = s.prog[1].len;
+    const NsStep *a = s.prog[0].step, *b = s.prog[1].step;
+    // longest common subsequence of the kinds of the two programs' suffixes
+    std::vector<int16_t> d((size_t)(n0 + 1) * (n1 + 1), 0);
+    auto D = [&](int i, int j) -> int16_t & { return d[(size_t)i * (n1 + 1) + j]; };
+    for (int i = n0 - 1; i >= 0; --i)
+        for (int j = n1 - 1; j >= 0; --j)
+            D(i, j) = a[i].kind == b[j].kind ? (int16_t)(D(i + 1, j + 1) + 1)
+                                              : std::max(D(i + 1, j), D(i, j + 1));
+    int i = 0, j = 0, t = 0;
+    while (i < n0 || j < n1) {
+        if (i < n0 && j < n1 && a[i].kind == b[j].kind) {
+            s.kind[t] = a[i].kind;
+            s.idx[0][t] = (int16_t)i++;
+            s.idx[1][t] = (int16_t)j++;
+        } else if (j == n1 || (i < n0 && D(i + 1, j) >= D(i, j + 1))) {
+            s.kind[t] = a[i].kind;
+            s.idx[0][t] = (int16_t)i++;
+            s.idx[1][t] = -1;
+        } else {
+            s.kind[t] = b[j].kind;
+            s.idx[0][t] = -1;
+            s.idx[1][t] = (int16_t)j++;
+        }
+        ++t;
+    }
+    s.nsteps = t;
+}
+
+hipError_t launch_ns_step(const NsGroupRef *refs, int nrefs, const NsSchedule &s, int t, float a,
+                          float b, float c, hipStream_t stream) {
+    if (nrefs < 1 || nrefs > kMaxCallGroups || t < 0 || t >= s.nsteps) return hipErrorInvalidValue;
+    LaunchPart all[2 * kMaxCallGroups];
+    int nall = 0;
+    const int kind = s.kind[t];
     for (int i = 0; i < nrefs; ++i) {
         const MuonGeom &g = *refs[i].geom;
-        for (const int t : {g.tile, g.tile_bx})
-            if ((t != 64 && t != 128 && t != 256) || g.mp % t != 0 || g.np % t != 0)
+        for (const int tl : {g.tile, g.tile_bx})
+            if ((tl != 64 && tl != 128 && tl != 256) || g.mp % tl != 0 || g.np % tl != 0)
                 return hipErrorInvalidValue;
+        const int p = g.gram ? 1 : 0;
+        const int k = s.idx[p][t];
+        if (k < 0) continue;
+        const NsStep &st = s.prog[p].step[k];
+        const int ns = kind == kSyrkXXT ? g.ksplit : 1;
+        for (int q = 0; q < st.nprod; ++q)
+            for (int sp = 0; sp < ns; ++sp) {
+                if (nall == 2 * kMaxCallGroups) return hipErrorInvalidValue;
+                LaunchPart lp{i, 0, g.batch, sp, ns};
+                lp.in1 = st.in1[q];
+                lp.in2 = st.in2[q];
+                lp.out = st.out[q];
+                lp.seg = st.seg;
+                lp.last = st.last_seg != 0;
+                lp.in_f16 = st.f16in != 0;
+                lp.out_f16 = st.f16out[q] != 0;
+                all[nall++] = lp;
+            }
     }
-    hipError_t e = run_mode<kSyrkXXT>(refs, nrefs, iter, last, a, b, c, stream);
-    if (e == hipSuccess) e = launch_xxt_fixups(refs, nrefs, iter, stream);
-    if (e == hipSuccess) e = run_mode<kSyrkAA>(refs, nrefs, iter, last, a, b, c, stream);
-    if (e == hipSuccess) e = run_mode<kGemmBX>(refs, nrefs, iter, last, a, b, c, stream);
-    return e;
+    switch (kind) {
+        case kSyrkXXT: {
+            const hipError_t e = run_mode<kSyrkXXT>(refs, all, nall, a, b, c, stream);
+            return e == hipSuccess ? launch_xxt_fixups(refs, all, nall, stream) : e;
+        }
+        case kSyrkAA:
+        case kSymLR: {
+            // one launch per operand type
+            LaunchPart by[2][2 * kMaxCallGroups];
+            int nby[2] = {0, 0};
+            for (int i = 0; i < nall; ++i) by[all[i].in_f16 ? 1 : 0][nby[all[i].in_f16 ? 1 : 0]++] = all[i];
+            hipError_t e = hipSuccess;
+            if (nby[0] > 0)
+                e = kind == kSyrkAA ? run_mode<kSyrkAA, false>(refs, by[0], nby[0], a, b, c, stream)
+                                    : run_mode<kSymLR, false>(refs, by[0], nby[0], a, b, c, stream);
+            if (e == hipSuccess && nby[1] > 0)
+                e = kind == kSyrkAA ? run_mode<kSyrkAA, true>(refs, by[1], nby[1], a, b, c, stream)
+                                    : run_mode<kSymLR, true>(refs, by[1], nby[1], a, b, c, stream);
+            return e;
+        }
+        default: return run_mode<kGemmBX>(refs, all, nall, a, b, c, stream);
+    }
 }
 
 }  // namespace zopt

@@ -6,9 +6,11 @@
 // stream without synchronising.  Nothing is enqueued unless every check
 // passes.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "zopt.h"
 #include "zopt_internal.h"
@@ -55,6 +57,11 @@ int64_t adamw_layout(int64_t n, int64_t bucket, int32_t world, int32_t rank,
 
 }  // namespace
 
+// The Newton-Schulz form (zopt_set_ns_form): 0 on the Gram matrix where the
+// shape favours it (its m x m chain in fp16 where the coefficients allow), 1
+// plain iterations throughout, 2 as 0 with the chain always in bf16.
+std::atomic<int> g_ns_form{0};
+
 MuonGeom muon_geometry(int32_t batch, int64_t rows, int64_t cols) {
     MuonGeom g{};
     g.batch = batch;
@@ -90,6 +97,11 @@ MuonGeom muon_geometry(int32_t batch, int64_t rows, int64_t cols) {
     const int64_t u256 = (g.mp + 255) / 256;
     g.ksplit = (g.np >= 8192 && (int64_t)batch * (u256 * (u256 + 1) / 2) < 256) ? 2 : 1;
     g.health_blocks = ns_health_blocks((int64_t)g.m * g.np);
+    // Newton-Schulz on the Gram matrix where the long side is at least twice
+    // the short one: a segment of L steps costs 3 m^2 n + (4 L - 3) m^3 flops
+    // against L (3 m^2 n + m^3) for plain iterations (five steps in segments
+    // of 3 and 2: 6 m^2 n + 14 m^3 against 15 m^2 n + 5 m^3)
+    g.gram = (g_ns_form.load(std::memory_order_relaxed) != 1 && (int64_t)g.n >= 2 * (int64_t)g.m) ? 1 : 0;
     return g;
 }
 
@@ -102,10 +114,15 @@ MuonWorkspace muon_workspace_layout(const MuonGeom &g) {
     L.x = off;   off += L.x_stride * g.batch;
     L.xt0 = off; off += L.x_stride * g.batch;
     L.xt1 = off; off += L.x_stride * g.batch;
-    L.a = off;   off += L.a_stride * g.batch;
-    L.b = off;   off += L.a_stride * g.batch;
-    L.da = off;  off += L.d_stride * g.batch;
-    L.db = off;  off += L.d_stride * g.batch;
+    L.nslots = g.gram ? kNsSlots : 2;
+    for (int k = 0; k < L.nslots; ++k) {
+        L.sm[k] = off;
+        off += L.a_stride * g.batch;
+    }
+    for (int k = 0; k < L.nslots; ++k) {
+        L.sd[k] = off;
+        off += L.d_stride * g.batch;
+    }
     L.part = off;
     if (g.ksplit > 1) off += round_up((size_t)g.ksplit * g.batch * g.mp * g.mp * 4, 256);
     L.partials = off;
@@ -313,6 +330,12 @@ ZOPT_EXPORT zopt_status zopt_set_ns_workgroup_limit(int32_t n) {
     return ZOPT_OK;
 }
 
+ZOPT_EXPORT zopt_status zopt_set_ns_form(int32_t form) {
+    if (form < 0 || form > 2) return ZOPT_ERR_HYPER;
+    g_ns_form.store(form, std::memory_order_relaxed);
+    return ZOPT_OK;
+}
+
 namespace {
 
 // The Newton-Schulz kernels address a panel of up to 256 rows of the padded
@@ -331,12 +354,12 @@ zopt_status muon_check_shape(int32_t batch, int64_t rows, int64_t cols) {
 
 // Where the Newton-Schulz result of a call lies, in the stored orientation:
 // X alternates between the x and xt0 regions (x after an even number of
-// iterations), and matrices stored transposed (rows > cols) find X^T in xt1,
-// which the last iteration (or, with no iterations, the pre-step) writes.
+// segments), and matrices stored transposed (rows > cols) find X^T in xt1,
+// which the last segment (or, with no iterations, the pre-step) writes.
 void muon_output(const MuonGeom &g, const MuonWorkspace &L, int32_t ns_steps, size_t &base,
                  int64_t &ld) {
     if (!g.transposed) {
-        base = (ns_steps % 2) ? L.xt0 : L.x;
+        base = (ns_segments(g, ns_steps) % 2) ? L.xt0 : L.x;
         ld = g.np;
     } else {
         base = L.xt1;
@@ -498,13 +521,15 @@ AuxStream *aux_stream(hipStream_t caller) {
 // The sides of a bin whose Newton-Schulz launches run on two streams: side[k]
 // is 0 (the caller's stream) or 1 (the second); the groups in order of
 // Newton-Schulz work, each to the side with less so far.
-void split_sides(const NsGroupRef *refs, int nb, int *side) {
+void split_sides(const NsGroupRef *refs, int nb, int ns_steps, int *side) {
     double work[kMaxCallGroups];
     int order[kMaxCallGroups];
     for (int k = 0; k < nb; ++k) {
         const MuonGeom &g = *refs[k].geom;
         const double m = g.m, n = g.n;
-        work[k] = g.batch * (3.0 * m * m * n + m * m * m);
+        const int nseg = ns_segments(g, ns_steps);
+        // 3 m^2 n + (4 L - 3) m^3 per segment of L steps
+        work[k] = g.batch * (nseg * 3.0 * m * m * n + (4.0 * ns_steps - 3.0 * nseg) * m * m * m);
         order[k] = k;
     }
     std::stable_sort(order, order + nb, [&](int x, int y) { return work[x] > work[y]; });
@@ -542,7 +567,7 @@ hipError_t muon_enqueue(const MuonCallPlan &c, char *ws, float lr, float mu, int
             lock.lock();
             aux = aux_stream(s);
             if (aux != nullptr)
-                split_sides(brefs, nb, side);
+                split_sides(brefs, nb, ns_steps, side);
             else
                 lock.unlock();
         }
@@ -566,19 +591,25 @@ hipError_t muon_enqueue(const MuonCallPlan &c, char *ws, float lr, float mu, int
             e = launch_muon_pre(c.plans[i].g, c.ptrs[i], mu, nesterov, ns_eps,
                                 ws + c.plans[i].base, c.plans[i].L, ns_steps == 0, dev, on(k));
         }
-        if (aux != nullptr) {
+        if (ns_steps > 0 && e == hipSuccess) {
+            // each side's groups in one merged sequence of launches, the two
+            // sides' launches enqueued in turn
             NsGroupRef r[2][kMaxCallGroups];
             int n[2] = {0, 0};
-            for (int k = 0; k < nb; ++k) r[side[k]][n[side[k]]++] = brefs[k];
-            for (int it = 0; it < ns_steps && e == hipSuccess; ++it) {
-                e = launch_ns_iteration(r[0], n[0], it, it + 1 == ns_steps, ns_a, ns_b, ns_c, s);
-                if (e == hipSuccess)
-                    e = launch_ns_iteration(r[1], n[1], it, it + 1 == ns_steps, ns_a, ns_b, ns_c,
-                                            aux->s);
+            for (int k = 0; k < nb; ++k) {
+                const int d = aux != nullptr ? side[k] : 0;
+                r[d][n[d]++] = brefs[k];
             }
-        } else {
-            for (int it = 0; it < ns_steps && e == hipSuccess; ++it)
-                e = launch_ns_iteration(brefs, nb, it, it + 1 == ns_steps, ns_a, ns_b, ns_c, s);
+            const bool f16 = g_ns_form.load(std::memory_order_relaxed) == 0 &&
+                             ns_gram_f16_safe(ns_steps, ns_a, ns_b, ns_c);
+            std::vector<NsSchedule> sch(2);
+            for (int d = 0; d < 2; ++d)
+                if (n[d] > 0) ns_schedule(r[d], n[d], ns_steps, f16, sch[d]);
+            const int steps = std::max(n[0] > 0 ? sch[0].nsteps : 0, n[1] > 0 ? sch[1].nsteps : 0);
+            for (int t = 0; t < steps && e == hipSuccess; ++t)
+                for (int d = 0; d < 2 && e == hipSuccess; ++d)
+                    if (n[d] > 0 && t < sch[d].nsteps)
+                        e = launch_ns_step(r[d], n[d], sch[d], t, ns_a, ns_b, ns_c, d ? aux->s : s);
         }
         if (health) {
             join();

@@ -108,6 +108,8 @@ struct MuonGeom {
     int32_t norm_blocks; // norm partials per matrix (room for either form of pass 1)
     int32_t ksplit;      // X X^T reduction split in this many parts (1: none)
     int32_t health_blocks;  // workgroups (and partials) per matrix of the health pass
+    int32_t gram;        // 1: Newton-Schulz in segments of up to kNsMaxSegment steps on the
+                         // Gram matrix (n >= 2 m); 0: plain iterations
 };
 
 struct MuonPtrs {
@@ -117,11 +119,21 @@ struct MuonPtrs {
     uint16_t *weight[kMaxBatch];
 };
 
+// Symmetric mp x mp matrices a group's Newton-Schulz keeps at once: A = X X^T
+// and P = a I + b A + c A A for plain iterations; up to five for a segment on
+// the Gram matrix (A, P, Q and the products on the way to the next A).
+constexpr int kNsSlots = 5;
+constexpr int kNsMaxSegment = 3;
+
 // Workspace carve-up (byte offsets; every region 256-byte aligned).  x and
-// xt0 hold X (mp x np) in turn, one per Newton-Schulz iteration; xt1 holds
-// the result transposed (np x mp) for matrices stored transposed.
+// xt0 hold X (mp x np) in turn, one per Newton-Schulz segment; xt1 holds the
+// result transposed (np x mp) for matrices stored transposed.  Slot k of the
+// symmetric pool is sm[k] (bf16 off-diagonal part, diagonal 0) with its fp32
+// diagonal at sd[k]; a group has nslots of them.
 struct MuonWorkspace {
-    size_t x, xt0, xt1, a, b, da, db, partials;
+    size_t x, xt0, xt1, partials;
+    size_t sm[kNsSlots], sd[kNsSlots];
+    int32_t nslots;
     size_t part;       // X X^T split: ksplit fp32 mp x mp partial products per matrix
     size_t hsum, hmax, hflag;  // health pass: fp64 / fp32 partials, per-matrix reject flags
     size_t total;
@@ -193,14 +205,58 @@ hipError_t launch_ns_health(const NsGroupRef *refs, const int *mat_first, int nr
 // (0 if none), from the nmat triples at health + 2.
 hipError_t launch_ns_health_total(float *health, int32_t nmat, hipStream_t stream);
 
-// Iteration `iter` (0-based) of Newton-Schulz for every group of a call:
-// A = X X^T, B = b A + c A A, X' = a X + B X, with X in the workspace's x
-// region at even iterations and in xt0 at odd ones (X' goes to the other);
-// the last iteration also writes X'^T to xt1 for groups stored transposed.
-// Three launches per tile size in use (more if over kMaxGroups groups share
-// a tile size).
-hipError_t launch_ns_iteration(const NsGroupRef *refs, int nrefs, int iter, bool last, float a,
-                               float b, float c, hipStream_t stream);
+// The segments of a group's ns_steps Newton-Schulz steps: steps of one each
+// for plain iterations; on the Gram matrix, ceil(ns_steps / kNsMaxSegment)
+// segments as even as possible, longer ones first (5 -> 3, 2).  Writes the
+// lengths to len (if not NULL; room for ns_steps) and returns the count.  X
+// lies in the workspace's x region before even segments and in xt0 before odd
+// ones; the result is where the count's parity puts it.
+int ns_segments(const MuonGeom &g, int ns_steps, int *len = nullptr);
+
+// One step of a group's Newton-Schulz program: one kind of product, once or
+// twice, on slots of the group's symmetric pool.
+//   kind 0  X X^T        -> out                        (a segment's first step)
+//   kind 1  a I + b A + c A A of A = in1 -> out        (P)
+//   kind 2  X' = P X, P = in1                          (a segment's last step)
+//   kind 3  L R of two commuting symmetric matrices in1, in2 -> out
+struct NsStep {
+    int8_t kind, nprod;
+    int8_t in1[2], in2[2], out[2];
+    int8_t f16in;      // the symmetric products' operands are fp16 (else bf16)
+    int8_t f16out[2];  // each product's output is fp16
+    int16_t seg;      // segment of the step
+    int8_t last_seg;  // 1: the segment is the last
+};
+constexpr int kNsMaxProgram = 4 * 100;
+constexpr int kNsMaxMerged = 2 * kNsMaxProgram;
+struct NsProgram {
+    int len;
+    NsStep step[kNsMaxProgram];
+};
+// The launches of a set of groups: their programs (0: plain, 1: Gram), merged
+// into one sequence of steps in which each launch computes the same kind of
+// product for every group whose program has that step next (the shortest
+// common supersequence of the two programs' kinds).  idx[p][t] is program p's
+// step in merged step t, or -1.
+struct NsSchedule {
+    NsProgram prog[2];
+    int used[2];  // whether any group runs program p
+    int nsteps;
+    int16_t idx[2][kNsMaxMerged];
+    int8_t kind[kNsMaxMerged];
+};
+// f16: segments of more than one step hold their m x m chain in fp16
+// (ns_gram_f16_safe), else in bf16.
+void ns_schedule(const NsGroupRef *refs, int nrefs, int ns_steps, bool f16, NsSchedule &s);
+
+// Whether fp16 holds every m x m matrix of the Gram segments of ns_steps steps
+// with coefficients (a, b, c) with room to spare (see the definition).
+bool ns_gram_f16_safe(int ns_steps, float a, float b, float c);
+
+// Merged step t of a schedule for every group: one launch per tile size in
+// use (more if over kMaxGroups products share a tile size).
+hipError_t launch_ns_step(const NsGroupRef *refs, int nrefs, const NsSchedule &s, int t, float a,
+                          float b, float c, hipStream_t stream);
 
 // Workgroups of the Newton-Schulz kernel with the given tile size that the
 // current device holds at once (one round of tiles).

@@ -68,3 +68,61 @@ def newton_schulz_bf16_model(u, steps=5, coeffs=oracle.NS_COEFFS, eps=oracle.NS_
             xn = _f32(xn * s, round_bf16)
         x = _bf(xn, round_bf16)
     return np.ascontiguousarray(x.T if tr else x)
+
+
+def gram_segments(steps, per=3):
+    """Segment lengths of `steps` Newton-Schulz steps on the Gram matrix:
+    ceil(steps / per) segments as even as possible, longer ones first."""
+    if steps <= 0:
+        return []
+    nseg = (steps + per - 1) // per
+    base, extra = divmod(steps, nseg)
+    return [base + (1 if i < extra else 0) for i in range(nseg)]
+
+
+def _f16(x):
+    return np.asarray(x, np.float32).astype(np.float16).astype(np.float64)
+
+
+def newton_schulz_gram_model(u, steps=5, coeffs=oracle.NS_COEFFS, eps=oracle.NS_EPS,
+                             chain="f16"):
+    """The same steps in segments on the m x m Gram matrix, as the kernels
+    run them for matrices whose long side is at least twice the short one.
+    Per segment of L steps from X: A = X X^T, then for j < L: P_j = a I +
+    b A_j + c A_j^2, Q_j = P_j Q_{j-1} (Q_0 = P_0), A_{j+1} = (P_j P_j) A_j;
+    X' = Q_{L-1} X.  Each m x m matrix is stored with its off-diagonal part
+    rounded to `chain` ("f16" or "bf16"; "bf16" for every matrix of a segment
+    of one step) and its diagonal in fp32, the upper triangle mirrored;
+    Q_{L-1} is rounded to bf16 for the product with the bf16 X, which is
+    rounded to bf16 after it.  The pre-scale is applied as in
+    newton_schulz_bf16_model (X0 = bf16(U s) here, outside the kernels' fold
+    range as well).  chain=None: no rounding anywhere, the float64 Gram
+    identities themselves (checked against the oracle in the CPU tests)."""
+    a, b, c = coeffs
+    on = chain is not None
+    x = np.asarray(u, np.float64)
+    tr = x.shape[0] > x.shape[1]
+    if tr:
+        x = x.T
+    s = 1.0 / (np.sqrt(float(np.sum(x * x))) + eps)
+    x = _bf(_f32(x * s, on), on)
+
+    def store(mat, rnd):
+        mat = np.triu(mat) + np.triu(mat, 1).T
+        if not on:
+            return mat
+        d = np.diag(mat).copy()
+        return rnd(mat - np.diag(d)) + np.diag(_f32(d, True))
+
+    bf = lambda v: _bf(v, True)  # noqa: E731
+    for L in gram_segments(steps):
+        rnd = _f16 if (chain == "f16" and L > 1) else bf
+        A = store(_f32(x @ x.T, on), rnd)
+        Q = None
+        for j in range(L):
+            P = store(a * np.eye(len(A)) + b * A + c * _f32(A @ A, on), rnd)
+            Q = P if Q is None else store(_f32(P @ Q, on), rnd)
+            if j + 1 < L:
+                A = store(_f32(store(_f32(P @ P, on), rnd) @ A, on), rnd)
+        x = _bf(_f32(store(Q, bf) @ x, on), on)
+    return np.ascontiguousarray(x.T if tr else x)

@@ -53,6 +53,15 @@ def test_ns_workgroup_limit_checks():
     assert L.zopt_set_ns_workgroup_limit(0) == z.ZOPT_OK
 
 
+def test_ns_form_checks():
+    L = z.lib()
+    assert L.zopt_set_ns_form(3) == z.ZOPT_ERR_HYPER
+    assert L.zopt_set_ns_form(-1) == z.ZOPT_ERR_HYPER
+    assert L.zopt_set_ns_form(z.NS_FORM_PLAIN) == z.ZOPT_OK
+    assert L.zopt_set_ns_form(z.NS_FORM_GRAM_BF16) == z.ZOPT_OK
+    assert L.zopt_set_ns_form(z.NS_FORM_AUTO) == z.ZOPT_OK
+
+
 def adamw(**kw):
     a = dict(master=FAKE, exp_avg=FAKE, exp_avg_sq=FAKE, grad=FAKE, weight=None, N=16,
              bucket=8, world=2, rank=0, shard_len=8, lr=1e-3, beta1=0.9, beta2=0.95,

@@ -140,6 +140,64 @@ def test_ns_coefficient_sets(coeffs, steps):
     check_step(1, 1100, 1300, seed=13, ns_steps=steps, coeffs=coeffs)
 
 
+@pytest.fixture
+def ns_form():
+    yield z.set_ns_form
+    z.set_ns_form(z.NS_FORM_AUTO)
+
+
+# Shapes whose long side is at least twice the short one: Newton-Schulz runs
+# in segments on the Gram matrix by default.  Both orientations, ragged sizes,
+# 64-, 128- and 256-tile symmetric products.
+GRAM_SHAPES = [(2, 96, 200), (1, 330, 100), (2, 200, 700), (1, 900, 300), (1, 1100, 2300)]
+
+
+@pytest.mark.parametrize("ns_steps", [1, 2, 3, 4, 5, 7])
+def test_gram_form_matches_oracle_and_plain_form(ns_form, ns_steps):
+    """Each form -- the default (fp16 chain), plain iterations and the Gram
+    form with a bf16 chain -- within NS_TOL of the float64 oracle, momentum and
+    post-step bit for bit (check_step); the default and the plain results
+    within NS_TOL of each other."""
+    forms = (z.NS_FORM_AUTO, z.NS_FORM_PLAIN, z.NS_FORM_GRAM_BF16)
+    for (b, r, c) in GRAM_SHAPES:
+        outs = {}
+        for form in forms:
+            ns_form(form)
+            worst, ws = check_step(b, r, c, seed=r + c + ns_steps, ns_steps=ns_steps)
+            outs[form] = oracle.bf16_bits_to_f32(
+                u16(z.muon_output_view(ws, b, r, c, ns_steps, 0))).astype(np.float64)
+            print(f"{b}x[{r}, {c}] ns_steps={ns_steps} form {form}: worst NS rel err {worst:.3e}",
+                  flush=True)
+        assert rel_fro(outs[z.NS_FORM_AUTO], outs[z.NS_FORM_PLAIN]) <= NS_TOL
+
+
+@pytest.mark.parametrize("coeffs,steps", [
+    ((1.5, -0.5, 0.0), 8),
+    ((2.0, -1.5, 0.5), 5),
+    ((3.4445, -4.7750, 2.0315), 3),
+])
+def test_gram_form_coefficient_sets(coeffs, steps):
+    check_step(2, 150, 420, seed=21, ns_steps=steps, coeffs=coeffs)
+    check_step(1, 1300, 520, seed=22, ns_steps=steps, coeffs=coeffs)
+
+
+def test_gram_form_large_coefficients_take_a_bf16_chain():
+    """Coefficients whose m x m chain could leave fp16's range (p(0)^3 = 21^3
+    > 2^13 in a segment of three steps) run the Gram form with its chain in
+    bf16.  The input has four equal singular values, 1/2 after the
+    pre-scale, where p(1/4) = 1 and the map's slope is 0, so every step keeps
+    X and rounding does not grow."""
+    rows, cols = 4, 320
+    rng = np.random.default_rng(31)
+    q, _ = np.linalg.qr(rng.standard_normal((cols, rows)))
+    G = [wl.to_bf16_bits((q.T * 1e-3).astype(np.float32))]
+    P = [(rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)]
+    M = [np.zeros((rows, cols), np.float32)]
+    worst, _ = check_step(1, rows, cols, 32, ns_steps=3, coeffs=(21.0, -158.0, 312.0), P=P, M=M,
+                          G=G)
+    print(f"coefficients (21, -158, 312), 3 steps: NS rel err {worst:.3e}", flush=True)
+
+
 @pytest.mark.parametrize("nesterov,adjust", [(False, 1), (True, 0), (False, 0)])
 def test_momentum_and_scale_variants(nesterov, adjust):
     check_step(2, 192, 320, seed=5, nesterov=nesterov, adjust=adjust)
