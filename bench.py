@@ -96,6 +96,8 @@ def parse():
                          "zopt_round_bf16 pass of known size: the calibration for HBM byte "
                          "counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-plain-form", action="store_true",
+                    help="skip the plain-form Newton-Schulz A/B timings (for profiles)")
     return ap.parse_args()
 
 
@@ -127,9 +129,14 @@ def group_flops(groups, steps, form=0):
                                      form) for g in groups)
 
 
+PLAIN_FORM_AB = [True]
+
+
 def timed_forms(z, timer, fn, K):
     """fn timed K times in the plain form (A/B against the default, on the
-    same buffers); the default form restored after."""
+    same buffers); the default form restored after.  NaN when skipped."""
+    if not PLAIN_FORM_AB[0]:
+        return float("nan")
     z.set_ns_form(z.NS_FORM_PLAIN)
     try:
         fn(0)
@@ -268,8 +275,9 @@ def bench_step(torch, z, timer, dev, K, W):
     t5p = timed_forms(z, timer, lambda _: muon_call(z, wm, groups, workspace, 5), K)
     per_group = dict(muon_call_ms=round(t5, 4), zero_step_call_ms=round(t0, 4),
                      ns_ms=round(ns_ms, 4),
-                     plain_form=dict(muon_call_ms=round(t5p, 4), ns_ms=round(t5p - t0, 4),
-                                     algorithmic_flops=group_flops(groups, 5, form=1)),
+                     plain_form=None if t5p != t5p else dict(
+                         muon_call_ms=round(t5p, 4), ns_ms=round(t5p - t0, 4),
+                         algorithmic_flops=group_flops(groups, 5, form=1)),
                      groups=[dict(shape=[g["rows"], g["cols"]], count=g["count"]) for g in groups],
                      ns_health=ns_health_check(torch, z, timer, wm, groups, workspace, K, t5))
     adamw_bytes = 28 * n
@@ -373,8 +381,9 @@ def bench_ns(torch, z, timer, dev, K, W, w=None):
     # call with steps writes bf16(U): the same bytes but for that transpose)
     ns_ms, call_ms = t5 - t0, t5
     t5p = timed_forms(z, timer, lambda _: muon_call(z, w, groups, workspace, w.ns_steps), K)
-    plain = dict(muon_ms_per_step=round(t5p, 3), ns_ms_per_step=round(t5p - t0, 3),
-                 algorithmic_flops_per_step=group_flops(groups, w.ns_steps, form=1))
+    plain = None if t5p != t5p else dict(
+        muon_ms_per_step=round(t5p, 3), ns_ms_per_step=round(t5p - t0, 3),
+        algorithmic_flops_per_step=group_flops(groups, w.ns_steps, form=1))
     rows = [dict(shape=[g["rows"], g["cols"]], count=g["count"]) for g in groups]
     health = ns_health_check(torch, z, timer, w, groups, workspace, K, t5)
     del groups, workspace
@@ -766,6 +775,7 @@ def cpu_baseline():
 
 def main():
     args = parse()
+    PLAIN_FORM_AB[0] = not args.no_plain_form
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one rank's optimizer step on one GPU; runs on more than "

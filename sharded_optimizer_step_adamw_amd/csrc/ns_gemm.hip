@@ -100,6 +100,9 @@ struct NsLaunch {
     float a, b, c;
 };
 
+// an LDS pointer in the LDS address space (for the direct-to-LDS loads)
+#define LDS_ADDR(p) ((__attribute__((address_space(3))) void *)(p))
+
 // lo, hi -> two bf16, round to nearest even, in one gfx950 instruction
 // (v_cvt_pk_bf16_f32).  Equal to rne_bf16_bits for every non-NaN input; a NaN
 // stays a NaN.  Used for the Newton-Schulz operands (X, A, B), which never
@@ -264,19 +267,25 @@ __device__ __forceinline__ void epilogue(const NsGroup &args, float ca, float cb
     };
     constexpr int TCHUNKS = SC * TCH;   // 16-byte chunks of the transposed image
 
-    // 1. A A: stage the input sub-block (row order) and complete the accumulators
+    // 1. A A and L R: stage the input sub-block (Aoff / Loff, row order) and
+    // complete the accumulators
+    constexpr bool kIn = MODE == kSyrkAA || MODE == kSymLR;
     float da_c[FN], da_r[FM][4];
-    if (MODE == kSyrkAA && !below) {
-        const uint16_t *E = args.E + batch * args.c_stride;
-        // (all of the wave's loads in flight at once: the accumulators are the
-        // only other live registers here; on 256 tiles the main loop's last
-        // stages have put the sub-block there already)
+    // the wave's sub-block of a tile-shaped 16-bit matrix (base at this
+    // matrix's element (0, 0)) into its region W, row order, chunk c of row i
+    // at slot c ^ (i % RCH), with plain loads and LDS stores
+    auto stage = [&](const uint16_t *src) __attribute__((always_inline)) {
 #pragma unroll
-        for (int k = 0; k < (BM == 256 ? 0 : SR * RCH / 64); ++k) {
+        for (int k = 0; k < SR * RCH / 64; ++k) {
             const int id = k * 64 + lane, i = id / RCH, c = id % RCH;
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(E + (int64_t)(R0 + i) * ldc + C0 + c * 8);
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(src + (int64_t)(R0 + i) * ldc + C0 + c * 8);
             *reinterpret_cast<u32x4 *>(W + i * (RCH * 16) + ((c ^ (i & (RCH - 1))) << 4)) = v;
         }
+    };
+    if (kIn && !below) {
+        // (on 256 tiles the main loop's last stages have put the sub-block
+        // there already)
+        if (BM != 256) stage(args.E + batch * args.c_stride);
 #pragma unroll
         for (int j = 0; j < FN; ++j) da_c[j] = dIn[C0 + j * 16 + col];
 #pragma unroll
@@ -285,9 +294,10 @@ __device__ __forceinline__ void epilogue(const NsGroup &args, float ca, float cb
             for (int r = 0; r < 4; ++r) da_r[i][r] = dIn[R0 + i * 16 + quad * 4 + r];
     }
     __syncthreads();
-    if (MODE == kSyrkAA && !below) {
-        // the input at the accumulators' positions: one transposing read per
-        // 16 x 16 block gives each lane its 4 rows of one column
+    // the staged input at the accumulators' positions: one transposing read
+    // per 16 x 16 block gives each lane its 4 rows of one column; f(i, j, in4)
+    // completes block (i, j)
+    auto each_block = [&](auto f) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
             u32x2 e[FN];
@@ -300,73 +310,69 @@ __device__ __forceinline__ void epilogue(const NsGroup &args, float ca, float cb
             for (int j = 1; j < FN; ++j) asm volatile("" : "+v"(e[j]));
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-                const int gj = C0 + j * 16 + col;
                 const float in4[4] = {from_el<F16>(e[j].x & 0xFFFFu), from_el<F16>(e[j].x >> 16),
                                       from_el<F16>(e[j].y & 0xFFFFu), from_el<F16>(e[j].y >> 16)};
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int gi = R0 + i * 16 + quad * 4 + r;
-                    const float in = in4[r], v = acc[i][j][r], da_i = da_r[i][r];
-                    float x = cb * in + cc * (v + (da_i + da_c[j]) * in);
-                    if (gi == gj) x = ca + (cb * da_i + cc * (v + da_i * da_i));
-                    acc[i][j][r] = x;
-                }
+                f(i, j, in4);
             }
         }
+    };
+    if (MODE == kSyrkAA && !below) {
+        // b Aoff + c (acc + (dA_i + dA_j) Aoff), diagonal a + b dA_i + c (acc + dA_i^2)
+        each_block([&](int i, int j, const float(&in4)[4]) __attribute__((always_inline)) {
+            const int gj = C0 + j * 16 + col;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int gi = R0 + i * 16 + quad * 4 + r;
+                const float in = in4[r], v = acc[i][j][r], da_i = da_r[i][r];
+                float x = cb * in + cc * (v + (da_i + da_c[j]) * in);
+                if (gi == gj) x = ca + (cb * da_i + cc * (v + da_i * da_i));
+                acc[i][j][r] = x;
+            }
+        });
     }
     if (MODE == kSymLR && !below) {
-        // C = L R of two symmetric matrices held as off-diagonal parts and
-        // diagonals: the accumulators hold Loff Roff; add dL_i Roff_ij +
-        // Loff_ij dR_j (both off-diagonal parts are 0 on the diagonal, where
-        // dL_i dR_i is added instead).  By symmetry Loff_ij = Loff_ji, so the
-        // lane's four rows of column j are four consecutive entries of row j:
-        // one 8-byte load per 16 x 16 block and operand, in NH rounds of the
-        // row blocks to bound the registers in flight.
-        const uint16_t *Lm = args.P + batch * args.p_stride;
+        // L R of two symmetric matrices held as off-diagonal parts and
+        // diagonals (acc = Loff Roff): acc + dL_i Roff_ij + Loff_ij dR_j,
+        // diagonal acc + dL_i dR_i (both off-diagonal parts are 0 there).
+        // Two passes over the wave's region: Loff (staged above) with dR_j
+        // and the diagonal; then Roff, loaded into the same region by this
+        // wave alone, with dL_i.
         const uint16_t *Rm = args.Q + batch * args.q_stride;
-        const float *dL = args.dIn + batch * args.d_stride;
         const float *dR = args.dIn2 + batch * args.d_stride;
-        const int64_t ld = args.ld;
-        float dr[FN];
 #pragma unroll
-        for (int j = 0; j < FN; ++j) dr[j] = dR[C0 + j * 16 + col];
-        constexpr int NH = FM >= 8 ? 4 : 2, FH = FM / NH;
-        static_assert(FM % NH == 0, "rounds of the row blocks");
+        for (int j = 0; j < FN; ++j) da_c[j] = dR[C0 + j * 16 + col];
+        each_block([&](int i, int j, const float(&in4)[4]) __attribute__((always_inline)) {
+            const int gj = C0 + j * 16 + col;
 #pragma unroll
-        for (int h = 0; h < NH; ++h) {
-            u32x2 lv[FH][FN], rv[FH][FN];
-            f32x4 dl[FH];
-#pragma unroll
-            for (int ii = 0; ii < FH; ++ii) {
-                const int r0 = R0 + (h * FH + ii) * 16 + quad * 4;
-                dl[ii] = *reinterpret_cast<const f32x4 *>(dL + r0);
-#pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const int64_t o = (int64_t)(C0 + j * 16 + col) * ld + r0;
-                    lv[ii][j] = *reinterpret_cast<const u32x2 *>(Lm + o);
-                    rv[ii][j] = *reinterpret_cast<const u32x2 *>(Rm + o);
-                }
+            for (int r = 0; r < 4; ++r) {
+                const int gi = R0 + i * 16 + quad * 4 + r;
+                const float v = acc[i][j][r];
+                acc[i][j][r] = gi == gj ? v + da_r[i][r] * da_c[j] : v + in4[r] * da_c[j];
             }
+        });
+        if constexpr (BM == 256) {
+            // direct to LDS: kilobyte k of the region is its rows 8k ..
+            // 8k+7; lane l takes row l / 8 and the chunk the swizzle puts
+            // at slot l % 8 (the layout of the main loop's prefetch)
+            const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(Rm + (int64_t)R0 * ldc + C0), (short)0, SR * (int)ldc * 2, 0x00020000);
+            const int rvoff = ((lane >> 3) * (int)ldc + (((lane & 7) ^ (lane >> 3)) << 3)) * 2;
 #pragma unroll
-            for (int ii = 0; ii < FH; ++ii) {
-                const int i = h * FH + ii;
-#pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const int gj = C0 + j * 16 + col;
-                    const float lo4[4] = {from_el<F16>(lv[ii][j].x & 0xFFFFu), from_el<F16>(lv[ii][j].x >> 16),
-                                          from_el<F16>(lv[ii][j].y & 0xFFFFu), from_el<F16>(lv[ii][j].y >> 16)};
-                    const float ro4[4] = {from_el<F16>(rv[ii][j].x & 0xFFFFu), from_el<F16>(rv[ii][j].x >> 16),
-                                          from_el<F16>(rv[ii][j].y & 0xFFFFu), from_el<F16>(rv[ii][j].y >> 16)};
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int gi = R0 + i * 16 + quad * 4 + r;
-                        const float v = acc[i][j][r];
-                        acc[i][j][r] = gi == gj ? v + dl[ii][r] * dr[j]
-                                                : v + dl[ii][r] * ro4[r] + lo4[r] * dr[j];
-                    }
-                }
-            }
+            for (int k = 0; k < SR / 8; ++k)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, LDS_ADDR(W + k * 1024), 16, rvoff,
+                                                         8 * k * (int)ldc * 2, 0, 0);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        } else {
+            stage(Rm);
         }
+        each_block([&](int i, int j, const float(&in4)[4]) __attribute__((always_inline)) {
+            const int gj = C0 + j * 16 + col;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int gi = R0 + i * 16 + quad * 4 + r;
+                if (gi != gj) acc[i][j][r] += da_r[i][r] * in4[r];
+            }
+        });
     }
     __syncthreads();
 
@@ -480,7 +486,6 @@ __device__ __forceinline__ bool round_tile(const NsGroup &G, int rel, int &t) {
 // (whose fragments were read in the previous iteration).
 constexpr int kStages = 4;
 constexpr int kBK = 32;
-#define LDS_ADDR(p) ((__attribute__((address_space(3))) void *)(p))
 // s_waitcnt: vmcnt <= n and lgkmcnt = 0 (gfx9 field layout: vmcnt[3:0],
 // expcnt[6:4], lgkmcnt[11:8], vmcnt high bits[15:14])
 #define WAIT_VM_LGKM0(n) ((((n) & 15) | (((n) >> 4) << 14) | (7 << 4)))
@@ -532,15 +537,15 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch 
     // and the chunk that the swizzle places at slot l % 4
     const int lrow = lane >> 2, lchunk = (lane & 3) ^ ((lrow >> 1) & 3);
     const int voff = (lrow * ld + lchunk * 8) * 2;
-    // A A on 256 tiles: the stages past the end of K (the last four
+    // A A and L R on 256 tiles: the stages past the end of K (the last four
     // iterations' loads, into the four buffers as they free up) fetch the
-    // input tile Aoff[m0.., n0..] that the epilogue needs, straight into the
+    // input tile Aoff[m0.., n0..] (L R: Loff) that the epilogue needs, straight into the
     // per-wave regions it reads it from (wave w's 128 x 64 sub-block, rows of
     // 128 bytes, chunk c of row i at slot c ^ (i % 8), at w x 16 KiB: the
     // buffer of stage s holds the regions of waves 2s and 2s + 1).  Kilobyte k
     // of a region is its rows 8k .. 8k+7; lane l takes row l / 8 of it and the
     // chunk the swizzle puts at slot l % 8.
-    constexpr bool kEpre = MODE == kSyrkAA && BM == 256;
+    constexpr bool kEpre = (MODE == kSyrkAA || MODE == kSymLR) && BM == 256;
     static_assert(!kEpre || (NSTG == 4 && NSTG * STAGE == BM * BM * 2), "four buffers hold the input tile");
     const uint16_t *Eb = kEpre ? G.E + batch * G.c_stride + (int64_t)m0 * G.ldc + n0 : nullptr;
     const int evoff = ((lane >> 3) * G.ldc + (((lane & 7) ^ (lane >> 3)) << 3)) * 2;
@@ -1135,7 +1140,7 @@ NsGroup product_group(int mode, const NsGroupRef &r, const LaunchPart &p, int ti
         s.p_stride = as; s.q_stride = as; s.ld = g.mp; s.K = g.mp;
         s.tiles_n = tm; s.tiles_pm = tm * (tm + 1) / 2;
         s.C = sm(p.out); s.c_stride = as; s.ldc = g.mp;
-        if (mode == kSyrkAA) s.E = sm(p.in1);
+        s.E = sm(p.in1);  // A A: Aoff; L R: Loff (the epilogue's staged input)
         s.dIn = sd(p.in1); s.dOut = sd(p.out);
         if (mode == kSymLR) s.dIn2 = sd(p.in2);
     } else {
@@ -1391,9 +1396,9 @@ hipError_t launch_xxt_fixups(const NsGroupRef *refs, const LaunchPart *all, int 
 // Every matrix on the way is a polynomial in A_0, so every product is of two
 // commuting symmetric matrices and is itself symmetric.  With L = 1 this is
 // the plain iteration (X X^T, P, P X).  Slots go lowest free first; five
-// suffice for any L.  In a segment of L > 1 steps the chain A_0 ... Q_{L-1}
-// is held in fp16 (f16 set) except Q_{L-1}, which X' = Q X reads beside the
-// bf16 X; with f16 clear, or L = 1, everything is bf16.
+// suffice for any L.  With f16 set the chain A_0 ... Q_{L-1} is held in fp16
+// except Q_{L-1} (P_0 when L = 1), which X' = Q X reads beside the bf16 X;
+// with f16 clear everything is bf16.
 void build_program(bool gram, int ns_steps, bool f16, NsProgram &pr) {
     MuonGeom g{};
     g.gram = gram ? 1 : 0;
@@ -1420,7 +1425,7 @@ void build_program(bool gram, int ns_steps, bool f16, NsProgram &pr) {
     for (int sg = 0; sg < nseg; ++sg) {
         const bool last = sg + 1 == nseg;
         const int L = len[sg];
-        h = f16 && L > 1;
+        h = f16;
         bool busy[kNsSlots] = {};
         auto alloc = [&]() {
             int k = 0;
@@ -1433,7 +1438,7 @@ void build_program(bool gram, int ns_steps, bool f16, NsProgram &pr) {
         int Q = -1;
         for (int j = 0; j < L; ++j) {
             const int P = alloc();
-            add(emit(kSyrkAA, sg, last), A, A, P);
+            add(emit(kSyrkAA, sg, last), A, A, P, L > 1);  // P_0 = Q_0 in bf16 when L = 1
             int S = -1, Qn = -1;
             if (j > 0 || j + 1 < L) {
                 NsStep &st = emit(kSymLR, sg, last);
