@@ -334,10 +334,8 @@ __device__ __forceinline__ void epilogue(const NsGroup &args, float ca, float cb
         // L R of two symmetric matrices held as off-diagonal parts and
         // diagonals (acc = Loff Roff): acc + dL_i Roff_ij + Loff_ij dR_j,
         // diagonal acc + dL_i dR_i (both off-diagonal parts are 0 there).
-        // Two passes over the wave's region: Loff (staged above) with dR_j
-        // and the diagonal; then Roff, loaded into the same region by this
-        // wave alone, with dL_i.
-        const uint16_t *Rm = args.Q + batch * args.q_stride;
+        // Loff (staged above) with dR_j and the diagonal here; the main loop
+        // has added dL_i Roff_ij.
         const float *dR = args.dIn2 + batch * args.d_stride;
 #pragma unroll
         for (int j = 0; j < FN; ++j) da_c[j] = dR[C0 + j * 16 + col];
@@ -348,29 +346,6 @@ __device__ __forceinline__ void epilogue(const NsGroup &args, float ca, float cb
                 const int gi = R0 + i * 16 + quad * 4 + r;
                 const float v = acc[i][j][r];
                 acc[i][j][r] = gi == gj ? v + da_r[i][r] * da_c[j] : v + in4[r] * da_c[j];
-            }
-        });
-        if constexpr (BM == 256) {
-            // direct to LDS: kilobyte k of the region is its rows 8k ..
-            // 8k+7; lane l takes row l / 8 and the chunk the swizzle puts
-            // at slot l % 8 (the layout of the main loop's prefetch)
-            const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(Rm + (int64_t)R0 * ldc + C0), (short)0, SR * (int)ldc * 2, 0x00020000);
-            const int rvoff = ((lane >> 3) * (int)ldc + (((lane & 7) ^ (lane >> 3)) << 3)) * 2;
-#pragma unroll
-            for (int k = 0; k < SR / 8; ++k)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, LDS_ADDR(W + k * 1024), 16, rvoff,
-                                                         8 * k * (int)ldc * 2, 0, 0);
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        } else {
-            stage(Rm);
-        }
-        each_block([&](int i, int j, const float(&in4)[4]) __attribute__((always_inline)) {
-            const int gj = C0 + j * 16 + col;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int gi = R0 + i * 16 + quad * 4 + r;
-                if (gi != gj) acc[i][j][r] += da_r[i][r] * in4[r];
             }
         });
     }
@@ -503,7 +478,10 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch 
     constexpr int NSTG = Cfg<BM>::SYM_STAGES;
     static_assert(LOADS >= 1 && LOADS * NW * 1024 == OPB, "tile");
     static_assert(NSTG * STAGE >= BM * BM * 2, "the epilogue regions fit in the stages");
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[NSTG * STAGE];
+    // L R: the tile's rows of dL, 1 KiB past the stage buffers
+    constexpr bool kDiagR = MODE == kSymLR;
+    constexpr int DLB = NSTG * STAGE;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[NSTG * STAGE + (kDiagR ? 1024 : 0)];
 
     // group, matrix and tile of this workgroup
     const int bid = blockIdx.x;
@@ -608,12 +586,70 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch 
                                                                         acc[i][j], 0, 0, 0);
     };
 
+    // L R: dL_i Roff_ij in the main loop.  R is symmetric, so the Q stage of
+    // a stage whose K range [32 s, 32 s + 32) lies inside the wave's rows
+    // [R0w, R0w + WTM) holds R[n0 + c][32 s + kk] = Roff[32 s + kk][n0 + c]:
+    // for the wave's row blocks 2q and 2q + 1 (32 s = R0w + 32 q), lane
+    // (col, quad) reads its four rows of column j in one 8-byte read and adds
+    // dL_row Roff to the accumulators.  dL of the tile's rows is in LDS (wave
+    // 0 loads it first, so the prologue's wait covers it).
+    const int R0w = m0 + wr * WTM;
+    if constexpr (kDiagR) {
+        if (wave == 0) {
+            const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(G.dIn + batch * G.d_stride + m0), (short)0, BM * 4, 0x00020000);
+            // (lanes past BM / 4 read zeros into the rest of the 1 KiB)
+            const int lo16 = lane * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, LDS_ADDR(&lds[DLB]), 16, lo16, 0, 0, 0);
+        }
+    }
+    // (one case per 32-row slice q, each with a marker of its own, so that
+    // the cases are not merged into one with a run-time index into acc,
+    // which would put acc in scratch memory)
+    auto diagq = [&](auto Q, int k0, int sbase) __attribute__((always_inline)) {
+        constexpr int q = decltype(Q)::value;
+        if (k0 != q * kBK) return;
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+            const int i = 2 * q + ii;
+            const f32x4 dl = *reinterpret_cast<const f32x4 *>(&lds[DLB + (wr * WTM + i * 16 + fh * 4) * 4]);
+            u32x2 qv[FN];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int row = wc * WTN + j * 16 + fr, ch = ii * 2 + (fh >> 1);
+                qv[j] = *reinterpret_cast<const u32x2 *>(
+                    &lds[sbase + OPB + row * ROW + ((ch ^ ((row >> 1) & 3)) << 4) + (fh & 1) * 8]);
+            }
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                acc[i][j][0] += dl[0] * from_el<F16>(qv[j].x & 0xFFFFu);
+                acc[i][j][1] += dl[1] * from_el<F16>(qv[j].x >> 16);
+                acc[i][j][2] += dl[2] * from_el<F16>(qv[j].y & 0xFFFFu);
+                acc[i][j][3] += dl[3] * from_el<F16>(qv[j].y >> 16);
+            }
+        }
+        asm volatile("; diag R slice %0" : : "n"(q));
+    };
+    auto diagR = [&](int s, int sbase) __attribute__((always_inline)) {
+        const int k0 = s * kBK - R0w;
+        static_assert(WTM / kBK >= 1 && WTM / kBK <= 4, "one to four 32-row slices per wave");
+        diagq(std::integral_constant<int, 0>{}, k0, sbase);
+        if constexpr (WTM / kBK > 1) diagq(std::integral_constant<int, 1>{}, k0, sbase);
+        if constexpr (WTM / kBK > 2) diagq(std::integral_constant<int, 2>{}, k0, sbase);
+        if constexpr (WTM / kBK > 3) diagq(std::integral_constant<int, 3>{}, k0, sbase);
+    };
+    // a wave whose sub-tile of a diagonal tile lies wholly below the diagonal
+    // computes nothing the epilogue stores: it only loads and synchronises
+    const bool dead = m0 == n0 && wr * WTM >= wc * WTN + WTN;
+
     const int KT = K / kBK;
 #pragma unroll
     for (int s = 0; s < NSTG; ++s) gload(s * STAGE, s * kBK);
     __builtin_amdgcn_s_waitcnt(WAIT_VM_LGKM0((NSTG - 1) * LPS));
     __syncthreads();
     read(0, 0);
+    if constexpr (kDiagR)
+        if (!dead) diagR(0, 0);
     int cur = 0;  // buffer of stage kt
     // (TAIL >= 0: one of the last NSTG stages of a 256-tile A A, whose
     // buffer TAIL receives the input tile's regions instead of zeros)
@@ -642,13 +678,11 @@ __attribute__((amdgpu_waves_per_eu(Cfg<BM>::WPE))) void ns_gemm_kernel(NsLaunch 
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
         }
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kDiagR && decltype(LIVE)::value) diagR(kt + 1, nxt * STAGE);
         cur = nxt;
     };
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
-    // a wave whose sub-tile of a diagonal tile lies wholly below the diagonal
-    // computes nothing the epilogue stores: it only loads and synchronises
-    const bool dead = m0 == n0 && wr * WTM >= wc * WTN + WTN;
     using NT = std::integral_constant<int, -1>;
     auto kloop = [&](auto LIVE) __attribute__((always_inline)) {
         int kt = 0;
