@@ -55,16 +55,28 @@ MEASURED_TRAFFIC = {
                         sha256="673b6ee27b692f43da0cb776f129120c95304617a7117f995f9273186f2e9bca",
                         bytes_per_launch=7.000e9,
                         profile="profiles/adamw_bucket_grid_kernel_zero2_2b_rank3.md"),
-    # the Newton-Schulz of one 5-step Muon call (every NS launch: the symmetric
-    # products, the fix-ups of split X X^T, P X / Q X), FETCH_SIZE + WRITE_SIZE summed
-    # over the call's dispatches and calibrated; the launch plan (which launches
-    # exist, on which stream) is in zopt_api.hip.  Not yet measured on this source.
-    "ns_call_gpt2": dict(source="sharded_optimizer_step_adamw_amd/csrc/ns_gemm.hip", sha256=None,
-                         bytes_per_launch=None, profile="profiles/ns_gemm_gpt2_small_step.md"),
-    "ns_call_llama8b": dict(source="sharded_optimizer_step_adamw_amd/csrc/ns_gemm.hip", sha256=None,
-                            bytes_per_launch=None, profile="profiles/ns_gemm_llama8b_rank0.md"),
-    "ns_call_llama1b": dict(source="sharded_optimizer_step_adamw_amd/csrc/ns_gemm.hip", sha256=None,
-                            bytes_per_launch=None, profile="profiles/ns_gemm_llama1b_rank0.md"),
+    # the Newton-Schulz of one 5-step Muon call: every NS launch of the call (the
+    # symmetric products, the fix-ups of split X X^T, P X / Q X), FETCH_SIZE + WRITE_SIZE
+    # summed over the call's dispatches and calibrated; the launch plan (which launches
+    # exist, on which stream) is in zopt_api.hip.
+    # GPT-2 small: 2.764 GB read, 1.591 GB written (32 launches on two streams)
+    "ns_call_gpt2": dict(source="sharded_optimizer_step_adamw_amd/csrc/ns_gemm.hip",
+                         sha256="c0cccef486f3eab2b4619fe5c614b93d57281323e67d1363088391c509e561f5",
+                         also=[("sharded_optimizer_step_adamw_amd/csrc/zopt_api.hip",
+                                "50ac681b60b07b3a302947ef0fc4b4728052f65481e22286cc740679e5d5bf72")],
+                         bytes_per_launch=4.354e9, profile="profiles/ns_gemm_gpt2_small_step.md"),
+    # 8B rank-0 share: 89.55 GB read, 14.68 GB written (23 launches)
+    "ns_call_llama8b": dict(source="sharded_optimizer_step_adamw_amd/csrc/ns_gemm.hip",
+                            sha256="c0cccef486f3eab2b4619fe5c614b93d57281323e67d1363088391c509e561f5",
+                            also=[("sharded_optimizer_step_adamw_amd/csrc/zopt_api.hip",
+                                   "50ac681b60b07b3a302947ef0fc4b4728052f65481e22286cc740679e5d5bf72")],
+                            bytes_per_launch=104.31e9, profile="profiles/ns_gemm_llama8b_rank0.md"),
+    # 1B rank-0 share: 4.519 GB read, 1.539 GB written (57 launches on two streams)
+    "ns_call_llama1b": dict(source="sharded_optimizer_step_adamw_amd/csrc/ns_gemm.hip",
+                            sha256="c0cccef486f3eab2b4619fe5c614b93d57281323e67d1363088391c509e561f5",
+                            also=[("sharded_optimizer_step_adamw_amd/csrc/zopt_api.hip",
+                                   "50ac681b60b07b3a302947ef0fc4b4728052f65481e22286cc740679e5d5bf72")],
+                            bytes_per_launch=6.060e9, profile="profiles/ns_gemm_llama1b_rank0.md"),
     "grad_sq_norm": dict(source="sharded_optimizer_step_adamw_amd/csrc/adamw_shard.hip",
                          sha256="673b6ee27b692f43da0cb776f129120c95304617a7117f995f9273186f2e9bca",
                          bytes_per_launch=0.5004e9,
