@@ -63,19 +63,19 @@ MEASURED_TRAFFIC = {
     "ns_call_gpt2": dict(source="sharded_optimizer_step_adamw_amd/csrc/ns_gemm.hip",
                          sha256="c0cccef486f3eab2b4619fe5c614b93d57281323e67d1363088391c509e561f5",
                          also=[("sharded_optimizer_step_adamw_amd/csrc/zopt_api.hip",
-                                "50ac681b60b07b3a302947ef0fc4b4728052f65481e22286cc740679e5d5bf72")],
+                                "a8bb444fe55d2ba505fe5d8ac002afcfb9f533df72a6d130b718a44c66a66953")],
                          bytes_per_launch=4.354e9, profile="profiles/ns_gemm_gpt2_small_step.md"),
     # 8B rank-0 share: 89.55 GB read, 14.68 GB written (23 launches)
     "ns_call_llama8b": dict(source="sharded_optimizer_step_adamw_amd/csrc/ns_gemm.hip",
                             sha256="c0cccef486f3eab2b4619fe5c614b93d57281323e67d1363088391c509e561f5",
                             also=[("sharded_optimizer_step_adamw_amd/csrc/zopt_api.hip",
-                                   "50ac681b60b07b3a302947ef0fc4b4728052f65481e22286cc740679e5d5bf72")],
+                                   "a8bb444fe55d2ba505fe5d8ac002afcfb9f533df72a6d130b718a44c66a66953")],
                             bytes_per_launch=104.31e9, profile="profiles/ns_gemm_llama8b_rank0.md"),
     # 1B rank-0 share: 4.519 GB read, 1.539 GB written (57 launches on two streams)
     "ns_call_llama1b": dict(source="sharded_optimizer_step_adamw_amd/csrc/ns_gemm.hip",
                             sha256="c0cccef486f3eab2b4619fe5c614b93d57281323e67d1363088391c509e561f5",
                             also=[("sharded_optimizer_step_adamw_amd/csrc/zopt_api.hip",
-                                   "50ac681b60b07b3a302947ef0fc4b4728052f65481e22286cc740679e5d5bf72")],
+                                   "a8bb444fe55d2ba505fe5d8ac002afcfb9f533df72a6d130b718a44c66a66953")],
                             bytes_per_launch=6.060e9, profile="profiles/ns_gemm_llama1b_rank0.md"),
     "grad_sq_norm": dict(source="sharded_optimizer_step_adamw_amd/csrc/adamw_shard.hip",
                          sha256="673b6ee27b692f43da0cb776f129120c95304617a7117f995f9273186f2e9bca",
@@ -123,22 +123,22 @@ def gram_segments(steps, per=3):
     return [base + (1 if i < extra else 0) for i in range(nseg)]
 
 
-def ns_flops(m, n, steps, form=0):
-    """Algorithmic flops of `steps` Newton-Schulz steps on an m x n input
-    (m <= n) as the library computes them.  Plain iterations (form 1, or
-    n < 2 m): per step upper-triangle X X^T (m^2 n), upper-triangle A A
-    (m^3), B X (2 m^2 n).  Gram form (forms 0 and 2 with n >= 2 m): per
-    segment of L steps X X^T (m^2 n), L upper-triangle A_j A_j, 3 (L - 1)
-    upper-triangle products of two symmetric m x m matrices (m^3 each),
-    Q X (2 m^2 n)."""
-    if form == 1 or n < 2 * m:
+def ns_flops(m, n, steps, form=0, batch=1):
+    """Algorithmic flops of `steps` Newton-Schulz steps on one m x n input
+    (m <= n) of a group of `batch`, as the library computes them.  Plain
+    iterations (form 1, n < 2 m, or batch m^2 (n - m) < 2^29): per step
+    upper-triangle X X^T (m^2 n), upper-triangle A A (m^3), B X (2 m^2 n).
+    Gram form otherwise: per segment of L steps X X^T (m^2 n), L
+    upper-triangle A_j A_j, 3 (L - 1) upper-triangle products of two
+    symmetric m x m matrices (m^3 each), Q X (2 m^2 n)."""
+    if form == 1 or n < 2 * m or batch * m * m * (n - m) < 2 ** 29:
         return steps * (3 * m * m * n + m ** 3)
     return sum(3 * m * m * n + (4 * L - 3) * m ** 3 for L in gram_segments(steps))
 
 
 def group_flops(groups, steps, form=0):
     return sum(g["count"] * ns_flops(min(g["rows"], g["cols"]), max(g["rows"], g["cols"]), steps,
-                                     form) for g in groups)
+                                     form, g["count"]) for g in groups)
 
 
 PLAIN_FORM_AB = [True]

@@ -306,7 +306,9 @@ int64_t zopt_shard_len(int64_t N, int64_t bucket, int32_t world);
  *      on bf16 matrix cores with fp32 accumulation; A, B and X are rounded to
  *      bf16 after each product; only the upper triangle of the symmetric A
  *      and B is computed and mirrored.  Where the long side is at least twice
- *      the short one (n >= 2 m) the same polynomial map runs in segments of
+ *      the short one (n >= 2 m) and the group is large enough for the flops
+ *      saved to pay for two more launches (batch m^2 (n - m) >= 2^29, a rule
+ *      on the group alone) the same polynomial map runs in segments of
  *      up to three steps on the m x m Gram matrix: with A_j = X_j X_j^T and
  *      P_j = a I + b A_j + c A_j^2, X_{j+1} = P_j X_j gives A_{j+1} =
  *      P_j^2 A_j and X_L = (P_{L-1} ... P_0) X_0, so a segment forms X X^T
@@ -563,8 +565,8 @@ zopt_status zopt_set_ns_workgroup_limit(int32_t n);
 
 /*
  * zopt_set_ns_form -- the Newton-Schulz form of later calls:
- *   0 (the default) runs matrices whose long side is at least twice the
- *     short one in segments on the Gram matrix (zopt_muon_step, step 3),
+ *   0 (the default) runs the groups that zopt_muon_step's step 3 names
+ *     (n >= 2 m, batch m^2 (n - m) >= 2^29) in segments on the Gram matrix,
  *     holding a segment's m x m chain in fp16 (3 more mantissa bits than
  *     bf16, the same matrix-core rate) when the coefficients keep every
  *     matrix of the chain below 2^13 in magnitude (checked on the scalar

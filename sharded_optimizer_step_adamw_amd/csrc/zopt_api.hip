@@ -100,8 +100,13 @@ MuonGeom muon_geometry(int32_t batch, int64_t rows, int64_t cols) {
     // Newton-Schulz on the Gram matrix where the long side is at least twice
     // the short one: a segment of L steps costs 3 m^2 n + (4 L - 3) m^3 flops
     // against L (3 m^2 n + m^3) for plain iterations (five steps in segments
-    // of 3 and 2: 6 m^2 n + 14 m^3 against 15 m^2 n + 5 m^3)
-    g.gram = (g_ns_form.load(std::memory_order_relaxed) != 1 && (int64_t)g.n >= 2 * (int64_t)g.m) ? 1 : 0;
+    // of 3 and 2: 6 m^2 n + 14 m^3 against 15 m^2 n + 5 m^3), and two more
+    // launches, so only for groups where the flops saved, 9 batch m^2 (n - m)
+    // for five steps, are worth more than those (batch m^2 (n - m) >= 2^29;
+    // 2 x [128, 512] stays plain: 0.099 ms per call against 0.107)
+    const double saved = (double)batch * g.m * g.m * ((double)g.n - g.m);
+    g.gram = (g_ns_form.load(std::memory_order_relaxed) != 1 && (int64_t)g.n >= 2 * (int64_t)g.m &&
+              saved >= (double)(1 << 29)) ? 1 : 0;
     return g;
 }
 

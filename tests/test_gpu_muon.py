@@ -146,10 +146,11 @@ def ns_form():
     z.set_ns_form(z.NS_FORM_AUTO)
 
 
-# Shapes whose long side is at least twice the short one: Newton-Schulz runs
-# in segments on the Gram matrix by default.  Both orientations, ragged sizes,
-# 64-, 128- and 256-tile symmetric products.
-GRAM_SHAPES = [(2, 96, 200), (1, 330, 100), (2, 200, 700), (1, 900, 300), (1, 1100, 2300)]
+# Groups whose long side is at least twice the short one and whose work
+# batch m^2 (n - m) reaches 2^29: Newton-Schulz runs in segments on the Gram
+# matrix by default.  Both orientations, ragged sizes, 64-, 128- and 256-tile
+# symmetric products.
+GRAM_SHAPES = [(48, 120, 1000), (64, 1000, 100), (8, 300, 1100), (4, 1500, 400), (1, 1100, 2300)]
 
 
 @pytest.mark.parametrize("ns_steps", [1, 2, 3, 4, 5, 7])
@@ -177,25 +178,28 @@ def test_gram_form_matches_oracle_and_plain_form(ns_form, ns_steps):
     ((3.4445, -4.7750, 2.0315), 3),
 ])
 def test_gram_form_coefficient_sets(coeffs, steps):
-    check_step(2, 150, 420, seed=21, ns_steps=steps, coeffs=coeffs)
-    check_step(1, 1300, 520, seed=22, ns_steps=steps, coeffs=coeffs)
+    check_step(40, 160, 800, seed=21, ns_steps=steps, coeffs=coeffs)
+    check_step(4, 1300, 520, seed=22, ns_steps=steps, coeffs=coeffs)
 
 
 def test_gram_form_large_coefficients_take_a_bf16_chain():
     """Coefficients whose m x m chain could leave fp16's range (p(0)^3 = 21^3
     > 2^13 in a segment of three steps) run the Gram form with its chain in
-    bf16.  The input has four equal singular values, 1/2 after the
-    pre-scale, where p(1/4) = 1 and the map's slope is 0, so every step keeps
-    X and rounding does not grow."""
-    rows, cols = 4, 320
+    bf16.  Each input has 16 equal singular values, 1/4 after the pre-scale,
+    where p(1/16) = 1 and the map's slope is 0, so every step keeps X and
+    rounding does not grow; 64 matrices of 16 x 32800 reach the Gram form's
+    work threshold."""
+    batch, rows, cols = 64, 16, 32800
     rng = np.random.default_rng(31)
-    q, _ = np.linalg.qr(rng.standard_normal((cols, rows)))
-    G = [wl.to_bf16_bits((q.T * 1e-3).astype(np.float32))]
-    P = [(rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)]
-    M = [np.zeros((rows, cols), np.float32)]
-    worst, _ = check_step(1, rows, cols, 32, ns_steps=3, coeffs=(21.0, -158.0, 312.0), P=P, M=M,
-                          G=G)
-    print(f"coefficients (21, -158, 312), 3 steps: NS rel err {worst:.3e}", flush=True)
+    G, P, M = [], [], []
+    for _ in range(batch):
+        q, _ = np.linalg.qr(rng.standard_normal((cols, rows)))
+        G.append(wl.to_bf16_bits((q.T * 1e-3).astype(np.float32)))
+        P.append((rng.standard_normal((rows, cols)) * 0.02).astype(np.float32))
+        M.append(np.zeros((rows, cols), np.float32))
+    worst, _ = check_step(batch, rows, cols, 32, ns_steps=3, coeffs=(21.0, -632.0, 4992.0), P=P,
+                          M=M, G=G)
+    print(f"coefficients (21, -632, 4992), 3 steps: worst NS rel err {worst:.3e}", flush=True)
 
 
 @pytest.mark.parametrize("nesterov,adjust", [(False, 1), (True, 0), (False, 0)])
