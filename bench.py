@@ -128,10 +128,10 @@ def ns_flops(m, n, steps, form=0, batch=1):
     (m <= n) of a group of `batch`, as the library computes them.  Plain
     iterations (form 1, n < 2 m, or batch m^2 (n - m) < 2^29): per step
     upper-triangle X X^T (m^2 n), upper-triangle A A (m^3), B X (2 m^2 n).
-    Gram form otherwise: per segment of L steps X X^T (m^2 n), L
+    Gram form otherwise (m <= 4096): per segment of L steps X X^T (m^2 n), L
     upper-triangle A_j A_j, 3 (L - 1) upper-triangle products of two
     symmetric m x m matrices (m^3 each), Q X (2 m^2 n)."""
-    if form == 1 or n < 2 * m or batch * m * m * (n - m) < 2 ** 29:
+    if form == 1 or n < 2 * m or m > 4096 or batch * m * m * (n - m) < 2 ** 29:
         return steps * (3 * m * m * n + m ** 3)
     return sum(3 * m * m * n + (4 * L - 3) * m ** 3 for L in gram_segments(steps))
 

@@ -306,9 +306,10 @@ int64_t zopt_shard_len(int64_t N, int64_t bucket, int32_t world);
  *      on bf16 matrix cores with fp32 accumulation; A, B and X are rounded to
  *      bf16 after each product; only the upper triangle of the symmetric A
  *      and B is computed and mirrored.  Where the long side is at least twice
- *      the short one (n >= 2 m) and the group is large enough for the flops
- *      saved to pay for two more launches (batch m^2 (n - m) >= 2^29, a rule
- *      on the group alone) the same polynomial map runs in segments of
+ *      the short one (n >= 2 m), m <= 4096 and the group is large enough for
+ *      the flops saved to pay for two more launches (batch m^2 (n - m) >=
+ *      2^29; a rule on the group alone) the same polynomial map runs in
+ *      segments of
  *      up to three steps on the m x m Gram matrix: with A_j = X_j X_j^T and
  *      P_j = a I + b A_j + c A_j^2, X_{j+1} = P_j X_j gives A_{j+1} =
  *      P_j^2 A_j and X_L = (P_{L-1} ... P_0) X_0, so a segment forms X X^T
@@ -566,12 +567,16 @@ zopt_status zopt_set_ns_workgroup_limit(int32_t n);
 /*
  * zopt_set_ns_form -- the Newton-Schulz form of later calls:
  *   0 (the default) runs the groups that zopt_muon_step's step 3 names
- *     (n >= 2 m, batch m^2 (n - m) >= 2^29) in segments on the Gram matrix,
+ *     (n >= 2 m, m <= 4096, batch m^2 (n - m) >= 2^29) in segments on the
+ *     Gram matrix,
  *     holding a segment's m x m chain in fp16 (3 more mantissa bits than
  *     bf16, the same matrix-core rate) when the coefficients keep every
  *     matrix of the chain below 2^13 in magnitude (checked on the scalar
  *     map over singular values in [0, 1.05]; true for the usual quintic and
- *     cubic coefficients), else in bf16;
+ *     cubic coefficients), else in bf16; plain iterations hold A in fp16
+ *     under the same condition for m <= 4096 (fp16's subnormal range
+ *     begins near the off-diagonal entries of larger matrices' A), in bf16
+ *     otherwise;
  *   1 runs plain iterations for every matrix;
  *   2 is form 0 with the chain always in bf16 (for comparison: less
  *     accurate than both others on some inputs).

@@ -280,7 +280,7 @@ NS_FORM_AUTO, NS_FORM_PLAIN, NS_FORM_GRAM_BF16 = 0, 1, 2
 
 def set_ns_form(form: int) -> None:
     """Newton-Schulz form of later calls: NS_FORM_AUTO (segments on the Gram
-    matrix for groups with n >= 2 m and batch m^2 (n - m) >= 2^29, the m x m
+    matrix for groups with n >= 2 m, m <= 4096 and batch m^2 (n - m) >= 2^29, the m x m
     chain in fp16 where the coefficients allow), NS_FORM_PLAIN (plain
     iterations throughout) or NS_FORM_GRAM_BF16 (as AUTO, chain in bf16)
     (zopt_set_ns_form)."""

@@ -1644,8 +1644,10 @@ hipError_t launch_ns_step(const NsGroupRef *refs, int nrefs, const NsSchedule &s
                 lp.out = st.out[q];
                 lp.seg = st.seg;
                 lp.last = st.last_seg != 0;
-                lp.in_f16 = st.f16in != 0;
-                lp.out_f16 = st.f16out[q] != 0;
+                // (a plain group whose m is past fp16's validated range keeps A in bf16)
+                const bool f16ok = g.m <= kNsF16MaxM;
+                lp.in_f16 = f16ok && st.f16in != 0;
+                lp.out_f16 = f16ok && st.f16out[q] != 0;
                 all[nall++] = lp;
             }
     }

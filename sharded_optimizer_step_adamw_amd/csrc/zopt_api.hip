@@ -106,7 +106,7 @@ MuonGeom muon_geometry(int32_t batch, int64_t rows, int64_t cols) {
     // 2 x [128, 512] stays plain: 0.099 ms per call against 0.107)
     const double saved = (double)batch * g.m * g.m * ((double)g.n - g.m);
     g.gram = (g_ns_form.load(std::memory_order_relaxed) != 1 && (int64_t)g.n >= 2 * (int64_t)g.m &&
-              saved >= (double)(1 << 29)) ? 1 : 0;
+              saved >= (double)(1 << 29) && g.m <= kNsF16MaxM) ? 1 : 0;
     return g;
 }
 

@@ -124,6 +124,16 @@ struct MuonPtrs {
 // the Gram matrix (A, P, Q and the products on the way to the next A).
 constexpr int kNsSlots = 5;
 constexpr int kNsMaxSegment = 3;
+// The largest short side m for which the symmetric m x m matrices may be held
+// in fp16 (the Gram form's chain, plain iterations' A): fp16 keeps 11 bits
+// only down to 2^-14, and the off-diagonal entries of A = X X^T of a
+// normalised m x n X are ~1 / (m sqrt(n)), subnormal in fp16 at m = 4096
+// (~2e-6 for n = 14336) and smaller beyond.  Measured at full size, the Gram
+// form with segments of 3 and 2 holds its error at 3.1e-3 up to m = 4096
+// (the plain bf16 iteration: 5e-3), while a first segment of four steps
+// degrades with m (3.2e-3 at m = 256, 4.9e-3 at 2048, 9.0e-3 at 4096).  Larger
+// matrices run plain iterations with every matrix in bf16.
+constexpr int kNsF16MaxM = 4096;
 
 // Workspace carve-up (byte offsets; every region 256-byte aligned).  x and
 // xt0 hold X (mp x np) in turn, one per Newton-Schulz segment; xt1 holds the

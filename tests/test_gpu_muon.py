@@ -172,6 +172,20 @@ def test_gram_form_matches_oracle_and_plain_form(ns_form, ns_steps):
         assert rel_fro(outs[z.NS_FORM_AUTO], outs[z.NS_FORM_PLAIN]) <= NS_TOL
 
 
+def test_short_side_past_fp16_range_runs_plain_bf16(ns_form):
+    """m = 4160 > 4096: the group runs plain iterations with every matrix in
+    bf16 (fp16 would hold A's off-diagonal entries in its subnormal range),
+    also when its shape would otherwise take the Gram form, and its result
+    equals the plain form's bit for bit."""
+    P, M, G = make_inputs(1, 4160, 8320, 41, momentum_nonzero=True)
+    worst, ws = check_step(1, 4160, 8320, 41, P=P, M=M, G=G)
+    o = u16(z.muon_output_view(ws, 1, 4160, 8320, 5, 0)).copy()
+    print(f"[4160, 8320]: NS rel err {worst:.3e}", flush=True)
+    ns_form(z.NS_FORM_PLAIN)
+    _, ws1 = check_step(1, 4160, 8320, 41, P=P, M=M, G=G, check_ns=False)
+    np.testing.assert_array_equal(u16(z.muon_output_view(ws1, 1, 4160, 8320, 5, 0)), o)
+
+
 @pytest.mark.parametrize("coeffs,steps", [
     ((1.5, -0.5, 0.0), 8),
     ((2.0, -1.5, 0.5), 5),
