@@ -374,7 +374,9 @@ zopt_status zopt_muon_step(int32_t batch, int64_t rows, int64_t cols,
  * `index` lies in a workspace that zopt_muon_step(batch, rows, cols, ...,
  * ns_steps, ...) has filled: bf16 O[r][c] (stored orientation, [rows, cols])
  * is at (*out)[r * (*row_stride) + c].  Host-only; enqueues nothing.  The view
- * is valid until the workspace is reused.  Errors: ZOPT_ERR_NULL,
+ * is valid until the workspace is reused, and assumes the Newton-Schulz form
+ * (zopt_set_ns_form) in effect when the workspace was filled: the form decides
+ * which buffer holds the result.  Errors: ZOPT_ERR_NULL,
  * ZOPT_ERR_SIZE (batch, rows, cols or index out of range), ZOPT_ERR_HYPER
  * (ns_steps out of range).
  */
