@@ -518,6 +518,20 @@ def grouped_vs_separate(specs, seed, ns_steps=5, ns_check=lambda b, r, c, i: Tru
     return worst
 
 
+@pytest.mark.parametrize("ns_steps", [4, 10])
+def test_gram_and_plain_groups_in_one_call(ns_steps):
+    """Gram-form groups (64-, 128- and 256-tile, one stored transposed) beside
+    plain ones in one call, their programs merged into one launch sequence --
+    at 10 steps four segments and 34 Gram steps: each matrix against the
+    oracle and bit for bit against separate calls.  (Many more steps leave
+    the 2e-2 bar on some Gaussian inputs in either form: at 20 steps the
+    plain bf16 iteration ends 4.0e-2 from float64 on one of 48 such
+    120 x 1000 matrices, the Gram form 3.3e-2.)"""
+    specs = [(48, 120, 1000), (2, 200, 200), (4, 1500, 400), (3, 300, 330), (1, 1100, 2300)]
+    worst = grouped_vs_separate(specs, seed=51, ns_steps=ns_steps)
+    print(f"{ns_steps} steps: worst NS rel err {worst:.3e}", flush=True)
+
+
 def test_groups_mixed_tiles_match_oracle_and_separate_calls():
     """Eight groups over all three tile sizes, both orientations and ragged
     sizes, in one call."""
