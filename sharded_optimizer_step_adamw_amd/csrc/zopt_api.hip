@@ -528,11 +528,14 @@ AuxStream *aux_stream(hipStream_t caller) {
 // program (plain iterations or Gram segments, on the same tile) share its
 // launches when they are on one side, while a plain and a Gram group on one
 // side make a merged program longer than either (15 and 17 launches for five
-// steps merge into 23).  So whole classes of such groups are placed, in order
-// of Newton-Schulz work, each on the side with less work so far.  Measured on
-// the 1B rank-0 share (two 2048-row Gram groups, the square plain group, the
-// 512-row Gram group on 128 tiles): 2.58 ms per call against 2.81 ms with the
-// groups placed one by one.
+// steps merge into 23).  So in a call that mixes the two forms, whole classes
+// of such groups are placed, in order of Newton-Schulz work, each on the side
+// with less work so far; in a call of one form the groups are placed so one
+// by one.  Measured on the 1B rank-0 share (two 2048-row Gram groups, the
+// square plain group, the 512-row Gram group on 128 tiles): 2.58 ms per call
+// against 2.81 ms with the groups placed one by one; all four in plain
+// iterations, one by one, Newton-Schulz 3.01 ms per call against 3.22 ms by
+// class (the three 2048-row groups on one stream).
 void split_sides(const NsGroupRef *refs, int nb, int ns_steps, int *side) {
     double work[kMaxCallGroups];
     int cls[kMaxCallGroups];
@@ -564,9 +567,9 @@ void split_sides(const NsGroupRef *refs, int nb, int ns_steps, int *side) {
         w[d] += cwork[c];
     }
     for (int k = 0; k < nb; ++k) side[k] = cside[cls[k]];
-    // (a single class: its groups one by one, as they would otherwise share
-    // one stream)
-    if (ncls == 1) {
+    bool mixed = false;
+    for (int k = 1; k < nb; ++k) mixed = mixed || refs[k].geom->gram != refs[0].geom->gram;
+    if (!mixed) {
         int ord[kMaxCallGroups];
         for (int k = 0; k < nb; ++k) ord[k] = k;
         std::stable_sort(ord, ord + nb, [&](int x, int y) { return work[x] > work[y]; });
