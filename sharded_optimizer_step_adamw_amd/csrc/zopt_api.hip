@@ -536,6 +536,14 @@ AuxStream *aux_stream(hipStream_t caller) {
 // against 2.81 ms with the groups placed one by one; all four in plain
 // iterations, one by one, Newton-Schulz 3.01 ms per call against 3.22 ms by
 // class (the three 2048-row groups on one stream).
+// Newton-Schulz multiply-adds of a group: 3 m^2 n + (4 L - 3) m^3 per matrix
+// and segment of L steps (a plain step is a segment of one)
+double ns_work(const MuonGeom &g, int ns_steps) {
+    const double m = g.m, n = g.n;
+    const int nseg = ns_segments(g, ns_steps);
+    return g.batch * (nseg * 3.0 * m * m * n + (4.0 * ns_steps - 3.0 * nseg) * m * m * m);
+}
+
 void split_sides(const NsGroupRef *refs, int nb, int ns_steps, int *side) {
     double work[kMaxCallGroups];
     int cls[kMaxCallGroups];
@@ -543,10 +551,7 @@ void split_sides(const NsGroupRef *refs, int nb, int ns_steps, int *side) {
     double cwork[kMaxCallGroups];
     for (int k = 0; k < nb; ++k) {
         const MuonGeom &g = *refs[k].geom;
-        const double m = g.m, n = g.n;
-        const int nseg = ns_segments(g, ns_steps);
-        // 3 m^2 n + (4 L - 3) m^3 per segment of L steps
-        work[k] = g.batch * (nseg * 3.0 * m * m * n + (4.0 * ns_steps - 3.0 * nseg) * m * m * m);
+        work[k] = ns_work(g, ns_steps);
         const int kk = g.gram * 1024 + g.tile;
         int c = 0;
         while (c < ncls && key[c] != kk) ++c;
@@ -612,10 +617,19 @@ hipError_t muon_enqueue(const MuonCallPlan &c, char *ws, float lr, float mu, int
             else
                 lock.unlock();
         }
-        // each side's groups in one merged sequence of launches; the side
-        // with the longer sequence runs on the caller's stream, whose work
-        // starts first (GPT-2-small: the two Gram groups there and the plain
-        // group on the second stream, 1.715 against 1.733 ms per call)
+        // each side's groups in one merged sequence of launches.  The side
+        // estimated to take longer runs on the caller's stream, whose work
+        // starts first, and its pre-passes run before the second stream
+        // forks, so that they have the memory to themselves and its
+        // iterations start as early as they can; the other side's pre-passes
+        // then run beside those iterations.  The estimate: 24 bytes per
+        // element of pre-pass and post-step at 6 TB/s, the multiply-adds at
+        // 0.6 T/s (1.2 PFLOP/s) and 40 us per launch.  It puts GPT-2-small's
+        // Gram groups (17 launches) before its plain group (15), and the 1B
+        // share's 2048-row Gram groups (69 M elements) before its square and
+        // 512-row groups (21 M elements in 30 launches): 1.741 -> 1.721 and
+        // 2.588 -> 2.581 ms per call against the longer merged program first
+        // and the fork before every pre-pass.
         NsGroupRef r[2][kMaxCallGroups];
         int n[2] = {0, 0};
         std::vector<NsSchedule> sch(2);
@@ -632,7 +646,28 @@ hipError_t muon_enqueue(const MuonCallPlan &c, char *ws, float lr, float mu, int
                     if (n[d] > 0) ns_schedule(r[d], n[d], ns_steps, f16, sch[d]);
             };
             plan_sides();
-            if (aux != nullptr && n[0] > 0 && n[1] > 0 && sch[1].nsteps > sch[0].nsteps) {
+            auto cost = [&](int d) {
+                double elems = 0.0, work = 0.0;
+                for (int k = 0; k < n[d]; ++k) {
+                    const MuonGeom &g = *r[d][k].geom;
+                    elems += (double)g.batch * g.rows * g.cols;
+                    work += ns_work(g, ns_steps);
+                }
+                int launches = 0;
+                for (int t = 0; t < sch[d].nsteps; ++t) {
+                    int tiles = 0;  // bit set of the step's tile sizes
+                    bool split = false;
+                    for (int k = 0; k < n[d]; ++k) {
+                        const MuonGeom &g = *r[d][k].geom;
+                        if (sch[d].idx[g.gram ? 1 : 0][t] < 0) continue;
+                        tiles |= sch[d].kind[t] == kNsKindBX ? g.tile_bx : g.tile;
+                        split = split || (sch[d].kind[t] == kNsKindXXT && g.ksplit > 1);
+                    }
+                    launches += __builtin_popcount(tiles) + (split ? 1 : 0);
+                }
+                return elems * 24.0 / 6e12 + work / 0.6e15 + launches * 40e-6;
+            };
+            if (aux != nullptr && n[0] > 0 && n[1] > 0 && cost(1) > cost(0)) {
                 for (int k = 0; k < nb; ++k) side[k] ^= 1;
                 plan_sides();
             }
@@ -648,15 +683,21 @@ hipError_t muon_enqueue(const MuonCallPlan &c, char *ws, float lr, float mu, int
             const hipError_t ew = ej == hipSuccess ? hipStreamWaitEvent(s, aux->join, 0) : ej;
             if (e == hipSuccess) e = ew;
         };
-        if (aux != nullptr) {
+        // the pre-passes of side d (all groups with one stream)
+        auto pre = [&](int d) {
+            for (int k = 0; k < nb && e == hipSuccess; ++k) {
+                if ((aux != nullptr ? side[k] : 0) != d) continue;
+                const int i = c.bins[bi][k];
+                e = launch_muon_pre(c.plans[i].g, c.ptrs[i], mu, nesterov, ns_eps,
+                                    ws + c.plans[i].base, c.plans[i].L, ns_steps == 0, dev, on(k));
+            }
+        };
+        pre(0);
+        if (aux != nullptr && e == hipSuccess) {
             e = hipEventRecord(aux->fork, s);
             if (e == hipSuccess) e = hipStreamWaitEvent(aux->s, aux->fork, 0);
         }
-        for (int k = 0; k < nb && e == hipSuccess; ++k) {
-            const int i = c.bins[bi][k];
-            e = launch_muon_pre(c.plans[i].g, c.ptrs[i], mu, nesterov, ns_eps,
-                                ws + c.plans[i].base, c.plans[i].L, ns_steps == 0, dev, on(k));
-        }
+        pre(1);
         if (ns_steps > 0 && e == hipSuccess) {
             // the two sides' launches enqueued in turn
             const int steps = std::max(n[0] > 0 ? sch[0].nsteps : 0, n[1] > 0 ? sch[1].nsteps : 0);

@@ -237,6 +237,7 @@ struct NsStep {
     int16_t seg;      // segment of the step
     int8_t last_seg;  // 1: the segment is the last
 };
+constexpr int kNsKindXXT = 0, kNsKindBX = 2;  // the kinds above by name
 constexpr int kNsMaxProgram = 4 * 100;
 constexpr int kNsMaxMerged = 2 * kNsMaxProgram;
 struct NsProgram {
