@@ -384,6 +384,7 @@ def bench_ns(torch, z, timer, dev, K, W, w=None):
     w = w or wl.LLAMA8B_MUON
     groups, workspace = muon_groups(torch, w, dev)
     total_flops = group_flops(groups, w.ns_steps)
+    plain_flops = group_flops(groups, w.ns_steps, form=1)
     timer.run(lambda _: muon_call(z, w, groups, workspace, w.ns_steps), max(1, W))
     t5 = timer.run(lambda _: muon_call(z, w, groups, workspace, w.ns_steps), K)
     t0 = timer.run(lambda _: muon_call(z, w, groups, workspace, 0), K)
@@ -414,10 +415,10 @@ def bench_ns(torch, z, timer, dev, K, W, w=None):
                   "and ns_gemm_kernel<256,3,fp16> on the m x m chain, ns_bx_kernel<256> Q X)")
         traffic, tunit = measured_traffic("ns_call_llama8b"), "HBM bytes per 5-step call (all NS launches)"
     else:
-        kernel = ("Newton-Schulz of the 12 matrices on two streams: the 11264 x 2048 pair (Gram "
-                  "segments; X X^T split along K plus its fix-up) on one, the other three groups "
-                  "(2048 x 5632 and 512 x 2048 in Gram segments, 2048 x 2048 in plain "
-                  "iterations) on the other")
+        kernel = ("Newton-Schulz of the 12 matrices on two streams: the two 2048-row groups in "
+                  "Gram segments (the 11264 x 2048 pair with X X^T split along K plus its "
+                  "fix-up, and 2048 x 5632) on the caller's, the 2048 x 2048 group in plain "
+                  "iterations and the 512 x 2048 group in Gram segments on the second")
         traffic, tunit = measured_traffic("ns_call_llama1b"), "HBM bytes per 5-step call (all NS launches)"
     roof = dict(kernel=kernel, bound="mfma", achieved=round(tf, 1), peak=BF16_PEAK_TFLOPS,
                 unit="TFLOP/s", frac=round(tf / BF16_PEAK_TFLOPS, 4), traffic=traffic,
@@ -427,6 +428,9 @@ def bench_ns(torch, z, timer, dev, K, W, w=None):
                 algorithmic_flops_per_step=total_flops, ns_ms_per_step=round(ns_ms, 3),
                 muon_ms_per_step=round(call_ms, 3), ns_tflops=round(tf, 1),
                 mfma_frac=round(tf / BF16_PEAK_TFLOPS, 4),
+                # the plain iteration's flops (5 (3 m^2 n + m^3) per matrix) over the measured
+                # time: the utilisation plain iterations would need to take this long
+                frac_on_plain_iteration_flops=round(plain_flops / ns_ms / 1e9 / BF16_PEAK_TFLOPS, 4),
                 muon_step_tflops=round(total_flops / call_ms / 1e9, 1), zero_step_call_ms=round(t0, 3),
                 plain_form=plain, groups=rows, steps=K, ns_health=health, roofline=roof)
 

@@ -642,14 +642,19 @@ def test_grouped_workspace_needs_no_initialisation():
 
 
 @pytest.mark.parametrize("ns_steps", [1, 5])
-def test_two_stream_groups(ns_steps):
+@pytest.mark.parametrize("form", ["auto", "plain"])
+def test_two_stream_groups(ns_steps, form, ns_form):
     """A call whose Newton-Schulz iterations run on two streams: three groups
     on 256 tiles whose X X^T launch holds 136 + 72 + 72 = 280 workgroups,
     under two rounds of the GPU's 256, so the groups are divided between
-    the caller's stream and the second one (the two plain groups on one,
-    the 2048 x 5632 group, on the Gram matrix, on the other).  Every matrix
-    equals the separate calls' (one group each: one stream) bit for bit; the
-    2048-row matrices against the oracle."""
+    the caller's stream and the second one: by default the two plain groups
+    on one and the 2048 x 5632 group, on the Gram matrix, on the other (a
+    call that mixes the forms is divided by class); in plain iterations
+    throughout the groups one by one (the 4096^2 group on one stream, the
+    others on the other).  Every matrix equals the separate calls' (one
+    group each: one stream) bit for bit; the 2048-row matrices against the
+    oracle."""
+    ns_form(z.NS_FORM_AUTO if form == "auto" else z.NS_FORM_PLAIN)
     specs = [(1, 4096, 4096), (2, 2048, 2048), (2, 2048, 5632)]
     grouped_vs_separate(specs, seed=123, ns_steps=ns_steps,
                         ns_check=lambda b, r, c, i: r == 2048 and i == 0)
