@@ -288,10 +288,22 @@ def set_ns_form(form: int) -> None:
 
 
 def _ptr_array(tensors) -> ctypes.Array:
-    arr = (ctypes.c_void_p * len(tensors))()
-    for i, t in enumerate(tensors):
-        arr[i] = t.data_ptr()
-    return arr
+    return (ctypes.c_void_p * len(tensors))(*[t.data_ptr() for t in tensors])
+
+
+def _check_matrices(lists, shape, device, prefix=""):
+    """Every tensor of `lists` [(tensors, dtype, name)] is a contiguous GPU
+    tensor of that dtype and `shape` on `device`: one combined test per
+    tensor, and the detailed checks (for the error message) only where it
+    fails."""
+    index = device.index if device.type == "cuda" else -2
+    for tensors, dt, nm in lists:
+        for i, t in enumerate(tensors):
+            if not (isinstance(t, torch.Tensor) and t.dtype == dt and t.is_cuda
+                    and t.get_device() == index and t.shape == shape and t.is_contiguous()):
+                name = f"{prefix}{nm}[{i}]"
+                _need(t, dt, shape[0] * shape[1], name, device)
+                raise ValueError(f"{name}: shape {tuple(t.shape)}, need {tuple(shape)}")
 
 
 def muon_workspace_bytes(batch: int, rows: int, cols: int) -> int:
@@ -317,16 +329,13 @@ def muon_step(master: Sequence[torch.Tensor], momentum: Sequence[torch.Tensor],
     if not (1 <= batch <= MAX_BATCH) or len(momentum) != batch or len(grad) != batch or (
             weight is not None and len(weight) != batch):
         raise ValueError("muon_step: need 1..64 matrices and equal-length lists")
-    rows, cols = master[0].shape
+    shape = master[0].shape
+    rows, cols = shape
     dev = master[0].device
-    for i in range(batch):
-        for t, dt, nm in ((master[i], torch.float32, "master"),
-                          (momentum[i], torch.float32, "momentum"),
-                          (grad[i], torch.bfloat16, "grad")) + (
-                ((weight[i], torch.bfloat16, "weight"),) if weight is not None else ()):
-            _need(t, dt, rows * cols, f"{nm}[{i}]", dev)
-            if tuple(t.shape) != (rows, cols):
-                raise ValueError(f"{nm}[{i}]: shape {tuple(t.shape)}, need {(rows, cols)}")
+    _check_matrices(((master, torch.float32, "master"), (momentum, torch.float32, "momentum"),
+                     (grad, torch.bfloat16, "grad"))
+                    + (((weight, torch.bfloat16, "weight"),) if weight is not None else ()),
+                    shape, dev)
     need = muon_workspace_bytes(batch, rows, cols)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -436,16 +445,12 @@ def _muon_group_tables(groups):
             raise ValueError(f"group {gi}: need 1..64 matrices and equal-length lists")
         if (weight is not None) != with_w or (weight is not None and len(weight) != batch):
             raise ValueError(f"group {gi}: weight lists must be given for all groups or none")
-        rows, cols = master[0].shape
-        for i in range(batch):
-            for t, dt, nm in ((master[i], torch.float32, "master"),
-                              (momentum[i], torch.float32, "momentum"),
-                              (grad[i], torch.bfloat16, "grad")) + (
-                    ((weight[i], torch.bfloat16, "weight"),) if weight is not None else ()):
-                _need(t, dt, rows * cols, f"group {gi} {nm}[{i}]", dev)
-                if tuple(t.shape) != (rows, cols):
-                    raise ValueError(f"group {gi} {nm}[{i}]: shape {tuple(t.shape)}, "
-                                     f"need {(rows, cols)}")
+        shape = master[0].shape
+        rows, cols = shape
+        _check_matrices(((master, torch.float32, "master"), (momentum, torch.float32, "momentum"),
+                         (grad, torch.bfloat16, "grad"))
+                        + (((weight, torch.bfloat16, "weight"),) if weight is not None else ()),
+                        shape, dev, f"group {gi} ")
         shapes.append((batch, rows, cols))
         M += list(master)
         Mo += list(momentum)

@@ -11,6 +11,8 @@ Shapes cover ragged sizes (tile padding), both orientations (rows > cols is
 transposed), every workload's shapes, and the scalar-polynomial closed form
 of Newton-Schulz on U diag(s) V^T inputs.
 """
+import re
+
 import numpy as np
 import pytest
 import torch
@@ -681,3 +683,32 @@ def test_split_reduction_groups(ns_steps):
     one iteration puts the pre-scale in the fix-up."""
     specs = [(1, 1100, 8300), (2, 8200, 1030), (1, 4096, 4096)]
     grouped_vs_separate(specs, seed=77, ns_steps=ns_steps, ns_check=lambda b, r, c, i: r != c)
+
+
+def test_binding_rejects_bad_tensors():
+    """The binding checks every tensor of a grouped call before anything is
+    enqueued: a wrong dtype, a non-contiguous view, a wrong shape or a host
+    tensor anywhere in a group is an error naming the group, list and index,
+    and the good call on the same buffers still runs."""
+    def good():
+        return [([torch.zeros(64, 96, device=DEV) for _ in range(3)],
+                 [torch.zeros(64, 96, device=DEV) for _ in range(3)],
+                 [torch.zeros(64, 96, dtype=torch.bfloat16, device=DEV) for _ in range(3)],
+                 [torch.zeros(64, 96, dtype=torch.bfloat16, device=DEV) for _ in range(3)]),
+                ([torch.zeros(32, 32, device=DEV)], [torch.zeros(32, 32, device=DEV)],
+                 [torch.zeros(32, 32, dtype=torch.bfloat16, device=DEV)],
+                 [torch.zeros(32, 32, dtype=torch.bfloat16, device=DEV)])]
+    cases = [
+        ((0, 2, 2), torch.zeros(64, 96, device=DEV), TypeError, "group 0 grad[2]: dtype"),
+        ((0, 0, 1), torch.zeros(96, 64, device=DEV).t(), ValueError, "group 0 master[1]: must be contiguous"),
+        ((1, 3, 0), torch.zeros(32, 33, dtype=torch.bfloat16, device=DEV), ValueError,
+         "group 1 weight[0]: shape (32, 33)"),
+        ((0, 1, 0), torch.zeros(64, 96), ValueError, "group 0 momentum[0]: must be a GPU tensor"),
+    ]
+    for (gi, li, i), bad, exc, msg in cases:
+        groups = good()
+        groups[gi][li][i] = bad
+        with pytest.raises(exc, match=re.escape(msg)):
+            z.muon_step_groups(groups, 1e-3, 0.95, True, 0.1, 5)
+    z.muon_step_groups(good(), 1e-3, 0.95, True, 0.1, 5)
+    torch.cuda.synchronize()
