@@ -604,8 +604,9 @@ hipError_t muon_enqueue(const MuonCallPlan &c, char *ws, float lr, float mu, int
         // A bin whose Newton-Schulz launches are short runs on two streams:
         // each group's pre-pass, iterations and (with no health pass) post-step
         // on its side's stream; the second stream forks from the caller's
-        // before the pre-passes and joins it before the health pass, or at the
-        // end.  The lock makes the fork ... join enqueue of one call atomic.
+        // after the caller's side's pre-passes and joins it before the health
+        // pass, or at the end.  The lock makes the fork ... join enqueue of one
+        // call atomic.
         std::unique_lock<std::mutex> lock(g_aux_mutex, std::defer_lock);
         AuxStream *aux = nullptr;
         int side[kMaxCallGroups] = {};
