@@ -402,19 +402,25 @@ zopt_status zopt_muon_output_view(int32_t batch, int64_t rows, int64_t cols,
  * give the X X^T launch fewer than two rounds of workgroups (2 x 256 on a
  * 256-CU GPU), each product's launch would leave much of the GPU idle in its
  * last round.  The groups then run on `stream` and on a second stream of the
- * library's, divided between the two by Newton-Schulz work (largest first,
- * each to the stream with less), each group's momentum pass, iterations and
- * (with no health pass) post-step on its stream: the second stream waits for
- * everything enqueued on `stream` before the call (an event), and `stream`
- * waits for the second stream's last launch (another event) before the
- * health pass, or at the end of the call, so the call is ordered on `stream`
- * as any other.  The results are the same bit for bit.  The second stream is
+ * library's.  In a call that mixes the two forms of step 3, the groups of one
+ * form and output tile stay on one stream (they share its launches), these
+ * classes placed by Newton-Schulz work (largest first, each to the stream
+ * with less); in a call of one form the groups are placed so one by one.  The
+ * side estimated to take longer runs on `stream`.  Each group's momentum
+ * pass, iterations and (with no health pass) post-step run on its side's
+ * stream: the second stream waits (an event) for everything enqueued on
+ * `stream` before the call and for the momentum passes of `stream`'s groups,
+ * and `stream` waits for the second stream's last launch (another event)
+ * before the health pass, or at the end of the call, so the call is ordered
+ * on `stream` as any other.  The results are the same bit for bit.  The
+ * second stream is
  * created at the first such call on the GPU that is not under stream capture
  * (a call under capture before that runs on one stream) and by
  * zopt_muon_graph_create before its capture; calls from several host threads
  * enqueue this part one at a time (a lock), and their work on the second
  * stream runs in that order.  Measured on the 1B rank-0 share (12 matrices,
- * four groups): Newton-Schulz 3.49 -> 3.05 ms per five-iteration call.
+ * four groups): 2.81 -> 2.58 ms per five-step call with the division by
+ * class (3.49 -> 3.05 ms when two streams first replaced one).
  *
  * Arguments
  *   ngroups      1 .. 16.
