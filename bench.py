@@ -833,7 +833,11 @@ def main():
             frac=round(tf / BF16_PEAK_TFLOPS, 4), traffic=measured_traffic("ns_call_gpt2"),
             traffic_unit="HBM bytes per 5-step call (all NS launches)",
             algorithmic_flops_per_unit=res_step["ns_flops"],
-            avg_unit_ms=round(res_step["ns_ms"], 4))
+            avg_unit_ms=round(res_step["ns_ms"], 4),
+            unit_time=("HIP-event time of the 5-step Muon call less that of the call with no "
+                       "steps; with two streams this credits to the iterations the overlap of one "
+                       "stream's pre-passes and post-steps with the other's iterations, so it is "
+                       "shorter than the traced span of the NS launches"))
     else:
         roof = None
     out.update(n_gpus=1, steps=K, warmup=W,
