@@ -662,6 +662,16 @@ def test_two_stream_groups(ns_steps, form, ns_form):
                         ns_check=lambda b, r, c, i: r == 2048 and i == 0)
 
 
+def test_gpt2_small_groups_equal_separate_calls():
+    """The headline's three GPT-2-small groups in one call -- on two streams,
+    the two 768 x 3072 Gram-form groups on the caller's with their momentum
+    passes before the fork, the 48 x [768, 768] plain group on the second --
+    equal three separate one-group calls (one stream each) bit for bit, and
+    the first matrix of each group the oracle."""
+    specs = [(48, 768, 768), (12, 3072, 768), (12, 768, 3072)]
+    grouped_vs_separate(specs, seed=2024, ns_check=lambda b, r, c, i: i == 0)
+
+
 def test_groups_of_768_to_1023_rows_on_256_tiles():
     """Groups whose short side is 768 or 897..1023 take 256 x 256 tiles when
     those pad it no further than 128 x 128 would: beside a 4096^2 group the
