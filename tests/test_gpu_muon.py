@@ -672,6 +672,17 @@ def test_gpt2_small_groups_equal_separate_calls():
     grouped_vs_separate(specs, seed=2024, ns_check=lambda b, r, c, i: i == 0)
 
 
+def test_llama1b_groups_equal_separate_calls():
+    """The 1B rank-0 share's four groups in one call -- on two streams, three
+    classes (2048-row Gram groups on 256 tiles, one with X X^T split along K;
+    the 512-row Gram group on 128 tiles; the square plain group), the Gram
+    class on the caller's stream -- equal four separate one-group calls bit
+    for bit; momentum and post-step of every matrix against the oracle (its
+    Newton-Schulz is checked against float64 in the full-size test)."""
+    specs = [(2, 11264, 2048), (2, 2048, 5632), (4, 2048, 2048), (4, 512, 2048)]
+    grouped_vs_separate(specs, seed=4096, ns_check=lambda b, r, c, i: False)
+
+
 def test_groups_of_768_to_1023_rows_on_256_tiles():
     """Groups whose short side is 768 or 897..1023 take 256 x 256 tiles when
     those pad it no further than 128 x 128 would: beside a 4096^2 group the
