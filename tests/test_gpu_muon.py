@@ -94,6 +94,16 @@ def check_step(batch, rows, cols, seed, ns_steps=5, nesterov=True, adjust=1, lr=
     return worst, ws
 
 
+@pytest.mark.parametrize("rows,cols", [(64, 1 << 21), (1 << 21, 64)])
+def test_longest_side_at_the_limit(rows, cols):
+    """The longest side the library accepts, 2^21, on a 64-row matrix in both
+    orientations (Gram form on 64 x 64 tiles, X X^T split along K over 2^21):
+    the kernels' 32-bit panel and stage offsets reach their largest values
+    here.  Momentum and post-step bit for bit, Newton-Schulz within the bar."""
+    worst, _ = check_step(1, rows, cols, seed=2 ** 21 + rows)
+    print(f"{rows} x {cols}: NS rel err {worst:.3e}", flush=True)
+
+
 def test_tiny_workload_ten_steps():
     """2 x [128, 512], 10 Muon steps carrying momentum and master across steps."""
     w = wl.TINY_MUON
