@@ -129,6 +129,7 @@ def test_tiny_workload_ten_steps():
     (1, 100, 300), (2, 300, 100), (3, 1, 17), (2, 17, 1), (1, 65, 130), (2, 130, 65),
     (1, 64, 64), (4, 257, 511), (1, 9, 1000), (2, 640, 200),
     (1, 1100, 1300), (2, 1300, 1100), (1, 1024, 1024), (1, 1030, 2100),
+    (1, 1, 1), (64, 1, 1), (64, 33, 70),
 ])
 def test_ragged_shapes(batch, rows, cols):
     check_step(batch, rows, cols, seed=rows * 7 + cols)
