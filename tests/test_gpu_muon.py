@@ -559,6 +559,19 @@ def test_groups_more_than_fit_one_launch():
     grouped_vs_separate(specs, seed=91)
 
 
+def test_sixteen_groups_mixed_on_two_streams():
+    """The most groups a call takes, 16: plain and Gram-form groups on all
+    three tile sizes, both orientations, vectors (1 x 17, 17 x 1) and a
+    1024-row group of 16 matrices whose 256-tile products, with the 768 x
+    3072 Gram groups', stay under two rounds -- so the call runs on two
+    streams, divided by class.  Every matrix equals its separate one-group
+    call bit for bit; the first matrix of the smaller groups the oracle."""
+    specs = [(16, 1024, 1024), (2, 768, 3072), (1, 3072, 768), (4, 300, 2000), (2, 2000, 300),
+             (3, 200, 520), (2, 520, 200), (1, 64, 64), (5, 96, 64), (1, 1, 17), (2, 17, 1),
+             (1, 257, 511), (1, 640, 200), (2, 130, 65), (1, 1030, 2100), (3, 512, 2048)]
+    grouped_vs_separate(specs, seed=1616, ns_check=lambda b, r, c, i: i == 0 and r * c <= 2_100_000)
+
+
 @pytest.mark.parametrize("ns_steps", [0, 1, 4])
 def test_groups_step_counts(ns_steps):
     grouped_vs_separate([(2, 130, 260), (1, 700, 300), (1, 1024, 1100)], seed=13,
