@@ -572,6 +572,68 @@ def test_sixteen_groups_mixed_on_two_streams():
     grouped_vs_separate(specs, seed=1616, ns_check=lambda b, r, c, i: i == 0 and r * c <= 2_100_000)
 
 
+def test_two_stream_calls_from_two_host_threads():
+    """Two host threads, each on a stream of its own, issue three two-stream
+    grouped calls apiece (GPT-2-small-like groups: 24 x [768, 768] on 256
+    tiles beside two Gram-form 768 x 3072 groups) on their own buffers: the
+    library's one second stream and its fork and join events serve both,
+    one call's enqueue at a time.  Every output equals the same calls made
+    one after another on one stream, bit for bit."""
+    import threading
+    specs = [(24, 768, 768), (2, 768, 3072), (2, 3072, 768)]
+    lr, mu, wd = f32(8e-4), f32(0.95), f32(0.1)
+
+    def state(seed):
+        host = [make_inputs(b, r, c, seed + 31 * k, momentum_nonzero=True)
+                for k, (b, r, c) in enumerate(specs)]
+        return [([dev_f32(p) for p in P], [dev_f32(m) for m in M], [dev_bf16(g) for g in G],
+                 [torch.empty((r, c), dtype=torch.bfloat16, device=DEV) for _ in range(b)])
+                for (b, r, c), (P, M, G) in zip(specs, host)]
+
+    def outputs(groups):
+        # per group: master and momentum bits (fp32), weight bits (bf16)
+        return [(np.concatenate([t.cpu().numpy().view(np.uint32).ravel() for t in g[0] + g[1]]),
+                 np.concatenate([u16(t).ravel() for t in g[3]]))
+                for g in groups]
+
+    seeds = (700, 900)
+    ref = []
+    for sd in seeds:
+        groups = state(sd)
+        for _ in range(3):
+            z.muon_step_groups(groups, lr, mu, True, wd, 5)
+        torch.cuda.synchronize()
+        ref.append(outputs(groups))
+
+    runs = [state(sd) for sd in seeds]
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(k):
+        try:
+            st = torch.cuda.Stream(device=DEV)
+            ws = torch.empty(z.muon_groups_workspace_bytes(specs), dtype=torch.uint8, device=DEV)
+            with torch.cuda.stream(st):
+                for _ in range(3):
+                    z.muon_step_groups(runs[k], lr, mu, True, wd, 5, workspace=ws, stream=st)
+            st.synchronize()
+        except Exception as e:  # reported by the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for k in range(2):
+        got = outputs(runs[k])
+        for gi in range(len(specs)):
+            for part in range(2):
+                assert np.array_equal(got[gi][part], ref[k][gi][part]), ("thread", k, "group", gi)
+
+
 @pytest.mark.parametrize("ns_steps", [0, 1, 4])
 def test_groups_step_counts(ns_steps):
     grouped_vs_separate([(2, 130, 260), (1, 700, 300), (1, 1024, 1100)], seed=13,
