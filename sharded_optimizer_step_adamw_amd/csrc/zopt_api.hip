@@ -545,46 +545,34 @@ double ns_work(const MuonGeom &g, int ns_steps) {
 }
 
 void split_sides(const NsGroupRef *refs, int nb, int ns_steps, int *side) {
-    double work[kMaxCallGroups];
-    int cls[kMaxCallGroups];
-    int ncls = 0, key[kMaxCallGroups];
-    double cwork[kMaxCallGroups];
-    for (int k = 0; k < nb; ++k) {
-        const MuonGeom &g = *refs[k].geom;
-        work[k] = ns_work(g, ns_steps);
-        const int kk = g.gram * 1024 + g.tile;
-        int c = 0;
-        while (c < ncls && key[c] != kk) ++c;
-        if (c == ncls) {
-            key[ncls] = kk;
-            cwork[ncls++] = 0.0;
-        }
-        cls[k] = c;
-        cwork[c] += work[k];
-    }
-    int order[kMaxCallGroups], cside[kMaxCallGroups];
-    for (int c = 0; c < ncls; ++c) order[c] = c;
-    std::stable_sort(order, order + ncls, [&](int x, int y) { return cwork[x] > cwork[y]; });
-    double w[2] = {0.0, 0.0};
-    for (int t = 0; t < ncls; ++t) {
-        const int c = order[t], d = w[0] <= w[1] ? 0 : 1;
-        cside[c] = d;
-        w[d] += cwork[c];
-    }
-    for (int k = 0; k < nb; ++k) side[k] = cside[cls[k]];
     bool mixed = false;
     for (int k = 1; k < nb; ++k) mixed = mixed || refs[k].geom->gram != refs[0].geom->gram;
-    if (!mixed) {
-        int ord[kMaxCallGroups];
-        for (int k = 0; k < nb; ++k) ord[k] = k;
-        std::stable_sort(ord, ord + nb, [&](int x, int y) { return work[x] > work[y]; });
-        w[0] = w[1] = 0.0;
-        for (int t = 0; t < nb; ++t) {
-            const int k = ord[t], d = w[0] <= w[1] ? 0 : 1;
-            side[k] = d;
-            w[d] += work[k];
+    // the items placed: classes (form and tile) in a mixed call, else groups
+    int item[kMaxCallGroups], key[kMaxCallGroups], nitems = 0;
+    double work[kMaxCallGroups];
+    for (int k = 0; k < nb; ++k) {
+        const MuonGeom &g = *refs[k].geom;
+        const int kk = mixed ? g.gram * 1024 + g.tile : k;
+        int c = 0;
+        while (c < nitems && key[c] != kk) ++c;
+        if (c == nitems) {
+            key[nitems] = kk;
+            work[nitems++] = 0.0;
         }
+        item[k] = c;
+        work[c] += ns_work(g, ns_steps);
     }
+    // largest first, each to the side with less work so far
+    int order[kMaxCallGroups], iside[kMaxCallGroups];
+    for (int c = 0; c < nitems; ++c) order[c] = c;
+    std::stable_sort(order, order + nitems, [&](int x, int y) { return work[x] > work[y]; });
+    double w[2] = {0.0, 0.0};
+    for (int t = 0; t < nitems; ++t) {
+        const int c = order[t], d = w[0] <= w[1] ? 0 : 1;
+        iside[c] = d;
+        w[d] += work[c];
+    }
+    for (int k = 0; k < nb; ++k) side[k] = iside[item[k]];
 }
 
 // Enqueues a planned call on stream s.  With dev (device scalars [lr,
