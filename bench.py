@@ -64,19 +64,19 @@ MEASURED_TRAFFIC = {
                          sha256="b194c209b68ecdfc860e298b700b2dfd768eab25cdd8f9ccad2017d401ce9bf3",
                          also=[("sharded_optimizer_step_adamw_amd/csrc/zopt_api.hip",
                                 "f9f3bae7e107017205a12a39b56884891e53c95f876d7cbd0364e70c42cf6db7")],
-                         bytes_per_launch=4.354e9, profile="profiles/ns_gemm_gpt2_small_step.md"),
-    # 8B rank-0 share: 86.46 GB read, 14.68 GB written (23 launches)
+                         bytes_per_launch=4.355e9, profile="profiles/ns_gemm_gpt2_small_step.md"),
+    # 8B rank-0 share: 88.22 GB read, 14.68 GB written (23 launches)
     "ns_call_llama8b": dict(source="sharded_optimizer_step_adamw_amd/csrc/ns_gemm.hip",
                             sha256="b194c209b68ecdfc860e298b700b2dfd768eab25cdd8f9ccad2017d401ce9bf3",
                             also=[("sharded_optimizer_step_adamw_amd/csrc/zopt_api.hip",
                                    "f9f3bae7e107017205a12a39b56884891e53c95f876d7cbd0364e70c42cf6db7")],
-                            bytes_per_launch=101.1e9, profile="profiles/ns_gemm_llama8b_rank0.md"),
-    # 1B rank-0 share: 4.653 GB read, 1.539 GB written (49 launches on two streams)
+                            bytes_per_launch=102.9e9, profile="profiles/ns_gemm_llama8b_rank0.md"),
+    # 1B rank-0 share: 4.655 GB read, 1.539 GB written (49 launches on two streams)
     "ns_call_llama1b": dict(source="sharded_optimizer_step_adamw_amd/csrc/ns_gemm.hip",
                             sha256="b194c209b68ecdfc860e298b700b2dfd768eab25cdd8f9ccad2017d401ce9bf3",
                             also=[("sharded_optimizer_step_adamw_amd/csrc/zopt_api.hip",
                                    "f9f3bae7e107017205a12a39b56884891e53c95f876d7cbd0364e70c42cf6db7")],
-                            bytes_per_launch=6.192e9, profile="profiles/ns_gemm_llama1b_rank0.md"),
+                            bytes_per_launch=6.194e9, profile="profiles/ns_gemm_llama1b_rank0.md"),
     "grad_sq_norm": dict(source="sharded_optimizer_step_adamw_amd/csrc/adamw_shard.hip",
                          sha256="673b6ee27b692f43da0cb776f129120c95304617a7117f995f9273186f2e9bca",
                          bytes_per_launch=0.5004e9,
